@@ -1,0 +1,283 @@
+"""Benchmark of the heterogeneous-batch LoRA linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+
+A step is one pass of the whole hot path over one batch: the grouping plan
+of the batch's adapter ids, then the LoRA linear of every module of the
+workload (shrink, base GEMM with the fused expand, single bf16 rounding).
+The default workload is the Llama-2-7B q_proj decode batch: 4096 -> 4096,
+64 tokens, 200 resident rank-16 adapters, ids uniform over the 200.
+
+Timing: hip events on the stream the library launches on, K steps between
+two device synchronisations.  Inputs (X, W, ids, the adapter pool) are
+resident in HBM; R independent copies are rotated so the 256 MB
+Infinity Cache cannot hold the working set.
+
+Printed: ONE JSON line with tokens/s, the LoRA overhead against the
+library's own base-only GEMM, the roofline of the dominant launch (the
+apply with a prebuilt plan) and the CPU oracle's throughput on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as wk  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "LoRA-linear tokens/sec at 1 GPU; % overhead vs base-only GEMM; % roofline"
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work (bytes and flops that the definition must touch)
+# ---------------------------------------------------------------------------
+def base_bytes(T: int, d_in: int, d_out: int) -> int:
+    """W once, X once, out once (bf16)."""
+    return 2 * (d_in * d_out + T * d_in + T * d_out)
+
+
+def lora_bytes(ids: np.ndarray, ranks: np.ndarray, d_in: int, d_out: int) -> int:
+    """A and B of every distinct adapter in the batch, at its true rank."""
+    return sum(2 * int(ranks[i]) * (d_in + d_out) for i in wk.distinct_adapters(ids))
+
+
+def flops(ids: np.ndarray, ranks: np.ndarray, d_in: int, d_out: int) -> int:
+    T = ids.shape[0]
+    lora = sum(2 * int(ranks[i]) * (d_in + d_out) for i in ids.tolist() if i >= 0)
+    return 2 * T * d_in * d_out + lora
+
+
+def extra_flop_fraction(rank: int, d_in: int, d_out: int) -> float:
+    """LoRA flops per token over base flops per token: r (d_in + d_out) / (d_in d_out)."""
+    return rank * (d_in + d_out) / (d_in * d_out)
+
+
+def step_work(wl: wk.Workload, ids: np.ndarray, ranks: np.ndarray):
+    """(base bytes, lora bytes, flops, t_roof seconds) of one step."""
+    bb = lb = fl = 0
+    t_roof = 0.0
+    for m in wl.modules:
+        b1 = base_bytes(ids.shape[0], m.d_in, m.d_out)
+        l1 = lora_bytes(ids, ranks, m.d_in, m.d_out)
+        f1 = flops(ids, ranks, m.d_in, m.d_out)
+        bb += b1
+        lb += l1
+        fl += f1
+        t_roof += max((b1 + l1) / (HBM_PEAK_GBS * 1e9), f1 / (MFMA_BF16_PEAK_TFS * 1e12))
+    return bb, lb, fl, t_roof
+
+
+# ---------------------------------------------------------------------------
+# GPU set-up
+# ---------------------------------------------------------------------------
+class Replica:
+    """One independent copy of the workload's resident state."""
+
+    def __init__(self, wl: wk.Workload, seed: int, torch, hrg):
+        self.ids_np = wk.adapter_ids(wl, seed)
+        self.ranks = wk.adapter_ranks(wl, seed)
+        self.T = wl.T
+        mods = wl.modules
+        self.pool = hrg.LoraPool(wl.n_adapters, wl.n_adapters, wl.max_rank,
+                                 [m.d_in for m in mods], [m.d_out for m in mods], wl.T)
+        for i in range(wl.n_adapters):
+            r = int(self.ranks[i])
+            A, B = [], []
+            for j in range(len(mods)):
+                a, b = wk.adapter_weights(wl, i, j, r, seed, "cuda")
+                A.append(a)
+                B.append(b)
+            self.pool.load_adapter(i, r, wk.adapter_alpha(wl, r), A, B)
+            del A, B
+        self.ids = torch.as_tensor(self.ids_np, device="cuda")
+        self.X = {}
+        for m in mods:
+            if m.input_group not in self.X:
+                self.X[m.input_group] = wk.activation(wl, m.input_group, m.d_in, seed, "cuda")
+        self.W = [wk.base_weight(wl, j, seed, "cuda") for j in range(len(mods))]
+        self.out = [torch.empty((wl.T, m.d_out), dtype=torch.bfloat16, device="cuda")
+                    for m in mods]
+        self.xin = [self.X[m.input_group] for m in mods]
+        self.plan = self.pool.plan_create()
+        self.pool.plan(self.ids, self.T, self.plan)
+
+
+def lora_step(rep: Replica, hrg):
+    h = rep.pool.handle
+    hrg.lora_plan(h, rep.ids, rep.T, rep.plan)
+    for j in range(len(rep.W)):
+        hrg.lora_apply(h, j, rep.xin[j], rep.ids, rep.T, rep.W[j], rep.out[j], rep.plan)
+
+
+def apply_only(rep: Replica, hrg):
+    h = rep.pool.handle
+    for j in range(len(rep.W)):
+        hrg.lora_apply(h, j, rep.xin[j], rep.ids, rep.T, rep.W[j], rep.out[j], rep.plan)
+
+
+def base_step(rep: Replica, hrg):
+    h = rep.pool.handle
+    for j in range(len(rep.W)):
+        hrg.lora_base_apply(h, j, rep.xin[j], rep.T, rep.W[j], rep.out[j])
+
+
+def time_steps(fn, reps, steps: int, warmup: int, torch, hrg) -> float:
+    """Average seconds per step over `steps` steps, rotating replicas."""
+    for i in range(warmup):
+        fn(reps[i % len(reps)], hrg)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(reps[i % len(reps)], hrg)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / steps
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline
+# ---------------------------------------------------------------------------
+def cpu_baseline(wl: wk.Workload, rep: Replica, seconds: float, torch):
+    import oracle
+    try:
+        import threadpoolctl
+        threads = max(int(i.get("num_threads", 1)) for i in threadpoolctl.threadpool_info()) \
+            if threadpoolctl.threadpool_info() else 1
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    mods = wl.modules
+    reg = oracle.Registry(wl.n_adapters, wl.n_adapters, wl.max_rank, [m.d_in for m in mods],
+                          [m.d_out for m in mods], wl.T)
+    # the oracle sees the same bf16 bits as the GPU (regenerated on the device, copied back)
+    used = wk.distinct_adapters(rep.ids_np)
+    for i in used:
+        r = int(rep.ranks[i])
+        A, B = [], []
+        for j in range(len(mods)):
+            a, b = wk.adapter_weights(wl, i, j, r, wl.default_seed, "cuda")
+            A.append(a.cpu())
+            B.append(b.cpu())
+        reg.load(i, r, wk.adapter_alpha(wl, r), A, B)
+    X = [x.cpu() for x in rep.xin]
+    W = [w.cpu() for w in rep.W]
+    n_lin = 0
+    t0 = time.perf_counter()
+    while True:
+        j = n_lin % len(mods)
+        oracle.lora_linear(reg, j, X[j], rep.ids_np, W[j])
+        n_lin += 1
+        el = time.perf_counter() - t0
+        if el >= seconds and n_lin % len(mods) == 0:
+            break
+        if el >= 4 * seconds:
+            break
+    tokens = wl.T * n_lin / len(mods)
+    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_lin} linears ({n_lin / len(mods):.2f} steps of {wl.T} tokens) of "
+                      f"workload '{wl.name}' in {el:.1f} s, float64 numpy"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, choices=sorted(wk.WORKLOADS))
+    ap.add_argument("--rotate", type=int, default=8, help="independent copies of the state")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
+              f"got --gpus {args.gpus}", file=sys.stderr)
+        return 2
+
+    import torch
+    import heterogeneous_rank_gemm_amd as hrg
+
+    wl = wk.WORKLOADS[args.workload]
+    R = 1 if wl.key == 5 else max(1, args.rotate)
+    print(f"[bench] workload {wl.key} '{wl.name}', {R} replica(s)", file=sys.stderr, flush=True)
+    reps = [Replica(wl, wl.default_seed + 1000 * r if r else wl.default_seed, torch, hrg)
+            for r in range(R)]
+    torch.cuda.synchronize()
+    print("[bench] state resident; timing", file=sys.stderr, flush=True)
+
+    t_step = time_steps(lora_step, reps, args.steps, args.warmup, torch, hrg)
+    t_apply = time_steps(apply_only, reps, args.steps, args.warmup, torch, hrg)
+    t_base = time_steps(base_step, reps, args.steps, args.warmup, torch, hrg)
+    for rp in reps:
+        st = rp.pool.status()
+        if st != "OK":
+            raise RuntimeError(f"device status {st}")
+
+    works = [step_work(wl, rp.ids_np, rp.ranks) for rp in reps]
+    bb = float(np.mean([w[0] for w in works]))
+    lb = float(np.mean([w[1] for w in works]))
+    fl = float(np.mean([w[2] for w in works]))
+    t_roof = float(np.mean([w[3] for w in works]))
+    n_launch = len(wl.modules)
+    hbm_bound = (bb + lb) / (HBM_PEAK_GBS * 1e9) >= fl / (MFMA_BF16_PEAK_TFS * 1e12)
+    if hbm_bound:
+        achieved = (bb + lb) / n_launch / (t_apply / n_launch) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = fl / n_launch / (t_apply / n_launch) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
+                "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, reps[0], args.cpu_seconds, torch)
+
+    line = {
+        "metric": METRIC,
+        "value": round(wl.T / t_step, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T,
+                   "modules": [[m.d_in, m.d_out] for m in wl.modules[:7]],
+                   "n_linears": len(wl.modules), "adapters": wl.n_adapters,
+                   "ranks": list(wl.rank_choices), "max_rank": wl.max_rank,
+                   "replicas_rotated": R},
+        "lora_overhead_pct": round(100.0 * (t_step - t_base) / t_base, 2),
+        "base_only_ms_per_step": round(t_base * 1e3, 5),
+        "apply_ms_per_step": round(t_apply * 1e3, 5),
+        "step_roofline_frac": round(t_roof / t_step, 4),
+        "algorithmic": {"base_bytes": bb, "lora_bytes": lb, "flops": fl,
+                        "t_roof_us": round(t_roof * 1e6, 3)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    for rp in reps:
+        rp.pool.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,177 @@
+"""ctypes binding of ``include/lora.h``: the same entry points, argument
+marshalling only.  Every step of the LoRA linear runs in the HIP library;
+nothing here computes.  Tensors are passed as raw device pointers
+(``tensor.data_ptr()``), streams as ``torch.cuda.Stream.cuda_stream``.
+
+Importing this module loads ``libhrglora.so`` and raises ``ImportError``
+if it is missing -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libhrglora.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python heterogeneous_rank_gemm_amd/build.py`")
+_lib = C.CDLL(LIB_PATH)
+
+STATUS_NAMES = {
+    0: "OK", 1: "INVALID_ARG", 2: "OOM", 3: "POOL_FULL", 4: "RANK", 5: "EXISTS",
+    6: "NOT_LOADED", 7: "ID_RANGE", 8: "HIP",
+}
+EXPORTED = (
+    "lora_status_string", "lora_pool_create", "lora_pool_destroy", "lora_load_adapter",
+    "lora_unload_adapter", "lora_pool_query", "lora_plan_create", "lora_plan_destroy",
+    "lora_plan", "lora_apply", "lora_base_apply", "lora_status", "lora_debug_read_plan",
+)
+
+_vp = C.c_void_p
+_i32 = C.c_int32
+_P_i32 = C.POINTER(C.c_int32)
+
+_lib.lora_status_string.restype = C.c_char_p
+_lib.lora_status_string.argtypes = [C.c_int]
+_sigs = {
+    "lora_pool_create": [C.POINTER(_vp), _i32, _i32, _i32, _i32, _P_i32, _P_i32, _i32, _vp],
+    "lora_pool_destroy": [_vp],
+    "lora_load_adapter": [_vp, _i32, _i32, C.c_float, C.POINTER(_vp), C.POINTER(_vp), _vp],
+    "lora_unload_adapter": [_vp, _i32, _vp],
+    "lora_pool_query": [_vp, _i32, _P_i32, _P_i32, C.POINTER(C.c_float)],
+    "lora_plan_create": [_vp, C.POINTER(_vp)],
+    "lora_plan_destroy": [_vp, _vp],
+    "lora_plan": [_vp, _vp, _i32, _vp, _vp],
+    "lora_apply": [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp],
+    "lora_base_apply": [_vp, _i32, _vp, _i32, _vp, _vp, _vp],
+    "lora_status": [_vp, _vp],
+    "lora_debug_read_plan": [_vp, _vp, _P_i32, _P_i32, _P_i32, _P_i32, _P_i32, _P_i32, _vp],
+}
+for _name, _args in _sigs.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = C.c_int
+
+
+class LoraError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = int(code)
+        self.status = STATUS_NAMES.get(self.code, f"UNKNOWN({code})")
+        super().__init__(f"{where}: {_lib.lora_status_string(self.code).decode()}")
+
+
+def _check(code: int, where: str) -> int:
+    if code != 0:
+        raise LoraError(code, where)
+    return code
+
+
+def _ptr(t) -> Optional[int]:
+    """Device/host address of a tensor (or an int address, or None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ---------------------------------------------------------------------------
+# entry points, same names as the C ABI
+# ---------------------------------------------------------------------------
+def lora_status_string(code: int) -> str:
+    return _lib.lora_status_string(int(code)).decode()
+
+
+def lora_pool_create(max_adapters: int, max_ids: int, max_rank: int, d_in: Sequence[int],
+                     d_out: Sequence[int], max_tokens: int, stream=None) -> int:
+    n = len(d_in)
+    if len(d_out) != n:
+        raise LoraError(1, "lora_pool_create")
+    din = (C.c_int32 * max(n, 1))(*d_in)
+    dout = (C.c_int32 * max(n, 1))(*d_out)
+    h = _vp()
+    _check(_lib.lora_pool_create(C.byref(h), max_adapters, max_ids, max_rank, n, din, dout,
+                                 max_tokens, _stream(stream)), "lora_pool_create")
+    return h.value
+
+
+def lora_pool_destroy(pool: int) -> None:
+    _check(_lib.lora_pool_destroy(pool), "lora_pool_destroy")
+
+
+def lora_load_adapter(pool: int, adapter_id: int, rank: int, alpha: float, A: Sequence,
+                      B: Sequence, stream=None) -> None:
+    n = len(A)
+    pa = (_vp * max(n, 1))(*[_ptr(a) for a in A])
+    pb = (_vp * max(n, 1))(*[_ptr(b) for b in B])
+    _check(_lib.lora_load_adapter(pool, adapter_id, rank, float(alpha), pa, pb, _stream(stream)),
+           "lora_load_adapter")
+
+
+def lora_unload_adapter(pool: int, adapter_id: int, stream=None) -> None:
+    _check(_lib.lora_unload_adapter(pool, adapter_id, _stream(stream)), "lora_unload_adapter")
+
+
+def lora_pool_query(pool: int, adapter_id: int):
+    slot, rank, scale = C.c_int32(), C.c_int32(), C.c_float()
+    _check(_lib.lora_pool_query(pool, adapter_id, C.byref(slot), C.byref(rank), C.byref(scale)),
+           "lora_pool_query")
+    return slot.value, rank.value, scale.value
+
+
+def lora_plan_create(pool: int) -> int:
+    h = _vp()
+    _check(_lib.lora_plan_create(pool, C.byref(h)), "lora_plan_create")
+    return h.value
+
+
+def lora_plan_destroy(pool: int, plan: int) -> None:
+    _check(_lib.lora_plan_destroy(pool, plan), "lora_plan_destroy")
+
+
+def lora_plan(pool: int, ids, T: int, plan: int, stream=None) -> None:
+    _check(_lib.lora_plan(pool, _ptr(ids), T, plan, _stream(stream)), "lora_plan")
+
+
+def lora_apply(pool: int, module: int, X, ids, T: int, W, out, plan: Optional[int] = None,
+               stream=None) -> None:
+    _check(_lib.lora_apply(pool, module, _ptr(X), _ptr(ids), T, _ptr(W), _ptr(out), plan,
+                           _stream(stream)), "lora_apply")
+
+
+def lora_base_apply(pool: int, module: int, X, T: int, W, out, stream=None) -> None:
+    _check(_lib.lora_base_apply(pool, module, _ptr(X), T, _ptr(W), _ptr(out), _stream(stream)),
+           "lora_base_apply")
+
+
+def lora_status(pool: int, stream=None) -> str:
+    """Synchronises, returns and clears the sticky device status (a name)."""
+    code = _lib.lora_status(pool, _stream(stream))
+    if code == 8:
+        raise LoraError(code, "lora_status")
+    return STATUS_NAMES.get(code, f"UNKNOWN({code})")
+
+
+def lora_debug_read_plan(pool: int, plan: Optional[int], max_tokens: int, stream=None):
+    """Returns (perm, inv, seg_id, seg_off) as Python lists."""
+    perm = (C.c_int32 * max(max_tokens, 1))()
+    inv = (C.c_int32 * max(max_tokens, 1))()
+    seg_id = (C.c_int32 * (max_tokens + 1))()
+    seg_off = (C.c_int32 * (max_tokens + 2))()
+    T, S = C.c_int32(), C.c_int32()
+    _check(_lib.lora_debug_read_plan(pool, plan, perm, inv, seg_id, seg_off, C.byref(T),
+                                     C.byref(S), _stream(stream)), "lora_debug_read_plan")
+    t, s = T.value, S.value
+    return list(perm[:t]), list(inv[:t]), list(seg_id[:s]), list(seg_off[:s + 1])

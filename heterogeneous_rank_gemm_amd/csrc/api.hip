@@ -1,0 +1,455 @@
+// Host side of the C ABI (include/lora.h): the unified adapter pool, its
+// routing tables, the load / unload path, plans, and the apply entry points.
+//
+// The pool follows the vLLM chapter "Multi-LoRA hot-plug: one model serving
+// many tenants" (section "how vLLM implements multi-LoRA": all adapters in
+// one device memory pool) and the routing table of the icman report
+// (section 2.1: adapter name -> location, loaded-in-VRAM flag), reduced to
+// an integer id -> slot table mirrored on host and device.
+#include <algorithm>
+#include <mutex>
+#include <new>
+#include <set>
+#include <vector>
+
+#include "internal.h"
+#include "lora.h"
+
+static_assert(hrg::kStatusNotLoaded == LORA_ERR_NOT_LOADED, "status code mismatch");
+static_assert(hrg::kStatusIdRange == LORA_ERR_ID_RANGE, "status code mismatch");
+
+struct lora_plan_s {
+  hrg::PlanTables tab;
+  int32_t T = -1;
+  const int32_t* ids = nullptr;
+  void* block = nullptr;  // one allocation backing every table
+};
+
+struct lora_pool_s {
+  int device = 0;
+  int32_t max_adapters = 0, max_ids = 0, max_rank = 0, rpad = 0, n_modules = 0, max_tokens = 0;
+  std::vector<int32_t> d_in, d_out;
+  std::vector<size_t> a_off, b_off;  // element offsets of each module's pages inside a slot
+  size_t slot_elems = 0;
+  uint16_t* pages = nullptr;         // [max_adapters][slot_elems]
+  int32_t* id2slot = nullptr;        // [max_ids]
+  int32_t* slot_rank = nullptr;      // [max_adapters]
+  float* slot_scale = nullptr;       // [max_adapters]
+  int32_t* status = nullptr;         // sticky device status
+  uint16_t* staging = nullptr;       // one module's A or B as received
+  float* upart = nullptr;            // [kMaxSplits][max_tokens][rpad]
+  size_t split_stride = 0;
+  std::vector<int32_t> h_id2slot, h_slot_rank;
+  std::vector<float> h_slot_scale;
+  std::set<int32_t> free_slots;      // lowest free slot first
+  lora_plan_s* internal = nullptr;
+  std::set<lora_plan_s*> plans;
+};
+
+namespace {
+
+using hrg::ceil_div;
+using hrg::round_up;
+
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    if (prev != dev) (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+  }
+};
+
+template <typename T>
+hipError_t dmalloc(T** p, size_t n) {
+  return hipMalloc(reinterpret_cast<void**>(p), std::max<size_t>(n, 1) * sizeof(T));
+}
+
+int max_tiles_for(const lora_pool_s* P) {
+  return std::min(P->max_tokens, P->max_adapters) + ceil_div(P->max_tokens, hrg::kShrinkRows) + 1;
+}
+
+lora_status_t plan_alloc(lora_pool_s* P, lora_plan_s** out) {
+  const size_t Tc = (size_t)P->max_tokens;
+  const int mt = max_tiles_for(P);
+  // perm, inv, row_seg (Tc each); seg_id, seg_slot, seg_rank, seg_scale (Tc+1);
+  // seg_off (Tc+2); tile_seg, tile_row0 (mt); counts (4)
+  const size_t n32 = 3 * Tc + 4 * (Tc + 1) + (Tc + 2) + 2 * (size_t)mt + 4;
+  lora_plan_s* pl = new (std::nothrow) lora_plan_s();
+  if (!pl) return LORA_ERR_OOM;
+  int32_t* blk = nullptr;
+  if (dmalloc(&blk, n32) != hipSuccess) {
+    delete pl;
+    (void)hipGetLastError();
+    return LORA_ERR_OOM;
+  }
+  pl->block = blk;
+  int32_t* c = blk;
+  auto take = [&](size_t n) { int32_t* r = c; c += n; return r; };
+  pl->tab.perm = take(Tc);
+  pl->tab.inv = take(Tc);
+  pl->tab.row_seg = take(Tc);
+  pl->tab.seg_id = take(Tc + 1);
+  pl->tab.seg_slot = take(Tc + 1);
+  pl->tab.seg_rank = take(Tc + 1);
+  pl->tab.seg_scale = reinterpret_cast<float*>(take(Tc + 1));
+  pl->tab.seg_off = take(Tc + 2);
+  pl->tab.tile_seg = take(mt);
+  pl->tab.tile_row0 = take(mt);
+  pl->tab.counts = take(4);
+  pl->tab.max_tiles = mt;
+  *out = pl;
+  return LORA_OK;
+}
+
+void plan_free(lora_plan_s* pl) {
+  if (!pl) return;
+  if (pl->block) (void)hipFree(pl->block);
+  delete pl;
+}
+
+lora_status_t run_plan(lora_pool_s* P, const int32_t* ids, int32_t T, lora_plan_s* pl, hipStream_t s) {
+  hrg::PlanArgs a{};
+  a.ids = ids;
+  a.T = T;
+  a.max_ids = P->max_ids;
+  a.id2slot = P->id2slot;
+  a.slot_rank = P->slot_rank;
+  a.slot_scale = P->slot_scale;
+  a.status = P->status;
+  a.tab = pl->tab;
+  if (hrg::launch_plan(a, s) != hipSuccess) return LORA_ERR_HIP;
+  pl->T = T;
+  pl->ids = ids;
+  return LORA_OK;
+}
+
+bool module_ok(const lora_pool_s* P, int32_t m) { return P && m >= 0 && m < P->n_modules; }
+
+}  // namespace
+
+extern "C" {
+
+const char* lora_status_string(lora_status_t s) {
+  switch (s) {
+    case LORA_OK: return "LORA_OK";
+    case LORA_ERR_INVALID_ARG: return "LORA_ERR_INVALID_ARG";
+    case LORA_ERR_OOM: return "LORA_ERR_OOM";
+    case LORA_ERR_POOL_FULL: return "LORA_ERR_POOL_FULL";
+    case LORA_ERR_RANK: return "LORA_ERR_RANK";
+    case LORA_ERR_EXISTS: return "LORA_ERR_EXISTS";
+    case LORA_ERR_NOT_LOADED: return "LORA_ERR_NOT_LOADED";
+    case LORA_ERR_ID_RANGE: return "LORA_ERR_ID_RANGE";
+    case LORA_ERR_HIP: return "LORA_ERR_HIP";
+  }
+  return "LORA_ERR_UNKNOWN";
+}
+
+lora_status_t lora_pool_create(lora_pool_t* pool, int32_t max_adapters, int32_t max_ids,
+                               int32_t max_rank, int32_t n_modules, const int32_t* d_in,
+                               const int32_t* d_out, int32_t max_tokens, hipStream_t stream) {
+  if (!pool || !d_in || !d_out) return LORA_ERR_INVALID_ARG;
+  if (max_adapters < 1 || max_ids < 1 || max_ids > hrg::kMaxIds) return LORA_ERR_INVALID_ARG;
+  if (max_rank < 1 || max_rank > hrg::kMaxRank) return LORA_ERR_INVALID_ARG;
+  if (n_modules < 1 || max_tokens < 1 || max_tokens > 65536) return LORA_ERR_INVALID_ARG;
+  for (int32_t m = 0; m < n_modules; ++m) {
+    if (d_in[m] < 8 || d_in[m] > 65536 || d_in[m] % 8) return LORA_ERR_INVALID_ARG;
+    if (d_out[m] < 8 || d_out[m] > 65536 || d_out[m] % 8) return LORA_ERR_INVALID_ARG;
+  }
+  lora_pool_s* P = new (std::nothrow) lora_pool_s();
+  if (!P) return LORA_ERR_OOM;
+  if (hipGetDevice(&P->device) != hipSuccess) {
+    delete P;
+    (void)hipGetLastError();
+    return LORA_ERR_HIP;
+  }
+  P->max_adapters = max_adapters;
+  P->max_ids = max_ids;
+  P->max_rank = max_rank;
+  P->rpad = round_up(max_rank, 16);
+  P->n_modules = n_modules;
+  P->max_tokens = max_tokens;
+  P->d_in.assign(d_in, d_in + n_modules);
+  P->d_out.assign(d_out, d_out + n_modules);
+  size_t off = 0, max_dim = 0;
+  for (int32_t m = 0; m < n_modules; ++m) {
+    P->a_off.push_back(off);
+    off += (size_t)max_rank * d_in[m];
+    P->b_off.push_back(off);
+    off += (size_t)max_rank * d_out[m];
+    max_dim = std::max<size_t>(max_dim, std::max(d_in[m], d_out[m]));
+  }
+  // keep every slot 256-byte aligned
+  P->slot_elems = (off + 127) / 128 * 128;
+  P->split_stride = (size_t)max_tokens * P->rpad;
+
+  bool ok = dmalloc(&P->pages, P->slot_elems * (size_t)max_adapters) == hipSuccess &&
+            dmalloc(&P->id2slot, max_ids) == hipSuccess &&
+            dmalloc(&P->slot_rank, max_adapters) == hipSuccess &&
+            dmalloc(&P->slot_scale, max_adapters) == hipSuccess &&
+            dmalloc(&P->status, 4) == hipSuccess &&
+            dmalloc(&P->staging, max_dim * max_rank) == hipSuccess &&
+            dmalloc(&P->upart, (size_t)hrg::kMaxSplits * P->split_stride) == hipSuccess;
+  if (ok) ok = plan_alloc(P, &P->internal) == LORA_OK;
+  if (!ok) {
+    (void)hipGetLastError();
+    lora_pool_destroy(P);
+    return LORA_ERR_OOM;
+  }
+  P->h_id2slot.assign(max_ids, -1);
+  P->h_slot_rank.assign(max_adapters, 0);
+  P->h_slot_scale.assign(max_adapters, 0.f);
+  for (int32_t i = 0; i < max_adapters; ++i) P->free_slots.insert(i);
+  if (hrg::launch_clear_i32(P->id2slot, max_ids, -1, stream) != hipSuccess ||
+      hrg::launch_clear_i32(P->slot_rank, max_adapters, 0, stream) != hipSuccess ||
+      hrg::launch_clear_i32(reinterpret_cast<int32_t*>(P->slot_scale), max_adapters, 0, stream) != hipSuccess ||
+      hrg::launch_clear_i32(P->status, 4, 0, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess) {
+    (void)hipGetLastError();
+    lora_pool_destroy(P);
+    return LORA_ERR_HIP;
+  }
+  *pool = P;
+  return LORA_OK;
+}
+
+lora_status_t lora_pool_destroy(lora_pool_t P) {
+  if (!P) return LORA_ERR_INVALID_ARG;
+  DeviceGuard g(P->device);
+  (void)hipDeviceSynchronize();
+  for (lora_plan_s* pl : P->plans) plan_free(pl);
+  plan_free(P->internal);
+  (void)hipFree(P->pages);
+  (void)hipFree(P->id2slot);
+  (void)hipFree(P->slot_rank);
+  (void)hipFree(P->slot_scale);
+  (void)hipFree(P->status);
+  (void)hipFree(P->staging);
+  (void)hipFree(P->upart);
+  delete P;
+  return LORA_OK;
+}
+
+lora_status_t lora_load_adapter(lora_pool_t P, int32_t id, int32_t rank, float alpha,
+                                const lora_bf16_t* const* A, const lora_bf16_t* const* B,
+                                hipStream_t stream) {
+  if (!P || !A || !B) return LORA_ERR_INVALID_ARG;
+  for (int32_t m = 0; m < P->n_modules; ++m)
+    if (!A[m] || !B[m]) return LORA_ERR_INVALID_ARG;
+  if (id < 0 || id >= P->max_ids) return LORA_ERR_ID_RANGE;
+  if (rank < 1 || rank > P->max_rank) return LORA_ERR_RANK;
+  if (P->h_id2slot[id] >= 0) return LORA_ERR_EXISTS;
+  if (P->free_slots.empty()) return LORA_ERR_POOL_FULL;
+  DeviceGuard g(P->device);
+  const int32_t slot = *P->free_slots.begin();
+  uint16_t* base = P->pages + (size_t)slot * P->slot_elems;
+  for (int32_t m = 0; m < P->n_modules; ++m) {
+    const size_t na = (size_t)P->d_in[m] * rank, nb = (size_t)rank * P->d_out[m];
+    hrg::PackArgs pa{};
+    if (hipMemcpyAsync(P->staging, A[m], na * 2, hipMemcpyDefault, stream) != hipSuccess)
+      return (void)hipGetLastError(), LORA_ERR_HIP;
+    pa = {P->staging, base + P->a_off[m], rank, P->max_rank, P->d_in[m], 1};
+    if (hrg::launch_pack(pa, stream) != hipSuccess) return LORA_ERR_HIP;
+    if (hipMemcpyAsync(P->staging, B[m], nb * 2, hipMemcpyDefault, stream) != hipSuccess)
+      return (void)hipGetLastError(), LORA_ERR_HIP;
+    pa = {P->staging, base + P->b_off[m], rank, P->max_rank, P->d_out[m], 0};
+    if (hrg::launch_pack(pa, stream) != hipSuccess) return LORA_ERR_HIP;
+  }
+  const float scale = alpha / (float)rank;
+  if (hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, id, slot, rank, scale, stream) !=
+          hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return LORA_ERR_HIP;
+  }
+  P->free_slots.erase(slot);
+  P->h_id2slot[id] = slot;
+  P->h_slot_rank[slot] = rank;
+  P->h_slot_scale[slot] = scale;
+  return LORA_OK;
+}
+
+lora_status_t lora_unload_adapter(lora_pool_t P, int32_t id, hipStream_t stream) {
+  if (!P) return LORA_ERR_INVALID_ARG;
+  if (id < 0 || id >= P->max_ids) return LORA_ERR_ID_RANGE;
+  const int32_t slot = P->h_id2slot[id];
+  if (slot < 0) return LORA_ERR_NOT_LOADED;
+  DeviceGuard g(P->device);
+  if (hipStreamSynchronize(stream) != hipSuccess ||
+      hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, id, -1, 0, 0.f, stream) !=
+          hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return LORA_ERR_HIP;
+  }
+  P->h_id2slot[id] = -1;
+  P->h_slot_rank[slot] = 0;
+  P->h_slot_scale[slot] = 0.f;
+  P->free_slots.insert(slot);
+  return LORA_OK;
+}
+
+lora_status_t lora_pool_query(lora_pool_t P, int32_t id, int32_t* slot, int32_t* rank, float* scale) {
+  if (!P) return LORA_ERR_INVALID_ARG;
+  if (id < 0 || id >= P->max_ids) return LORA_ERR_ID_RANGE;
+  const int32_t sl = P->h_id2slot[id];
+  if (sl < 0) return LORA_ERR_NOT_LOADED;
+  if (slot) *slot = sl;
+  if (rank) *rank = P->h_slot_rank[sl];
+  if (scale) *scale = P->h_slot_scale[sl];
+  return LORA_OK;
+}
+
+lora_status_t lora_plan_create(lora_pool_t P, lora_plan_t* plan) {
+  if (!P || !plan) return LORA_ERR_INVALID_ARG;
+  DeviceGuard g(P->device);
+  lora_plan_s* pl = nullptr;
+  lora_status_t st = plan_alloc(P, &pl);
+  if (st != LORA_OK) return st;
+  P->plans.insert(pl);
+  *plan = pl;
+  return LORA_OK;
+}
+
+lora_status_t lora_plan_destroy(lora_pool_t P, lora_plan_t plan) {
+  if (!P || !plan || !P->plans.count(plan)) return LORA_ERR_INVALID_ARG;
+  DeviceGuard g(P->device);
+  (void)hipDeviceSynchronize();
+  P->plans.erase(plan);
+  plan_free(plan);
+  return LORA_OK;
+}
+
+lora_status_t lora_plan(lora_pool_t P, const int32_t* ids, int32_t T, lora_plan_t plan,
+                        hipStream_t stream) {
+  if (!P || !plan || (plan != P->internal && !P->plans.count(plan))) return LORA_ERR_INVALID_ARG;
+  if (T < 0 || T > P->max_tokens || (T > 0 && !ids)) return LORA_ERR_INVALID_ARG;
+  DeviceGuard g(P->device);
+  return run_plan(P, ids, T, plan, stream);
+}
+
+static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t* X,
+                                const int32_t* ids, int32_t T, const lora_bf16_t* W,
+                                lora_bf16_t* out, lora_plan_t plan, bool lora, hipStream_t stream) {
+  if (!module_ok(P, module)) return LORA_ERR_INVALID_ARG;
+  if (T < 0 || T > P->max_tokens) return LORA_ERR_INVALID_ARG;
+  if (T == 0) return LORA_OK;
+  if (!X || !W || !out || (lora && !ids)) return LORA_ERR_INVALID_ARG;
+  if (plan) {
+    if (!P->plans.count(plan) || plan->T != T || plan->ids != ids) return LORA_ERR_INVALID_ARG;
+  }
+  DeviceGuard g(P->device);
+  const int K = P->d_in[module], N = P->d_out[module];
+  hrg::GemmArgs ga{};
+  ga.X = X;
+  ga.W = W;
+  ga.out = out;
+  ga.T = T;
+  ga.N = N;
+  ga.K = K;
+  ga.status = P->status;
+  if (!lora) {
+    ga.perm = nullptr;
+    return hrg::launch_gemm(ga, false, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+  }
+  lora_plan_s* pl = plan;
+  if (!pl) {
+    pl = P->internal;
+    lora_status_t st = run_plan(P, ids, T, pl, stream);
+    if (st != LORA_OK) return st;
+  }
+  // shrink: (tile, K-split) grid; tiles beyond the plan's count exit at once
+  const int grid_tiles = std::min(T, P->max_adapters) + ceil_div(T, hrg::kShrinkRows);
+  int ksplit = std::max(1, std::min(ceil_div(1024, grid_tiles), std::min(hrg::kMaxSplits, ceil_div(K, 128))));
+  const int kchunk = round_up(ceil_div(K, ksplit), 128);
+  ksplit = ceil_div(K, kchunk);
+  hrg::ShrinkArgs sa{};
+  sa.X = X;
+  sa.K = K;
+  sa.perm = pl->tab.perm;
+  sa.seg_off = pl->tab.seg_off;
+  sa.seg_slot = pl->tab.seg_slot;
+  sa.seg_rank = pl->tab.seg_rank;
+  sa.tile_seg = pl->tab.tile_seg;
+  sa.tile_row0 = pl->tab.tile_row0;
+  sa.counts = pl->tab.counts;
+  sa.pages = P->pages;
+  sa.slot_stride = P->slot_elems;
+  sa.a_off = P->a_off[module];
+  sa.upart = P->upart;
+  sa.split_stride = P->split_stride;
+  sa.u_ld = P->rpad;
+  sa.kchunk = kchunk;
+  sa.status = P->status;
+  if (hrg::launch_shrink(sa, grid_tiles, ksplit, stream) != hipSuccess) return LORA_ERR_HIP;
+  ga.perm = pl->tab.perm;
+  ga.upart = P->upart;
+  ga.split_stride = P->split_stride;
+  ga.u_ld = P->rpad;
+  ga.nsplit = ksplit;
+  ga.row_seg = pl->tab.row_seg;
+  ga.seg_id = pl->tab.seg_id;
+  ga.seg_off = pl->tab.seg_off;
+  ga.seg_slot = pl->tab.seg_slot;
+  ga.seg_rank = pl->tab.seg_rank;
+  ga.seg_scale = pl->tab.seg_scale;
+  ga.pages = P->pages;
+  ga.slot_stride = P->slot_elems;
+  ga.b_off = P->b_off[module];
+  return hrg::launch_gemm(ga, true, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+lora_status_t lora_apply(lora_pool_t P, int32_t module, const lora_bf16_t* X, const int32_t* ids,
+                         int32_t T, const lora_bf16_t* W, lora_bf16_t* out, lora_plan_t plan,
+                         hipStream_t stream) {
+  return apply_impl(P, module, X, ids, T, W, out, plan, true, stream);
+}
+
+lora_status_t lora_base_apply(lora_pool_t P, int32_t module, const lora_bf16_t* X, int32_t T,
+                              const lora_bf16_t* W, lora_bf16_t* out, hipStream_t stream) {
+  return apply_impl(P, module, X, nullptr, T, W, out, nullptr, false, stream);
+}
+
+lora_status_t lora_status(lora_pool_t P, hipStream_t stream) {
+  if (!P) return LORA_ERR_INVALID_ARG;
+  DeviceGuard g(P->device);
+  int32_t st = 0;
+  if (hipStreamSynchronize(stream) != hipSuccess ||
+      hipMemcpy(&st, P->status, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess ||
+      hrg::launch_clear_i32(P->status, 1, 0, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return LORA_ERR_HIP;
+  }
+  return (lora_status_t)st;
+}
+
+lora_status_t lora_debug_read_plan(lora_pool_t P, lora_plan_t plan, int32_t* perm, int32_t* inv,
+                                   int32_t* seg_id, int32_t* seg_off, int32_t* T_out,
+                                   int32_t* S_out, hipStream_t stream) {
+  if (!P) return LORA_ERR_INVALID_ARG;
+  lora_plan_s* pl = plan ? plan : P->internal;
+  if (plan && !P->plans.count(plan)) return LORA_ERR_INVALID_ARG;
+  if (pl->T < 0) return LORA_ERR_INVALID_ARG;  // never built
+  DeviceGuard g(P->device);
+  int32_t counts[4] = {0, 0, 0, 0};
+  if (hipStreamSynchronize(stream) != hipSuccess ||
+      hipMemcpy(counts, pl->tab.counts, sizeof(counts), hipMemcpyDeviceToHost) != hipSuccess)
+    return (void)hipGetLastError(), LORA_ERR_HIP;
+  const int32_t T = pl->T, S = counts[0];
+  if (T_out) *T_out = T;
+  if (S_out) *S_out = S;
+  if (S < 0 || S > T + 1) return LORA_ERR_HIP;
+  bool ok = true;
+  if (perm && T) ok &= hipMemcpy(perm, pl->tab.perm, T * 4, hipMemcpyDeviceToHost) == hipSuccess;
+  if (inv && T) ok &= hipMemcpy(inv, pl->tab.inv, T * 4, hipMemcpyDeviceToHost) == hipSuccess;
+  if (seg_id && S) ok &= hipMemcpy(seg_id, pl->tab.seg_id, S * 4, hipMemcpyDeviceToHost) == hipSuccess;
+  if (seg_off) ok &= hipMemcpy(seg_off, pl->tab.seg_off, (S + 1) * 4, hipMemcpyDeviceToHost) == hipSuccess;
+  if (!ok) return (void)hipGetLastError(), LORA_ERR_HIP;
+  return LORA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Device helpers shared by the HIP kernels of the LoRA library (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+namespace hrg {
+
+// 16-byte global load of 8 bf16 values (caller guarantees 16-byte alignment).
+__device__ __forceinline__ bf16x8 ld_bf16x8(const uint16_t* p) {
+  uint4 v = *reinterpret_cast<const uint4*>(p);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  return __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
+}
+
+__device__ __forceinline__ bf16x8 lds_bf16x8(const uint16_t* p) {
+  uint4 v = *reinterpret_cast<const uint4*>(p);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// fp32 -> bf16 bits, round to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+// C[16x16] += A[16x32] B[32x16].  Lane l supplies A row (l%16) and B column
+// (l%16), each with k in [8*(l/16), 8*(l/16)+8).  Result: lane l holds column
+// (l%16), rows 4*(l/16) + i, i = 0..3.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// C[32x32] += A[32x16] B[16x32].  Lane l supplies A row (l%32) and B column
+// (l%32), each with k in [8*(l/32), 8*(l/32)+8).  Result register r of lane l
+// is row 8*(r/4) + 4*(l/32) + (r%4), column (l%32).
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+}  // namespace hrg

@@ -1,0 +1,107 @@
+// Internal interface between the host API (api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hrg {
+
+constexpr int kMaxIds = 16384;       // plan histogram lives in LDS
+constexpr int kMaxRank = 64;
+constexpr int kShrinkRows = 64;      // rows per shrink work tile
+constexpr int kMaxSplits = 32;       // K-splits of the shrink
+// Device status codes (values of lora_status_t; a larger code wins).
+constexpr int kStatusNotLoaded = 6;
+constexpr int kStatusIdRange = 7;
+
+inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
+inline int ceil_div(int x, int m) { return (x + m - 1) / m; }
+
+// Device tables of one plan.  Sizes: T_cap = pool max_tokens.
+struct PlanTables {
+  int32_t* perm;       // [T_cap]   sorted position -> token
+  int32_t* inv;        // [T_cap]   token -> sorted position
+  int32_t* row_seg;    // [T_cap]   sorted position -> segment
+  int32_t* seg_id;     // [T_cap+1] segment -> adapter id (-1 first if present)
+  int32_t* seg_off;    // [T_cap+2] segment start offsets, seg_off[S] = T
+  int32_t* seg_slot;   // [T_cap+1] pool slot (-1 for the base segment)
+  int32_t* seg_rank;   // [T_cap+1] true rank (0 for the base segment)
+  float* seg_scale;    // [T_cap+1] alpha / rank
+  int32_t* tile_seg;   // [max_tiles] shrink work tile -> segment
+  int32_t* tile_row0;  // [max_tiles] first sorted row of the tile
+  int32_t* counts;     // [0] = S, [1] = number of shrink tiles, [2] = T
+  int32_t max_tiles;
+};
+
+struct PlanArgs {
+  const int32_t* ids;
+  int32_t T;
+  int32_t max_ids;
+  const int32_t* id2slot;
+  const int32_t* slot_rank;
+  const float* slot_scale;
+  int32_t* status;
+  PlanTables tab;
+};
+
+struct ShrinkArgs {
+  const uint16_t* X;      // [T][K]
+  int32_t K;
+  const int32_t* perm;
+  const int32_t* seg_off;
+  const int32_t* seg_slot;
+  const int32_t* seg_rank;
+  const int32_t* tile_seg;
+  const int32_t* tile_row0;
+  const int32_t* counts;
+  const uint16_t* pages;  // A^T page of (slot, module): pages + slot*slot_stride + a_off, [rmax][K]
+  size_t slot_stride;
+  size_t a_off;
+  float* upart;           // [split][T_cap][u_ld]
+  size_t split_stride;
+  int32_t u_ld;
+  int32_t kchunk;
+  const int32_t* status;
+};
+
+struct GemmArgs {
+  const uint16_t* X;      // [T][K]
+  const uint16_t* W;      // [N][K]
+  uint16_t* out;          // [T][N]
+  int32_t T, N, K;
+  const int32_t* perm;    // sorted row -> token; nullptr = identity (base-only)
+  // LoRA epilogue (unused by the base-only instantiation)
+  const float* upart;
+  size_t split_stride;
+  int32_t u_ld;
+  int32_t nsplit;
+  const int32_t* row_seg;
+  const int32_t* seg_id;
+  const int32_t* seg_off;
+  const int32_t* seg_slot;
+  const int32_t* seg_rank;
+  const float* seg_scale;
+  const uint16_t* pages;  // B page of (slot, module): pages + slot*slot_stride + b_off, [rmax][N]
+  size_t slot_stride;
+  size_t b_off;
+  const int32_t* status;
+};
+
+struct PackArgs {
+  const uint16_t* src;    // staged A (rows x rank) or B (rank x cols)
+  uint16_t* dst;          // page [rmax][cols]
+  int32_t rank, rmax;
+  int32_t cols;           // d_in for A (transposed), d_out for B
+  int32_t transpose;      // 1: src is cols x rank (A), 0: src is rank x cols (B)
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_shrink(const ShrinkArgs& a, int grid_tiles, int ksplit, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& a, bool lora, hipStream_t s);
+hipError_t launch_pack(const PackArgs& a, hipStream_t s);
+hipError_t launch_set_slot(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int32_t id,
+                           int32_t slot, int32_t rank, float scale, hipStream_t s);
+hipError_t launch_clear_i32(int32_t* p, int32_t n, int32_t value, hipStream_t s);
+
+}  // namespace hrg

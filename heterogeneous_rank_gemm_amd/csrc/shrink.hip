@@ -1,0 +1,118 @@
+// Grouped "shrink": U[p, q] = sum_k X[perm[p], k] * A_s[k, q] for every
+// sorted row p of adapter segment s and q < rank(s).  Evaluating X A first
+// gives the low-rank intermediate of the LoRA-Land post (section "2.
+// multi-LoRA batch scheduling"), which keeps the extra work small.
+//
+// Work unit: (shrink tile, K-split).  A tile is up to 64 sorted rows of ONE
+// segment, so the adapter's A^T page (rank-major, r_max x d_in) is streamed
+// once per tile and K-split; the 16x16x32 bf16 MFMA does the contraction.
+// Each of the 4 waves covers an interleaved quarter of the K range; the four
+// partial results are summed in a fixed order through LDS (deterministic),
+// and each K-split writes its own fp32 partial plane of U.  The GEMM
+// epilogue sums the planes in split order.
+#include "common.h"
+#include "internal.h"
+
+namespace hrg {
+
+constexpr int kShrinkThreads = 256;
+constexpr int kRedLd = 65;  // padded row of the cross-wave reduction buffer
+
+__global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
+  __shared__ float red[4][64 * kRedLd];
+  if (*a.status != 0) return;
+  const int tile = blockIdx.x;
+  if (tile >= a.counts[1]) return;
+
+  const int seg = a.tile_seg[tile];
+  const int row0 = a.tile_row0[tile];
+  const int rows = min(kShrinkRows, a.seg_off[seg + 1] - row0);
+  const int slot = a.seg_slot[seg];
+  const int rank = a.seg_rank[seg];
+  const int nq = (rank + 15) / 16;  // 16-wide rank blocks actually computed
+  const int nm = (rows + 15) / 16;  // 16-row blocks with at least one row
+  const int K = a.K;
+  const int k0 = blockIdx.y * a.kchunk;
+  const int k1 = min(K, k0 + a.kchunk);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const uint16_t* Ap = a.pages + (size_t)slot * a.slot_stride + a.a_off;
+
+  const uint16_t* xrow[4];
+  bool rv[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int p = 16 * mb + (l & 15);
+    rv[mb] = p < rows;
+    const int tok = a.perm[row0 + (rv[mb] ? p : 0)];
+    xrow[mb] = a.X + (size_t)tok * K;
+  }
+  const uint16_t* arow[4];
+  bool qv[4];
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int q = 16 * nb + (l & 15);
+    qv[nb] = q < rank;
+    arow[nb] = Ap + (size_t)(qv[nb] ? q : 0) * K;
+  }
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int koff = 8 * (l >> 4);
+  for (int k = k0 + 32 * w; k < k1; k += 128) {
+    const int kk = k + koff;
+    const bool kv = kk < k1;  // K is a multiple of 8: a lane's 8 elements are all in or all out
+    bf16x8 xa[4], ab[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+      xa[mb] = (mb < nm && rv[mb] && kv) ? ld_bf16x8(xrow[mb] + kk) : zero_bf16x8();
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      ab[nb] = (nb < nq && qv[nb] && kv) ? ld_bf16x8(arow[nb] + kk) : zero_bf16x8();
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      if (mb >= nm) continue;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        if (nb >= nq) continue;
+        acc[mb][nb] = mfma16(xa[mb], ab[nb], acc[mb][nb]);
+      }
+    }
+  }
+
+  // cross-wave reduction in fixed wave order
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    if (mb >= nm) continue;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      if (nb >= nq) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mb + 4 * (l >> 4) + i;
+        const int q = 16 * nb + (l & 15);
+        red[w][r * kRedLd + q] = acc[mb][nb][i];
+      }
+    }
+  }
+  __syncthreads();
+  const int width = nq * 16;
+  float* up = a.upart + (size_t)blockIdx.y * a.split_stride + (size_t)row0 * a.u_ld;
+  for (int idx = threadIdx.x; idx < rows * width; idx += kShrinkThreads) {
+    const int r = idx / width, q = idx % width;
+    const float v = ((red[0][r * kRedLd + q] + red[1][r * kRedLd + q]) + red[2][r * kRedLd + q]) +
+                    red[3][r * kRedLd + q];
+    up[(size_t)r * a.u_ld + q] = v;
+  }
+}
+
+hipError_t launch_shrink(const ShrinkArgs& a, int grid_tiles, int ksplit, hipStream_t s) {
+  if (grid_tiles <= 0 || ksplit <= 0) return hipSuccess;
+  hipLaunchKernelGGL(shrink_kernel, dim3(grid_tiles, ksplit), dim3(kShrinkThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace hrg

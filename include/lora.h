@@ -1,0 +1,203 @@
+/*
+ * lora.h -- C ABI of the heterogeneous-batch LoRA-augmented linear for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One call computes, for every token row t of a batch,
+ *
+ *     out[t, :] = bf16( X[t, :] W^T  +  (alpha_i / r_i) (X[t, :] A_i) B_i ),
+ *     i = ids[t]; id -1 means "base only" (no LoRA term at all),
+ *
+ * with fp32 accumulation and exactly one round-to-nearest-even to bf16 per
+ * output.  All adapters live in one device pool owned by the library.
+ *
+ * Pages this interface follows (cited by title and section):
+ *   [LoRA-Land]  "LoRA-Land: turning the LLM into an operating system with
+ *                hot-pluggable multi-task fine-tuned serving" (blog.itodd.wang)
+ *   [vLLM-ch7]   "Multi-LoRA hot-plug: one model serving many tenants"
+ *                (gufacode.com, vLLM chapter 7)
+ *   [icman]      field report on Multi-LoRA in managed inference
+ *                (icman.com.cn news 62580)
+ *
+ * Conventions for every entry point
+ *   - All matrices are row-major and hold bf16 bit patterns (lora_bf16_t).
+ *   - W is d_out x d_in, X is T x d_in, out is T x d_out   (out = X W^T ...).
+ *     A is d_in x r and B is r x d_out ([vLLM-ch7] "LoRA at a glance" gives
+ *     A (d x r), B (r x d); [LoRA-Land] section "2. multi-LoRA batch
+ *     scheduling" evaluates X A first, then B).
+ *   - X, W, ids and out are caller-owned DEVICE buffers; the library never
+ *     frees or keeps them beyond the call's stream work.
+ *   - Every call returns a lora_status_t.  Errors that the host can detect
+ *     (null pointers, shapes, module index, sizes, rank, capacity) return
+ *     synchronously and have no side effects.
+ *   - Work is enqueued on the caller's stream; calls on one pool must be
+ *     ordered on one stream (they share the pool's workspace).  Calls that
+ *     overlap on different streams race.
+ *   - d_in and d_out must be multiples of 8 (16-byte rows of bf16).
+ */
+#ifndef HRG_LORA_H
+#define HRG_LORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t lora_bf16_t;              /* bf16 bit pattern */
+typedef struct lora_pool_s* lora_pool_t;     /* opaque adapter pool */
+typedef struct lora_plan_s* lora_plan_t;     /* opaque grouping plan */
+
+typedef enum {
+  LORA_OK = 0,
+  LORA_ERR_INVALID_ARG = 1, /* null pointer, bad shape, bad module, T > max_tokens, ... */
+  LORA_ERR_OOM = 2,         /* device allocation failed (create, plan_create only) */
+  LORA_ERR_POOL_FULL = 3,   /* every resident slot is in use */
+  LORA_ERR_RANK = 4,        /* rank outside [1, max_rank] */
+  LORA_ERR_EXISTS = 5,      /* id already loaded (no silent overwrite) */
+  LORA_ERR_NOT_LOADED = 6,  /* id not resident (strict mode: never falls back to base) */
+  LORA_ERR_ID_RANGE = 7,    /* id outside [-1, max_ids) */
+  LORA_ERR_HIP = 8          /* a HIP runtime call failed */
+} lora_status_t;
+
+/* Human-readable name of a status code (static string). */
+const char* lora_status_string(lora_status_t s);
+
+/*
+ * lora_pool_create -- the unified adapter pool ([vLLM-ch7] "how vLLM
+ * implements multi-LoRA": all adapters in one device memory pool;
+ * [LoRA-Land] "3. hot-plug API": the kernel object sized by max_adapters).
+ *
+ *   pool          out: the new pool handle
+ *   max_adapters  resident slots (like --max-loras / --max-active-adapters)
+ *   max_ids       adapter ids are valid in [0, max_ids); 1..16384
+ *   max_rank      page rank; every adapter's pages are zero-padded to it
+ *                 ([vLLM-ch7] "performance notes": mixed ranks are aligned
+ *                 to the largest); 1..64 (--max-lora-rank 64)
+ *   n_modules     number of LoRA-augmented linears served by the pool
+ *   d_in, d_out   host arrays [n_modules]; multiples of 8, 8..65536
+ *   max_tokens    largest T accepted by lora_apply / lora_plan; 1..65536
+ *   stream        stream used to initialise the device tables
+ *
+ * Memory: max_adapters * sum_m max_rank*(d_in[m]+d_out[m]) * 2 bytes of
+ * pages plus O(max_ids + max_tokens*max_rank) of tables and workspace, all
+ * allocated here.  Returns INVALID_ARG, OOM or HIP; *pool is untouched on error.
+ */
+lora_status_t lora_pool_create(lora_pool_t* pool, int32_t max_adapters, int32_t max_ids,
+                               int32_t max_rank, int32_t n_modules, const int32_t* d_in,
+                               const int32_t* d_out, int32_t max_tokens, hipStream_t stream);
+
+/* Frees the pool and every plan still attached to it.  Synchronises the device. */
+lora_status_t lora_pool_destroy(lora_pool_t pool);
+
+/*
+ * lora_load_adapter -- hot-load one adapter ([LoRA-Land] "3. hot-plug API":
+ * load moves A and B to the GPU and builds an index; [vLLM-ch7] "dynamic
+ * online/offline": loading without restarting the service).
+ *
+ *   id     adapter id in [0, max_ids)                      else ID_RANGE
+ *   rank   true rank r, 1 <= r <= max_rank                 else RANK
+ *   alpha  scaling numerator; the scale is alpha / r (fp32)
+ *          ([vLLM-ch7] PEFT config lora_alpha=32 at r=16; [icman] 3.2)
+ *   A      host array [n_modules] of pointers, A[m] is d_in[m] x r
+ *   B      host array [n_modules] of pointers, B[m] is r x d_out[m]
+ *          A[m], B[m] may point to host or device memory; they are copied
+ *          before the call returns and may be freed afterwards.
+ *
+ * Takes the lowest free slot.  An id already resident returns EXISTS
+ * ([icman] 4.3 warns against silent overwrites); a full pool returns
+ * POOL_FULL (eviction is the caller's policy).  Synchronises `stream`.
+ */
+lora_status_t lora_load_adapter(lora_pool_t pool, int32_t id, int32_t rank, float alpha,
+                                const lora_bf16_t* const* A, const lora_bf16_t* const* B,
+                                hipStream_t stream);
+
+/*
+ * lora_unload_adapter -- release an adapter's slot ([LoRA-Land] "3. hot-plug
+ * API": unload frees the adapter's caches; [vLLM-ch7] unload endpoint).
+ * Waits for `stream` first, so work already enqueued there never reads a
+ * recycled page.  NOT_LOADED if the id is not resident, ID_RANGE if out of range.
+ */
+lora_status_t lora_unload_adapter(lora_pool_t pool, int32_t id, hipStream_t stream);
+
+/* Host-side lookup: slot, true rank and scale of a resident id (any out
+ * pointer may be NULL).  NOT_LOADED / ID_RANGE as above. */
+lora_status_t lora_pool_query(lora_pool_t pool, int32_t id, int32_t* slot, int32_t* rank,
+                              float* scale);
+
+/*
+ * Plans: the grouping of a batch by adapter id ([LoRA-Land] section "2.
+ * multi-LoRA batch scheduling": group the batch by LoRA id, "Grouped
+ * Multi-LoRA Execution").  The plan is a stable sort of token indices by
+ * (id ascending, index ascending), -1 first, plus the segment table of the
+ * maximal runs of equal id.  One plan can serve every linear of a step.
+ *
+ * lora_plan_create allocates device tables sized for the pool's max_tokens.
+ */
+lora_status_t lora_plan_create(lora_pool_t pool, lora_plan_t* plan);
+lora_status_t lora_plan_destroy(lora_pool_t pool, lora_plan_t plan);
+
+/*
+ * lora_plan -- build `plan` from device ids[T] on `stream` (no host sync).
+ * Ids are validated on the device (strict mode, [icman] 4.1): an id outside
+ * [-1, max_ids) or not resident sets the pool's sticky error status; every
+ * later lora_apply on the pool then leaves its output untouched until
+ * lora_status() reports and clears the error.  T = 0 is valid (S = 0).
+ * INVALID_ARG if T < 0, T > max_tokens, or ids is NULL with T > 0.
+ */
+lora_status_t lora_plan(lora_pool_t pool, const int32_t* ids, int32_t T, lora_plan_t plan,
+                        hipStream_t stream);
+
+/*
+ * lora_apply -- the heterogeneous-batch LoRA linear for module `module`
+ * ([LoRA-Land] section 2 formula; [vLLM-ch7] "heterogeneous batching": one
+ * forward computes every request's own side path; [icman] 2.1 dynamic
+ * batching mode).
+ *
+ *   X     device, T x d_in[module]
+ *   ids   device int32[T], each -1 or a resident id
+ *   W     device, d_out[module] x d_in[module] (the frozen base weight)
+ *   out   device, T x d_out[module]; written in the original token order
+ *   plan  NULL: the call plans `ids` itself.  Otherwise a plan built by
+ *         lora_plan from the same `ids` pointer and T (INVALID_ARG if not).
+ *
+ * Asynchronous; id errors are reported through the sticky status (see
+ * lora_plan / lora_status), and then `out` is not written.  T = 0 is a no-op.
+ * Rows with id -1 are bit-identical to lora_base_apply's rows.
+ */
+lora_status_t lora_apply(lora_pool_t pool, int32_t module, const lora_bf16_t* X,
+                         const int32_t* ids, int32_t T, const lora_bf16_t* W, lora_bf16_t* out,
+                         lora_plan_t plan, hipStream_t stream);
+
+/*
+ * lora_base_apply -- out = bf16(X W^T) with the same GEMM kernels and tile
+ * choice as lora_apply but no LoRA term ([vLLM-ch7] "switching LoRA per
+ * request": a request naming no LoRA runs the plain base).  It is the
+ * denominator of the LoRA-overhead figure.  Same argument rules as lora_apply.
+ */
+lora_status_t lora_base_apply(lora_pool_t pool, int32_t module, const lora_bf16_t* X, int32_t T,
+                              const lora_bf16_t* W, lora_bf16_t* out, hipStream_t stream);
+
+/*
+ * lora_status -- synchronise `stream`, return the pool's sticky device
+ * status (OK, NOT_LOADED or ID_RANGE; ID_RANGE wins if both occurred) and
+ * clear it.
+ */
+lora_status_t lora_status(lora_pool_t pool, hipStream_t stream);
+
+/*
+ * lora_debug_read_plan -- copy a plan's tables to host memory (testing aid;
+ * synchronises `stream`).  plan NULL reads the pool's internal plan (the one
+ * the last lora_apply without a plan built).  Host buffers: perm[T], inv[T],
+ * seg_id[S], seg_off[S+1] with T <= max_tokens and S <= T + 1; *T_out and
+ * *S_out receive the sizes.  Any table pointer may be NULL to skip it.
+ */
+lora_status_t lora_debug_read_plan(lora_pool_t pool, lora_plan_t plan, int32_t* perm,
+                                   int32_t* inv, int32_t* seg_id, int32_t* seg_off,
+                                   int32_t* T_out, int32_t* S_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HRG_LORA_H */

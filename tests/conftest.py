@@ -11,3 +11,13 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU test")
+
+
+def pytest_sessionstart(session):
+    # The C-ABI library is a build product (git-ignored).  Cross-compile it
+    # once if this tree does not have it yet; hipcc needs no GPU for that.
+    lib = os.path.join(ROOT, "heterogeneous_rank_gemm_amd", "libhrglora.so")
+    if not os.path.exists(lib):
+        import runpy
+        runpy.run_path(os.path.join(ROOT, "heterogeneous_rank_gemm_amd", "build.py"),
+                       run_name="hrg_build")["build"]()

@@ -1,0 +1,90 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every entry point
+that include/lora.h declares, and rejects bad arguments on the host before
+touching the GPU (no compute call is made here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:lora_status_t|const char\*)\s+(lora_\w+)\s*\(", src,
+                                 flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("lora_pool_create", "lora_pool_destroy", "lora_load_adapter",
+              "lora_unload_adapter", "lora_apply", "lora_plan", "lora_base_apply",
+              "lora_status", "lora_debug_read_plan", "lora_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import heterogeneous_rank_gemm_amd as hrg
+    lib = C.CDLL(hrg._lora.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert sorted(hrg.EXPORTED) == _declared()
+
+
+def test_status_strings():
+    import heterogeneous_rank_gemm_amd as hrg
+    for code, name in hrg.STATUS_NAMES.items():
+        assert hrg.lora_status_string(code) == "LORA_" + ("OK" if name == "OK" else "ERR_" + name)
+
+
+def _raw():
+    import heterogeneous_rank_gemm_amd as hrg
+    return hrg._lora._lib
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(max_rank=0), 1), (dict(max_rank=65), 1), (dict(max_ids=0), 1),
+    (dict(max_ids=16385), 1), (dict(max_adapters=0), 1), (dict(max_tokens=0), 1),
+    (dict(d_in=[1020]), 1), (dict(d_out=[4]), 1), (dict(n_modules=0), 1),
+])
+def test_pool_create_rejects_bad_arguments_on_host(kw, code):
+    args = dict(max_adapters=4, max_ids=4, max_rank=8, d_in=[64], d_out=[64], max_tokens=64,
+                n_modules=None)
+    args.update(kw)
+    n = len(args["d_in"]) if args["n_modules"] is None else args["n_modules"]
+    din = (C.c_int32 * 1)(*args["d_in"])
+    dout = (C.c_int32 * 1)(*args["d_out"])
+    h = C.c_void_p()
+    r = _raw().lora_pool_create(C.byref(h), args["max_adapters"], args["max_ids"],
+                                args["max_rank"], n, din, dout, args["max_tokens"], None)
+    assert r == code
+    assert h.value is None
+
+
+def test_null_handles_are_rejected():
+    lib = _raw()
+    assert lib.lora_pool_destroy(None) == 1
+    assert lib.lora_apply(None, 0, None, None, 0, None, None, None, None) == 1
+    assert lib.lora_base_apply(None, 0, None, 0, None, None, None) == 1
+    assert lib.lora_unload_adapter(None, 0, None) == 1
+    assert lib.lora_status(None, None) == 1
+    assert lib.lora_plan(None, None, 0, None, None) == 1
+    h = C.c_void_p()
+    assert lib.lora_pool_create(None, 1, 1, 8, 1, None, None, 1, None) == 1
+    assert lib.lora_plan_create(None, C.byref(h)) == 1
+
+
+def test_package_fails_loudly_without_library(tmp_path, monkeypatch):
+    # the binding refuses to import from a tree without the built library
+    import importlib.util
+    src = os.path.join(ROOT, "heterogeneous_rank_gemm_amd", "_lora.py")
+    pkg = tmp_path / "pkg"
+    pkg.mkdir()
+    (pkg / "_lora.py").write_text(open(src).read())
+    spec = importlib.util.spec_from_file_location("lonely_lora", pkg / "_lora.py")
+    mod = importlib.util.module_from_spec(spec)
+    with pytest.raises(ImportError):
+        spec.loader.exec_module(mod)
