@@ -113,17 +113,28 @@ class Replica:
         self.pool.plan(self.ids, self.T, self.plan)
 
 
+# Up to 64 tokens (decode) one lora_apply launch groups the batch itself, so a
+# step is just the applies; larger batches build one plan per step and every
+# linear of the step reuses it.
+DECODE_MAX_T = 64
+
+
 def lora_step(rep: Replica, hrg):
     h = rep.pool.handle
-    hrg.lora_plan(h, rep.ids, rep.T, rep.plan)
+    plan = None
+    if rep.T > DECODE_MAX_T:
+        hrg.lora_plan(h, rep.ids, rep.T, rep.plan)
+        plan = rep.plan
     for j in range(len(rep.W)):
-        hrg.lora_apply(h, j, rep.xin[j], rep.ids, rep.T, rep.W[j], rep.out[j], rep.plan)
+        hrg.lora_apply(h, j, rep.xin[j], rep.ids, rep.T, rep.W[j], rep.out[j], plan)
 
 
 def apply_only(rep: Replica, hrg):
+    """The step without its plan launch (identical to lora_step at decode)."""
     h = rep.pool.handle
+    plan = rep.plan if rep.T > DECODE_MAX_T else None
     for j in range(len(rep.W)):
-        hrg.lora_apply(h, j, rep.xin[j], rep.ids, rep.T, rep.W[j], rep.out[j], rep.plan)
+        hrg.lora_apply(h, j, rep.xin[j], rep.ids, rep.T, rep.W[j], rep.out[j], plan)
 
 
 def base_step(rep: Replica, hrg):

@@ -39,6 +39,9 @@ struct lora_pool_s {
   uint16_t* staging = nullptr;       // one module's A or B as received
   float* upart = nullptr;            // [kMaxSplits][max_tokens][rpad]
   size_t split_stride = 0;
+  // decode-path workspace
+  float* dec_part = nullptr;         // [ceil(max d_in / 512)][64][max d_out] base partials
+  float* dec_upart = nullptr;        // [ceil(max d_in / 512)][64][rpad] shrink partials
   std::vector<int32_t> h_id2slot, h_slot_rank;
   std::vector<float> h_slot_scale;
   std::set<int32_t> free_slots;      // lowest free slot first
@@ -129,6 +132,41 @@ lora_status_t run_plan(lora_pool_s* P, const int32_t* ids, int32_t T, lora_plan_
 
 bool module_ok(const lora_pool_s* P, int32_t m) { return P && m >= 0 && m < P->n_modules; }
 
+lora_status_t decode_apply(lora_pool_s* P, int32_t module, const lora_bf16_t* X, const int32_t* ids,
+                           int32_t T, const lora_bf16_t* W, lora_bf16_t* out, bool lora,
+                           hipStream_t stream) {
+  const int K = P->d_in[module], N = P->d_out[module];
+  hrg::DecodeArgs a{};
+  a.X = X;
+  a.W = W;
+  a.out = out;
+  a.ids = ids;
+  a.T = T;
+  a.N = N;
+  a.K = K;
+  a.max_ids = P->max_ids;
+  a.id2slot = P->id2slot;
+  a.slot_rank = P->slot_rank;
+  a.slot_scale = P->slot_scale;
+  a.pages = P->pages;
+  a.slot_stride = P->slot_elems;
+  a.a_off = P->a_off[module];
+  a.b_off = P->b_off[module];
+  a.part = P->dec_part;
+  a.upart = P->dec_upart;
+  a.u_ld = P->rpad;
+  a.status = P->status;
+  a.NT = ceil_div(N, hrg::kDecodeTileRows);
+  a.KS = ceil_div(K, hrg::kDecodeChunk);
+  a.lora = lora ? 1 : 0;
+  if (lora) {
+    // A-tile items: (adapter, 16-rank block); at most min(T, resident) adapters
+    const int loaded = P->max_adapters - (int)P->free_slots.size();
+    a.n_atiles = ceil_div(std::min(T, loaded) * (P->rpad / 16), 8);
+  }
+  return hrg::launch_decode(a, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -193,6 +231,15 @@ lora_status_t lora_pool_create(lora_pool_t* pool, int32_t max_adapters, int32_t 
             dmalloc(&P->status, 4) == hipSuccess &&
             dmalloc(&P->staging, max_dim * max_rank) == hipSuccess &&
             dmalloc(&P->upart, (size_t)hrg::kMaxSplits * P->split_stride) == hipSuccess;
+  size_t max_din = 0, max_dout = 0;
+  for (int32_t m = 0; m < n_modules; ++m) {
+    max_din = std::max<size_t>(max_din, d_in[m]);
+    max_dout = std::max<size_t>(max_dout, d_out[m]);
+  }
+  const size_t ks_max = (max_din + hrg::kDecodeChunk - 1) / hrg::kDecodeChunk;
+  if (ok)
+    ok = dmalloc(&P->dec_upart, ks_max * hrg::kDecodeMaxT * P->rpad) == hipSuccess &&
+         dmalloc(&P->dec_part, ks_max * hrg::kDecodeMaxT * max_dout) == hipSuccess;
   if (ok) ok = plan_alloc(P, &P->internal) == LORA_OK;
   if (!ok) {
     (void)hipGetLastError();
@@ -229,6 +276,8 @@ lora_status_t lora_pool_destroy(lora_pool_t P) {
   (void)hipFree(P->status);
   (void)hipFree(P->staging);
   (void)hipFree(P->upart);
+  (void)hipFree(P->dec_upart);
+  (void)hipFree(P->dec_part);
   delete P;
   return LORA_OK;
 }
@@ -343,6 +392,7 @@ static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t
   }
   DeviceGuard g(P->device);
   const int K = P->d_in[module], N = P->d_out[module];
+  if (T <= hrg::kDecodeMaxT) return decode_apply(P, module, X, ids, T, W, out, lora, stream);
   hrg::GemmArgs ga{};
   ga.X = X;
   ga.W = W;

@@ -1,0 +1,314 @@
+// Decode-shaped LoRA linear (T <= 64 tokens): two launches, no inter-block
+// waiting.
+//
+// At decode the linear is bound by bytes: W once, plus the A and B pages of
+// every distinct adapter in the batch.  X is small (T x K), but every column
+// tile needs all of it, so it is staged once per K chunk in LDS and never
+// re-read from L2 per 16 columns.
+//
+// Launch 1 (decode_main): a grid of (row tile, 512-wide K chunk) blocks of
+// 8 waves.  Every block stages X[:, chunk] (64 x 512 bf16) in LDS; each wave
+// owns a block of 16 rows, loads its whole 16 x 512 slice up front, and runs
+// the bf16 MFMA 16x16x32 against the X chunk.  Two kinds of row tiles:
+//   * W tiles: 8 x 16 rows of the base weight; the fp32 partial sums go to
+//     part[chunk][t][n].
+//   * A tiles: 8 items (adapter, 16 ranks), i.e. 16 rows of an adapter's A^T
+//     page.  The block groups the batch by adapter id (LoRA-Land post,
+//     section "2. multi-LoRA batch scheduling": Grouped Multi-LoRA
+//     Execution), so each adapter's page is streamed once per chunk; the
+//     partial shrink U_c[t, q] = X[t, chunk] . A[chunk, q] is kept for the
+//     adapter's own tokens in upart[chunk][t][q].
+// Launch 2 (decode_combine), one thread per (token, 4 columns):
+//     V[t, q]   = (alpha/r) * sum_chunks upart[c][t][q]
+//     out[t, n] = bf16( sum_chunks part[c][t][n]  +  sum_q V[t, q] B_i[q, n] )
+//   chunks added in order, the expand in fp32, a single rounding (icman
+//   report, section 2.1: the low-rank branch is added back to the main path).
+//   Rows with id -1 get no LoRA term at all.
+//
+// The base-only entry runs the same launches without A tiles and without the
+// expand, so id -1 rows match it bit for bit.  Every block that depends on the
+// ids validates all of them the same way (strict mode, icman report section
+// 4.1): on an invalid batch nothing is written to `out`.
+#include "common.h"
+#include "internal.h"
+
+namespace hrg {
+
+constexpr int kMainThreads = 512;
+constexpr int kMainWaves = kMainThreads / 64;
+constexpr int kSteps = kDecodeChunk / 32;  // MFMA K steps per chunk
+constexpr int kXs = kDecodeChunk + 8;      // LDS row of the X chunk (16-byte pad)
+static_assert(kMainWaves * 16 == kDecodeTileRows, "tile rows");
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+// v if keep, else zero -- with a mask, so the compiler never selects between
+// addresses (which would push register arrays to scratch memory)
+__device__ __forceinline__ uint4 keep_if(bool keep, uint4 v) {
+  const uint32_t m = keep ? 0xffffffffu : 0u;
+  return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+__device__ __forceinline__ float lo_f(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
+__device__ __forceinline__ float hi_f(uint32_t v) { return __builtin_bit_cast(float, v & 0xffff0000u); }
+
+// Token t's adapter lookup (lane t of a wave, t < 64): id, pool slot, true
+// rank and scale, or bad = the status code of an invalid id.  All lanes load
+// in parallel, so a wave pays one round of dependent loads, not one per token.
+struct TokInfo {
+  int id = -1, slot = -1, rank = 0, bad = 0;
+  float scale = 0.f;
+};
+
+__device__ __forceinline__ TokInfo token_info(const DecodeArgs& a, int t) {
+  TokInfo ti;
+  if (t < a.T) {
+    const int id = a.ids[t];
+    if (id < -1 || id >= a.max_ids) {
+      ti.bad = kStatusIdRange;
+    } else if (id >= 0) {
+      const int slot = a.id2slot[id];
+      if (slot < 0) {
+        ti.bad = kStatusNotLoaded;
+      } else {
+        ti.id = id;
+        ti.slot = slot;
+        ti.rank = a.slot_rank[slot];
+        ti.scale = a.slot_scale[slot];
+      }
+    }
+  }
+  return ti;
+}
+
+__global__ __launch_bounds__(kMainThreads) void decode_main(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[64 * kXs];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const int T = a.T, N = a.N, K = a.K;
+  if (a.lora && *a.status != 0) return;
+
+  // XCD-aware order: the hardware hands block b to XCD (b mod 8); each XCD
+  // takes a contiguous run of (tile, chunk) pairs, so the chunks of a tile
+  // share that XCD's L2.
+  const int G = gridDim.x;
+  const int xcd = blockIdx.x % 8, qd = G / 8, rm = G % 8;
+  const int logical = xcd * qd + min(xcd, rm) + blockIdx.x / 8;
+  const int tile = logical / a.KS, c = logical % a.KS;
+  const bool a_tile = tile >= a.NT;
+  const int k0 = c * kDecodeChunk, klen = min(K, k0 + kDecodeChunk) - k0;
+
+  // ---- this wave's 16 rows ----
+  const uint16_t* row = nullptr;  // row r16 of the block of 16, at k0
+  bool row_ok = false;
+  int n0 = 0;                     // W tile: first column
+  int qb = 0;                     // A tile: rank block of the adapter
+  uint64_t members = 0;           // A tile: tokens of the adapter
+  if (!a_tile) {
+    n0 = tile * kDecodeTileRows + 16 * w;
+    row_ok = n0 + r16 < N;
+    row = a.W + (size_t)(row_ok ? n0 + r16 : 0) * K + k0;
+  } else {
+    // one round of lookups: lane t holds token t's id, slot and rank
+    TokInfo ti = token_info(a, lane);
+    if (w == 0 && lane == 0) s_bad = 0;
+    __syncthreads();
+    if (w == 0 && ti.bad) atomicMax(&s_bad, ti.bad);
+    __syncthreads();
+    if (s_bad) return;  // the combine launch rejects the batch
+    // item = the (8 (tile - NT) + w)-th (adapter, 16-rank block) of the batch,
+    // adapters in order of first occurrence
+    const int item = 8 * (tile - a.NT) + w;
+    uint64_t todo = __ballot(ti.id >= 0);
+    int seen = 0;
+    while (todo) {
+      const int leader = __builtin_ctzll(todo);
+      const int v = __shfl(ti.id, leader, 64);
+      const int r = __shfl(ti.rank, leader, 64);
+      const uint64_t m = __ballot(ti.id == v) & todo;
+      todo &= ~m;
+      const int nq = (r + 15) / 16;
+      if (item < seen + nq) {
+        const int slot = __shfl(ti.slot, leader, 64);
+        qb = item - seen;
+        members = m;
+        const int q = 16 * qb + r16;
+        row_ok = q < r;
+        row = a.pages + (size_t)slot * a.slot_stride + a.a_off + (size_t)(row_ok ? q : 0) * K + k0;
+        break;
+      }
+      seen += nq;
+    }
+  }
+  const bool active = row != nullptr;  // an A-tile wave past the last item has nothing to do
+  if (!active) row = a.X + k0;         // dummy in-bounds source, results discarded
+
+  // ---- loads: X chunk first (needed first), then the whole 16 x 512 slice ----
+  // X rows go straight to LDS, one 1 KB row per wave instruction (lane l
+  // writes bytes [16 l, 16 l + 16) of the row).  Rows >= T are not loaded
+  // (their MFMA output rows are discarded); in a short last chunk the lanes
+  // past the end read an in-bounds duplicate that meets zeroed W values.
+  static_assert(kDecodeChunk == 64 * 8, "one wave instruction per X row");
+  for (int r = w; r < T; r += kMainWaves)
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(a.X + (size_t)r * K + k0 + min(8 * lane, klen - 8)),
+        (__attribute__((address_space(3))) void*)(xs + r * kXs), 16, 0, 0);
+  // keep the issue order: X loads, then the slice, so waiting for X does not
+  // wait for the slice (the vector-memory counter retires in order)
+  __builtin_amdgcn_sched_barrier(0);
+  uint4 rw[kSteps];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) rw[s] = ld16(row + min(32 * s + 8 * g4, klen - 8));
+  __builtin_amdgcn_sched_barrier(0);
+  __syncthreads();
+  if (!active) return;
+
+  const int nm = (T + 15) / 16;
+  f32x4 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const int k = 32 * s + 8 * g4;
+    const bf16x8 wb = __builtin_bit_cast(bf16x8, keep_if(k < klen && row_ok, rw[s]));
+    // all four 16-token row blocks: rows >= T hold stale LDS and are never stored
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = mfma16(lds_bf16x8(xs + (16 * i + r16) * kXs + k), wb, acc[i]);
+  }
+
+  // ---- partial tile out: acc[i][e] is token 16 i + 4 g4 + e, row r16 of the block ----
+  if (!a_tile) {
+    if (row_ok) {
+      float* pp = a.part + (size_t)c * 64 * N + n0 + r16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i >= nm) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * i + 4 * g4 + e;
+          if (t < T) pp[(size_t)t * N] = acc[i][e];
+        }
+      }
+    }
+  } else if (row_ok) {
+    float* up = a.upart + (size_t)c * 64 * a.u_ld + 16 * qb + r16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i >= nm) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * i + 4 * g4 + e;
+        if ((members >> t) & 1ull) up[(size_t)t * a.u_ld] = acc[i][e];
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// combine: block = 16 tokens x 64 columns, thread = (token, 4 columns)
+constexpr int kCombThreads = 256;
+
+__global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
+  __shared__ float vsh[16][kMaxRank + 1];
+  __shared__ int t_slot[16], t_rank[16];
+  __shared__ float t_scale[16];
+  __shared__ int flag;
+  const int tid = threadIdx.x;
+  const int T = a.T, N = a.N, KS = a.KS;
+  const int t0 = blockIdx.y * 16;
+  if (a.lora) {
+    if (*a.status != 0) return;
+    if (tid == 0) flag = 0;
+    __syncthreads();
+    if (tid < 64) {
+      const TokInfo ti = token_info(a, tid);  // every token: strict-mode check
+      if (ti.bad) atomicMax(&flag, ti.bad);
+      if (tid >= t0 && tid < t0 + 16) {
+        t_slot[tid - t0] = ti.slot;
+        t_rank[tid - t0] = ti.rank;
+        t_scale[tid - t0] = ti.scale;
+      }
+    }
+    __syncthreads();
+    if (flag) {
+      if (tid == 0 && blockIdx.x == 0 && blockIdx.y == 0) atomicMax(a.status, flag);
+      return;  // strict mode: out untouched
+    }
+    // V[t][q] = (alpha / r) * sum of the shrink partials in chunk order
+    for (int idx = tid; idx < 16 * kMaxRank; idx += kCombThreads) {
+      const int r = idx / kMaxRank, q = idx % kMaxRank;
+      float v = 0.f;
+      if (t0 + r < T && q < t_rank[r]) {
+        const float* up = a.upart + (size_t)(t0 + r) * a.u_ld + q;
+        float u = up[0];
+        for (int c0 = 1; c0 < KS; c0 += 8) {
+          float pv[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pv[j] = up[(size_t)min(c0 + j, KS - 1) * 64 * a.u_ld];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (c0 + j < KS) u += pv[j];
+        }
+        v = t_scale[r] * u;
+      }
+      vsh[r][q] = v;
+    }
+    __syncthreads();
+  }
+  const int tr = tid >> 4, quad = tid & 15;
+  const int t = t0 + tr;
+  const int n = blockIdx.x * 64 + quad * 4;
+  if (t >= T || n >= N) return;
+  // base: chunk partials in chunk order (loads batched 8 at a time)
+  const float* pp = a.part + (size_t)t * N + n;
+  float4 s = *reinterpret_cast<const float4*>(pp);
+  for (int c0 = 1; c0 < KS; c0 += 8) {
+    float4 pv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pv[j] = *reinterpret_cast<const float4*>(pp + (size_t)min(c0 + j, KS - 1) * 64 * N);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (c0 + j < KS) {
+        s.x += pv[j].x;
+        s.y += pv[j].y;
+        s.z += pv[j].z;
+        s.w += pv[j].w;
+      }
+    }
+  }
+  if (a.lora && t_slot[tr] >= 0) {
+    const int rank = t_rank[tr];
+    const uint16_t* Bp = a.pages + (size_t)t_slot[tr] * a.slot_stride + a.b_off + n;
+    float e0 = 0.f, e1 = 0.f, e2 = 0.f, e3 = 0.f;
+    for (int q0 = 0; q0 < rank; q0 += 16) {
+      uint2 bv[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        bv[q] = *reinterpret_cast<const uint2*>(Bp + (size_t)min(q0 + q, rank - 1) * N);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const float v = q0 + q < rank ? vsh[tr][q0 + q] : 0.f;
+        e0 += v * lo_f(bv[q].x);
+        e1 += v * hi_f(bv[q].x);
+        e2 += v * lo_f(bv[q].y);
+        e3 += v * hi_f(bv[q].y);
+      }
+    }
+    s.x += e0;
+    s.y += e1;
+    s.z += e2;
+    s.w += e3;
+  }
+  const uint32_t o0 = (uint32_t)f32_to_bf16_bits(s.x) | ((uint32_t)f32_to_bf16_bits(s.y) << 16);
+  const uint32_t o1 = (uint32_t)f32_to_bf16_bits(s.z) | ((uint32_t)f32_to_bf16_bits(s.w) << 16);
+  *reinterpret_cast<uint2*>(a.out + (size_t)t * N + n) = make_uint2(o0, o1);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(decode_main, dim3((a.NT + a.n_atiles) * a.KS), dim3(kMainThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine, dim3((a.N + 63) / 64, (a.T + 15) / 16), dim3(kCombThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace hrg

@@ -87,6 +87,35 @@ struct GemmArgs {
   const int32_t* status;
 };
 
+// Decode path (T <= kDecodeMaxT): launch 1 computes the K-chunk partials of
+// the base GEMM (W tiles) and of the shrink (A tiles), launch 2 combines them
+// with the expand.  Workspace: part [KS][64][N] and upart [KS][64][u_ld] (fp32).
+constexpr int kDecodeMaxT = 64;
+constexpr int kDecodeTileRows = 128;  // rows per tile (8 waves x 16)
+constexpr int kDecodeChunk = 512;     // K per block
+
+struct DecodeArgs {
+  const uint16_t* X;      // [T][K]
+  const uint16_t* W;      // [N][K]
+  uint16_t* out;          // [T][N]
+  const int32_t* ids;     // [T]
+  int32_t T, N, K;
+  int32_t max_ids;
+  const int32_t* id2slot;
+  const int32_t* slot_rank;
+  const float* slot_scale;
+  const uint16_t* pages;
+  size_t slot_stride;
+  size_t a_off, b_off;
+  float* part;            // [KS][64][N]
+  float* upart;           // [KS][64][u_ld]
+  int32_t u_ld;
+  int32_t* status;
+  int32_t NT, n_atiles;   // W tiles, A tiles (0 on the base-only path)
+  int32_t KS;             // K chunks
+  int32_t lora;
+};
+
 struct PackArgs {
   const uint16_t* src;    // staged A (rows x rank) or B (rank x cols)
   uint16_t* dst;          // page [rmax][cols]
@@ -99,6 +128,7 @@ struct PackArgs {
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_shrink(const ShrinkArgs& a, int grid_tiles, int ksplit, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, bool lora, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 hipError_t launch_set_slot(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int32_t id,
                            int32_t slot, int32_t rank, float scale, hipStream_t s);

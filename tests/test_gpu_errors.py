@@ -130,6 +130,15 @@ def test_strict_mode_leaves_output_untouched(bad, status):
     p.apply(0, X, ok_ids, W, out)
     torch.cuda.synchronize()
     assert not torch.equal(out, sentinel)
+    # after the error the pool computes exactly what a fresh pool computes
+    q = _pool()
+    q.load_adapter(0, 4, 8.0, *_ab(4))
+    ref = torch.empty_like(out)
+    q.apply(0, X, ok_ids, W, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    assert q.status() == "OK"
+    q.close()
     p.close()
 
 

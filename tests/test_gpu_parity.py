@@ -64,11 +64,18 @@ def test_plan_adversarial_bit_exact(name):
     ids = np.asarray(PLAN_IDS[name], np.int32)
     wl = wk.small_workload(len(ids), 64, 64, max(16, int(ids.max()) + 1), 8, (8,))
     c = _case(wl, ids=ids, max_tokens=256)
-    c.apply(0)
-    got = c.pool.debug_read_plan()
+    plan = c.pool.plan_create()
+    c.pool.plan(c.ids, c.T, plan)
+    got = c.pool.debug_read_plan(plan)
     want = oracle.plan(ids, wl.n_adapters)
     for g, w in zip(got, want):
         assert g == w.tolist()
+    if c.T > 64:
+        # above the decode size an apply without a plan builds the pool's own
+        c.apply(0)
+        got = c.pool.debug_read_plan()
+        for g, w in zip(got, want):
+            assert g == w.tolist()
     assert c.pool.status() == "OK"
     c.close()
 
@@ -119,8 +126,12 @@ def test_plan_2000_distinct():
 # values: small ragged shapes that span several tiles
 # --------------------------------------------------------------------------
 RAGGED = [
-    # (T, d_in, d_out, ranks, max_rank, id_lo)
+    # (T, d_in, d_out, ranks, max_rank, id_lo); T <= 64 runs the one-launch decode kernel
     (1, 64, 64, (8,), 8, 0),
+    (17, 1032, 520, (64, 3, 17), 64, -1),
+    (48, 264, 2056, (16, 2), 16, -1),
+    (64, 4104, 200, (8, 16, 32, 64), 64, -1),
+    (64, 11008, 256, (16,), 16, 0),
     (3, 200, 136, (1, 5, 16), 16, -1),
     (64, 1024, 1024, (8,), 8, -1),
     (65, 520, 264, (16, 3), 16, -1),
@@ -227,13 +238,18 @@ def test_permutation_invariance_bit_exact():
     c.close()
 
 
-def test_determinism_bit_exact():
-    _say("[invariant] determinism")
-    c = _case(wk.WORKLOADS[4])
+@pytest.mark.parametrize("key", [2, 4])
+def test_determinism_bit_exact(key):
+    _say(f"[invariant] determinism, workload {key}")
+    c = _case(wk.WORKLOADS[key])
     a = c.apply(0)
-    b = c.apply(0)
+    outs = [c.apply(0) for _ in range(3)]
     torch.cuda.synchronize()
-    assert torch.equal(a, b)
+    for b in outs:
+        assert torch.equal(a, b)
+    base = [c.base_apply(0) for _ in range(2)]
+    torch.cuda.synchronize()
+    assert torch.equal(base[0], base[1])
     c.close()
 
 
