@@ -35,6 +35,7 @@ struct lora_pool_s {
   int32_t* id2slot = nullptr;        // [max_ids]
   int32_t* slot_rank = nullptr;      // [max_adapters]
   float* slot_scale = nullptr;       // [max_adapters]
+  int4* id_info = nullptr;           // [max_ids] {slot, rank, scale bits, 0}
   int32_t* status = nullptr;         // sticky device status
   uint16_t* staging = nullptr;       // one module's A or B as received
   float* upart = nullptr;            // [kMaxSplits][max_tokens][rpad]
@@ -145,9 +146,7 @@ lora_status_t decode_apply(lora_pool_s* P, int32_t module, const lora_bf16_t* X,
   a.N = N;
   a.K = K;
   a.max_ids = P->max_ids;
-  a.id2slot = P->id2slot;
-  a.slot_rank = P->slot_rank;
-  a.slot_scale = P->slot_scale;
+  a.id_info = P->id_info;
   a.pages = P->pages;
   a.slot_stride = P->slot_elems;
   a.a_off = P->a_off[module];
@@ -163,6 +162,7 @@ lora_status_t decode_apply(lora_pool_s* P, int32_t module, const lora_bf16_t* X,
     // A-tile items: (adapter, 16-rank block); at most min(T, resident) adapters
     const int loaded = P->max_adapters - (int)P->free_slots.size();
     a.n_atiles = ceil_div(std::min(T, loaded) * (P->rpad / 16), 8);
+    a.a_blocks = round_up(a.n_atiles * a.KS, 8);
   }
   return hrg::launch_decode(a, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
@@ -228,6 +228,7 @@ lora_status_t lora_pool_create(lora_pool_t* pool, int32_t max_adapters, int32_t 
             dmalloc(&P->id2slot, max_ids) == hipSuccess &&
             dmalloc(&P->slot_rank, max_adapters) == hipSuccess &&
             dmalloc(&P->slot_scale, max_adapters) == hipSuccess &&
+            dmalloc(&P->id_info, max_ids) == hipSuccess &&
             dmalloc(&P->status, 4) == hipSuccess &&
             dmalloc(&P->staging, max_dim * max_rank) == hipSuccess &&
             dmalloc(&P->upart, (size_t)hrg::kMaxSplits * P->split_stride) == hipSuccess;
@@ -251,6 +252,7 @@ lora_status_t lora_pool_create(lora_pool_t* pool, int32_t max_adapters, int32_t 
   P->h_slot_scale.assign(max_adapters, 0.f);
   for (int32_t i = 0; i < max_adapters; ++i) P->free_slots.insert(i);
   if (hrg::launch_clear_i32(P->id2slot, max_ids, -1, stream) != hipSuccess ||
+      hrg::launch_clear_i32(reinterpret_cast<int32_t*>(P->id_info), 4 * max_ids, -1, stream) != hipSuccess ||
       hrg::launch_clear_i32(P->slot_rank, max_adapters, 0, stream) != hipSuccess ||
       hrg::launch_clear_i32(reinterpret_cast<int32_t*>(P->slot_scale), max_adapters, 0, stream) != hipSuccess ||
       hrg::launch_clear_i32(P->status, 4, 0, stream) != hipSuccess ||
@@ -273,6 +275,7 @@ lora_status_t lora_pool_destroy(lora_pool_t P) {
   (void)hipFree(P->id2slot);
   (void)hipFree(P->slot_rank);
   (void)hipFree(P->slot_scale);
+  (void)hipFree(P->id_info);
   (void)hipFree(P->status);
   (void)hipFree(P->staging);
   (void)hipFree(P->upart);
@@ -308,7 +311,8 @@ lora_status_t lora_load_adapter(lora_pool_t P, int32_t id, int32_t rank, float a
     if (hrg::launch_pack(pa, stream) != hipSuccess) return LORA_ERR_HIP;
   }
   const float scale = alpha / (float)rank;
-  if (hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, id, slot, rank, scale, stream) !=
+  if (hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, id, slot, rank, scale,
+                           stream) !=
           hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess) {
     (void)hipGetLastError();
@@ -328,7 +332,7 @@ lora_status_t lora_unload_adapter(lora_pool_t P, int32_t id, hipStream_t stream)
   if (slot < 0) return LORA_ERR_NOT_LOADED;
   DeviceGuard g(P->device);
   if (hipStreamSynchronize(stream) != hipSuccess ||
-      hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, id, -1, 0, 0.f, stream) !=
+      hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, id, -1, 0, 0.f, stream) !=
           hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess) {
     (void)hipGetLastError();

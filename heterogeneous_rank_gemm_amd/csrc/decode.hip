@@ -65,21 +65,21 @@ __device__ __forceinline__ TokInfo token_info(const DecodeArgs& a, int t) {
     if (id < -1 || id >= a.max_ids) {
       ti.bad = kStatusIdRange;
     } else if (id >= 0) {
-      const int slot = a.id2slot[id];
-      if (slot < 0) {
+      const int4 e = a.id_info[id];  // {slot, rank, scale bits}: one load after ids
+      if (e.x < 0) {
         ti.bad = kStatusNotLoaded;
       } else {
         ti.id = id;
-        ti.slot = slot;
-        ti.rank = a.slot_rank[slot];
-        ti.scale = a.slot_scale[slot];
+        ti.slot = e.x;
+        ti.rank = e.y;
+        ti.scale = __builtin_bit_cast(float, e.z);
       }
     }
   }
   return ti;
 }
 
-__global__ __launch_bounds__(kMainThreads) void decode_main(DecodeArgs a) {
+__global__ __launch_bounds__(kMainThreads) __attribute__((amdgpu_waves_per_eu(4))) void decode_main(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[64 * kXs];
   __shared__ int s_bad;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -87,14 +87,26 @@ __global__ __launch_bounds__(kMainThreads) void decode_main(DecodeArgs a) {
   const int T = a.T, N = a.N, K = a.K;
   if (a.lora && *a.status != 0) return;
 
-  // XCD-aware order: the hardware hands block b to XCD (b mod 8); each XCD
-  // takes a contiguous run of (tile, chunk) pairs, so the chunks of a tile
-  // share that XCD's L2.
-  const int G = gridDim.x;
-  const int xcd = blockIdx.x % 8, qd = G / 8, rm = G % 8;
-  const int logical = xcd * qd + min(xcd, rm) + blockIdx.x / 8;
-  const int tile = logical / a.KS, c = logical % a.KS;
-  const bool a_tile = tile >= a.NT;
+  // Block order: the A blocks first (a_blocks, a multiple of 8, so they start
+  // early and spread over all XCDs round-robin), then the W blocks.  For the W
+  // blocks the hardware hands block b to XCD (b mod 8); each XCD takes a
+  // contiguous run of (tile, chunk) pairs so neighbouring tiles share its L2.
+  int tile, c;
+  bool a_tile;
+  if ((int)blockIdx.x < a.a_blocks) {
+    a_tile = true;
+    tile = a.NT + (int)blockIdx.x / a.KS;
+    c = (int)blockIdx.x % a.KS;
+    if (tile >= a.NT + a.n_atiles) return;  // padding block
+  } else {
+    a_tile = false;
+    const int g = (int)blockIdx.x - a.a_blocks;
+    const int G = a.NT * a.KS;
+    const int xcd = g % 8, qd = G / 8, rm = G % 8;
+    const int logical = xcd * qd + min(xcd, rm) + g / 8;
+    tile = logical / a.KS;
+    c = logical % a.KS;
+  }
   const int k0 = c * kDecodeChunk, klen = min(K, k0 + kDecodeChunk) - k0;
 
   // ---- this wave's 16 rows ----
@@ -121,14 +133,14 @@ __global__ __launch_bounds__(kMainThreads) void decode_main(DecodeArgs a) {
     uint64_t todo = __ballot(ti.id >= 0);
     int seen = 0;
     while (todo) {
-      const int leader = __builtin_ctzll(todo);
-      const int v = __shfl(ti.id, leader, 64);
-      const int r = __shfl(ti.rank, leader, 64);
+      const int leader = __builtin_ctzll(todo);  // wave-uniform: readlane, not an LDS shuffle
+      const int v = __builtin_amdgcn_readlane(ti.id, leader);
+      const int r = __builtin_amdgcn_readlane(ti.rank, leader);
       const uint64_t m = __ballot(ti.id == v) & todo;
       todo &= ~m;
       const int nq = (r + 15) / 16;
       if (item < seen + nq) {
-        const int slot = __shfl(ti.slot, leader, 64);
+        const int slot = __builtin_amdgcn_readlane(ti.slot, leader);
         qb = item - seen;
         members = m;
         const int q = 16 * qb + r16;
@@ -143,22 +155,28 @@ __global__ __launch_bounds__(kMainThreads) void decode_main(DecodeArgs a) {
   if (!active) row = a.X + k0;         // dummy in-bounds source, results discarded
 
   // ---- loads: X chunk first (needed first), then the whole 16 x 512 slice ----
-  // X rows go straight to LDS, one 1 KB row per wave instruction (lane l
-  // writes bytes [16 l, 16 l + 16) of the row).  Rows >= T are not loaded
-  // (their MFMA output rows are discarded); in a short last chunk the lanes
-  // past the end read an in-bounds duplicate that meets zeroed W values.
-  static_assert(kDecodeChunk == 64 * 8, "one wave instruction per X row");
-  for (int r = w; r < T; r += kMainWaves)
-    __builtin_amdgcn_global_load_lds(
-        (const void*)(a.X + (size_t)r * K + k0 + min(8 * lane, klen - 8)),
-        (__attribute__((address_space(3))) void*)(xs + r * kXs), 16, 0, 0);
-  // keep the issue order: X loads, then the slice, so waiting for X does not
-  // wait for the slice (the vector-memory counter retires in order)
+  // X goes through registers (8 x 16 bytes per thread) so that writing it to
+  // LDS waits only for the X loads; the slice's MFMAs then start as soon as
+  // their own step has landed (the vector-memory counter retires in order).
+  constexpr int kXLoads = 64 * (kDecodeChunk / 8) / kMainThreads;  // 8 per thread
+  uint4 xv[kXLoads];
+#pragma unroll
+  for (int i = 0; i < kXLoads; ++i) {
+    const int idx = tid + i * kMainThreads;
+    const int r = idx / (kDecodeChunk / 8), kc = (idx % (kDecodeChunk / 8)) * 8;
+    xv[i] = ld16(a.X + (size_t)min(r, T - 1) * K + k0 + min(kc, klen - 8));
+  }
   __builtin_amdgcn_sched_barrier(0);
   uint4 rw[kSteps];
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) rw[s] = ld16(row + min(32 * s + 8 * g4, klen - 8));
   __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < kXLoads; ++i) {
+    const int idx = tid + i * kMainThreads;
+    const int r = idx / (kDecodeChunk / 8), kc = (idx % (kDecodeChunk / 8)) * 8;
+    *reinterpret_cast<uint4*>(xs + r * kXs + kc) = keep_if(r < T && kc < klen, xv[i]);
+  }
   __syncthreads();
   if (!active) return;
 
@@ -233,6 +251,25 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
       if (tid == 0 && blockIdx.x == 0 && blockIdx.y == 0) atomicMax(a.status, flag);
       return;  // strict mode: out untouched
     }
+  }
+  const int tr = tid >> 4, quad = tid & 15;
+  const int t = t0 + tr;
+  const int n = blockIdx.x * 64 + quad * 4;
+  const bool mine = t < T && n < N;
+  // independent loads first: the chunk partials and the first 16 rows of B
+  const float* pp = a.part + (size_t)min(t, T - 1) * N + min(n, N - 4);
+  float4 pv[8];
+  const int slot = a.lora ? t_slot[tr] : -1;
+  const int rank = a.lora ? t_rank[tr] : 0;
+  const uint16_t* Bp = a.pages + (size_t)max(slot, 0) * a.slot_stride + a.b_off + min(n, N - 4);
+  uint2 bv[16];
+  if (slot >= 0) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) bv[q] = *reinterpret_cast<const uint2*>(Bp + (size_t)min(q, rank - 1) * N);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pv[j] = *reinterpret_cast<const float4*>(pp + (size_t)min(j, KS - 1) * 64 * N);
+  if (a.lora) {
     // V[t][q] = (alpha / r) * sum of the shrink partials in chunk order
     for (int idx = tid; idx < 16 * kMaxRank; idx += kCombThreads) {
       const int r = idx / kMaxRank, q = idx % kMaxRank;
@@ -241,12 +278,12 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
         const float* up = a.upart + (size_t)(t0 + r) * a.u_ld + q;
         float u = up[0];
         for (int c0 = 1; c0 < KS; c0 += 8) {
-          float pv[8];
+          float uv[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) pv[j] = up[(size_t)min(c0 + j, KS - 1) * 64 * a.u_ld];
+          for (int j = 0; j < 8; ++j) uv[j] = up[(size_t)min(c0 + j, KS - 1) * 64 * a.u_ld];
 #pragma unroll
           for (int j = 0; j < 8; ++j)
-            if (c0 + j < KS) u += pv[j];
+            if (c0 + j < KS) u += uv[j];
         }
         v = t_scale[r] * u;
       }
@@ -254,20 +291,18 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
     }
     __syncthreads();
   }
-  const int tr = tid >> 4, quad = tid & 15;
-  const int t = t0 + tr;
-  const int n = blockIdx.x * 64 + quad * 4;
-  if (t >= T || n >= N) return;
-  // base: chunk partials in chunk order (loads batched 8 at a time)
-  const float* pp = a.part + (size_t)t * N + n;
-  float4 s = *reinterpret_cast<const float4*>(pp);
-  for (int c0 = 1; c0 < KS; c0 += 8) {
-    float4 pv[8];
+  if (!mine) return;
+  // base: chunk partials in chunk order
+  float4 s = pv[0];
+  for (int c0 = 0; c0 < KS; c0 += 8) {
+    if (c0 > 0) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pv[j] = *reinterpret_cast<const float4*>(pp + (size_t)min(c0 + j, KS - 1) * 64 * N);
+      for (int j = 0; j < 8; ++j)
+        pv[j] = *reinterpret_cast<const float4*>(pp + (size_t)min(c0 + j, KS - 1) * 64 * N);
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (c0 + j < KS) {
+      if (c0 + j > 0 && c0 + j < KS) {
         s.x += pv[j].x;
         s.y += pv[j].y;
         s.z += pv[j].z;
@@ -275,15 +310,14 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
       }
     }
   }
-  if (a.lora && t_slot[tr] >= 0) {
-    const int rank = t_rank[tr];
-    const uint16_t* Bp = a.pages + (size_t)t_slot[tr] * a.slot_stride + a.b_off + n;
+  if (slot >= 0) {
     float e0 = 0.f, e1 = 0.f, e2 = 0.f, e3 = 0.f;
     for (int q0 = 0; q0 < rank; q0 += 16) {
-      uint2 bv[16];
+      if (q0 > 0) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q)
-        bv[q] = *reinterpret_cast<const uint2*>(Bp + (size_t)min(q0 + q, rank - 1) * N);
+        for (int q = 0; q < 16; ++q)
+          bv[q] = *reinterpret_cast<const uint2*>(Bp + (size_t)min(q0 + q, rank - 1) * N);
+      }
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const float v = q0 + q < rank ? vsh[tr][q0 + q] : 0.f;
@@ -304,7 +338,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(decode_main, dim3((a.NT + a.n_atiles) * a.KS), dim3(kMainThreads), 0, s, a);
+  hipLaunchKernelGGL(decode_main, dim3(a.a_blocks + a.NT * a.KS), dim3(kMainThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine, dim3((a.N + 63) / 64, (a.T + 15) / 16), dim3(kCombThreads), 0, s, a);

@@ -101,9 +101,7 @@ struct DecodeArgs {
   const int32_t* ids;     // [T]
   int32_t T, N, K;
   int32_t max_ids;
-  const int32_t* id2slot;
-  const int32_t* slot_rank;
-  const float* slot_scale;
+  const int4* id_info;    // [max_ids] {slot (-1: not resident), rank, scale bits, 0}
   const uint16_t* pages;
   size_t slot_stride;
   size_t a_off, b_off;
@@ -113,6 +111,7 @@ struct DecodeArgs {
   int32_t* status;
   int32_t NT, n_atiles;   // W tiles, A tiles (0 on the base-only path)
   int32_t KS;             // K chunks
+  int32_t a_blocks;       // blocks of the A tiles, n_atiles * KS rounded up to 8
   int32_t lora;
 };
 
@@ -130,8 +129,8 @@ hipError_t launch_shrink(const ShrinkArgs& a, int grid_tiles, int ksplit, hipStr
 hipError_t launch_gemm(const GemmArgs& a, bool lora, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
-hipError_t launch_set_slot(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int32_t id,
-                           int32_t slot, int32_t rank, float scale, hipStream_t s);
+hipError_t launch_set_slot(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
+                           int32_t id, int32_t slot, int32_t rank, float scale, hipStream_t s);
 hipError_t launch_clear_i32(int32_t* p, int32_t n, int32_t value, hipStream_t s);
 
 }  // namespace hrg

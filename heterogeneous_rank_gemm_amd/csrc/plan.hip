@@ -128,8 +128,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       uint64_t todo = __ballot(valid);
       int pos = 0;
       while (todo) {
-        const int leader = __builtin_ctzll(todo);
-        const int vb = __shfl(b, leader, 64);
+        const int leader = __builtin_ctzll(todo);  // wave-uniform
+        const int vb = __builtin_amdgcn_readlane(b, leader);
         const uint64_t m = __ballot(b == vb) & todo;
         const int cur = start[vb];
         if ((m >> lane) & 1ull) pos = cur + __popcll(m & ((1ull << lane) - 1ull));
@@ -206,7 +206,10 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-__global__ void set_slot_kernel(int32_t* id2slot, int32_t* slot_rank, float* slot_scale,
+// Routing-table update of one id: the id -> slot map, the per-slot rank and
+// scale, and the packed per-id entry {slot, rank, scale} the decode kernels
+// read with one load.
+__global__ void set_slot_kernel(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
                                 int32_t id, int32_t slot, int32_t rank, float scale) {
   if (threadIdx.x == 0) {
     if (slot >= 0) {
@@ -214,13 +217,14 @@ __global__ void set_slot_kernel(int32_t* id2slot, int32_t* slot_rank, float* slo
       slot_scale[slot] = scale;
     }
     id2slot[id] = slot;
+    id_info[id] = make_int4(slot, slot >= 0 ? rank : 0, __builtin_bit_cast(int, scale), 0);
   }
 }
 
-hipError_t launch_set_slot(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int32_t id,
-                           int32_t slot, int32_t rank, float scale, hipStream_t s) {
-  hipLaunchKernelGGL(set_slot_kernel, dim3(1), dim3(64), 0, s, id2slot, slot_rank, slot_scale, id,
-                     slot, rank, scale);
+hipError_t launch_set_slot(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
+                           int32_t id, int32_t slot, int32_t rank, float scale, hipStream_t s) {
+  hipLaunchKernelGGL(set_slot_kernel, dim3(1), dim3(64), 0, s, id2slot, slot_rank, slot_scale, id_info,
+                     id, slot, rank, scale);
   return hipGetLastError();
 }
 
