@@ -35,6 +35,11 @@ if ROOT not in sys.path:
 import workloads as wk  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+# Measured HBM traffic per apply, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+# (scaled by a plain copy of known size); valid only for the kernel source it
+# was measured on.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_llama2-7b-q_proj-T64_pmc_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "heterogeneous_rank_gemm_amd", "csrc", "decode.hip")
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "LoRA-linear tokens/sec at 1 GPU; % overhead vs base-only GEMM; % roofline"
 
@@ -143,6 +148,22 @@ def base_step(rep: Replica, hrg):
         hrg.lora_base_apply(h, j, rep.xin[j], rep.T, rep.W[j], rep.out[j])
 
 
+def measured_traffic(workload_name: str):
+    """HBM bytes per apply recorded for this workload, if the decode kernel
+    source is unchanged since the counters were taken; else None."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+        src_hash = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m = re.search(r"traffic_bytes_per_apply:\s*(\d+)\s+workload:\s*(\S+)\s+source_sha256:\s*([0-9a-f]+)", text)
+    if not m or m.group(2) != workload_name or m.group(3) != src_hash:
+        return None
+    return int(m.group(1))
+
+
 def time_steps(fn, reps, steps: int, warmup: int, torch, hrg) -> float:
     """Average seconds per step over `steps` steps, rotating replicas."""
     for i in range(warmup):
@@ -210,6 +231,11 @@ def main(argv=None) -> int:
     ap.add_argument("--rotate", type=int, default=8, help="independent copies of the state")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--phase", choices=["all", "lora", "base"], default="all",
+                    help="time only the LoRA apply or only the base-only GEMM (for profiling)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (x steps), to scale "
+                         "the rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
@@ -217,6 +243,16 @@ def main(argv=None) -> int:
         return 2
 
     import torch
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n,
+                          "launches": args.steps}), flush=True)
+        return 0
     import heterogeneous_rank_gemm_amd as hrg
 
     wl = wk.WORKLOADS[args.workload]
@@ -227,6 +263,14 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     print("[bench] state resident; timing", file=sys.stderr, flush=True)
 
+    if args.phase == "lora":
+        t_step = time_steps(lora_step, reps, args.steps, args.warmup, torch, hrg)
+        print(json.dumps({"phase": "lora", "ms_per_step": t_step * 1e3}), flush=True)
+        return 0
+    if args.phase == "base":
+        t_base = time_steps(base_step, reps, args.steps, args.warmup, torch, hrg)
+        print(json.dumps({"phase": "base", "ms_per_step": t_base * 1e3}), flush=True)
+        return 0
     t_step = time_steps(lora_step, reps, args.steps, args.warmup, torch, hrg)
     t_apply = time_steps(apply_only, reps, args.steps, args.warmup, torch, hrg)
     t_base = time_steps(base_step, reps, args.steps, args.warmup, torch, hrg)
@@ -244,13 +288,18 @@ def main(argv=None) -> int:
     hbm_bound = (bb + lb) / (HBM_PEAK_GBS * 1e9) >= fl / (MFMA_BF16_PEAK_TFS * 1e12)
     if hbm_bound:
         achieved = (bb + lb) / n_launch / (t_apply / n_launch) / 1e9
+        traffic = measured_traffic(wl.name) if wl.T <= DECODE_MAX_T else None
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "lora_apply = decode_main + decode_combine" if wl.T <= DECODE_MAX_T
+                else "lora_apply = shrink_kernel + gemm_kernel",
+                "algorithmic_bytes_per_apply": round((bb + lb) / n_launch)}
     else:
         achieved = fl / n_launch / (t_apply / n_launch) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
-                "traffic": None}
+                "traffic": None, "kernel": "lora_apply = shrink_kernel + gemm_kernel",
+                "algorithmic_flops_per_apply": round(fl / n_launch)}
 
     cpu = None
     if not args.no_cpu_baseline:
