@@ -38,8 +38,10 @@ struct lora_pool_s {
   int4* id_info = nullptr;           // [max_ids] {slot, rank, scale bits, 0}
   int32_t* status = nullptr;         // sticky device status
   uint16_t* staging = nullptr;       // one module's A or B as received
-  float* upart = nullptr;            // [kMaxSplits][max_tokens][rpad]
+  float* upart = nullptr;            // [kMaxSplits][max_tokens][rpad] shrink partial planes
   size_t split_stride = 0;
+  uint16_t* v_hi = nullptr;          // [max_tokens][rpad] s * U, bf16 high part (sorted rows)
+  uint16_t* v_lo = nullptr;          // [max_tokens][rpad] bf16 low part
   // decode-path workspace
   float* dec_part = nullptr;         // [ceil(max d_in / 512)][64][max d_out] base partials
   float* dec_upart = nullptr;        // [ceil(max d_in / 512)][64][rpad] shrink partials
@@ -217,7 +219,7 @@ lora_status_t lora_pool_create(lora_pool_t* pool, int32_t max_adapters, int32_t 
     P->a_off.push_back(off);
     off += (size_t)max_rank * d_in[m];
     P->b_off.push_back(off);
-    off += (size_t)max_rank * d_out[m];
+    off += (size_t)P->rpad * d_out[m];  // B^T in 16-rank chunks
     max_dim = std::max<size_t>(max_dim, std::max(d_in[m], d_out[m]));
   }
   // keep every slot 256-byte aligned
@@ -231,7 +233,9 @@ lora_status_t lora_pool_create(lora_pool_t* pool, int32_t max_adapters, int32_t 
             dmalloc(&P->id_info, max_ids) == hipSuccess &&
             dmalloc(&P->status, 4) == hipSuccess &&
             dmalloc(&P->staging, max_dim * max_rank) == hipSuccess &&
-            dmalloc(&P->upart, (size_t)hrg::kMaxSplits * P->split_stride) == hipSuccess;
+            dmalloc(&P->upart, (size_t)hrg::kMaxSplits * P->split_stride) == hipSuccess &&
+            dmalloc(&P->v_hi, (size_t)max_tokens * P->rpad) == hipSuccess &&
+            dmalloc(&P->v_lo, (size_t)max_tokens * P->rpad) == hipSuccess;
   size_t max_din = 0, max_dout = 0;
   for (int32_t m = 0; m < n_modules; ++m) {
     max_din = std::max<size_t>(max_din, d_in[m]);
@@ -279,6 +283,8 @@ lora_status_t lora_pool_destroy(lora_pool_t P) {
   (void)hipFree(P->status);
   (void)hipFree(P->staging);
   (void)hipFree(P->upart);
+  (void)hipFree(P->v_hi);
+  (void)hipFree(P->v_lo);
   (void)hipFree(P->dec_upart);
   (void)hipFree(P->dec_part);
   delete P;
@@ -303,11 +309,11 @@ lora_status_t lora_load_adapter(lora_pool_t P, int32_t id, int32_t rank, float a
     hrg::PackArgs pa{};
     if (hipMemcpyAsync(P->staging, A[m], na * 2, hipMemcpyDefault, stream) != hipSuccess)
       return (void)hipGetLastError(), LORA_ERR_HIP;
-    pa = {P->staging, base + P->a_off[m], rank, P->max_rank, P->d_in[m], 1};
+    pa = {P->staging, base + P->a_off[m], rank, P->max_rank, P->d_in[m], 0};
     if (hrg::launch_pack(pa, stream) != hipSuccess) return LORA_ERR_HIP;
     if (hipMemcpyAsync(P->staging, B[m], nb * 2, hipMemcpyDefault, stream) != hipSuccess)
       return (void)hipGetLastError(), LORA_ERR_HIP;
-    pa = {P->staging, base + P->b_off[m], rank, P->max_rank, P->d_out[m], 0};
+    pa = {P->staging, base + P->b_off[m], rank, P->rpad, P->d_out[m], 1};
     if (hrg::launch_pack(pa, stream) != hipSuccess) return LORA_ERR_HIP;
   }
   const float scale = alpha / (float)rank;
@@ -397,6 +403,8 @@ static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t
   DeviceGuard g(P->device);
   const int K = P->d_in[module], N = P->d_out[module];
   if (T <= hrg::kDecodeMaxT) return decode_apply(P, module, X, ids, T, W, out, lora, stream);
+  // the batched path addresses X with 32-bit byte offsets
+  if ((size_t)T * K * 2 > (size_t)INT32_MAX) return LORA_ERR_INVALID_ARG;
   hrg::GemmArgs ga{};
   ga.X = X;
   ga.W = W;
@@ -407,7 +415,7 @@ static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t
   ga.status = P->status;
   if (!lora) {
     ga.perm = nullptr;
-    return hrg::launch_gemm(ga, false, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+    return hrg::launch_prefill(ga, false, -1, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
   }
   lora_plan_s* pl = plan;
   if (!pl) {
@@ -430,6 +438,7 @@ static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t
   sa.tile_seg = pl->tab.tile_seg;
   sa.tile_row0 = pl->tab.tile_row0;
   sa.counts = pl->tab.counts;
+  sa.seg_scale = pl->tab.seg_scale;
   sa.pages = P->pages;
   sa.slot_stride = P->slot_elems;
   sa.a_off = P->a_off[module];
@@ -437,23 +446,24 @@ static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t
   sa.split_stride = P->split_stride;
   sa.u_ld = P->rpad;
   sa.kchunk = kchunk;
+  sa.row_seg = pl->tab.row_seg;
+  sa.v_hi = P->v_hi;
+  sa.v_lo = P->v_lo;
   sa.status = P->status;
-  if (hrg::launch_shrink(sa, grid_tiles, ksplit, stream) != hipSuccess) return LORA_ERR_HIP;
+  if (hrg::launch_shrink(sa, grid_tiles, ksplit, T, stream) != hipSuccess) return LORA_ERR_HIP;
   ga.perm = pl->tab.perm;
-  ga.upart = P->upart;
-  ga.split_stride = P->split_stride;
+  ga.v_hi = P->v_hi;
+  ga.v_lo = P->v_lo;
   ga.u_ld = P->rpad;
-  ga.nsplit = ksplit;
   ga.row_seg = pl->tab.row_seg;
   ga.seg_id = pl->tab.seg_id;
   ga.seg_off = pl->tab.seg_off;
   ga.seg_slot = pl->tab.seg_slot;
   ga.seg_rank = pl->tab.seg_rank;
-  ga.seg_scale = pl->tab.seg_scale;
   ga.pages = P->pages;
   ga.slot_stride = P->slot_elems;
   ga.b_off = P->b_off[module];
-  return hrg::launch_gemm(ga, true, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+  return hrg::launch_prefill(ga, true, -1, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
 lora_status_t lora_apply(lora_pool_t P, int32_t module, const lora_bf16_t* X, const int32_t* ids,

@@ -261,11 +261,13 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
   float4 pv[8];
   const int slot = a.lora ? t_slot[tr] : -1;
   const int rank = a.lora ? t_rank[tr] : 0;
-  const uint16_t* Bp = a.pages + (size_t)max(slot, 0) * a.slot_stride + a.b_off + min(n, N - 4);
-  uint2 bv[16];
+  // B^T page in 16-rank chunks [rpad/16][N][16]: the 4 columns' first chunk is
+  // 64 contiguous values (ranks past the adapter's rank are zero)
+  const uint16_t* Bp = a.pages + (size_t)max(slot, 0) * a.slot_stride + a.b_off + (size_t)min(n, N - 4) * 16;
+  uint4 bv[8];
   if (slot >= 0) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) bv[q] = *reinterpret_cast<const uint2*>(Bp + (size_t)min(q, rank - 1) * N);
+    for (int k = 0; k < 8; ++k) bv[k] = *reinterpret_cast<const uint4*>(Bp + 8 * k);
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) pv[j] = *reinterpret_cast<const float4*>(pp + (size_t)min(j, KS - 1) * 64 * N);
@@ -311,26 +313,34 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
     }
   }
   if (slot >= 0) {
-    float e0 = 0.f, e1 = 0.f, e2 = 0.f, e3 = 0.f;
-    for (int q0 = 0; q0 < rank; q0 += 16) {
-      if (q0 > 0) {
+    float e[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; 16 * c < rank; ++c) {
+      if (c > 0) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q)
-          bv[q] = *reinterpret_cast<const uint2*>(Bp + (size_t)min(q0 + q, rank - 1) * N);
+        for (int k = 0; k < 8; ++k) bv[k] = *reinterpret_cast<const uint4*>(Bp + (size_t)c * N * 16 + 8 * k);
       }
+      const float* v = &vsh[tr][16 * c];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const float v = q0 + q < rank ? vsh[tr][q0 + q] : 0.f;
-        e0 += v * lo_f(bv[q].x);
-        e1 += v * hi_f(bv[q].x);
-        e2 += v * lo_f(bv[q].y);
-        e3 += v * hi_f(bv[q].y);
+      for (int col = 0; col < 4; ++col) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint4 u = bv[2 * col + h];
+          const float* vh = v + 8 * h;
+          e[col] += vh[0] * lo_f(u.x);
+          e[col] += vh[1] * hi_f(u.x);
+          e[col] += vh[2] * lo_f(u.y);
+          e[col] += vh[3] * hi_f(u.y);
+          e[col] += vh[4] * lo_f(u.z);
+          e[col] += vh[5] * hi_f(u.z);
+          e[col] += vh[6] * lo_f(u.w);
+          e[col] += vh[7] * hi_f(u.w);
+        }
       }
     }
-    s.x += e0;
-    s.y += e1;
-    s.z += e2;
-    s.w += e3;
+    s.x += e[0];
+    s.y += e[1];
+    s.z += e[2];
+    s.w += e[3];
   }
   const uint32_t o0 = (uint32_t)f32_to_bf16_bits(s.x) | ((uint32_t)f32_to_bf16_bits(s.y) << 16);
   const uint32_t o1 = (uint32_t)f32_to_bf16_bits(s.z) | ((uint32_t)f32_to_bf16_bits(s.w) << 16);

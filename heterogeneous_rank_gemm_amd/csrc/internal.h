@@ -54,35 +54,37 @@ struct ShrinkArgs {
   const int32_t* tile_seg;
   const int32_t* tile_row0;
   const int32_t* counts;
+  const float* seg_scale;
   const uint16_t* pages;  // A^T page of (slot, module): pages + slot*slot_stride + a_off, [rmax][K]
   size_t slot_stride;
   size_t a_off;
-  float* upart;           // [split][T_cap][u_ld]
+  float* upart;           // [split][T_cap][u_ld] fp32 partial planes
   size_t split_stride;
   int32_t u_ld;
   int32_t kchunk;
+  const int32_t* row_seg;
+  uint16_t* v_hi;         // [T_cap][u_ld] bf16 high part of s * U (sorted rows)
+  uint16_t* v_lo;         // [T_cap][u_ld] bf16 low part, s * U - hi
   const int32_t* status;
 };
 
 struct GemmArgs {
-  const uint16_t* X;      // [T][K]
+  const uint16_t* X;      // [T][K], T * K * 2 < 2^31
   const uint16_t* W;      // [N][K]
   uint16_t* out;          // [T][N]
   int32_t T, N, K;
   const int32_t* perm;    // sorted row -> token; nullptr = identity (base-only)
-  // LoRA epilogue (unused by the base-only instantiation)
-  const float* upart;
-  size_t split_stride;
+  // expand (unused by the base-only instantiation)
+  const uint16_t* v_hi;   // [T_cap][u_ld] s * U, bf16 high part, sorted rows
+  const uint16_t* v_lo;   // [T_cap][u_ld] bf16 low part
   int32_t u_ld;
-  int32_t nsplit;
   const int32_t* row_seg;
   const int32_t* seg_id;
   const int32_t* seg_off;
   const int32_t* seg_slot;
   const int32_t* seg_rank;
-  const float* seg_scale;
-  const uint16_t* pages;  // B page of (slot, module): pages + slot*slot_stride + b_off, [rmax][N]
-  size_t slot_stride;
+  const uint16_t* pages;  // B^T page of (slot, module): pages + slot*slot_stride + b_off,
+  size_t slot_stride;     //   16-rank chunks [rpad/16][N][16]
   size_t b_off;
   const int32_t* status;
 };
@@ -115,18 +117,26 @@ struct DecodeArgs {
   int32_t lora;
 };
 
+// Page layouts inside a slot (rows past the adapter's rank are zero):
+//   A page: A^T, rank-major [rmax][d_in]          (pack mode 0, src d_in x rank)
+//   B page: B^T in 16-rank chunks [rpad/16][d_out][16], element (q, n) at
+//           (q / 16) * d_out * 16 + n * 16 + q % 16  (pack mode 1, src rank x d_out)
 struct PackArgs {
-  const uint16_t* src;    // staged A (rows x rank) or B (rank x cols)
-  uint16_t* dst;          // page [rmax][cols]
-  int32_t rank, rmax;
-  int32_t cols;           // d_in for A (transposed), d_out for B
-  int32_t transpose;      // 1: src is cols x rank (A), 0: src is rank x cols (B)
+  const uint16_t* src;    // staged A (d_in x rank) or B (rank x d_out), row-major
+  uint16_t* dst;
+  int32_t rank, rows;     // true rank; page rows (rmax for A, rpad for B)
+  int32_t cols;           // d_in for A, d_out for B
+  int32_t mode;           // 0: A page, 1: B page
 };
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
-hipError_t launch_shrink(const ShrinkArgs& a, int grid_tiles, int ksplit, hipStream_t s);
-hipError_t launch_gemm(const GemmArgs& a, bool lora, hipStream_t s);
+// Shrink partial planes, then the split reduction into V (two launches).
+hipError_t launch_shrink(const ShrinkArgs& a, int grid_tiles, int ksplit, int T, hipStream_t s);
+// shape < 0 picks the tile shape from (T, N); 0..3 force 256x256, 256x128,
+// 128x256, 128x128 (tokens x columns).  Every shape gives the same bits.
+hipError_t launch_prefill(const GemmArgs& a, bool lora, int shape, hipStream_t s);
+int prefill_choose(int T, int N);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 hipError_t launch_set_slot(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,

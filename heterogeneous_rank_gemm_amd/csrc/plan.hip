@@ -119,23 +119,31 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __syncthreads();
 
   if (wave == 0) {
-    // 4a. stable placement, 64 tokens at a time in index order.  Within a
-    // chunk, lanes holding the same id are ranked by lane (= index) order.
+    // 4a. stable placement, 64 tokens at a time in index order.  The ballot
+    // loop only groups the lanes by id (leader = lowest lane, rank = lanes of
+    // the group below); then every group leader claims its run of positions
+    // with one LDS atomic and the members read the base from their leader.
+    // Chunks are placed one after another, so equal ids keep index order.
     for (int base = 0; base < T; base += 64) {
       const int t = base + lane;
       const bool valid = t < T;
       const int b = valid ? a.ids[t] + 1 : -1;
       uint64_t todo = __ballot(valid);
-      int pos = 0;
+      int leader = 0, rank = 0, cnt = 0;
       while (todo) {
-        const int leader = __builtin_ctzll(todo);  // wave-uniform
-        const int vb = __builtin_amdgcn_readlane(b, leader);
+        const int ld = __builtin_ctzll(todo);  // wave-uniform
+        const int vb = __builtin_amdgcn_readlane(b, ld);
         const uint64_t m = __ballot(b == vb) & todo;
-        const int cur = start[vb];
-        if ((m >> lane) & 1ull) pos = cur + __popcll(m & ((1ull << lane) - 1ull));
-        if (lane == leader) start[vb] = cur + __popcll(m);
+        if ((m >> lane) & 1ull) {
+          leader = ld;
+          rank = __popcll(m & ((1ull << lane) - 1ull));
+          cnt = __popcll(m);
+        }
         todo &= ~m;
       }
+      int first = 0;
+      if (valid && lane == leader) first = atomicAdd(&start[b], cnt);
+      const int pos = __shfl(first, leader, 64) + rank;
       if (valid) {
         a.tab.perm[pos] = t;
         a.tab.inv[t] = pos;
@@ -184,23 +192,32 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
 // ---------------------------------------------------------------------------
 // Small kernels of the load / unload path.
 
-// Writes one adapter page: dst[q][c] for q < rmax, c < cols.  Rows q >= rank
-// are zero ("mixed ranks are aligned to the maximum rank", vLLM chapter
-// "Multi-LoRA hot-plug", performance notes).  A arrives d_in x r and is
-// stored transposed (rank-major, r x d_in); B arrives r x d_out as is.
+// Writes one adapter page.  Ranks q >= rank are zero ("mixed ranks are
+// aligned to the maximum rank", vLLM chapter "Multi-LoRA hot-plug",
+// performance notes).  A arrives d_in x r and is stored rank-major (A^T,
+// rows x d_in); B arrives r x d_out and is stored as B^T in 16-rank chunks
+// (rows/16 x d_out x 16), so a 16-byte read gives 8 ranks of one column.
 __global__ void pack_kernel(PackArgs a) {
-  const size_t n = (size_t)a.rmax * a.cols;
+  const size_t n = (size_t)a.rows * a.cols;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x) {
-    const int q = (int)(i / a.cols), c = (int)(i % a.cols);
+    int q, c;
+    if (a.mode == 0) {  // A^T [rows][cols]
+      q = (int)(i / a.cols);
+      c = (int)(i % a.cols);
+    } else {  // B^T chunks [rows/16][cols][16]
+      const size_t chunk = i / ((size_t)a.cols * 16), rem = i % ((size_t)a.cols * 16);
+      c = (int)(rem / 16);
+      q = (int)(chunk * 16 + rem % 16);
+    }
     uint16_t v = 0;
-    if (q < a.rank) v = a.transpose ? a.src[(size_t)c * a.rank + q] : a.src[(size_t)q * a.cols + c];
+    if (q < a.rank) v = a.mode == 0 ? a.src[(size_t)c * a.rank + q] : a.src[(size_t)q * a.cols + c];
     a.dst[i] = v;
   }
 }
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
-  const size_t n = (size_t)a.rmax * a.cols;
+  const size_t n = (size_t)a.rows * a.cols;
   const int grid = (int)std::min<size_t>((n + 255) / 256, 4096);
   hipLaunchKernelGGL(pack_kernel, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();

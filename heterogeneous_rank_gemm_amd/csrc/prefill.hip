@@ -1,0 +1,392 @@
+// Batched path (T > 64): one tiled bf16 MFMA GEMM per linear,
+//
+//   out[t, :] = bf16( s_i (U_t B_i)  +  X[t, :] W^T ),   i = ids[t],
+//
+// i.e. the LoRA-Land formula (section "2. multi-LoRA batch scheduling"): the
+// shared base product plus every token's own low-rank term, rounded once.  The
+// low-rank term enters as the accumulator's starting value ("expand first"),
+// then the base product is accumulated on top in K order.  A row's arithmetic
+// depends only on its own data (never on its neighbours in the tile), so id -1
+// rows equal the base-only call bit for bit and rows may be permuted freely.
+//
+// Tile: BM tokens x BN output columns, K in steps of 64, 4 waves in a 2 x 2
+// grid, each wave (BN/2) x (BM/2) as 32x32x16 MFMA blocks.  The MFMA
+// A-operand is the W tile and the B-operand the X tile, so a lane ends up
+// with 4 consecutive output columns of one token (8-byte stores).
+//
+// Operands move HBM -> LDS with buffer_load ... lds (no register staging)
+// into two stages that live in separate LDS arrays: the compiler then knows
+// the reads of one stage never wait for the DMA into the other.  One barrier
+// per K-step of 64 publishes the next stage; the fragment reads of a stage
+// are spread over the MFMAs of the step before, and the DMA of the step after
+// next is spread over the first 16-deep MFMA group.  LDS rows are 128 bytes,
+// swizzled as chunk ^ (row & 7) ^ ((row >> 3) & 1), which keeps ds_read_b128
+// free of bank conflicts.
+//
+// Out-of-range rows and the K tail read through the buffer resource's range
+// check (zeros), so the loop has no branches.  K-steps past K (when their
+// count is odd) add exact zeros.
+#include "common.h"
+#include "internal.h"
+
+namespace hrg {
+namespace prefill_detail {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+constexpr int kBK = 64;
+constexpr uint32_t kOob = 0x80000000u;  // buffer offset beyond every operand (< 2 GiB)
+
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ __forceinline__ bf16x8 masked(bool keep, uint4 v) {
+  const uint32_t m = keep ? 0xffffffffu : 0u;
+  return __builtin_bit_cast(bf16x8, make_uint4(v.x & m, v.y & m, v.z & m, v.w & m));
+}
+
+// XCD-aware tile order: workgroup b runs on XCD (b mod 8); each XCD gets a
+// contiguous range of logical tiles, walked in groups of 8 token-tiles so that
+// neighbours share X and W rows in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int b, int nblocks, int tiles_m, int tiles_n, int& tm,
+                                            int& tn) {
+  constexpr int kXcd = 8, kGroupM = 8;
+  const int xcd = b % kXcd, idx = b / kXcd;
+  const int q = nblocks / kXcd, r = nblocks % kXcd;
+  const int logical = xcd * q + min(xcd, r) + idx;
+  const int per_group = kGroupM * tiles_n;
+  const int g = logical / per_group;
+  const int first_m = g * kGroupM;
+  const int gsize = min(tiles_m - first_m, kGroupM);
+  const int in = logical % per_group;
+  tm = first_m + in % gsize;
+  tn = in / gsize;
+}
+
+// Scheduling hint: kM MFMAs with kX instructions of class kMask spread
+// evenly between them (0x020 = global/buffer load, 0x100 = LDS read).
+template <int kM, int kX, int kMask, int Q = 0>
+__device__ __forceinline__ void interleave() {
+  if constexpr (Q < kM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int n = kX * (Q + 1) / kM - kX * Q / kM;
+    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(kMask, n, 0);
+    interleave<kM, kX, kMask, Q + 1>();
+  }
+}
+
+// Issues one K-step (64 deep) of the W and X tiles into an LDS stage.  A lane
+// whose 16-byte chunk lies past K reads out of range (zeros).  (A helper
+// rather than a lambda: with hipcc, a lambda that captures a buffer resource
+// inside a template kernel makes the host pass drop the kernel's launch stub.)
+template <int NWB, int NXB>
+__device__ __forceinline__ void dma_issue(__amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rx, uint16_t* ws,
+                                          uint16_t* xs, const uint32_t* woff, const uint32_t* xoff, int wid,
+                                          int c0, int K, int k0) {
+  const uint32_t kb0 = (uint32_t)(k0 + c0 * 8 >= K) << 31;
+  const uint32_t kb1 = (uint32_t)(k0 + (c0 ^ 1) * 8 >= K) << 31;
+  const uint32_t k2 = 2u * (uint32_t)k0;
+#pragma unroll
+  for (int i = 0; i < NWB; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t*)(ws + (wid * NWB + i) * 512), 16,
+                                             (woff[i] + k2) | ((i & 1) ? kb1 : kb0), 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < NXB; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(xs + (wid * NXB + i) * 512), 16,
+                                             (xoff[i] + k2) | ((i & 1) ? kb1 : kb0), 0, 0, 0);
+}
+
+}  // namespace prefill_detail
+using namespace prefill_detail;
+
+// QC: rank chunks of 16 held per segment in the expand (0 for base-only).
+template <int BM, int BN, bool LORA, int QC>
+__global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
+  constexpr int FM = BM / 64, FN = BN / 64;    // 32x32 blocks per wave (tokens, columns)
+  constexpr int NXB = BM / 32, NWB = BN / 32;  // 1-KB DMA blocks per wave and stage
+  __shared__ __attribute__((aligned(16))) uint16_t w0[BN * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t x0[BM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t w1[BN * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t x1[BM * kBK];
+
+  if constexpr (LORA) {
+    if (*a.status != 0) return;  // strict mode: a failed plan leaves out untouched
+  }
+  const int T = a.T, N = a.N, K = a.K;
+  const int tiles_m = (T + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int l = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wn = wid & 1, wm = wid >> 1;
+
+  // ---- DMA addressing: wave wid, instruction i covers rows 8b..8b+7 of block b
+  // (b = wid * NB + i); lane l fetches row 8b + l/8, 16-byte chunk
+  // (l & 7) ^ swz(row) so that the lane-ordered LDS write lands swizzled.
+  const uint16_t* wtile = a.W + (size_t)n0 * K;
+  const int wrows = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc((void*)wtile, (short)0, wrows * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)a.X, (short)0, T * K * 2, 0x00020000);
+  const int c0 = (l & 7) ^ (l >> 3);  // chunk of even blocks; odd blocks fetch c0 ^ 1
+  uint32_t woff[NWB], xoff[NXB];
+#pragma unroll
+  for (int i = 0; i < NWB; ++i) {
+    const int row = 8 * (wid * NWB + i) + (l >> 3);
+    woff[i] = row < wrows ? (uint32_t)(row * K + (c0 ^ (i & 1)) * 8) * 2u : kOob;
+  }
+#pragma unroll
+  for (int i = 0; i < NXB; ++i) {
+    const int p = m0 + 8 * (wid * NXB + i) + (l >> 3);
+    const int tok = p < T ? (a.perm ? a.perm[p] : p) : 0;
+    xoff[i] = p < T ? (uint32_t)(tok * K + (c0 ^ (i & 1)) * 8) * 2u : kOob;
+  }
+  auto issue = [&](uint16_t* ws, uint16_t* xs, int k0) __attribute__((always_inline)) {
+    dma_issue<NWB, NXB>(rw, rx, ws, xs, woff, xoff, wid, c0, K, k0);
+  };
+
+  f32x16 acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // the first K-step's DMA goes out before the expand, so its latency and
+  // the expand's page loads overlap
+  issue(w0, x0, 0);
+
+  if constexpr (LORA) {
+    // ---- expand first: acc = s_i * (U_t B_i) for every token of an adapter
+    // segment.  V = s U arrives from the shrink as bf16 hi + lo parts
+    // (V ~= hi + lo to about 2^-16); the B page is stored transposed in
+    // 16-rank chunks, [rpad/16][N][16], so both operands are 16-byte reads.
+    // Per 32-row block: V is loaded once (all chunks); the B fragments of the
+    // next (segment, chunk pair) are loaded while the current one's MFMAs run.
+    const int qc_pool = a.u_ld >> 4;
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int rb = m0 + wm * (BM / 2) + 32 * j;  // first sorted row of this 32-row block
+      if (rb < T) {
+        const int p = rb + (l & 31);
+        const int pc = min(p, T - 1);
+        bf16x8 vh[QC], vl[QC];
+#pragma unroll
+        for (int qc = 0; qc < QC; ++qc) {
+          const size_t e = (size_t)pc * a.u_ld + 16 * qc + 8 * (l >> 5);
+          if (qc < qc_pool) {
+            vh[qc] = __builtin_bit_cast(bf16x8, ld16(a.v_hi + e));
+            vl[qc] = __builtin_bit_cast(bf16x8, ld16(a.v_lo + e));
+          } else {
+            vh[qc] = zero_bf16x8();
+            vl[qc] = zero_bf16x8();
+          }
+        }
+        const int s_last = a.row_seg[min(rb + 31, T - 1)];
+        int sg = a.row_seg[rb];
+        if (a.seg_id[sg] < 0) ++sg;  // only the first segment can be the base run
+        // work items (segment, first chunk cb), QB chunks each, double-buffered
+        constexpr int QB = QC < 2 ? QC : 2;
+        bf16x8 b0[QB][FN], b1[QB][FN];
+        auto load_b = [&](bf16x8 (&bb)[QB][FN], int s, int cb) __attribute__((always_inline)) {
+          const int nqc = (a.seg_rank[s] + 15) >> 4;
+          const uint16_t* bt = a.pages + (size_t)a.seg_slot[s] * a.slot_stride + a.b_off;
+#pragma unroll
+          for (int qc = 0; qc < QB; ++qc) {
+            if (cb + qc < nqc) {
+#pragma unroll
+              for (int i = 0; i < FN; ++i) {
+                const int n = min(n0 + wn * (BN / 2) + 32 * i + (l & 31), N - 1);
+                bb[qc][i] = __builtin_bit_cast(
+                    bf16x8, ld16(bt + ((size_t)(cb + qc) * N + n) * 16 + 8 * (l >> 5)));
+              }
+            }
+          }
+        };
+        auto apply_b = [&](const bf16x8 (&bb)[QB][FN], int s, int cb) __attribute__((always_inline)) {
+          const bool in = p >= a.seg_off[s] && p < a.seg_off[s + 1];
+          const int nqc = (a.seg_rank[s] + 15) >> 4;
+          const uint32_t m = in ? 0xffffffffu : 0u;
+          const uint32_t lo_half = cb == 0 ? 0xffffffffu : 0u;  // chunk cb + qc: qc or qc + 2
+#pragma unroll
+          for (int qc = 0; qc < QB; ++qc) {
+            if (cb + qc < nqc) {
+              uint4 h = __builtin_bit_cast(uint4, vh[qc]), o = __builtin_bit_cast(uint4, vl[qc]);
+              if constexpr (QC > QB) {
+                const uint4 h2 = __builtin_bit_cast(uint4, vh[qc + QB]);
+                const uint4 o2 = __builtin_bit_cast(uint4, vl[qc + QB]);
+                h = make_uint4((h.x & lo_half) | (h2.x & ~lo_half), (h.y & lo_half) | (h2.y & ~lo_half),
+                               (h.z & lo_half) | (h2.z & ~lo_half), (h.w & lo_half) | (h2.w & ~lo_half));
+                o = make_uint4((o.x & lo_half) | (o2.x & ~lo_half), (o.y & lo_half) | (o2.y & ~lo_half),
+                               (o.z & lo_half) | (o2.z & ~lo_half), (o.w & lo_half) | (o2.w & ~lo_half));
+              }
+              const bf16x8 mh = __builtin_bit_cast(bf16x8, make_uint4(h.x & m, h.y & m, h.z & m, h.w & m));
+              const bf16x8 ml = __builtin_bit_cast(bf16x8, make_uint4(o.x & m, o.y & m, o.z & m, o.w & m));
+#pragma unroll
+              for (int i = 0; i < FN; ++i) {
+                acc[i][j] = mfma32(bb[qc][i], mh, acc[i][j]);
+                acc[i][j] = mfma32(bb[qc][i], ml, acc[i][j]);
+              }
+            }
+          }
+        };
+        auto next = [&](int& s, int& cb) __attribute__((always_inline)) {
+          cb += QB;
+          if (cb >= ((a.seg_rank[s] + 15) >> 4)) {
+            ++s;
+            cb = 0;
+          }
+        };
+        int cb = 0;
+        if (sg <= s_last) load_b(b0, sg, 0);
+        while (sg <= s_last) {
+          int s2 = sg, c2 = cb;
+          next(s2, c2);
+          if (s2 <= s_last) load_b(b1, s2, c2);
+          apply_b(b0, sg, cb);
+          sg = s2;
+          cb = c2;
+          if (sg > s_last) break;
+          next(s2, c2);
+          if (s2 <= s_last) load_b(b0, s2, c2);
+          apply_b(b1, sg, cb);
+          sg = s2;
+          cb = c2;
+        }
+      }
+    }
+  }
+
+  // ---- base product, K-steps of 64 through two LDS stages
+  bf16x8 fa[2][FN], fb[2][FM];
+  auto rd = [&](const uint16_t* ws, const uint16_t* xs, int kk, int f) __attribute__((always_inline)) {
+    const int cc = 2 * kk + (l >> 5);
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const int row = wn * (BN / 2) + 32 * i + (l & 31);
+      fa[f][i] = lds_bf16x8(ws + row * kBK + ((cc ^ swz(row)) * 8));
+    }
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int row = wm * (BM / 2) + 32 * j + (l & 31);
+      fb[f][j] = lds_bf16x8(xs + row * kBK + ((cc ^ swz(row)) * 8));
+    }
+  };
+  auto mm = [&](int f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) acc[i][j] = mfma32(fa[f][i], fb[f][j], acc[i][j]);
+  };
+  // One barrier per K-step.  Between two barriers: the DMA of the step after
+  // next, this step's fragment reads, the previous step's last 16-deep MFMA
+  // group and this step's first three.
+  auto step = [&](uint16_t* ws, uint16_t* xs, uint16_t* wnx, uint16_t* xnx, int knext)
+                  __attribute__((always_inline)) {
+    issue(wnx, xnx, knext);
+    rd(ws, xs, 0, 0);
+    mm(1);
+    rd(ws, xs, 1, 1);
+    mm(0);
+    rd(ws, xs, 2, 0);
+    mm(1);
+    rd(ws, xs, 3, 1);
+    mm(0);
+    constexpr int kM = FN * FM, kD = FN + FM, kV = NWB + NXB;
+    __builtin_amdgcn_sched_group_barrier(0x100, kD, 0);
+    interleave<kM, kV, 0x020>();
+    interleave<kM, kD, 0x100>();
+    interleave<kM, kD, 0x100>();
+    interleave<kM, kD, 0x100>();
+    __syncthreads();
+  };
+#pragma unroll
+  for (int i = 0; i < FN; ++i) fa[1][i] = zero_bf16x8();
+#pragma unroll
+  for (int j = 0; j < FM; ++j) fb[1][j] = zero_bf16x8();
+  const int nk = (K + kBK - 1) / kBK;
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(w0, x0, w1, x1, (kt + 1) * kBK);
+    step(w1, x1, w0, x0, (kt + 2) * kBK);
+  }
+  mm(1);
+
+  // ---- single rounding, 4 consecutive columns per lane and 32-row block
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    const int p = m0 + wm * (BM / 2) + 32 * j + (l & 31);
+    if (p >= T) continue;
+    const int tok = a.perm ? a.perm[p] : p;
+    uint16_t* orow = a.out + (size_t)tok * N;
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = n0 + wn * (BN / 2) + 32 * i + 8 * g + 4 * (l >> 5);
+        if (n >= N) continue;  // N % 8 == 0: the 4 columns are all in or all out
+        const uint32_t lo = (uint32_t)f32_to_bf16_bits(acc[i][j][4 * g + 0]) |
+                            ((uint32_t)f32_to_bf16_bits(acc[i][j][4 * g + 1]) << 16);
+        const uint32_t hi = (uint32_t)f32_to_bf16_bits(acc[i][j][4 * g + 2]) |
+                            ((uint32_t)f32_to_bf16_bits(acc[i][j][4 * g + 3]) << 16);
+        *reinterpret_cast<uint2*>(orow + n) = make_uint2(lo, hi);
+      }
+    }
+  }
+}
+
+template <int BM, int BN>
+static hipError_t launch_cfg(const GemmArgs& a, bool lora, hipStream_t s) {
+  const int tiles = ((a.T + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  if (!lora) {
+    hipLaunchKernelGGL((prefill_kernel<BM, BN, false, 0>), dim3(tiles), dim3(256), 0, s, a);
+  } else {
+    const int qc = a.u_ld / 16;  // 16-rank chunks in the pool's pages
+    if (qc <= 1)
+      hipLaunchKernelGGL((prefill_kernel<BM, BN, true, 1>), dim3(tiles), dim3(256), 0, s, a);
+    else if (qc == 2)
+      hipLaunchKernelGGL((prefill_kernel<BM, BN, true, 2>), dim3(tiles), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_kernel<BM, BN, true, 4>), dim3(tiles), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+// Relative time of one tile (per unit of K) for each shape, measured on
+// MI355X; the launcher picks the shape with the least estimated time, counting
+// whole rounds of 256 tiles (one tile per compute unit).
+int prefill_choose(int T, int N) {
+  struct Shape {
+    int bm, bn;
+    double cost;
+  };
+  static const Shape shapes[] = {{256, 256, 1.00}, {256, 128, 0.56}, {128, 256, 0.56}, {128, 128, 0.32}};
+  int best = 0;
+  double best_t = 1e30;
+  for (int i = 0; i < 4; ++i) {
+    const long tiles = (long)((T + shapes[i].bm - 1) / shapes[i].bm) * ((N + shapes[i].bn - 1) / shapes[i].bn);
+    const long rounds = (tiles + 255) / 256;
+    const double t = rounds * shapes[i].cost;
+    if (t < best_t * 0.999) {
+      best_t = t;
+      best = i;
+    }
+  }
+  return best;
+}
+
+hipError_t launch_prefill(const GemmArgs& a, bool lora, int shape, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  if (shape < 0) shape = prefill_choose(a.T, a.N);
+  switch (shape) {
+    case 0: return launch_cfg<256, 256>(a, lora, s);
+    case 1: return launch_cfg<256, 128>(a, lora, s);
+    case 2: return launch_cfg<128, 256>(a, lora, s);
+    default: return launch_cfg<128, 128>(a, lora, s);
+  }
+}
+
+}  // namespace hrg

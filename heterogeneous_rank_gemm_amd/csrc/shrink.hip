@@ -8,8 +8,12 @@
 // once per tile and K-split; the 16x16x32 bf16 MFMA does the contraction.
 // Each of the 4 waves covers an interleaved quarter of the K range; the four
 // partial results are summed in a fixed order through LDS (deterministic),
-// and each K-split writes its own fp32 partial plane of U.  The GEMM
-// epilogue sums the planes in split order.
+// and each K-split writes its own fp32 partial plane of U.  A second launch
+// sums the planes in split order (deterministic), scales by s = alpha/r and
+// writes V = s U as bf16 hi + lo parts (V ~= hi + lo to about 2^-16) for the
+// GEMM's expand.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -107,11 +111,39 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
                     red[3][r * kRedLd + q];
     up[(size_t)r * a.u_ld + q] = v;
   }
+
 }
 
-hipError_t launch_shrink(const ShrinkArgs& a, int grid_tiles, int ksplit, hipStream_t s) {
-  if (grid_tiles <= 0 || ksplit <= 0) return hipSuccess;
+// V = s * (sum of the partial planes in split order), written as bf16 hi + lo
+// for every sorted row of an adapter segment and q < 16 * ceil(rank / 16).
+// A separate launch: the kernel boundary orders the planes' writes before
+// these reads without a device-scope fence per block.
+__global__ __launch_bounds__(256) void shrink_finalize_kernel(ShrinkArgs a, int nsplit, int T) {
+  if (*a.status != 0) return;
+  const int w = a.u_ld;
+  for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < T * w; idx += gridDim.x * blockDim.x) {
+    const int p = idx / w, q = idx % w;
+    const int sg = a.row_seg[p];
+    if (a.seg_slot[sg] < 0 || q >= ((a.seg_rank[sg] + 15) & ~15)) continue;
+    const float* u0 = a.upart + (size_t)p * w + q;
+    float u = u0[0];
+    for (int sp = 1; sp < nsplit; ++sp) u += u0[(size_t)sp * a.split_stride];
+    const float v = a.seg_scale[sg] * u;
+    const __bf16 hi = (__bf16)v;
+    const __bf16 lo = (__bf16)(v - (float)hi);
+    a.v_hi[(size_t)p * w + q] = __builtin_bit_cast(uint16_t, hi);
+    a.v_lo[(size_t)p * w + q] = __builtin_bit_cast(uint16_t, lo);
+  }
+}
+
+hipError_t launch_shrink(const ShrinkArgs& a, int grid_tiles, int ksplit, int T, hipStream_t s) {
+  if (grid_tiles <= 0 || ksplit <= 0 || T <= 0) return hipSuccess;
   hipLaunchKernelGGL(shrink_kernel, dim3(grid_tiles, ksplit), dim3(kShrinkThreads), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n = T * a.u_ld;
+  const int grid = std::min((n + 255) / 256, 2048);
+  hipLaunchKernelGGL(shrink_finalize_kernel, dim3(grid), dim3(256), 0, s, a, ksplit, T);
   return hipGetLastError();
 }
 
