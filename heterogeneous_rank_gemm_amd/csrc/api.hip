@@ -423,11 +423,12 @@ static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t
     lora_status_t st = run_plan(P, ids, T, pl, stream);
     if (st != LORA_OK) return st;
   }
-  // shrink: (tile, K-split) grid; tiles beyond the plan's count exit at once
-  const int grid_tiles = std::min(T, P->max_adapters) + ceil_div(T, hrg::kShrinkRows);
-  int ksplit = std::max(1, std::min(ceil_div(1024, grid_tiles), std::min(hrg::kMaxSplits, ceil_div(K, 128))));
-  const int kchunk = round_up(ceil_div(K, ksplit), 128);
-  ksplit = ceil_div(K, kchunk);
+  // shrink: a fixed grid walks the plan's (tile, K-split) items; K splits of
+  // at least 512 (at most kMaxSplits planes)
+  const int kchunk = std::max(512, round_up(ceil_div(K, hrg::kMaxSplits), 128));
+  const int ksplit = ceil_div(K, kchunk);
+  const int max_items = max_tiles_for(P) * ksplit;
+  const int grid = std::min(max_items, 512);
   hrg::ShrinkArgs sa{};
   sa.X = X;
   sa.K = K;
@@ -446,11 +447,12 @@ static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t
   sa.split_stride = P->split_stride;
   sa.u_ld = P->rpad;
   sa.kchunk = kchunk;
+  sa.nsplit = ksplit;
   sa.row_seg = pl->tab.row_seg;
   sa.v_hi = P->v_hi;
   sa.v_lo = P->v_lo;
   sa.status = P->status;
-  if (hrg::launch_shrink(sa, grid_tiles, ksplit, T, stream) != hipSuccess) return LORA_ERR_HIP;
+  if (hrg::launch_shrink(sa, grid, ksplit, T, stream) != hipSuccess) return LORA_ERR_HIP;
   ga.perm = pl->tab.perm;
   ga.v_hi = P->v_hi;
   ga.v_lo = P->v_lo;

@@ -61,7 +61,8 @@ struct ShrinkArgs {
   float* upart;           // [split][T_cap][u_ld] fp32 partial planes
   size_t split_stride;
   int32_t u_ld;
-  int32_t kchunk;
+  int32_t kchunk;         // K per split
+  int32_t nsplit;         // splits (planes) per tile
   const int32_t* row_seg;
   uint16_t* v_hi;         // [T_cap][u_ld] bf16 high part of s * U (sorted rows)
   uint16_t* v_lo;         // [T_cap][u_ld] bf16 low part, s * U - hi
@@ -132,7 +133,7 @@ struct PackArgs {
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 // Shrink partial planes, then the split reduction into V (two launches).
-hipError_t launch_shrink(const ShrinkArgs& a, int grid_tiles, int ksplit, int T, hipStream_t s);
+hipError_t launch_shrink(const ShrinkArgs& a, int grid, int ksplit, int T, hipStream_t s);
 // shape < 0 picks the tile shape from (T, N); 0..3 force 256x256, 256x128,
 // 128x256, 128x128 (tokens x columns).  Every shape gives the same bits.
 hipError_t launch_prefill(const GemmArgs& a, bool lora, int shape, hipStream_t s);

@@ -10,6 +10,7 @@
 namespace hrg {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kStageTok = 8192;  // tokens whose buckets are staged in LDS at a time
 
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
@@ -33,6 +34,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ int s_err;
   __shared__ int s_wsum[2][kPlanThreads / 64];
   __shared__ int s_tot[2];
+  __shared__ uint16_t s_bucket[kStageTok];  // id + 1 of the tokens of one placement block
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T;
   if (*a.status != 0) return;  // a sticky error is pending: leave the tables alone
@@ -118,39 +120,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   }
   __syncthreads();
 
-  if (wave == 0) {
-    // 4a. stable placement, 64 tokens at a time in index order.  The ballot
-    // loop only groups the lanes by id (leader = lowest lane, rank = lanes of
-    // the group below); then every group leader claims its run of positions
-    // with one LDS atomic and the members read the base from their leader.
-    // Chunks are placed one after another, so equal ids keep index order.
-    for (int base = 0; base < T; base += 64) {
-      const int t = base + lane;
-      const bool valid = t < T;
-      const int b = valid ? a.ids[t] + 1 : -1;
-      uint64_t todo = __ballot(valid);
-      int leader = 0, rank = 0, cnt = 0;
-      while (todo) {
-        const int ld = __builtin_ctzll(todo);  // wave-uniform
-        const int vb = __builtin_amdgcn_readlane(b, ld);
-        const uint64_t m = __ballot(b == vb) & todo;
-        if ((m >> lane) & 1ull) {
-          leader = ld;
-          rank = __popcll(m & ((1ull << lane) - 1ull));
-          cnt = __popcll(m);
-        }
-        todo &= ~m;
-      }
-      int first = 0;
-      if (valid && lane == leader) first = atomicAdd(&start[b], cnt);
-      const int pos = __shfl(first, leader, 64) + rank;
-      if (valid) {
-        a.tab.perm[pos] = t;
-        a.tab.inv[t] = pos;
-        a.tab.row_seg[pos] = segidx[b];
-      }
-    }
-  } else if (wave == 1) {
+  if (wave == 1) {
     // 4b. shrink work tiles: every adapter segment split into runs of
     // kShrinkRows sorted rows (the base segment has no tiles).
     int run = 0;
@@ -172,6 +142,43 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       run += __shfl(inc, 63, 64);
     }
     if (lane == 0) a.tab.counts[1] = min(run, a.tab.max_tiles);
+  }
+
+  // 4a. stable placement in blocks of kStageTok tokens whose buckets are
+  // staged in LDS by all waves; wave 0 then places the block, 64 at a time.
+  for (int blk0 = 0; blk0 < T; blk0 += kStageTok) {
+    const int blk1 = min(T, blk0 + kStageTok);
+    __syncthreads();  // the previous block is placed
+    for (int t = blk0 + tid; t < blk1; t += kPlanThreads) s_bucket[t - blk0] = (uint16_t)(a.ids[t] + 1);
+    __syncthreads();
+    if (wave == 0) {
+      for (int base = blk0; base < blk1; base += 64) {
+        const int t = base + lane;
+        const bool valid = t < blk1;
+        const int b = valid ? (int)s_bucket[t - blk0] : -1;
+        uint64_t todo = __ballot(valid);
+        int leader = 0, rank = 0, cnt = 0;
+        while (todo) {
+          const int ld = __builtin_ctzll(todo);  // wave-uniform
+          const int vb = __builtin_amdgcn_readlane(b, ld);
+          const uint64_t m = __ballot(b == vb) & todo;
+          if ((m >> lane) & 1ull) {
+            leader = ld;
+            rank = __popcll(m & ((1ull << lane) - 1ull));
+            cnt = __popcll(m);
+          }
+          todo &= ~m;
+        }
+        int first = 0;
+        if (valid && lane == leader) first = atomicAdd(&start[b], cnt);
+        const int pos = __shfl(first, leader, 64) + rank;
+        if (valid) {
+          a.tab.perm[pos] = t;
+          a.tab.inv[t] = pos;
+          a.tab.row_seg[pos] = segidx[b];
+        }
+      }
+    }
   }
 }
 

@@ -164,99 +164,161 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
     // segment.  V = s U arrives from the shrink as bf16 hi + lo parts
     // (V ~= hi + lo to about 2^-16); the B page is stored transposed in
     // 16-rank chunks, [rpad/16][N][16], so both operands are 16-byte reads.
-    // Per 32-row block: V is loaded once (all chunks); the B fragments of the
-    // next (segment, chunk pair) are loaded while the current one's MFMAs run.
+    // Each 32-row block j of the wave walks its own work items (segment,
+    // pair of rank chunks); the FM walkers advance in lockstep, each with its
+    // next item's B fragments in flight while the current one's MFMAs run.
+    constexpr int QB = QC < 2 ? QC : 2;  // rank chunks per work item
+    // walkers per group: the expand's registers (V, two B buffers) stay
+    // within about 160 VGPRs
+    constexpr int kPerWalker = 2 * QB * FN * 4 + QC * 8;
+    constexpr int JG = kPerWalker * FM <= 160 ? FM : (kPerWalker * 2 <= 160 ? 2 : 1);
     const int qc_pool = a.u_ld >> 4;
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const int rb = m0 + wm * (BM / 2) + 32 * j;  // first sorted row of this 32-row block
-      if (rb < T) {
-        const int p = rb + (l & 31);
-        const int pc = min(p, T - 1);
-        bf16x8 vh[QC], vl[QC];
+    for (int g = 0; g < FM / JG; ++g) {
+      bf16x8 vh[JG][QC], vl[JG][QC];
+      int sg[JG], cb[JG], sl[JG], pj[JG];
+      bool act[JG];
+#pragma unroll
+      for (int j = 0; j < JG; ++j) {
+        const int rb = m0 + wm * (BM / 2) + 32 * (g * JG + j);  // first sorted row of block g*JG+j
+        act[j] = rb < T;
+        pj[j] = rb + (l & 31);
+        const int pc = min(pj[j], T - 1);
 #pragma unroll
         for (int qc = 0; qc < QC; ++qc) {
           const size_t e = (size_t)pc * a.u_ld + 16 * qc + 8 * (l >> 5);
-          if (qc < qc_pool) {
-            vh[qc] = __builtin_bit_cast(bf16x8, ld16(a.v_hi + e));
-            vl[qc] = __builtin_bit_cast(bf16x8, ld16(a.v_lo + e));
+          if (act[j] && qc < qc_pool) {
+            vh[j][qc] = __builtin_bit_cast(bf16x8, ld16(a.v_hi + e));
+            vl[j][qc] = __builtin_bit_cast(bf16x8, ld16(a.v_lo + e));
           } else {
-            vh[qc] = zero_bf16x8();
-            vl[qc] = zero_bf16x8();
+            vh[j][qc] = zero_bf16x8();
+            vl[j][qc] = zero_bf16x8();
           }
         }
-        const int s_last = a.row_seg[min(rb + 31, T - 1)];
-        int sg = a.row_seg[rb];
-        if (a.seg_id[sg] < 0) ++sg;  // only the first segment can be the base run
-        // work items (segment, first chunk cb), QB chunks each, double-buffered
-        constexpr int QB = QC < 2 ? QC : 2;
-        bf16x8 b0[QB][FN], b1[QB][FN];
-        auto load_b = [&](bf16x8 (&bb)[QB][FN], int s, int cb) __attribute__((always_inline)) {
-          const int nqc = (a.seg_rank[s] + 15) >> 4;
-          const uint16_t* bt = a.pages + (size_t)a.seg_slot[s] * a.slot_stride + a.b_off;
-#pragma unroll
-          for (int qc = 0; qc < QB; ++qc) {
-            if (cb + qc < nqc) {
-#pragma unroll
-              for (int i = 0; i < FN; ++i) {
-                const int n = min(n0 + wn * (BN / 2) + 32 * i + (l & 31), N - 1);
-                bb[qc][i] = __builtin_bit_cast(
-                    bf16x8, ld16(bt + ((size_t)(cb + qc) * N + n) * 16 + 8 * (l >> 5)));
-              }
-            }
-          }
-        };
-        auto apply_b = [&](const bf16x8 (&bb)[QB][FN], int s, int cb) __attribute__((always_inline)) {
-          const bool in = p >= a.seg_off[s] && p < a.seg_off[s + 1];
-          const int nqc = (a.seg_rank[s] + 15) >> 4;
-          const uint32_t m = in ? 0xffffffffu : 0u;
-          const uint32_t lo_half = cb == 0 ? 0xffffffffu : 0u;  // chunk cb + qc: qc or qc + 2
-#pragma unroll
-          for (int qc = 0; qc < QB; ++qc) {
-            if (cb + qc < nqc) {
-              uint4 h = __builtin_bit_cast(uint4, vh[qc]), o = __builtin_bit_cast(uint4, vl[qc]);
-              if constexpr (QC > QB) {
-                const uint4 h2 = __builtin_bit_cast(uint4, vh[qc + QB]);
-                const uint4 o2 = __builtin_bit_cast(uint4, vl[qc + QB]);
-                h = make_uint4((h.x & lo_half) | (h2.x & ~lo_half), (h.y & lo_half) | (h2.y & ~lo_half),
-                               (h.z & lo_half) | (h2.z & ~lo_half), (h.w & lo_half) | (h2.w & ~lo_half));
-                o = make_uint4((o.x & lo_half) | (o2.x & ~lo_half), (o.y & lo_half) | (o2.y & ~lo_half),
-                               (o.z & lo_half) | (o2.z & ~lo_half), (o.w & lo_half) | (o2.w & ~lo_half));
-              }
-              const bf16x8 mh = __builtin_bit_cast(bf16x8, make_uint4(h.x & m, h.y & m, h.z & m, h.w & m));
-              const bf16x8 ml = __builtin_bit_cast(bf16x8, make_uint4(o.x & m, o.y & m, o.z & m, o.w & m));
-#pragma unroll
-              for (int i = 0; i < FN; ++i) {
-                acc[i][j] = mfma32(bb[qc][i], mh, acc[i][j]);
-                acc[i][j] = mfma32(bb[qc][i], ml, acc[i][j]);
-              }
-            }
-          }
-        };
-        auto next = [&](int& s, int& cb) __attribute__((always_inline)) {
-          cb += QB;
-          if (cb >= ((a.seg_rank[s] + 15) >> 4)) {
-            ++s;
-            cb = 0;
-          }
-        };
-        int cb = 0;
-        if (sg <= s_last) load_b(b0, sg, 0);
-        while (sg <= s_last) {
-          int s2 = sg, c2 = cb;
-          next(s2, c2);
-          if (s2 <= s_last) load_b(b1, s2, c2);
-          apply_b(b0, sg, cb);
-          sg = s2;
-          cb = c2;
-          if (sg > s_last) break;
-          next(s2, c2);
-          if (s2 <= s_last) load_b(b0, s2, c2);
-          apply_b(b1, sg, cb);
-          sg = s2;
-          cb = c2;
+        sg[j] = 0;
+        sl[j] = -1;
+        cb[j] = 0;
+        if (act[j]) {
+          sg[j] = a.row_seg[rb];
+          if (a.seg_id[sg[j]] < 0) ++sg[j];  // only the first segment can be the base run
+          sl[j] = a.row_seg[min(rb + 31, T - 1)];
+          act[j] = sg[j] <= sl[j];
         }
       }
+      bf16x8 b0[JG][QB][FN], b1[JG][QB][FN];
+      auto load_b = [&](bf16x8 (&bb)[QB][FN], int s, int c) __attribute__((always_inline)) {
+        const int nqc = (a.seg_rank[s] + 15) >> 4;
+        const uint16_t* bt = a.pages + (size_t)a.seg_slot[s] * a.slot_stride + a.b_off;
+#pragma unroll
+        for (int qc = 0; qc < QB; ++qc) {
+          if (c + qc < nqc) {
+#pragma unroll
+            for (int i = 0; i < FN; ++i) {
+              const int n = min(n0 + wn * (BN / 2) + 32 * i + (l & 31), N - 1);
+              bb[qc][i] = __builtin_bit_cast(bf16x8, ld16(bt + ((size_t)(c + qc) * N + n) * 16 + 8 * (l >> 5)));
+            }
+          }
+        }
+      };
+      // acc[.][j] += B^T (V masked to the rows of segment s), chunks c .. c+QB-1
+      auto apply_b = [&](const bf16x8 (&bb)[QB][FN], const bf16x8 (&h_)[QC], const bf16x8 (&l_)[QC],
+                         f32x16 (&accj)[FN], int p, int s, int c) __attribute__((always_inline)) {
+        const bool in = p >= a.seg_off[s] && p < a.seg_off[s + 1];
+        const int nqc = (a.seg_rank[s] + 15) >> 4;
+        const uint32_t m = in ? 0xffffffffu : 0u;
+        const uint32_t first = c == 0 ? 0xffffffffu : 0u;  // chunk c + qc is qc or qc + QB
+#pragma unroll
+        for (int qc = 0; qc < QB; ++qc) {
+          if (c + qc < nqc) {
+            uint4 h = __builtin_bit_cast(uint4, h_[qc]), o = __builtin_bit_cast(uint4, l_[qc]);
+            if constexpr (QC > QB) {
+              const uint4 h2 = __builtin_bit_cast(uint4, h_[qc + QB]);
+              const uint4 o2 = __builtin_bit_cast(uint4, l_[qc + QB]);
+              h = make_uint4((h.x & first) | (h2.x & ~first), (h.y & first) | (h2.y & ~first),
+                             (h.z & first) | (h2.z & ~first), (h.w & first) | (h2.w & ~first));
+              o = make_uint4((o.x & first) | (o2.x & ~first), (o.y & first) | (o2.y & ~first),
+                             (o.z & first) | (o2.z & ~first), (o.w & first) | (o2.w & ~first));
+            }
+            const bf16x8 mh = __builtin_bit_cast(bf16x8, make_uint4(h.x & m, h.y & m, h.z & m, h.w & m));
+            const bf16x8 ml = __builtin_bit_cast(bf16x8, make_uint4(o.x & m, o.y & m, o.z & m, o.w & m));
+#pragma unroll
+            for (int i = 0; i < FN; ++i) {
+              accj[i] = mfma32(bb[qc][i], mh, accj[i]);
+              accj[i] = mfma32(bb[qc][i], ml, accj[i]);
+            }
+          }
+        }
+      };
+      auto advance = [&](int& s, int& c) __attribute__((always_inline)) {
+        c += QB;
+        if (c >= ((a.seg_rank[s] + 15) >> 4)) {
+          ++s;
+          c = 0;
+        }
+      };
+      f32x16 accT[JG][FN];  // acc transposed so a block's columns pass as one array
+#pragma unroll
+      for (int j = 0; j < JG; ++j)
+#pragma unroll
+        for (int i = 0; i < FN; ++i) accT[j][i] = acc[i][g * JG + j];
+#pragma unroll
+      for (int j = 0; j < JG; ++j)
+        if (act[j]) load_b(b0[j], sg[j], cb[j]);
+      bool any = false;
+#pragma unroll
+      for (int j = 0; j < JG; ++j) any |= act[j];
+      while (any) {
+        // items held in b0 are current; load the next ones into b1
+        int s2[JG], c2[JG];
+#pragma unroll
+        for (int j = 0; j < JG; ++j) {
+          s2[j] = sg[j];
+          c2[j] = cb[j];
+          if (act[j]) {
+            advance(s2[j], c2[j]);
+            if (s2[j] <= sl[j]) load_b(b1[j], s2[j], c2[j]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < JG; ++j) {
+          if (act[j]) {
+            apply_b(b0[j], vh[j], vl[j], accT[j], pj[j], sg[j], cb[j]);
+            sg[j] = s2[j];
+            cb[j] = c2[j];
+            act[j] = sg[j] <= sl[j];
+          }
+        }
+        any = false;
+#pragma unroll
+        for (int j = 0; j < JG; ++j) any |= act[j];
+        if (!any) break;
+        // items held in b1 are current; load the next ones into b0
+#pragma unroll
+        for (int j = 0; j < JG; ++j) {
+          s2[j] = sg[j];
+          c2[j] = cb[j];
+          if (act[j]) {
+            advance(s2[j], c2[j]);
+            if (s2[j] <= sl[j]) load_b(b0[j], s2[j], c2[j]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < JG; ++j) {
+          if (act[j]) {
+            apply_b(b1[j], vh[j], vl[j], accT[j], pj[j], sg[j], cb[j]);
+            sg[j] = s2[j];
+            cb[j] = c2[j];
+            act[j] = sg[j] <= sl[j];
+          }
+        }
+        any = false;
+#pragma unroll
+        for (int j = 0; j < JG; ++j) any |= act[j];
+      }
+#pragma unroll
+      for (int j = 0; j < JG; ++j)
+#pragma unroll
+        for (int i = 0; i < FN; ++i) acc[i][g * JG + j] = accT[j][i];
     }
   }
 

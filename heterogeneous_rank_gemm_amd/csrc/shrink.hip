@@ -22,12 +22,7 @@ namespace hrg {
 constexpr int kShrinkThreads = 256;
 constexpr int kRedLd = 65;  // padded row of the cross-wave reduction buffer
 
-__global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
-  __shared__ float red[4][64 * kRedLd];
-  if (*a.status != 0) return;
-  const int tile = blockIdx.x;
-  if (tile >= a.counts[1]) return;
-
+__device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64 * kRedLd], int tile, int split) {
   const int seg = a.tile_seg[tile];
   const int row0 = a.tile_row0[tile];
   const int rows = min(kShrinkRows, a.seg_off[seg + 1] - row0);
@@ -36,7 +31,7 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
   const int nq = (rank + 15) / 16;  // 16-wide rank blocks actually computed
   const int nm = (rows + 15) / 16;  // 16-row blocks with at least one row
   const int K = a.K;
-  const int k0 = blockIdx.y * a.kchunk;
+  const int k0 = split * a.kchunk;
   const int k1 = min(K, k0 + a.kchunk);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const uint16_t* Ap = a.pages + (size_t)slot * a.slot_stride + a.a_off;
@@ -104,7 +99,7 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
   }
   __syncthreads();
   const int width = nq * 16;
-  float* up = a.upart + (size_t)blockIdx.y * a.split_stride + (size_t)row0 * a.u_ld;
+  float* up = a.upart + (size_t)split * a.split_stride + (size_t)row0 * a.u_ld;
   for (int idx = threadIdx.x; idx < rows * width; idx += kShrinkThreads) {
     const int r = idx / width, q = idx % width;
     const float v = ((red[0][r * kRedLd + q] + red[1][r * kRedLd + q]) + red[2][r * kRedLd + q]) +
@@ -113,6 +108,19 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
   }
 
 }
+
+// A fixed grid walks the (tile, split) items of the plan's tile list; the
+// split count is fixed by K on the host, the tile count only on the device.
+__global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
+  __shared__ float red[4][64 * kRedLd];
+  if (*a.status != 0) return;
+  const int nitems = a.counts[1] * a.nsplit;
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    __syncthreads();  // the previous item is done with red
+    shrink_item(a, red, item / a.nsplit, item % a.nsplit);
+  }
+}
+
 
 // V = s * (sum of the partial planes in split order), written as bf16 hi + lo
 // for every sorted row of an adapter segment and q < 16 * ceil(rank / 16).
@@ -136,14 +144,14 @@ __global__ __launch_bounds__(256) void shrink_finalize_kernel(ShrinkArgs a, int 
   }
 }
 
-hipError_t launch_shrink(const ShrinkArgs& a, int grid_tiles, int ksplit, int T, hipStream_t s) {
-  if (grid_tiles <= 0 || ksplit <= 0 || T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(shrink_kernel, dim3(grid_tiles, ksplit), dim3(kShrinkThreads), 0, s, a);
+hipError_t launch_shrink(const ShrinkArgs& a, int grid, int ksplit, int T, hipStream_t s) {
+  if (grid <= 0 || ksplit <= 0 || T <= 0) return hipSuccess;
+  hipLaunchKernelGGL(shrink_kernel, dim3(grid), dim3(kShrinkThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = T * a.u_ld;
-  const int grid = std::min((n + 255) / 256, 2048);
-  hipLaunchKernelGGL(shrink_finalize_kernel, dim3(grid), dim3(256), 0, s, a, ksplit, T);
+  const int fgrid = std::min((n + 255) / 256, 2048);
+  hipLaunchKernelGGL(shrink_finalize_kernel, dim3(fgrid), dim3(256), 0, s, a, ksplit, T);
   return hipGetLastError();
 }
 
