@@ -179,10 +179,35 @@ def time_steps(fn, reps, steps: int, warmup: int, torch, hrg) -> float:
     return e0.elapsed_time(e1) * 1e-3 / steps
 
 
+def capture(fn, rep, torch, hrg):
+    """The step `fn` on `rep` captured as one hipGraph (after an eager warm-up
+    on the capture stream); the decode path records kernel launches only."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(rep, hrg)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn(rep, hrg)
+    torch.cuda.synchronize()
+    return g
+
+
+def graphed(fn, reps, torch, hrg):
+    """A step function that replays `fn` captured per replica."""
+    graphs = {id(rp): capture(fn, rp, torch, hrg) for rp in reps}
+    return lambda rp, _hrg: graphs[id(rp)].replay()
+
+
 # ---------------------------------------------------------------------------
 # CPU oracle baseline
 # ---------------------------------------------------------------------------
 def cpu_baseline(wl: wk.Workload, rep: Replica, seconds: float, torch):
+    """The oracle timed on the host over a bounded sample: the linears of the
+    first layer (all of them for one-layer workloads), repeated for about
+    `seconds`, scaled to whole steps."""
     import oracle
     try:
         import threadpoolctl
@@ -190,7 +215,8 @@ def cpu_baseline(wl: wk.Workload, rep: Replica, seconds: float, torch):
             if threadpoolctl.threadpool_info() else 1
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    mods = wl.modules
+    n_sample = min(7, len(wl.modules))
+    mods = wl.modules[:n_sample]
     reg = oracle.Registry(wl.n_adapters, wl.n_adapters, wl.max_rank, [m.d_in for m in mods],
                           [m.d_out for m in mods], wl.T)
     # the oracle sees the same bf16 bits as the GPU (regenerated on the device, copied back)
@@ -198,28 +224,30 @@ def cpu_baseline(wl: wk.Workload, rep: Replica, seconds: float, torch):
     for i in used:
         r = int(rep.ranks[i])
         A, B = [], []
-        for j in range(len(mods)):
+        for j in range(n_sample):
             a, b = wk.adapter_weights(wl, i, j, r, wl.default_seed, "cuda")
             A.append(a.cpu())
             B.append(b.cpu())
         reg.load(i, r, wk.adapter_alpha(wl, r), A, B)
-    X = [x.cpu() for x in rep.xin]
-    W = [w.cpu() for w in rep.W]
+    X = [x.cpu() for x in rep.xin[:n_sample]]
+    W = [w.cpu() for w in rep.W[:n_sample]]
     n_lin = 0
     t0 = time.perf_counter()
     while True:
-        j = n_lin % len(mods)
+        j = n_lin % n_sample
         oracle.lora_linear(reg, j, X[j], rep.ids_np, W[j])
         n_lin += 1
         el = time.perf_counter() - t0
-        if el >= seconds and n_lin % len(mods) == 0:
+        if el >= seconds and n_lin % n_sample == 0:
             break
         if el >= 4 * seconds:
             break
-    tokens = wl.T * n_lin / len(mods)
-    return {"value": tokens / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_lin} linears ({n_lin / len(mods):.2f} steps of {wl.T} tokens) of "
-                      f"workload '{wl.name}' in {el:.1f} s, float64 numpy"}
+    # seconds per sampled layer -> seconds per step of len(wl.modules) linears
+    t_step = el / (n_lin / n_sample) * (len(wl.modules) / n_sample)
+    return {"value": wl.T / t_step, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_lin} linears ({n_lin / n_sample:.2f} passes over the first {n_sample} "
+                      f"of the {len(wl.modules)} linears of workload '{wl.name}', {wl.T} tokens) "
+                      f"in {el:.1f} s, float64 numpy; scaled to a whole step"}
 
 
 def main(argv=None) -> int:
@@ -231,6 +259,9 @@ def main(argv=None) -> int:
     ap.add_argument("--rotate", type=int, default=8, help="independent copies of the state")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
+                    help="replay each step as one captured hipGraph (auto: for multi-linear "
+                         "decode steps)")
     ap.add_argument("--phase", choices=["all", "lora", "base"], default="all",
                     help="time only the LoRA apply or only the base-only GEMM (for profiling)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -263,17 +294,25 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     print("[bench] state resident; timing", file=sys.stderr, flush=True)
 
+    use_graph = args.graph == "on" or (args.graph == "auto" and wl.T <= DECODE_MAX_T
+                                       and len(wl.modules) > 1)
+    f_lora, f_apply, f_base = lora_step, apply_only, base_step
+    if use_graph:
+        print("[bench] capturing the steps as hipGraphs", file=sys.stderr, flush=True)
+        f_lora = graphed(lora_step, reps, torch, hrg)
+        f_apply = f_lora if wl.T <= DECODE_MAX_T else graphed(apply_only, reps, torch, hrg)
+        f_base = graphed(base_step, reps, torch, hrg)
     if args.phase == "lora":
-        t_step = time_steps(lora_step, reps, args.steps, args.warmup, torch, hrg)
+        t_step = time_steps(f_lora, reps, args.steps, args.warmup, torch, hrg)
         print(json.dumps({"phase": "lora", "ms_per_step": t_step * 1e3}), flush=True)
         return 0
     if args.phase == "base":
-        t_base = time_steps(base_step, reps, args.steps, args.warmup, torch, hrg)
+        t_base = time_steps(f_base, reps, args.steps, args.warmup, torch, hrg)
         print(json.dumps({"phase": "base", "ms_per_step": t_base * 1e3}), flush=True)
         return 0
-    t_step = time_steps(lora_step, reps, args.steps, args.warmup, torch, hrg)
-    t_apply = time_steps(apply_only, reps, args.steps, args.warmup, torch, hrg)
-    t_base = time_steps(base_step, reps, args.steps, args.warmup, torch, hrg)
+    t_step = time_steps(f_lora, reps, args.steps, args.warmup, torch, hrg)
+    t_apply = time_steps(f_apply, reps, args.steps, args.warmup, torch, hrg)
+    t_base = time_steps(f_base, reps, args.steps, args.warmup, torch, hrg)
     for rp in reps:
         st = rp.pool.status()
         if st != "OK":
@@ -323,7 +362,7 @@ def main(argv=None) -> int:
                    "modules": [[m.d_in, m.d_out] for m in wl.modules[:7]],
                    "n_linears": len(wl.modules), "adapters": wl.n_adapters,
                    "ranks": list(wl.rank_choices), "max_rank": wl.max_rank,
-                   "replicas_rotated": R},
+                   "replicas_rotated": R, "hipgraph": use_graph},
         "lora_overhead_pct": round(100.0 * (t_step - t_base) / t_base, 2),
         "base_only_ms_per_step": round(t_base * 1e3, 5),
         "apply_ms_per_step": round(t_apply * 1e3, 5),

@@ -19,7 +19,8 @@ class Case:
     """A loaded pool plus inputs for a subset of a workload's modules."""
 
     def __init__(self, wl: wk.Workload, seed=None, modules=None, max_rank=None,
-                 adapters=None, ids=None, max_tokens=None, max_adapters=None):
+                 adapters=None, ids=None, max_tokens=None, max_adapters=None,
+                 oracle_modules=None):
         self.wl = wl
         self.seed = wl.default_seed if seed is None else seed
         self.modules = list(range(wl.n_modules)) if modules is None else list(modules)
@@ -32,8 +33,11 @@ class Case:
                              [m.d_in for m in mods], [m.d_out for m in mods],
                              max(max_tokens or self.T, 1))
         self.adapters = list(range(wl.n_adapters)) if adapters is None else list(adapters)
+        # the oracle registry may hold a subset of the modules (positions j)
+        self.oj = list(range(len(self.modules))) if oracle_modules is None else list(oracle_modules)
+        omods = [mods[j] for j in self.oj]
         self.reg = oracle.Registry(max_adapters or wl.n_adapters, wl.n_adapters, self.max_rank,
-                                   [m.d_in for m in mods], [m.d_out for m in mods],
+                                   [m.d_in for m in omods], [m.d_out for m in omods],
                                    max(max_tokens or self.T, 1))
         # the oracle only needs the adapters this batch uses
         self.used = set(wk.distinct_adapters(self.ids_np))
@@ -60,7 +64,7 @@ class Case:
             B.append(b)
         self.pool.load_adapter(i, r, al, A, B)
         if i in self.used:
-            self.reg.load(i, r, al, [a.cpu() for a in A], [b.cpu() for b in B])
+            self.reg.load(i, r, al, [A[j].cpu() for j in self.oj], [B[j].cpu() for j in self.oj])
 
     def unload(self, i: int):
         self.pool.unload_adapter(i)
@@ -91,10 +95,11 @@ class Case:
     def oracle(self, j: int, rows=None):
         X = self.x_for(j).cpu()
         W = self.W[j].cpu()
+        k = self.oj.index(j)  # the module's index in the oracle registry
         if rows is None:
-            return oracle.lora_linear(self.reg, j, X, self.ids_np, W)
+            return oracle.lora_linear(self.reg, k, X, self.ids_np, W)
         rows = np.asarray(rows)
-        return oracle.lora_linear_sampled(self.reg, j, X[torch.as_tensor(rows)],
+        return oracle.lora_linear_sampled(self.reg, k, X[torch.as_tensor(rows)],
                                           self.ids_np[rows], W)
 
     def close(self):
