@@ -15,17 +15,20 @@
 // with 4 consecutive output columns of one token (8-byte stores).
 //
 // Operands move HBM -> LDS with buffer_load ... lds (no register staging)
-// into two stages that live in separate LDS arrays: the compiler then knows
-// the reads of one stage never wait for the DMA into the other.  One barrier
-// per K-step of 64 publishes the next stage; the fragment reads of a stage
-// are spread over the MFMAs of the step before, and the DMA of the step after
-// next is spread over the first 16-deep MFMA group.  LDS rows are 128 bytes,
+// into 2-4 stages (as many 64-deep K-steps as fit: smaller tiles have shorter
+// steps and need more DMA in flight) that live in separate LDS arrays: the
+// compiler then knows the reads of one stage never wait for the DMA into the
+// others.  One barrier per K-step publishes the next stage; the fragment
+// reads of a stage are spread over the MFMAs of the step before, and the DMA
+// of the step NS-1 ahead over the first 16-deep MFMA group.  LDS rows are 128 bytes,
 // swizzled as chunk ^ (row & 7) ^ ((row >> 3) & 1), which keeps ds_read_b128
 // free of bank conflicts.
 //
 // Out-of-range rows and the K tail read through the buffer resource's range
 // check (zeros), so the loop has no branches.  K-steps past K (when their
 // count is odd) add exact zeros.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -96,6 +99,24 @@ __device__ __forceinline__ void dma_issue(__amdgpu_buffer_rsrc_t rw, __amdgpu_bu
                                              (xoff[i] + k2) | ((i & 1) ? kb1 : kb0), 0, 0, 0);
 }
 
+// Waits until at most N of this wave's buffer loads are outstanding (the
+// older ones -- the next stage's DMA -- have landed in LDS) and every LDS
+// access has completed, then joins the workgroup barrier.  Unlike
+// __syncthreads() it does not wait for the DMA of the stages further ahead.
+template <int N>
+__device__ __forceinline__ void barrier_after_dma() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(N) : "memory");
+}
+
+// Calls f(integral_constant<int, S>) for S = 0 .. NS-1, in order.
+template <int NS, int S = 0, class F>
+__device__ __forceinline__ void for_each_stage(F&& f) {
+  if constexpr (S < NS) {
+    f(std::integral_constant<int, S>{});
+    for_each_stage<NS, S + 1>(f);
+  }
+}
+
 }  // namespace prefill_detail
 using namespace prefill_detail;
 
@@ -104,10 +125,17 @@ template <int BM, int BN, bool LORA, int QC>
 __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
   constexpr int FM = BM / 64, FN = BN / 64;    // 32x32 blocks per wave (tokens, columns)
   constexpr int NXB = BM / 32, NWB = BN / 32;  // 1-KB DMA blocks per wave and stage
+  // LDS stages: as many 64-deep K steps as fit in 128-144 KB (2 for 256x256,
+  // 3 for 256x128 and 128x256, 4 for 128x128), each in its own arrays
+  constexpr int NS = (BM + BN) >= 512 ? 2 : (BM + BN) >= 384 ? 3 : 4;
   __shared__ __attribute__((aligned(16))) uint16_t w0[BN * kBK];
   __shared__ __attribute__((aligned(16))) uint16_t x0[BM * kBK];
   __shared__ __attribute__((aligned(16))) uint16_t w1[BN * kBK];
   __shared__ __attribute__((aligned(16))) uint16_t x1[BM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t w2[NS > 2 ? BN * kBK : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t x2[NS > 2 ? BM * kBK : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t w3[NS > 3 ? BN * kBK : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t x3[NS > 3 ? BM * kBK : 8];
 
   if constexpr (LORA) {
     if (*a.status != 0) return;  // strict mode: a failed plan leaves out untouched
@@ -155,9 +183,19 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // the first K-step's DMA goes out before the expand, so its latency and
-  // the expand's page loads overlap
-  issue(w0, x0, 0);
+  // DMA of the first NS-1 K-steps; it goes out before the expand, so its
+  // latency and the expand's page loads overlap
+  auto prologue = [&]() __attribute__((always_inline)) {
+    for_each_stage<NS>([&](auto sc) __attribute__((always_inline)) {
+      constexpr int S = decltype(sc)::value;
+      if constexpr (S < NS - 1) {
+        if constexpr (S == 0) issue(w0, x0, 0);
+        else if constexpr (S == 1) issue(w1, x1, kBK);
+        else issue(w2, x2, 2 * kBK);
+      }
+    });
+  };
+  prologue();
 
   if constexpr (LORA) {
     // ---- expand first: acc = s_i * (U_t B_i) for every token of an adapter
@@ -168,10 +206,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
     // pair of rank chunks); the FM walkers advance in lockstep, each with its
     // next item's B fragments in flight while the current one's MFMAs run.
     constexpr int QB = QC < 2 ? QC : 2;  // rank chunks per work item
-    // walkers per group: the expand's registers (V, two B buffers) stay
-    // within about 160 VGPRs
-    constexpr int kPerWalker = 2 * QB * FN * 4 + QC * 8;
-    constexpr int JG = kPerWalker * FM <= 160 ? FM : (kPerWalker * 2 <= 160 ? 2 : 1);
+    // walkers per group: the expand's registers (V, D B buffers) stay
+    // within a budget
+    // ring of D items in flight per walker: deeper where the tile leaves
+    // registers free (one block per compute unit)
+    constexpr int D = (FN * QB <= 4 && FM <= 2) ? 4 : 2;
+    constexpr int kPerWalker = D * QB * FN * 4 + QC * 8;
+    constexpr int kBudget = FN >= 4 ? 48 : 192;  // 256-column tiles keep 256 accumulators live
+    constexpr int JG = kPerWalker * FM <= kBudget ? FM : (kPerWalker * 2 <= kBudget ? 2 : 1);
     const int qc_pool = a.u_ld >> 4;
 #pragma unroll
     for (int g = 0; g < FM / JG; ++g) {
@@ -205,7 +247,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
           act[j] = sg[j] <= sl[j];
         }
       }
-      bf16x8 b0[JG][QB][FN], b1[JG][QB][FN];
+      bf16x8 bq[D][JG][QB][FN];
       auto load_b = [&](bf16x8 (&bb)[QB][FN], int s, int c) __attribute__((always_inline)) {
         const int nqc = (a.seg_rank[s] + 15) >> 4;
         const uint16_t* bt = a.pages + (size_t)a.seg_slot[s] * a.slot_stride + a.b_off;
@@ -261,59 +303,57 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
       for (int j = 0; j < JG; ++j)
 #pragma unroll
         for (int i = 0; i < FN; ++i) accT[j][i] = acc[i][g * JG + j];
+      // (ls, lc): the last item whose B fragments were requested, per walker
+      int ls[JG], lc[JG];
 #pragma unroll
-      for (int j = 0; j < JG; ++j)
-        if (act[j]) load_b(b0[j], sg[j], cb[j]);
+      for (int j = 0; j < JG; ++j) {
+        ls[j] = sg[j];
+        lc[j] = cb[j];
+        if (act[j]) load_b(bq[0][j], ls[j], lc[j]);
+      }
+      auto load_next = [&](auto bufc) __attribute__((always_inline)) {
+        constexpr int B = decltype(bufc)::value;
+#pragma unroll
+        for (int j = 0; j < JG; ++j) {
+          if (ls[j] <= sl[j]) {
+            advance(ls[j], lc[j]);
+            if (ls[j] <= sl[j]) load_b(bq[B][j], ls[j], lc[j]);
+          }
+        }
+      };
+      // items 1 .. D-2 (each phase then requests the item D-1 ahead)
+      for_each_stage<D - 2>([&](auto dc) __attribute__((always_inline)) {
+        load_next(std::integral_constant<int, decltype(dc)::value + 1>{});
+      });
       bool any = false;
 #pragma unroll
       for (int j = 0; j < JG; ++j) any |= act[j];
+      // phase P: items held in bq[P] are current; the item D-1 ahead goes to bq[(P+D-1)%D]
+      auto phase = [&](auto pc) __attribute__((always_inline)) {
+        constexpr int P = decltype(pc)::value;
+        load_next(std::integral_constant<int, (P + D - 1) % D>{});
+#pragma unroll
+        for (int j = 0; j < JG; ++j) {
+          if (act[j]) {
+            apply_b(bq[P][j], vh[j], vl[j], accT[j], pj[j], sg[j], cb[j]);
+            advance(sg[j], cb[j]);
+            act[j] = sg[j] <= sl[j];
+          }
+        }
+        any = false;
+#pragma unroll
+        for (int j = 0; j < JG; ++j) any |= act[j];
+      };
       while (any) {
-        // items held in b0 are current; load the next ones into b1
-        int s2[JG], c2[JG];
-#pragma unroll
-        for (int j = 0; j < JG; ++j) {
-          s2[j] = sg[j];
-          c2[j] = cb[j];
-          if (act[j]) {
-            advance(s2[j], c2[j]);
-            if (s2[j] <= sl[j]) load_b(b1[j], s2[j], c2[j]);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < JG; ++j) {
-          if (act[j]) {
-            apply_b(b0[j], vh[j], vl[j], accT[j], pj[j], sg[j], cb[j]);
-            sg[j] = s2[j];
-            cb[j] = c2[j];
-            act[j] = sg[j] <= sl[j];
-          }
-        }
-        any = false;
-#pragma unroll
-        for (int j = 0; j < JG; ++j) any |= act[j];
+        phase(std::integral_constant<int, 0>{});
         if (!any) break;
-        // items held in b1 are current; load the next ones into b0
-#pragma unroll
-        for (int j = 0; j < JG; ++j) {
-          s2[j] = sg[j];
-          c2[j] = cb[j];
-          if (act[j]) {
-            advance(s2[j], c2[j]);
-            if (s2[j] <= sl[j]) load_b(b0[j], s2[j], c2[j]);
-          }
+        phase(std::integral_constant<int, 1>{});
+        if constexpr (D > 2) {
+          if (!any) break;
+          phase(std::integral_constant<int, 2>{});
+          if (!any) break;
+          phase(std::integral_constant<int, 3>{});
         }
-#pragma unroll
-        for (int j = 0; j < JG; ++j) {
-          if (act[j]) {
-            apply_b(b1[j], vh[j], vl[j], accT[j], pj[j], sg[j], cb[j]);
-            sg[j] = s2[j];
-            cb[j] = c2[j];
-            act[j] = sg[j] <= sl[j];
-          }
-        }
-        any = false;
-#pragma unroll
-        for (int j = 0; j < JG; ++j) any |= act[j];
       }
 #pragma unroll
       for (int j = 0; j < JG; ++j)
@@ -343,9 +383,27 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < FM; ++j) acc[i][j] = mfma32(fa[f][i], fb[f][j], acc[i][j]);
   };
-  // One barrier per K-step.  Between two barriers: the DMA of the step after
-  // next, this step's fragment reads, the previous step's last 16-deep MFMA
-  // group and this step's first three.
+  // One barrier per K-step.  Between two barriers: the DMA of the step NS-1
+  // ahead (into the stage read by the step before), this step's fragment
+  // reads, the previous step's last 16-deep MFMA group and this step's first
+  // three.  The barrier waits only for the next step's DMA.
+  constexpr int kM = FN * FM, kD = FN + FM, kV = NWB + NXB;
+  // stage S's arrays, named directly (through a pointer table the compiler
+  // loses which LDS object a read touches and waits for every DMA in flight)
+  auto wst = [&](auto sc) -> uint16_t* {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) return w0;
+    else if constexpr (S == 1) return w1;
+    else if constexpr (S == 2) return w2;
+    else return w3;
+  };
+  auto xst = [&](auto sc) -> uint16_t* {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) return x0;
+    else if constexpr (S == 1) return x1;
+    else if constexpr (S == 2) return x2;
+    else return x3;
+  };
   auto step = [&](uint16_t* ws, uint16_t* xs, uint16_t* wnx, uint16_t* xnx, int knext)
                   __attribute__((always_inline)) {
     issue(wnx, xnx, knext);
@@ -357,23 +415,26 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
     mm(1);
     rd(ws, xs, 3, 1);
     mm(0);
-    constexpr int kM = FN * FM, kD = FN + FM, kV = NWB + NXB;
     __builtin_amdgcn_sched_group_barrier(0x100, kD, 0);
     interleave<kM, kV, 0x020>();
     interleave<kM, kD, 0x100>();
     interleave<kM, kD, 0x100>();
     interleave<kM, kD, 0x100>();
-    __syncthreads();
+    barrier_after_dma<(NS - 2) * kV>();
   };
 #pragma unroll
   for (int i = 0; i < FN; ++i) fa[1][i] = zero_bf16x8();
 #pragma unroll
   for (int j = 0; j < FM; ++j) fb[1][j] = zero_bf16x8();
   const int nk = (K + kBK - 1) / kBK;
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(w0, x0, w1, x1, (kt + 1) * kBK);
-    step(w1, x1, w0, x0, (kt + 2) * kBK);
+  // K-steps 0 .. NS-2 went out before the expand
+  barrier_after_dma<(NS - 2) * kV>();
+  for (int kt = 0; kt < nk; kt += NS) {
+    for_each_stage<NS>([&](auto sc) __attribute__((always_inline)) {
+      constexpr int S = decltype(sc)::value;
+      const auto pc = std::integral_constant<int, (S + NS - 1) % NS>{};  // the stage read last step
+      step(wst(sc), xst(sc), wst(pc), xst(pc), (kt + S + NS - 1) * kBK);
+    });
   }
   mm(1);
 

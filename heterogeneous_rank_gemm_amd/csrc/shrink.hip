@@ -22,6 +22,15 @@ namespace hrg {
 constexpr int kShrinkThreads = 256;
 constexpr int kRedLd = 65;  // padded row of the cross-wave reduction buffer
 
+__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ bf16x8 keep_bf(bool keep, uint4 v) {
+  const uint32_t m = keep ? 0xffffffffu : 0u;
+  return __builtin_bit_cast(bf16x8, make_uint4(v.x & m, v.y & m, v.z & m, v.w & m));
+}
+
+// NQ: 16-rank blocks held per item (the pool's rank rounded up to 16, in
+// blocks; an adapter of lower rank masks the rest)
+template <int NQ>
 __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64 * kRedLd], int tile, int split) {
   const int seg = a.tile_seg[tile];
   const int row0 = a.tile_row0[tile];
@@ -45,39 +54,47 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
     const int tok = a.perm[row0 + (rv[mb] ? p : 0)];
     xrow[mb] = a.X + (size_t)tok * K;
   }
-  const uint16_t* arow[4];
-  bool qv[4];
+  const uint16_t* arow[NQ];
+  bool qv[NQ];
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
+  for (int nb = 0; nb < NQ; ++nb) {
     const int q = 16 * nb + (l & 15);
     qv[nb] = q < rank;
     arow[nb] = Ap + (size_t)(qv[nb] ? q : 0) * K;
   }
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][NQ];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < NQ; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // 512-deep sub-chunks: wave w takes the 32-deep steps 32 w + 128 s of each;
+  // all of a sub-chunk's loads go out first (addresses clamped in bounds,
+  // values past the range masked), then its MFMAs
   const int koff = 8 * (l >> 4);
-  for (int k = k0 + 32 * w; k < k1; k += 128) {
-    const int kk = k + koff;
-    const bool kv = kk < k1;  // K is a multiple of 8: a lane's 8 elements are all in or all out
-    bf16x8 xa[4], ab[4];
+  for (int kb = k0; kb < k1; kb += 512) {
+    uint4 xv[4][4], av[4][NQ];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-      xa[mb] = (mb < nm && rv[mb] && kv) ? ld_bf16x8(xrow[mb] + kk) : zero_bf16x8();
+    for (int st = 0; st < 4; ++st) {
+      const int kc = min(kb + 128 * st + 32 * w + koff, K - 8);
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      ab[nb] = (nb < nq && qv[nb] && kv) ? ld_bf16x8(arow[nb] + kk) : zero_bf16x8();
+      for (int mb = 0; mb < 4; ++mb) xv[st][mb] = ld16(xrow[mb] + kc);
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      if (mb >= nm) continue;
+      for (int nb = 0; nb < NQ; ++nb) av[st][nb] = ld16(arow[nb] + kc);
+    }
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        if (nb >= nq) continue;
-        acc[mb][nb] = mfma16(xa[mb], ab[nb], acc[mb][nb]);
+    for (int st = 0; st < 4; ++st) {
+      const bool kv = kb + 128 * st + 32 * w + koff < k1;  // a lane's 8 elements are all in or out
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        if (mb >= nm) continue;
+        const bf16x8 xa = keep_bf(rv[mb] && kv, xv[st][mb]);
+#pragma unroll
+        for (int nb = 0; nb < NQ; ++nb) {
+          if (nb >= nq) continue;
+          acc[mb][nb] = mfma16(xa, keep_bf(qv[nb] && kv, av[st][nb]), acc[mb][nb]);
+        }
       }
     }
   }
@@ -87,7 +104,7 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
   for (int mb = 0; mb < 4; ++mb) {
     if (mb >= nm) continue;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
+    for (int nb = 0; nb < NQ; ++nb) {
       if (nb >= nq) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -111,16 +128,16 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
 
 // A fixed grid walks the (tile, split) items of the plan's tile list; the
 // split count is fixed by K on the host, the tile count only on the device.
+template <int NQ>
 __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
   __shared__ float red[4][64 * kRedLd];
   if (*a.status != 0) return;
   const int nitems = a.counts[1] * a.nsplit;
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
     __syncthreads();  // the previous item is done with red
-    shrink_item(a, red, item / a.nsplit, item % a.nsplit);
+    shrink_item<NQ>(a, red, item / a.nsplit, item % a.nsplit);
   }
 }
-
 
 // V = s * (sum of the partial planes in split order), written as bf16 hi + lo
 // for every sorted row of an adapter segment and q < 16 * ceil(rank / 16).
@@ -146,7 +163,13 @@ __global__ __launch_bounds__(256) void shrink_finalize_kernel(ShrinkArgs a, int 
 
 hipError_t launch_shrink(const ShrinkArgs& a, int grid, int ksplit, int T, hipStream_t s) {
   if (grid <= 0 || ksplit <= 0 || T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(shrink_kernel, dim3(grid), dim3(kShrinkThreads), 0, s, a);
+  const int nq = a.u_ld / 16;
+  if (nq <= 1)
+    hipLaunchKernelGGL(shrink_kernel<1>, dim3(grid), dim3(kShrinkThreads), 0, s, a);
+  else if (nq == 2)
+    hipLaunchKernelGGL(shrink_kernel<2>, dim3(grid), dim3(kShrinkThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(shrink_kernel<4>, dim3(grid), dim3(kShrinkThreads), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n = T * a.u_ld;
