@@ -43,8 +43,8 @@ struct lora_pool_s {
   uint16_t* v_hi = nullptr;          // [max_tokens][rpad] s * U, bf16 high part (sorted rows)
   uint16_t* v_lo = nullptr;          // [max_tokens][rpad] bf16 low part
   // decode-path workspace
-  float* dec_part = nullptr;         // [ceil(max d_in / 512)][64][max d_out] base partials
-  float* dec_upart = nullptr;        // [ceil(max d_in / 512)][64][rpad] shrink partials
+  float* dec_part = nullptr;         // [ceil(max d_in / 1024)][64][max d_out] base partials
+  float* dec_upart = nullptr;        // [ceil(max d_in / 1024)][64][rpad] shrink partials
   std::vector<int32_t> h_id2slot, h_slot_rank;
   std::vector<float> h_slot_scale;
   std::set<int32_t> free_slots;      // lowest free slot first
@@ -155,16 +155,23 @@ lora_status_t decode_apply(lora_pool_s* P, int32_t module, const lora_bf16_t* X,
   a.b_off = P->b_off[module];
   a.part = P->dec_part;
   a.upart = P->dec_upart;
+  a.direct = P->max_ids <= P->max_adapters ? 1 : 0;
+  a.max_slots = P->max_adapters;
+  a.rmax = P->max_rank;
   a.u_ld = P->rpad;
   a.status = P->status;
   a.NT = ceil_div(N, hrg::kDecodeTileRows);
   a.KS = ceil_div(K, hrg::kDecodeChunk);
   a.lora = lora ? 1 : 0;
   if (lora) {
-    // A-tile items: (adapter, 16-rank block); at most min(T, resident) adapters
+    // A items: (adapter, 16-rank block); at most min(T, resident) adapters.
+    // They ride in the W-tile blocks (na waves each, 1, 2 or 4); the rest
+    // get extra blocks of A waves only.
     const int loaded = P->max_adapters - (int)P->free_slots.size();
-    a.n_atiles = ceil_div(std::min(T, loaded) * (P->rpad / 16), 8);
-    a.a_blocks = round_up(a.n_atiles * a.KS, 8);
+    const int items = std::min(T, loaded) * (P->rpad / 16);
+    const int per_tile = ceil_div(items, a.NT);
+    a.na = per_tile <= 1 ? 1 : per_tile <= 2 ? 2 : 4;
+    a.a_tiles = ceil_div(std::max(0, items - a.NT * a.na), 4 + a.na);
   }
   return hrg::launch_decode(a, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
@@ -302,7 +309,8 @@ lora_status_t lora_load_adapter(lora_pool_t P, int32_t id, int32_t rank, float a
   if (P->h_id2slot[id] >= 0) return LORA_ERR_EXISTS;
   if (P->free_slots.empty()) return LORA_ERR_POOL_FULL;
   DeviceGuard g(P->device);
-  const int32_t slot = *P->free_slots.begin();
+  // a direct-mapped pool (max_ids <= max_adapters) keeps adapter id in slot id
+  const int32_t slot = P->max_ids <= P->max_adapters ? id : *P->free_slots.begin();
   uint16_t* base = P->pages + (size_t)slot * P->slot_elems;
   for (int32_t m = 0; m < P->n_modules; ++m) {
     const size_t na = (size_t)P->d_in[m] * rank, nb = (size_t)rank * P->d_out[m];

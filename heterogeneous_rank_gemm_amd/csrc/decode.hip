@@ -6,18 +6,26 @@
 // tile needs all of it, so it is staged once per K chunk in LDS and never
 // re-read from L2 per 16 columns.
 //
-// Launch 1 (decode_main): a grid of (row tile, 512-wide K chunk) blocks of
-// 8 waves.  Every block stages X[:, chunk] (64 x 512 bf16) in LDS; each wave
-// owns a block of 16 rows, loads its whole 16 x 512 slice up front, and runs
-// the bf16 MFMA 16x16x32 against the X chunk.  Two kinds of row tiles:
-//   * W tiles: 8 x 16 rows of the base weight; the fp32 partial sums go to
-//     part[chunk][t][n].
-//   * A tiles: 8 items (adapter, 16 ranks), i.e. 16 rows of an adapter's A^T
-//     page.  The block groups the batch by adapter id (LoRA-Land post,
-//     section "2. multi-LoRA batch scheduling": Grouped Multi-LoRA
-//     Execution), so each adapter's page is streamed once per chunk; the
-//     partial shrink U_c[t, q] = X[t, chunk] . A[chunk, q] is kept for the
-//     adapter's own tokens in upart[chunk][t][q].
+// Launch 1 (decode_main): a grid of (column tile, 1024-deep K chunk) blocks.
+// Each block's first four waves copy X[:, chunk] (64 x 1024 bf16, 132 KB with
+// row padding) into LDS by direct DMA and own 16 rows of W each; every wave
+// loads its whole 16 x 1024 slice into registers up front (32 KB in flight per
+// wave) and runs bf16 MFMA 16x16x32 against the X chunk as the slice lands.
+// Two kinds of waves:
+//   * W waves (the first four of a block): 16 rows of the base weight; the
+//     fp32 partial sums go to part[chunk][t][n].
+//   * A waves (the rest): one item (adapter, 16 ranks) each, i.e. 16 rows of
+//     an adapter's A^T page.  The wave groups the batch by adapter id
+//     (LoRA-Land post, section "2. multi-LoRA batch scheduling": Grouped
+//     Multi-LoRA Execution), so each adapter's page is streamed once per
+//     chunk; the partial shrink U_c[t, q] = X[t, chunk] . A[chunk, q] is kept
+//     for the adapter's own tokens in upart[chunk][t][q].
+// Riding in the W tiles' blocks, the A items add no second round of blocks.
+// Items past what those waves hold go to extra blocks of A waves only.  The
+// A waves' id loads go out before the weight stream fills the memory
+// queues; a load issued behind that stream waits for most of it, so every
+// further dependent round costs several microseconds.  A direct-mapped pool
+// (adapter id in slot id) therefore needs no slot-table round at all.
 // Launch 2 (decode_combine), one thread per (token, 4 columns):
 //     V[t, q]   = (alpha/r) * sum_chunks upart[c][t][q]
 //     out[t, n] = bf16( sum_chunks part[c][t][n]  +  sum_q V[t, q] B_i[q, n] )
@@ -25,20 +33,21 @@
 //   report, section 2.1: the low-rank branch is added back to the main path).
 //   Rows with id -1 get no LoRA term at all.
 //
-// The base-only entry runs the same launches without A tiles and without the
-// expand, so id -1 rows match it bit for bit.  Every block that depends on the
-// ids validates all of them the same way (strict mode, icman report section
-// 4.1): on an invalid batch nothing is written to `out`.
+// The base-only entry runs the same launches without A waves and without the
+// expand, so id -1 rows match it bit for bit.  Every combine block validates
+// all the ids the same way (strict mode, icman report section 4.1): on an
+// invalid batch nothing is written to `out`.
 #include "common.h"
 #include "internal.h"
 
 namespace hrg {
 
-constexpr int kMainThreads = 512;
-constexpr int kMainWaves = kMainThreads / 64;
-constexpr int kSteps = kDecodeChunk / 32;  // MFMA K steps per chunk
+constexpr int kSteps = kDecodeChunk / 32;  // MFMA K steps per chunk (32)
 constexpr int kXs = kDecodeChunk + 8;      // LDS row of the X chunk (16-byte pad)
-static_assert(kMainWaves * 16 == kDecodeTileRows, "tile rows");
+constexpr uint32_t kOobOff = 0x80000000u;  // buffer offset past every operand
+static_assert(4 * 16 == kDecodeTileRows, "tile rows");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 __device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 // v if keep, else zero -- with a mask, so the compiler never selects between
@@ -79,105 +88,129 @@ __device__ __forceinline__ TokInfo token_info(const DecodeArgs& a, int t) {
   return ti;
 }
 
-__global__ __launch_bounds__(kMainThreads) __attribute__((amdgpu_waves_per_eu(4))) void decode_main(DecodeArgs a) {
+// Waits until at most N of this wave's vector-memory operations are
+// outstanding and every LDS access has completed, then joins the workgroup
+// barrier.  (__syncthreads() would wait for all of them.)
+template <int N>
+__device__ __forceinline__ void barrier_after(void) {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(N) : "memory");
+}
+
+// NA: A waves riding in each W-tile block (0 on the base-only path).
+template <int NA>
+__global__ __launch_bounds__(64 * (4 + NA)) void decode_main(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[64 * kXs];
-  __shared__ int s_bad;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g4 = lane >> 4, r16 = lane & 15;
   const int T = a.T, N = a.N, K = a.K;
-  if (a.lora && *a.status != 0) return;
 
-  // Block order: the A blocks first (a_blocks, a multiple of 8, so they start
-  // early and spread over all XCDs round-robin), then the W blocks.  For the W
-  // blocks the hardware hands block b to XCD (b mod 8); each XCD takes a
-  // contiguous run of (tile, chunk) pairs so neighbouring tiles share its L2.
+  // Block order: the W tiles first, the hardware handing block b to XCD
+  // (b mod 8) -- each XCD takes a contiguous run of (tile, chunk) pairs so
+  // neighbouring tiles share its L2 -- then the blocks of A waves only.
+  const int G = a.NT * a.KS;
   int tile, c;
-  bool a_tile;
-  if ((int)blockIdx.x < a.a_blocks) {
-    a_tile = true;
-    tile = a.NT + (int)blockIdx.x / a.KS;
-    c = (int)blockIdx.x % a.KS;
-    if (tile >= a.NT + a.n_atiles) return;  // padding block
-  } else {
-    a_tile = false;
-    const int g = (int)blockIdx.x - a.a_blocks;
-    const int G = a.NT * a.KS;
+  bool w_block;
+  if ((int)blockIdx.x < G) {
+    w_block = true;
+    const int g = (int)blockIdx.x;
     const int xcd = g % 8, qd = G / 8, rm = G % 8;
     const int logical = xcd * qd + min(xcd, rm) + g / 8;
     tile = logical / a.KS;
     c = logical % a.KS;
+  } else {
+    w_block = false;
+    const int g = (int)blockIdx.x - G;
+    tile = g / a.KS;
+    c = g % a.KS;
   }
   const int k0 = c * kDecodeChunk, klen = min(K, k0 + kDecodeChunk) - k0;
 
   // ---- this wave's 16 rows ----
   const uint16_t* row = nullptr;  // row r16 of the block of 16, at k0
   bool row_ok = false;
-  int n0 = 0;                     // W tile: first column
-  int qb = 0;                     // A tile: rank block of the adapter
-  uint64_t members = 0;           // A tile: tokens of the adapter
-  if (!a_tile) {
+  int n0 = 0;                     // W wave: first column
+  int qb = 0;                     // A wave: rank block of the adapter
+  uint64_t members = 0;           // A wave: tokens of the adapter
+  const bool a_wave = !w_block || w >= 4;
+  if (!a_wave) {
     n0 = tile * kDecodeTileRows + 16 * w;
     row_ok = n0 + r16 < N;
     row = a.W + (size_t)(row_ok ? n0 + r16 : 0) * K + k0;
   } else {
-    // one round of lookups: lane t holds token t's id, slot and rank
-    TokInfo ti = token_info(a, lane);
-    if (w == 0 && lane == 0) s_bad = 0;
-    __syncthreads();
-    if (w == 0 && ti.bad) atomicMax(&s_bad, ti.bad);
-    __syncthreads();
-    if (s_bad) return;  // the combine launch rejects the batch
-    // item = the (8 (tile - NT) + w)-th (adapter, 16-rank block) of the batch,
-    // adapters in order of first occurrence
-    const int item = 8 * (tile - a.NT) + w;
-    uint64_t todo = __ballot(ti.id >= 0);
-    int seen = 0;
-    while (todo) {
-      const int leader = __builtin_ctzll(todo);  // wave-uniform: readlane, not an LDS shuffle
-      const int v = __builtin_amdgcn_readlane(ti.id, leader);
-      const int r = __builtin_amdgcn_readlane(ti.rank, leader);
-      const uint64_t m = __ballot(ti.id == v) & todo;
-      todo &= ~m;
-      const int nq = (r + 15) / 16;
-      if (item < seen + nq) {
-        const int slot = __builtin_amdgcn_readlane(ti.slot, leader);
-        qb = item - seen;
-        members = m;
-        const int q = 16 * qb + r16;
-        row_ok = q < r;
-        row = a.pages + (size_t)slot * a.slot_stride + a.a_off + (size_t)(row_ok ? q : 0) * K + k0;
-        break;
-      }
-      seen += nq;
+    // item = the item-th (adapter, 16-rank block) of the batch, adapters in
+    // order of first occurrence.  Lane t holds token t's id.  A direct-mapped
+    // pool keeps adapter id in slot id, so the page address follows from the
+    // ids alone (every rank block up to the pool's padded rank is an item;
+    // rows past an adapter's rank are zero); otherwise one more round of
+    // loads fetches each token's slot and rank.  Both load rounds go out
+    // before the weight stream fills the memory queues.
+    const int item = w_block ? tile + a.NT * (w - 4) : a.NT * NA + (4 + NA) * tile + w;
+    int id = -1, slot = -1, rank = 0, bad = 0;
+    if (a.direct) {
+      if (lane < T) id = a.ids[lane];
+      if (id >= a.max_slots || id < -1) bad = 1;  // the combine launch rejects the batch
+      slot = id;
+      rank = a.u_ld;
+    } else {
+      const TokInfo ti = token_info(a, lane);
+      id = ti.id;
+      slot = ti.slot;
+      rank = ti.rank;
+      bad = ti.bad;
     }
+    if (__ballot(bad != 0) == 0) {
+      uint64_t todo = __ballot(id >= 0);
+      int seen = 0;
+      while (todo) {
+        const int leader = __builtin_ctzll(todo);  // wave-uniform: readlane, not an LDS shuffle
+        const int v = __builtin_amdgcn_readlane(id, leader);
+        const int r = __builtin_amdgcn_readlane(rank, leader);
+        const uint64_t m = __ballot(id == v) & todo;
+        todo &= ~m;
+        const int nq = (r + 15) / 16;
+        if (item < seen + nq) {
+          const int sl = __builtin_amdgcn_readlane(slot, leader);
+          qb = item - seen;
+          members = m;
+          const int q = 16 * qb + r16;
+          row_ok = q < min(r, a.rmax);
+          row = a.pages + (size_t)sl * a.slot_stride + a.a_off + (size_t)(row_ok ? q : 0) * K + k0;
+          break;
+        }
+        seen += nq;
+      }
+    }
+    // drain the lookups here, so that no wait for them is left to the merge
+    // with the W path (where it would also wait for the X DMA below)
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   }
-  const bool active = row != nullptr;  // an A-tile wave past the last item has nothing to do
+  const bool active = row != nullptr;  // an A wave past the last item has nothing to do
   if (!active) row = a.X + k0;         // dummy in-bounds source, results discarded
 
-  // ---- loads: X chunk first (needed first), then the whole 16 x 512 slice ----
-  // X goes through registers (8 x 16 bytes per thread) so that writing it to
-  // LDS waits only for the X loads; the slice's MFMAs then start as soon as
-  // their own step has landed (the vector-memory counter retires in order).
-  constexpr int kXLoads = 64 * (kDecodeChunk / 8) / kMainThreads;  // 8 per thread
-  uint4 xv[kXLoads];
+  // ---- X chunk -> LDS by DMA: waves 0..3 copy tokens 16w .. 16w+15, two
+  // 1-KB pieces per token row.  Rows >= T and columns >= K read zeros.  (An
+  // A wave's lookups above have completed, so no wait for them lands between
+  // this DMA and the slice loads below.)
+  if (w < 4) {
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.X, (short)0, T * K * 2, 0x00020000);
 #pragma unroll
-  for (int i = 0; i < kXLoads; ++i) {
-    const int idx = tid + i * kMainThreads;
-    const int r = idx / (kDecodeChunk / 8), kc = (idx % (kDecodeChunk / 8)) * 8;
-    xv[i] = ld16(a.X + (size_t)min(r, T - 1) * K + k0 + min(kc, klen - 8));
+    for (int i = 0; i < 32; ++i) {
+      const int r = 16 * w + (i >> 1), h = i & 1;
+      const int k = k0 + 512 * h + 8 * lane;
+      const uint32_t off = (r < T && k < K) ? (uint32_t)(r * K + k) * 2u : kOobOff;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(xs + r * kXs + 512 * h), 16, off, 0, 0, 0);
+    }
   }
-  __builtin_amdgcn_sched_barrier(0);
+
+
+  // ---- the whole 16 x 1024 slice, issued at once ----
   uint4 rw[kSteps];
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) rw[s] = ld16(row + min(32 * s + 8 * g4, klen - 8));
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < kXLoads; ++i) {
-    const int idx = tid + i * kMainThreads;
-    const int r = idx / (kDecodeChunk / 8), kc = (idx % (kDecodeChunk / 8)) * 8;
-    *reinterpret_cast<uint4*>(xs + r * kXs + kc) = keep_if(r < T && kc < klen, xv[i]);
-  }
-  __syncthreads();
+  // the X DMA (issued before the slice) has landed in every wave
+  barrier_after<kSteps>();
   if (!active) return;
 
   const int nm = (T + 15) / 16;
@@ -188,13 +221,13 @@ __global__ __launch_bounds__(kMainThreads) __attribute__((amdgpu_waves_per_eu(4)
   for (int s = 0; s < kSteps; ++s) {
     const int k = 32 * s + 8 * g4;
     const bf16x8 wb = __builtin_bit_cast(bf16x8, keep_if(k < klen && row_ok, rw[s]));
-    // all four 16-token row blocks: rows >= T hold stale LDS and are never stored
+    // all four 16-token row blocks: rows >= T hold zeros and are never stored
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = mfma16(lds_bf16x8(xs + (16 * i + r16) * kXs + k), wb, acc[i]);
   }
 
   // ---- partial tile out: acc[i][e] is token 16 i + 4 g4 + e, row r16 of the block ----
-  if (!a_tile) {
+  if (!a_wave) {
     if (row_ok) {
       float* pp = a.part + (size_t)c * 64 * N + n0 + r16;
 #pragma unroll
@@ -222,88 +255,129 @@ __global__ __launch_bounds__(kMainThreads) __attribute__((amdgpu_waves_per_eu(4)
 }
 
 // ---------------------------------------------------------------------------
-// combine: block = 16 tokens x 64 columns, thread = (token, 4 columns)
+// combine: block = 16 tokens x 64 columns, thread = (token, 4 columns).
+// Round 1 of loads depends on nothing: the ids, the chunk partials and the
+// shrink partials of the block's V.  Round 2: every token's {slot, rank,
+// scale} (each block checks the whole batch, strict mode) and, in a
+// direct-mapped pool, the thread's B rows.  Otherwise the B rows need the slot
+// and come in a third round.
 constexpr int kCombThreads = 256;
+constexpr int kVPer = 16 * kMaxRank / kCombThreads;  // V elements per thread
+
+// sum over the KS chunk planes p[c * stride], c = 0, 1, ... in order; loads
+// issued four at a time
+__device__ __forceinline__ float sum_chunks(const float* p, size_t stride, int KS) {
+  float s = 0.f;
+  for (int c0 = 0; c0 < KS; c0 += 4) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = p[(size_t)min(c0 + j, KS - 1) * stride];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (c0 + j < KS) s += v[j];
+  }
+  return s;
+}
 
 __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
   __shared__ float vsh[16][kMaxRank + 1];
-  __shared__ int t_slot[16], t_rank[16];
-  __shared__ float t_scale[16];
-  __shared__ int flag;
+  __shared__ int s_id[64];
+  __shared__ int4 s_info[16];  // the block's tokens: {slot (-1: none), rank, scale bits, 0}
+  __shared__ int s_bad;
   const int tid = threadIdx.x;
   const int T = a.T, N = a.N, KS = a.KS;
   const int t0 = blockIdx.y * 16;
-  if (a.lora) {
-    if (*a.status != 0) return;
-    if (tid == 0) flag = 0;
-    __syncthreads();
-    if (tid < 64) {
-      const TokInfo ti = token_info(a, tid);  // every token: strict-mode check
-      if (ti.bad) atomicMax(&flag, ti.bad);
-      if (tid >= t0 && tid < t0 + 16) {
-        t_slot[tid - t0] = ti.slot;
-        t_rank[tid - t0] = ti.rank;
-        t_scale[tid - t0] = ti.scale;
-      }
-    }
-    __syncthreads();
-    if (flag) {
-      if (tid == 0 && blockIdx.x == 0 && blockIdx.y == 0) atomicMax(a.status, flag);
-      return;  // strict mode: out untouched
-    }
-  }
   const int tr = tid >> 4, quad = tid & 15;
   const int t = t0 + tr;
   const int n = blockIdx.x * 64 + quad * 4;
   const bool mine = t < T && n < N;
-  // independent loads first: the chunk partials and the first 16 rows of B
+
+  // ---- round 1 ----
+  int st = 0;
+  if (a.lora) {
+    st = *a.status;
+    if (tid < 64) s_id[tid] = tid < T ? a.ids[tid] : -1;
+    if (tid == 0) s_bad = 0;
+  }
   const float* pp = a.part + (size_t)min(t, T - 1) * N + min(n, N - 4);
-  float4 pv[8];
-  const int slot = a.lora ? t_slot[tr] : -1;
-  const int rank = a.lora ? t_rank[tr] : 0;
-  // B^T page in 16-rank chunks [rpad/16][N][16]: the 4 columns' first chunk is
-  // 64 contiguous values (ranks past the adapter's rank are zero)
-  const uint16_t* Bp = a.pages + (size_t)max(slot, 0) * a.slot_stride + a.b_off + (size_t)min(n, N - 4) * 16;
+  float4 pv[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) pv[j] = *reinterpret_cast<const float4*>(pp + (size_t)min(j, KS - 1) * 64 * N);
+  float u[kVPer];
   uint4 bv[8];
-  if (slot >= 0) {
+  int slot = -1, rank = 0;
+  const uint16_t* Bp = nullptr;
+  if (a.lora) {
+    // V[t][q] = (alpha / r) * sum of the shrink partials in chunk order
+#pragma unroll
+    for (int e = 0; e < kVPer; ++e) {
+      const int idx = tid + kCombThreads * e;
+      const int r = idx / kMaxRank, q = idx % kMaxRank;
+      const int tt = min(t0 + r, T - 1);
+      u[e] = q < a.u_ld ? sum_chunks(a.upart + (size_t)tt * a.u_ld + q, (size_t)64 * a.u_ld, KS) : 0.f;
+    }
+    __syncthreads();  // s_id
+
+    // ---- round 2 ----
+    if (tid < 64) {
+      const int id = s_id[tid];
+      int bad = 0;
+      int4 e = make_int4(-1, 0, 0, 0);
+      if (id < -1 || id >= a.max_ids) {
+        bad = kStatusIdRange;
+      } else if (id >= 0) {
+        e = a.id_info[id];  // {slot, rank, scale bits}
+        if (e.x < 0) bad = kStatusNotLoaded;
+      }
+      if (bad) atomicMax(&s_bad, bad);
+      if (tid >= t0 && tid < t0 + 16) s_info[tid - t0] = bad ? make_int4(-1, 0, 0, 0) : e;
+    }
+    // B^T page in 16-rank chunks [rpad/16][N][16]: the 4 columns' chunk is 64
+    // contiguous values (ranks past the adapter's rank are zero)
+    if (a.direct && mine) {
+      const int id = s_id[t];
+      if (id >= 0 && id < a.max_slots) {
+        Bp = a.pages + (size_t)id * a.slot_stride + a.b_off + (size_t)n * 16;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) bv[k] = *reinterpret_cast<const uint4*>(Bp + 8 * k);
+      }
+    }
+    __syncthreads();  // s_bad, s_info
+    if (s_bad) {
+      if (tid == 0 && blockIdx.x == 0 && blockIdx.y == 0) atomicMax(a.status, s_bad);
+      return;  // strict mode: out untouched
+    }
+    if (st != 0) return;  // a pending error (st is the same in every thread)
+#pragma unroll
+    for (int e = 0; e < kVPer; ++e) {
+      const int idx = tid + kCombThreads * e;
+      const int r = idx / kMaxRank, q = idx % kMaxRank;
+      const int4 inf = s_info[r];
+      const bool on = t0 + r < T && inf.x >= 0 && q < inf.y;
+      vsh[r][q] = on ? __builtin_bit_cast(float, inf.z) * u[e] : 0.f;
+    }
+    __syncthreads();  // vsh
+    slot = s_info[tr].x;
+    rank = s_info[tr].y;
+  }
+  if (!mine) return;
+  if (slot >= 0 && !a.direct) {
+    // ---- round 3 (pool not direct-mapped) ----
+    Bp = a.pages + (size_t)slot * a.slot_stride + a.b_off + (size_t)n * 16;
 #pragma unroll
     for (int k = 0; k < 8; ++k) bv[k] = *reinterpret_cast<const uint4*>(Bp + 8 * k);
   }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) pv[j] = *reinterpret_cast<const float4*>(pp + (size_t)min(j, KS - 1) * 64 * N);
-  if (a.lora) {
-    // V[t][q] = (alpha / r) * sum of the shrink partials in chunk order
-    for (int idx = tid; idx < 16 * kMaxRank; idx += kCombThreads) {
-      const int r = idx / kMaxRank, q = idx % kMaxRank;
-      float v = 0.f;
-      if (t0 + r < T && q < t_rank[r]) {
-        const float* up = a.upart + (size_t)(t0 + r) * a.u_ld + q;
-        float u = up[0];
-        for (int c0 = 1; c0 < KS; c0 += 8) {
-          float uv[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) uv[j] = up[(size_t)min(c0 + j, KS - 1) * 64 * a.u_ld];
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (c0 + j < KS) u += uv[j];
-        }
-        v = t_scale[r] * u;
-      }
-      vsh[r][q] = v;
-    }
-    __syncthreads();
-  }
-  if (!mine) return;
+
   // base: chunk partials in chunk order
   float4 s = pv[0];
-  for (int c0 = 0; c0 < KS; c0 += 8) {
+  for (int c0 = 0; c0 < KS; c0 += 4) {
     if (c0 > 0) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
+      for (int j = 0; j < 4; ++j)
         pv[j] = *reinterpret_cast<const float4*>(pp + (size_t)min(c0 + j, KS - 1) * 64 * N);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
       if (c0 + j > 0 && c0 + j < KS) {
         s.x += pv[j].x;
         s.y += pv[j].y;
@@ -324,16 +398,16 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
       for (int col = 0; col < 4; ++col) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const uint4 u = bv[2 * col + h];
+          const uint4 w = bv[2 * col + h];
           const float* vh = v + 8 * h;
-          e[col] += vh[0] * lo_f(u.x);
-          e[col] += vh[1] * hi_f(u.x);
-          e[col] += vh[2] * lo_f(u.y);
-          e[col] += vh[3] * hi_f(u.y);
-          e[col] += vh[4] * lo_f(u.z);
-          e[col] += vh[5] * hi_f(u.z);
-          e[col] += vh[6] * lo_f(u.w);
-          e[col] += vh[7] * hi_f(u.w);
+          e[col] += vh[0] * lo_f(w.x);
+          e[col] += vh[1] * hi_f(w.x);
+          e[col] += vh[2] * lo_f(w.y);
+          e[col] += vh[3] * hi_f(w.y);
+          e[col] += vh[4] * lo_f(w.z);
+          e[col] += vh[5] * hi_f(w.z);
+          e[col] += vh[6] * lo_f(w.w);
+          e[col] += vh[7] * hi_f(w.w);
         }
       }
     }
@@ -348,7 +422,14 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(decode_main, dim3(a.a_blocks + a.NT * a.KS), dim3(kMainThreads), 0, s, a);
+  const dim3 grid((a.NT + a.a_tiles) * a.KS);
+  switch (a.na) {
+    case 0: hipLaunchKernelGGL(decode_main<0>, grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL(decode_main<1>, grid, dim3(320), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(decode_main<2>, grid, dim3(384), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(decode_main<4>, grid, dim3(512), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine, dim3((a.N + 63) / 64, (a.T + 15) / 16), dim3(kCombThreads), 0, s, a);

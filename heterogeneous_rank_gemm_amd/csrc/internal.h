@@ -94,8 +94,8 @@ struct GemmArgs {
 // the base GEMM (W tiles) and of the shrink (A tiles), launch 2 combines them
 // with the expand.  Workspace: part [KS][64][N] and upart [KS][64][u_ld] (fp32).
 constexpr int kDecodeMaxT = 64;
-constexpr int kDecodeTileRows = 128;  // rows per tile (8 waves x 16)
-constexpr int kDecodeChunk = 512;     // K per block
+constexpr int kDecodeTileRows = 64;   // W rows per block (4 waves x 16)
+constexpr int kDecodeChunk = 1024;    // K per block
 
 struct DecodeArgs {
   const uint16_t* X;      // [T][K]
@@ -110,11 +110,15 @@ struct DecodeArgs {
   size_t a_off, b_off;
   float* part;            // [KS][64][N]
   float* upart;           // [KS][64][u_ld]
+  int32_t direct;         // pool keeps adapter id in slot id (max_ids <= max_adapters)
+  int32_t max_slots;      // resident slots of the pool
+  int32_t rmax;           // rows of an A page (the pool's max rank)
   int32_t u_ld;
   int32_t* status;
-  int32_t NT, n_atiles;   // W tiles, A tiles (0 on the base-only path)
+  int32_t NT;             // W tiles (kDecodeTileRows rows each)
   int32_t KS;             // K chunks
-  int32_t a_blocks;       // blocks of the A tiles, n_atiles * KS rounded up to 8
+  int32_t na;             // A waves riding in each W-tile block: 0, 1, 2 or 4 (0: base-only)
+  int32_t a_tiles;        // extra blocks of 4 + na A waves, per K chunk
   int32_t lora;
 };
 

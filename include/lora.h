@@ -105,7 +105,10 @@ lora_status_t lora_pool_destroy(lora_pool_t pool);
  *          A[m], B[m] may point to host or device memory; they are copied
  *          before the call returns and may be freed afterwards.
  *
- * Takes the lowest free slot.  An id already resident returns EXISTS
+ * Slot choice: a pool with max_ids <= max_adapters is direct-mapped and
+ * keeps adapter id in slot id (the decode kernels then address its pages
+ * from the ids alone, without a round of slot-table loads); otherwise the
+ * adapter takes the lowest free slot.  An id already resident returns EXISTS
  * ([icman] 4.3 warns against silent overwrites); a full pool returns
  * POOL_FULL (eviction is the caller's policy).  Synchronises `stream`.
  */

@@ -104,9 +104,12 @@ def test_apply_argument_errors():
     p.close()
 
 
+@pytest.mark.parametrize("slots", [3, 8], ids=["slot-table", "direct-mapped"])
 @pytest.mark.parametrize("bad,status", [(3, "NOT_LOADED"), (8, "ID_RANGE"), (-2, "ID_RANGE")])
-def test_strict_mode_leaves_output_untouched(bad, status):
-    p = _pool()
+def test_strict_mode_leaves_output_untouched(bad, status, slots):
+    # 8 slots for 8 ids: the pool keeps adapter id in slot id; 3 slots: ids
+    # reach their pages through the slot table
+    p = _pool(max_adapters=slots)
     p.load_adapter(0, 4, 8.0, *_ab(4))
     T = 40
     X = torch.randn((T, 128), device="cuda").to(torch.bfloat16)
@@ -131,7 +134,7 @@ def test_strict_mode_leaves_output_untouched(bad, status):
     torch.cuda.synchronize()
     assert not torch.equal(out, sentinel)
     # after the error the pool computes exactly what a fresh pool computes
-    q = _pool()
+    q = _pool(max_adapters=slots)
     q.load_adapter(0, 4, 8.0, *_ab(4))
     ref = torch.empty_like(out)
     q.apply(0, X, ok_ids, W, ref)

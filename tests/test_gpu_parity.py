@@ -160,6 +160,31 @@ def test_ragged_parity(T, d_in, d_out, ranks, max_rank, id_lo):
     c.close()
 
 
+# a pool with more ids than slots reaches pages through the slot table (slot !=
+# id); one with as many slots as ids keeps adapter id in slot id
+INDIRECT = [
+    (40, 1032, 520, (64, 3, 17), 64),
+    (64, 4104, 264, (16,), 16),
+    (130, 520, 1160, (8, 16, 32), 32),
+]
+
+
+@pytest.mark.parametrize("T,d_in,d_out,ranks,max_rank", INDIRECT)
+def test_slot_table_pool_parity(T, d_in, d_out, ranks, max_rank):
+    _say(f"[slot table] T={T} d_in={d_in} d_out={d_out} ranks={ranks}")
+    n_ids, resident = 9, [1, 4, 5, 7, 8]   # 5 slots for 9 ids: slots 0..4 hold ids 1, 4, 5, 7, 8
+    wl = wk.small_workload(T, d_in, d_out, n_ids, max_rank, ranks, key=300 + T)
+    rng = np.random.Generator(np.random.PCG64(T))
+    ids = rng.choice(np.array([-1] + resident, np.int32), size=T)
+    c = _case(wl, ids=ids, adapters=resident, max_adapters=len(resident))
+    assert [c.pool.query(i)[0] for i in resident] == list(range(len(resident)))
+    out = c.apply(0)
+    torch.cuda.synchronize()
+    assert c.pool.status() == "OK"
+    _parity(out, c.oracle(0), f"slot table T={T}")
+    c.close()
+
+
 # --------------------------------------------------------------------------
 # the five workloads
 # --------------------------------------------------------------------------
