@@ -43,6 +43,7 @@ struct lora_pool_s {
   uint16_t* v_hi = nullptr;          // [max_tokens][rpad] s * U, bf16 high part (sorted rows)
   uint16_t* v_lo = nullptr;          // [max_tokens][rpad] bf16 low part
   // decode-path workspace
+  float* E = nullptr;                // [kMaxSmallRows][max d_out] small-segment expand rows
   float* dec_part = nullptr;         // [ceil(max d_in / 1024)][64][max d_out] base partials
   float* dec_upart = nullptr;        // [ceil(max d_in / 1024)][64][rpad] shrink partials
   std::vector<int32_t> h_id2slot, h_slot_rank;
@@ -81,9 +82,9 @@ int max_tiles_for(const lora_pool_s* P) {
 lora_status_t plan_alloc(lora_pool_s* P, lora_plan_s** out) {
   const size_t Tc = (size_t)P->max_tokens;
   const int mt = max_tiles_for(P);
-  // perm, inv, row_seg (Tc each); seg_id, seg_slot, seg_rank, seg_scale (Tc+1);
-  // seg_off (Tc+2); tile_seg, tile_row0 (mt); counts (4)
-  const size_t n32 = 3 * Tc + 4 * (Tc + 1) + (Tc + 2) + 2 * (size_t)mt + 4;
+  // perm, inv, row_seg, erow (Tc each); seg_id, seg_slot, seg_rank, seg_scale,
+  // seg_e0 (Tc+1); seg_off (Tc+2); tile_seg, tile_row0 (mt); small_seg; counts (4)
+  const size_t n32 = 4 * Tc + 5 * (Tc + 1) + (Tc + 2) + 2 * (size_t)mt + hrg::kMaxSmallRows + 4;
   lora_plan_s* pl = new (std::nothrow) lora_plan_s();
   if (!pl) return LORA_ERR_OOM;
   int32_t* blk = nullptr;
@@ -105,6 +106,9 @@ lora_status_t plan_alloc(lora_pool_s* P, lora_plan_s** out) {
   pl->tab.seg_off = take(Tc + 2);
   pl->tab.tile_seg = take(mt);
   pl->tab.tile_row0 = take(mt);
+  pl->tab.erow = take(Tc);
+  pl->tab.seg_e0 = take(Tc + 1);
+  pl->tab.small_seg = take(hrg::kMaxSmallRows);
   pl->tab.counts = take(4);
   pl->tab.max_tiles = mt;
   *out = pl;
@@ -250,7 +254,8 @@ lora_status_t lora_pool_create(lora_pool_t* pool, int32_t max_adapters, int32_t 
   }
   const size_t ks_max = (max_din + hrg::kDecodeChunk - 1) / hrg::kDecodeChunk;
   if (ok)
-    ok = dmalloc(&P->dec_upart, ks_max * hrg::kDecodeMaxT * P->rpad) == hipSuccess &&
+    ok = dmalloc(&P->E, (size_t)hrg::kMaxSmallRows * max_dout) == hipSuccess &&
+         dmalloc(&P->dec_upart, ks_max * hrg::kDecodeMaxT * P->rpad) == hipSuccess &&
          dmalloc(&P->dec_part, ks_max * hrg::kDecodeMaxT * max_dout) == hipSuccess;
   if (ok) ok = plan_alloc(P, &P->internal) == LORA_OK;
   if (!ok) {
@@ -294,6 +299,7 @@ lora_status_t lora_pool_destroy(lora_pool_t P) {
   (void)hipFree(P->v_lo);
   (void)hipFree(P->dec_upart);
   (void)hipFree(P->dec_part);
+  (void)hipFree(P->E);
   delete P;
   return LORA_OK;
 }
@@ -473,6 +479,12 @@ static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t
   ga.pages = P->pages;
   ga.slot_stride = P->slot_elems;
   ga.b_off = P->b_off[module];
+  ga.seg_e0 = pl->tab.seg_e0;
+  ga.erow = pl->tab.erow;
+  ga.small_seg = pl->tab.small_seg;
+  ga.counts = pl->tab.counts;
+  ga.E = P->E;
+  if (hrg::launch_expand_small(ga, stream) != hipSuccess) return LORA_ERR_HIP;
   return hrg::launch_prefill(ga, true, -1, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 

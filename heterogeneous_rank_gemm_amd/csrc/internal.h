@@ -10,6 +10,11 @@ constexpr int kMaxIds = 16384;       // plan histogram lives in LDS
 constexpr int kMaxRank = 64;
 constexpr int kShrinkRows = 64;      // rows per shrink work tile
 constexpr int kMaxSplits = 32;       // K-splits of the shrink
+// Segments of at most kSmallRows tokens are expanded by a separate launch into
+// fp32 rows of E (at most kMaxSmallRows such tokens per plan); the GEMM starts
+// those rows' accumulators from E instead of walking every small segment.
+constexpr int kSmallRows = 8;
+constexpr int kMaxSmallRows = 512;
 // Device status codes (values of lora_status_t; a larger code wins).
 constexpr int kStatusNotLoaded = 6;
 constexpr int kStatusIdRange = 7;
@@ -29,7 +34,10 @@ struct PlanTables {
   float* seg_scale;    // [T_cap+1] alpha / rank
   int32_t* tile_seg;   // [max_tiles] shrink work tile -> segment
   int32_t* tile_row0;  // [max_tiles] first sorted row of the tile
-  int32_t* counts;     // [0] = S, [1] = number of shrink tiles, [2] = T
+  int32_t* seg_e0;     // [T_cap+1] first E row of a small segment, -1 otherwise
+  int32_t* erow;       // [T_cap]   sorted position -> E row, -1 if not in a small segment
+  int32_t* small_seg;  // [kMaxSmallRows] the small segments, in order
+  int32_t* counts;     // [0] = S, [1] = number of shrink tiles, [2] = T, [3] = small segments
   int32_t max_tiles;
 };
 
@@ -88,6 +96,12 @@ struct GemmArgs {
   size_t slot_stride;     //   16-rank chunks [rpad/16][N][16]
   size_t b_off;
   const int32_t* status;
+  // small segments: their rows' s (U B) terms in fp32, E [kMaxSmallRows][N]
+  const int32_t* seg_e0;
+  const int32_t* erow;
+  const int32_t* small_seg;
+  const int32_t* counts;
+  float* E;
 };
 
 // Decode path (T <= kDecodeMaxT): launch 1 computes the K-chunk partials of
@@ -141,6 +155,8 @@ hipError_t launch_shrink(const ShrinkArgs& a, int grid, int ksplit, int T, hipSt
 // shape < 0 picks the tile shape from (T, N); 0..3 force 256x256, 256x128,
 // 128x256, 128x128 (tokens x columns).  Every shape gives the same bits.
 hipError_t launch_prefill(const GemmArgs& a, bool lora, int shape, hipStream_t s);
+// The E rows of the small segments (one launch, before the GEMM).
+hipError_t launch_expand_small(const GemmArgs& a, hipStream_t s);
 int prefill_choose(int T, int N);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);

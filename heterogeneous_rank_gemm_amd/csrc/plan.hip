@@ -12,17 +12,6 @@ namespace hrg {
 constexpr int kPlanThreads = 1024;
 constexpr int kStageTok = 8192;  // tokens whose buckets are staged in LDS at a time
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int l = __lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(v, d, 64);
-    if (l >= d) v += u;
-  }
-  return v;
-}
-
 // One workgroup.  LDS: start[nb] (bucket counts, then exclusive offsets, then
 // placement cursors) and segidx[nb] (segment index of each non-empty bucket),
 // nb = max_ids + 1; bucket b holds id b - 1.
@@ -144,6 +133,29 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     if (lane == 0) a.tab.counts[1] = min(run, a.tab.max_tiles);
   }
 
+  if (wave == 2) {
+    // 4c. small segments (adapter segments of at most kSmallRows tokens): E
+    // rows in segment order while they fit in kMaxSmallRows
+    int rows_run = 0, n_small = 0;
+    for (int base = 0; base < S; base += 64) {
+      const int s = base + lane;
+      int rows = 0;
+      if (s < S && a.tab.seg_id[s] >= 0) {
+        const int len = a.tab.seg_off[s + 1] - a.tab.seg_off[s];
+        if (len <= kSmallRows) rows = len;
+      }
+      const int inc = wave_incl_scan(rows);
+      const int e0 = rows_run + inc - rows;
+      const bool take = rows > 0 && e0 + rows <= kMaxSmallRows;
+      const uint64_t tk = __ballot(take);
+      if (s < S) a.tab.seg_e0[s] = take ? e0 : -1;
+      if (take) a.tab.small_seg[n_small + __popcll(tk & ((1ull << lane) - 1ull))] = s;
+      n_small += __popcll(tk);
+      rows_run += __shfl(inc, 63, 64);
+    }
+    if (lane == 0) a.tab.counts[3] = n_small;
+  }
+
   // 4a. stable placement in blocks of kStageTok tokens whose buckets are
   // staged in LDS by all waves; wave 0 then places the block, 64 at a time.
   for (int blk0 = 0; blk0 < T; blk0 += kStageTok) {
@@ -179,6 +191,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         }
       }
     }
+  }
+
+  // 5. E row of every sorted position (-1 outside the small segments)
+  __syncthreads();
+  for (int p = tid; p < T; p += kPlanThreads) {
+    const int sg = a.tab.row_seg[p];
+    const int e0 = a.tab.seg_e0[sg];
+    a.tab.erow[p] = e0 >= 0 ? e0 + p - a.tab.seg_off[sg] : -1;
   }
 }
 

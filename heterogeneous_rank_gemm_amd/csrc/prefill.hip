@@ -198,38 +198,70 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
   prologue();
 
   if constexpr (LORA) {
-    // ---- expand first: acc = s_i * (U_t B_i) for every token of an adapter
-    // segment.  V = s U arrives from the shrink as bf16 hi + lo parts
-    // (V ~= hi + lo to about 2^-16); the B page is stored transposed in
-    // 16-rank chunks, [rpad/16][N][16], so both operands are 16-byte reads.
+    // ---- rows of small segments start from their fp32 E rows (the same
+    // MFMA chain as below, run by the small-segment launch)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int p = m0 + wm * (BM / 2) + 32 * j + (l & 31);
+      const int er = p < T ? a.erow[p] : -1;
+      if (er >= 0) {
+        const float* erow = a.E + (size_t)er * N;
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = n0 + wn * (BN / 2) + 32 * i + 8 * q + 4 * (l >> 5);
+            if (col < N) {
+              const float4 v = *reinterpret_cast<const float4*>(erow + col);
+              acc[i][j][4 * q + 0] = v.x;
+              acc[i][j][4 * q + 1] = v.y;
+              acc[i][j][4 * q + 2] = v.z;
+              acc[i][j][4 * q + 3] = v.w;
+            }
+          }
+        }
+      }
+    }
+
+    // ---- expand first: acc = s_i * (U_t B_i) for every token of a (not
+    // small) adapter segment.  V = s U arrives from the shrink as bf16 hi +
+    // lo parts (V ~= hi + lo to about 2^-16); the B page is stored transposed
+    // in 16-rank chunks, [rpad/16][N][16], so both operands are 16-byte reads.
     // Each 32-row block j of the wave walks its own work items (segment,
-    // pair of rank chunks); the FM walkers advance in lockstep, each with its
-    // next item's B fragments in flight while the current one's MFMAs run.
+    // pair of rank chunks).  Its segments' table entries arrive in one round
+    // of loads (lane i: the block's i-th segment), so an item's slot, rows
+    // and rank are register reads; the FM walkers advance in lockstep through
+    // a ring of D items whose B fragments are requested D-1 items ahead.
+    // Every ring load is issued (an item past a walker's last reads a valid
+    // page and is not applied), so the loads' completion is counted exactly.
     constexpr int QB = QC < 2 ? QC : 2;  // rank chunks per work item
-    // walkers per group: the expand's registers (V, D B buffers) stay
-    // within a budget
     // ring of D items in flight per walker: deeper where the tile leaves
     // registers free (one block per compute unit)
     constexpr int D = (FN * QB <= 4 && FM <= 2) ? 4 : 2;
-    constexpr int kPerWalker = D * QB * FN * 4 + QC * 8;
-    constexpr int kBudget = FN >= 4 ? 48 : 192;  // 256-column tiles keep 256 accumulators live
+    constexpr int kPerWalker = D * QB * FN * 4 + QC * 8 + 6;
+    constexpr int kBudget = FN >= 4 ? 54 : 198;  // 256-column tiles keep 256 accumulators live
+    // walkers per group: the expand's registers (V, D B buffers) stay
+    // within a budget
     constexpr int JG = kPerWalker * FM <= kBudget ? FM : (kPerWalker * 2 <= kBudget ? 2 : 1);
     const int qc_pool = a.u_ld >> 4;
+    const uint16_t* dummy_page = a.pages + a.b_off;  // slot 0: any valid address
 #pragma unroll
     for (int g = 0; g < FM / JG; ++g) {
       bf16x8 vh[JG][QC], vl[JG][QC];
-      int sg[JG], cb[JG], sl[JG], pj[JG];
-      bool act[JG];
+      int pj[JG], nit[JG];
+      // lane i (mod 32): the block's i-th segment -- first row, end, slot,
+      // number of items, first item
+      int s_off[JG], s_end[JG], s_slot[JG], s_nqc[JG], s_it0[JG], s_nit[JG];
 #pragma unroll
       for (int j = 0; j < JG; ++j) {
         const int rb = m0 + wm * (BM / 2) + 32 * (g * JG + j);  // first sorted row of block g*JG+j
-        act[j] = rb < T;
+        const bool act = rb < T;
         pj[j] = rb + (l & 31);
         const int pc = min(pj[j], T - 1);
 #pragma unroll
         for (int qc = 0; qc < QC; ++qc) {
           const size_t e = (size_t)pc * a.u_ld + 16 * qc + 8 * (l >> 5);
-          if (act[j] && qc < qc_pool) {
+          if (act && qc < qc_pool) {
             vh[j][qc] = __builtin_bit_cast(bf16x8, ld16(a.v_hi + e));
             vl[j][qc] = __builtin_bit_cast(bf16x8, ld16(a.v_lo + e));
           } else {
@@ -237,36 +269,56 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
             vl[j][qc] = zero_bf16x8();
           }
         }
-        sg[j] = 0;
-        sl[j] = -1;
-        cb[j] = 0;
-        if (act[j]) {
-          sg[j] = a.row_seg[rb];
-          if (a.seg_id[sg[j]] < 0) ++sg[j];  // only the first segment can be the base run
-          sl[j] = a.row_seg[min(rb + 31, T - 1)];
-          act[j] = sg[j] <= sl[j];
-        }
+        const int sg = act ? a.row_seg[rb] : 0;
+        const int sl = act ? a.row_seg[min(rb + 31, T - 1)] : -1;
+        const int sx = sg + (l & 31);
+        const bool mine = sx <= sl && l < 32;
+        const int sc = min(sx, max(sl, 0));
+        s_off[j] = a.seg_off[sc];
+        s_end[j] = a.seg_off[sc + 1];
+        s_slot[j] = a.seg_slot[sc];
+        s_nqc[j] = (a.seg_rank[sc] + 15) >> 4;
+        const bool big = mine && a.seg_id[sc] >= 0 && a.seg_e0[sc] < 0;
+        s_nit[j] = big ? (s_nqc[j] + QB - 1) / QB : 0;
+        const int inc = wave_incl_scan(s_nit[j]);
+        s_it0[j] = inc - s_nit[j];
+        nit[j] = __builtin_amdgcn_readlane(inc, 63);
       }
+      // item k of walker j: (segment lane, first chunk), or -1 past its last
+      auto item_lane = [&](int j, int k) __attribute__((always_inline)) -> int {
+        const uint64_t m = __ballot(k >= s_it0[j] && k < s_it0[j] + s_nit[j]);
+        return m ? (int)__builtin_ctzll(m) : -1;
+      };
       bf16x8 bq[D][JG][QB][FN];
-      auto load_b = [&](bf16x8 (&bb)[QB][FN], int s, int c) __attribute__((always_inline)) {
-        const int nqc = (a.seg_rank[s] + 15) >> 4;
-        const uint16_t* bt = a.pages + (size_t)a.seg_slot[s] * a.slot_stride + a.b_off;
+      auto load_b = [&](bf16x8 (&bb)[QB][FN], int j, int k) __attribute__((always_inline)) {
+        const int il = item_lane(j, k);
+        const uint16_t* bt = dummy_page;
+        int c = 0;
+        if (il >= 0) {
+          bt = a.pages + (size_t)__builtin_amdgcn_readlane(s_slot[j], il) * a.slot_stride + a.b_off;
+          c = (k - __builtin_amdgcn_readlane(s_it0[j], il)) * QB;
+        }
+        // a chunk past the adapter's rank reads chunk 0 again (not applied)
 #pragma unroll
         for (int qc = 0; qc < QB; ++qc) {
-          if (c + qc < nqc) {
+          const int cq = il >= 0 && c + qc < __builtin_amdgcn_readlane(s_nqc[j], max(il, 0)) ? c + qc : 0;
 #pragma unroll
-            for (int i = 0; i < FN; ++i) {
-              const int n = min(n0 + wn * (BN / 2) + 32 * i + (l & 31), N - 1);
-              bb[qc][i] = __builtin_bit_cast(bf16x8, ld16(bt + ((size_t)(c + qc) * N + n) * 16 + 8 * (l >> 5)));
-            }
+          for (int i = 0; i < FN; ++i) {
+            const int n = min(n0 + wn * (BN / 2) + 32 * i + (l & 31), N - 1);
+            bb[qc][i] = __builtin_bit_cast(bf16x8, ld16(bt + ((size_t)cq * N + n) * 16 + 8 * (l >> 5)));
           }
         }
       };
-      // acc[.][j] += B^T (V masked to the rows of segment s), chunks c .. c+QB-1
+      // acc[.][j] += B^T (V masked to the rows of the item's segment), chunks c .. c+QB-1
       auto apply_b = [&](const bf16x8 (&bb)[QB][FN], const bf16x8 (&h_)[QC], const bf16x8 (&l_)[QC],
-                         f32x16 (&accj)[FN], int p, int s, int c) __attribute__((always_inline)) {
-        const bool in = p >= a.seg_off[s] && p < a.seg_off[s + 1];
-        const int nqc = (a.seg_rank[s] + 15) >> 4;
+                         f32x16 (&accj)[FN], int p, int j, int k) __attribute__((always_inline)) {
+        const int il = item_lane(j, k);
+        if (il < 0) return;
+        const int off = __builtin_amdgcn_readlane(s_off[j], il);
+        const int end = __builtin_amdgcn_readlane(s_end[j], il);
+        const int nqc = __builtin_amdgcn_readlane(s_nqc[j], il);
+        const int c = (k - __builtin_amdgcn_readlane(s_it0[j], il)) * QB;
+        const bool in = p >= off && p < end;
         const uint32_t m = in ? 0xffffffffu : 0u;
         const uint32_t first = c == 0 ? 0xffffffffu : 0u;  // chunk c + qc is qc or qc + QB
 #pragma unroll
@@ -291,74 +343,49 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
           }
         }
       };
-      auto advance = [&](int& s, int& c) __attribute__((always_inline)) {
-        c += QB;
-        if (c >= ((a.seg_rank[s] + 15) >> 4)) {
-          ++s;
-          c = 0;
-        }
-      };
-      f32x16 accT[JG][FN];  // acc transposed so a block's columns pass as one array
+      int nmax = 0;
 #pragma unroll
-      for (int j = 0; j < JG; ++j)
+      for (int j = 0; j < JG; ++j) nmax = max(nmax, nit[j]);
+      if (nmax > 0) {
+        f32x16 accT[JG][FN];  // acc transposed so a block's columns pass as one array
 #pragma unroll
-        for (int i = 0; i < FN; ++i) accT[j][i] = acc[i][g * JG + j];
-      // (ls, lc): the last item whose B fragments were requested, per walker
-      int ls[JG], lc[JG];
+        for (int j = 0; j < JG; ++j)
 #pragma unroll
-      for (int j = 0; j < JG; ++j) {
-        ls[j] = sg[j];
-        lc[j] = cb[j];
-        if (act[j]) load_b(bq[0][j], ls[j], lc[j]);
-      }
-      auto load_next = [&](auto bufc) __attribute__((always_inline)) {
-        constexpr int B = decltype(bufc)::value;
+          for (int i = 0; i < FN; ++i) accT[j][i] = acc[i][g * JG + j];
+        // items 0 .. D-2; each phase then requests the item D-1 ahead
+        for_each_stage<D - 1>([&](auto dc) __attribute__((always_inline)) {
+          constexpr int B = decltype(dc)::value;
 #pragma unroll
-        for (int j = 0; j < JG; ++j) {
-          if (ls[j] <= sl[j]) {
-            advance(ls[j], lc[j]);
-            if (ls[j] <= sl[j]) load_b(bq[B][j], ls[j], lc[j]);
+          for (int j = 0; j < JG; ++j) load_b(bq[B][j], j, B);
+        });
+        // phase P of round k0: item k0 + P is in bq[P]; item k0 + P + D - 1
+        // goes to bq[(P + D - 1) % D]
+        bool more = true;
+        auto phase = [&](auto pc, int k0) __attribute__((always_inline)) {
+          constexpr int P = decltype(pc)::value;
+          const int k = k0 + P;
+#pragma unroll
+          for (int j = 0; j < JG; ++j) load_b(bq[(P + D - 1) % D][j], j, k + D - 1);
+#pragma unroll
+          for (int j = 0; j < JG; ++j) apply_b(bq[P][j], vh[j], vl[j], accT[j], pj[j], j, k);
+          more = k + 1 < nmax;
+        };
+        for (int k0 = 0; more; k0 += D) {
+          phase(std::integral_constant<int, 0>{}, k0);
+          if (!more) break;
+          phase(std::integral_constant<int, 1>{}, k0);
+          if constexpr (D > 2) {
+            if (!more) break;
+            phase(std::integral_constant<int, 2>{}, k0);
+            if (!more) break;
+            phase(std::integral_constant<int, 3>{}, k0);
           }
         }
-      };
-      // items 1 .. D-2 (each phase then requests the item D-1 ahead)
-      for_each_stage<D - 2>([&](auto dc) __attribute__((always_inline)) {
-        load_next(std::integral_constant<int, decltype(dc)::value + 1>{});
-      });
-      bool any = false;
 #pragma unroll
-      for (int j = 0; j < JG; ++j) any |= act[j];
-      // phase P: items held in bq[P] are current; the item D-1 ahead goes to bq[(P+D-1)%D]
-      auto phase = [&](auto pc) __attribute__((always_inline)) {
-        constexpr int P = decltype(pc)::value;
-        load_next(std::integral_constant<int, (P + D - 1) % D>{});
+        for (int j = 0; j < JG; ++j)
 #pragma unroll
-        for (int j = 0; j < JG; ++j) {
-          if (act[j]) {
-            apply_b(bq[P][j], vh[j], vl[j], accT[j], pj[j], sg[j], cb[j]);
-            advance(sg[j], cb[j]);
-            act[j] = sg[j] <= sl[j];
-          }
-        }
-        any = false;
-#pragma unroll
-        for (int j = 0; j < JG; ++j) any |= act[j];
-      };
-      while (any) {
-        phase(std::integral_constant<int, 0>{});
-        if (!any) break;
-        phase(std::integral_constant<int, 1>{});
-        if constexpr (D > 2) {
-          if (!any) break;
-          phase(std::integral_constant<int, 2>{});
-          if (!any) break;
-          phase(std::integral_constant<int, 3>{});
-        }
+          for (int i = 0; i < FN; ++i) acc[i][g * JG + j] = accT[j][i];
       }
-#pragma unroll
-      for (int j = 0; j < JG; ++j)
-#pragma unroll
-        for (int i = 0; i < FN; ++i) acc[i][g * JG + j] = accT[j][i];
     }
   }
 
@@ -459,6 +486,87 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
       }
     }
   }
+}
+
+// Small segments (at most kSmallRows tokens): E[e0 + p - off][n] = s (U_p B)[n]
+// in fp32 for every token p of the segment.  In the GEMM such a segment would
+// cost a walker item (a full 32-row MFMA block) per segment per column tile,
+// all on the few tiles that hold the batch's long tail of rare adapters; here
+// the items spread over the whole chip.  One wave per (segment, 128 columns).
+// The arithmetic is the GEMM expand's exactly: the same 32-row blocks and
+// lanes (rows of other segments masked to zero), the same MFMA, chunk order
+// and hi-then-lo order, starting from zero -- so the GEMM, starting those
+// rows' accumulators from E, gives the bits it would give walking them.
+template <int QC>
+__global__ __launch_bounds__(256) void expand_small_kernel(GemmArgs a) {
+  if (*a.status != 0) return;  // strict mode: a failed plan leaves out untouched
+  const int N = a.N, T = a.T;
+  const int ng = (N + 127) / 128;
+  const int nitems = a.counts[3] * ng;
+  const int l = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  for (int item = blockIdx.x * 4 + wid; item < nitems; item += gridDim.x * 4) {
+    const int s = a.small_seg[item / ng], g = item % ng;
+    const int off = a.seg_off[s], end = a.seg_off[s + 1];
+    const int nqc = (a.seg_rank[s] + 15) >> 4;
+    const int e0 = a.seg_e0[s];
+    const uint16_t* bt = a.pages + (size_t)a.seg_slot[s] * a.slot_stride + a.b_off;
+    for (int rb = off & ~31; rb < end; rb += 32) {
+      const int p = rb + (l & 31);
+      const uint32_t m = p >= off && p < end ? 0xffffffffu : 0u;
+      f32x16 acc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+#pragma unroll
+      for (int qc = 0; qc < QC; ++qc) {
+        if (qc < nqc) {
+          const size_t e = (size_t)min(p, T - 1) * a.u_ld + 16 * qc + 8 * (l >> 5);
+          const uint4 h = ld16(a.v_hi + e), o = ld16(a.v_lo + e);
+          bf16x8 bb[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int n = min(g * 128 + 32 * i + (l & 31), N - 1);
+            bb[i] = __builtin_bit_cast(bf16x8, ld16(bt + ((size_t)qc * N + n) * 16 + 8 * (l >> 5)));
+          }
+          const bf16x8 mh = __builtin_bit_cast(bf16x8, make_uint4(h.x & m, h.y & m, h.z & m, h.w & m));
+          const bf16x8 ml = __builtin_bit_cast(bf16x8, make_uint4(o.x & m, o.y & m, o.z & m, o.w & m));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[i] = mfma32(bb[i], mh, acc[i]);
+            acc[i] = mfma32(bb[i], ml, acc[i]);
+          }
+        }
+      }
+      if (m) {
+        float* er = a.E + (size_t)(e0 + p - off) * N;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = g * 128 + 32 * i + 8 * q + 4 * (l >> 5);
+            if (col < N)
+              *reinterpret_cast<float4*>(er + col) =
+                  make_float4(acc[i][4 * q], acc[i][4 * q + 1], acc[i][4 * q + 2], acc[i][4 * q + 3]);
+          }
+      }
+    }
+  }
+}
+
+hipError_t launch_expand_small(const GemmArgs& a, hipStream_t s) {
+  // a fixed grid: at most kMaxSmallRows segments x ceil(N / 128) items
+  const int items = kMaxSmallRows * ((a.N + 127) / 128);
+  const int grid = std::min((items + 3) / 4, 1024);
+  const int qc = a.u_ld / 16;
+  if (qc <= 1)
+    hipLaunchKernelGGL(expand_small_kernel<1>, dim3(grid), dim3(256), 0, s, a);
+  else if (qc == 2)
+    hipLaunchKernelGGL(expand_small_kernel<2>, dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(expand_small_kernel<4>, dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 template <int BM, int BN>
