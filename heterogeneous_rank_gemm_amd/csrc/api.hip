@@ -126,9 +126,7 @@ lora_status_t run_plan(lora_pool_s* P, const int32_t* ids, int32_t T, lora_plan_
   a.ids = ids;
   a.T = T;
   a.max_ids = P->max_ids;
-  a.id2slot = P->id2slot;
-  a.slot_rank = P->slot_rank;
-  a.slot_scale = P->slot_scale;
+  a.id_info = P->id_info;
   a.status = P->status;
   a.tab = pl->tab;
   if (hrg::launch_plan(a, s) != hipSuccess) return LORA_ERR_HIP;

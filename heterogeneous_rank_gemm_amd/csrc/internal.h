@@ -45,9 +45,7 @@ struct PlanArgs {
   const int32_t* ids;
   int32_t T;
   int32_t max_ids;
-  const int32_t* id2slot;
-  const int32_t* slot_rank;
-  const float* slot_scale;
+  const int4* id_info;     // [max_ids] {slot (-1: not resident), rank, scale bits, 0}
   int32_t* status;
   PlanTables tab;
 };
@@ -147,6 +145,11 @@ struct PackArgs {
   int32_t cols;           // d_in for A, d_out for B
   int32_t mode;           // 0: A page, 1: B page
 };
+
+// Blocks of `fn` (block size `threads`, dynamic LDS `lds`) the current device
+// holds at once: the occupancy per compute unit times the compute units.
+// Cached per kernel; at least 1.
+int resident_blocks(const void* fn, int threads, size_t lds);
 
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);

@@ -4,32 +4,76 @@
 // id" is the "Grouped Multi-LoRA Execution" of the LoRA-Land post (section
 // "2. multi-LoRA batch scheduling"); ids are validated here in strict mode
 // (icman report section 4.1: reject, never silently serve the base).
+#include <map>
+#include <mutex>
+
 #include "common.h"
 #include "internal.h"
 
 namespace hrg {
 
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kStageTok = 8192;  // tokens whose buckets are staged in LDS at a time
 
+// Waves that place tokens in parallel: each takes a contiguous share of a
+// staged block and owns a row of nb cursors in LDS (PW * nb ints, <= 64 KB).
+__host__ __device__ inline int plan_place_waves(int nb) {
+  return nb <= 1024 ? 16 : nb <= 2048 ? 8 : nb <= 4096 ? 4 : 1;
+}
+
+// Exclusive prefix sums, in thread order over the workgroup, of three
+// per-thread values; tot[] gets the totals.
+__device__ __forceinline__ void block_excl_scan3(int v[3], int* tot, int (*red)[kPlanWaves]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int inc[3];
+#pragma unroll
+  for (int i = 0; i < 3; ++i) {
+    inc[i] = wave_incl_scan(v[i]);
+    if (lane == 63) red[i][wave] = inc[i];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int x = lane < kPlanWaves ? red[i][lane] : 0;
+      const int xi = wave_incl_scan(x);
+      if (lane < kPlanWaves) red[i][lane] = xi - x;
+      if (lane == 63) tot[i] = xi;  // lanes past the last wave add zeros
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 3; ++i) v[i] = red[i][wave] + inc[i] - v[i];
+}
+
 // One workgroup.  LDS: start[nb] (bucket counts, then exclusive offsets, then
-// placement cursors) and segidx[nb] (segment index of each non-empty bucket),
-// nb = max_ids + 1; bucket b holds id b - 1.
+// running bases), segidx[nb] (segment index of each non-empty bucket) and,
+// with PW > 1, PW rows of nb placement cursors; nb = max_ids + 1, bucket b
+// holds id b - 1.  Dependent global rounds: the ids, one id_info lookup per
+// token (validation) and one per segment (its table entry); the rest works
+// from LDS and registers.
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   extern __shared__ int smem[];
   const int nb = a.max_ids + 1;
+  const int PW = plan_place_waves(nb);
   int* start = smem;
   int* segidx = smem + nb;
-  __shared__ int s_err;
-  __shared__ int s_wsum[2][kPlanThreads / 64];
-  __shared__ int s_tot[2];
+  int* cur = smem + 2 * nb;  // [PW][nb] when PW > 1
+  __shared__ int s_err, s_nsmall;
+  __shared__ int s_red[3][kPlanWaves];
+  __shared__ int s_tot[3];
   __shared__ uint16_t s_bucket[kStageTok];  // id + 1 of the tokens of one placement block
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T;
   if (*a.status != 0) return;  // a sticky error is pending: leave the tables alone
 
-  if (tid == 0) s_err = 0;
+  if (tid == 0) {
+    s_err = 0;
+    s_nsmall = 0;
+  }
   for (int b = tid; b < nb; b += kPlanThreads) start[b] = 0;
+  for (int p = tid; p < T; p += kPlanThreads) a.tab.erow[p] = -1;
   __syncthreads();
 
   // 1. validate every id and count tokens per bucket
@@ -38,7 +82,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     if (id < -1 || id >= a.max_ids) {
       atomicMax(&s_err, kStatusIdRange);
     } else {
-      if (id >= 0 && a.id2slot[id] < 0) atomicMax(&s_err, kStatusNotLoaded);
+      if (id >= 0 && a.id_info[id].x < 0) atomicMax(&s_err, kStatusNotLoaded);
       atomicAdd(&start[id + 1], 1);
     }
   }
@@ -51,122 +95,138 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   // 2. exclusive scans: counts -> bucket start offsets, non-empty -> segment index
   const int per = (nb + kPlanThreads - 1) / kPlanThreads;
   const int b0 = min(nb, tid * per), b1 = min(nb, b0 + per);
-  int csum = 0, nsum = 0;
-  for (int b = b0; b < b1; ++b) {
-    const int c = start[b];
-    csum += c;
-    nsum += (c > 0);
-  }
-  const int ci = wave_incl_scan(csum), ni = wave_incl_scan(nsum);
-  if (lane == 63) {
-    s_wsum[0][wave] = ci;
-    s_wsum[1][wave] = ni;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    const int nw = kPlanThreads / 64;
-    const int v0 = lane < nw ? s_wsum[0][lane] : 0, v1 = lane < nw ? s_wsum[1][lane] : 0;
-    const int i0 = wave_incl_scan(v0), i1 = wave_incl_scan(v1);
-    if (lane < nw) {
-      s_wsum[0][lane] = i0 - v0;
-      s_wsum[1][lane] = i1 - v1;
+  {
+    int v[3] = {0, 0, 0};
+    for (int b = b0; b < b1; ++b) {
+      v[0] += start[b];
+      v[1] += start[b] > 0;
     }
-    if (lane == nw - 1) {
-      s_tot[0] = i0;
-      s_tot[1] = i1;
+    block_excl_scan3(v, s_tot, s_red);
+    int crun = v[0], nrun = v[1];
+    for (int b = b0; b < b1; ++b) {
+      const int c = start[b];
+      start[b] = crun;
+      segidx[b] = nrun;
+      crun += c;
+      nrun += (c > 0);
     }
-  }
-  __syncthreads();
-  int crun = s_wsum[0][wave] + ci - csum, nrun = s_wsum[1][wave] + ni - nsum;
-  for (int b = b0; b < b1; ++b) {
-    const int c = start[b];
-    start[b] = crun;
-    segidx[b] = nrun;
-    crun += c;
-    nrun += (c > 0);
   }
   __syncthreads();
   const int S = s_tot[1];
 
-  // 3. segment table (ascending id, -1 first)
-  for (int b = tid; b < nb; b += kPlanThreads) {
+  // 3. segment table (ascending id, -1 first), then the shrink tiles (each
+  // adapter segment cut into runs of kShrinkRows sorted rows) and the small
+  // segments (adapter segments of at most kSmallRows tokens; E rows in
+  // segment order while they fit in kMaxSmallRows), placed by prefix sums
+  // over the threads' buckets
+  int v3[3] = {0, 0, 0};  // tiles, small rows, small segments
+  for (int b = b0; b < b1; ++b) {
     const int nxt = (b + 1 < nb) ? start[b + 1] : T;
-    if (nxt > start[b]) {
+    const int len = nxt - start[b];
+    if (len > 0) {
       const int s = segidx[b];
       const int id = b - 1;
-      const int slot = id >= 0 ? a.id2slot[id] : -1;
+      const int4 inf = id >= 0 ? a.id_info[id] : make_int4(-1, 0, 0, 0);
       a.tab.seg_id[s] = id;
       a.tab.seg_off[s] = start[b];
-      a.tab.seg_slot[s] = slot;
-      a.tab.seg_rank[s] = slot >= 0 ? a.slot_rank[slot] : 0;
-      a.tab.seg_scale[s] = slot >= 0 ? a.slot_scale[slot] : 0.f;
+      a.tab.seg_slot[s] = inf.x;
+      a.tab.seg_rank[s] = id >= 0 ? inf.y : 0;
+      a.tab.seg_scale[s] = id >= 0 ? __builtin_bit_cast(float, inf.z) : 0.f;
+      if (id >= 0) {
+        v3[0] += (len + kShrinkRows - 1) / kShrinkRows;
+        if (len <= kSmallRows) {
+          v3[1] += len;
+          v3[2] += 1;
+        }
+      }
     }
   }
+  block_excl_scan3(v3, s_tot, s_red);
+  for (int b = b0; b < b1; ++b) {
+    const int nxt = (b + 1 < nb) ? start[b + 1] : T;
+    const int off = start[b], len = nxt - off;
+    if (len <= 0) continue;
+    const int s = segidx[b];
+    int e0 = -1;
+    if (b > 0) {
+      const int nt = (len + kShrinkRows - 1) / kShrinkRows;
+      for (int j = 0; j < nt; ++j) {
+        if (v3[0] + j < a.tab.max_tiles) {
+          a.tab.tile_seg[v3[0] + j] = s;
+          a.tab.tile_row0[v3[0] + j] = off + j * kShrinkRows;
+        }
+      }
+      v3[0] += nt;
+      if (len <= kSmallRows) {
+        if (v3[1] + len <= kMaxSmallRows) {
+          e0 = v3[1];
+          a.tab.small_seg[v3[2]] = s;
+          atomicMax(&s_nsmall, v3[2] + 1);
+          for (int i = 0; i < len; ++i) a.tab.erow[off + i] = e0 + i;
+        }
+        v3[1] += len;
+        v3[2] += 1;
+      }
+    }
+    a.tab.seg_e0[s] = e0;
+  }
+  __syncthreads();  // s_nsmall, s_tot
   if (tid == 0) {
     a.tab.seg_off[S] = T;
     a.tab.counts[0] = S;
+    a.tab.counts[1] = min(s_tot[0], a.tab.max_tiles);
     a.tab.counts[2] = T;
-  }
-  __syncthreads();
-
-  if (wave == 1) {
-    // 4b. shrink work tiles: every adapter segment split into runs of
-    // kShrinkRows sorted rows (the base segment has no tiles).
-    int run = 0;
-    for (int base = 0; base < S; base += 64) {
-      const int s = base + lane;
-      int nt = 0, off0 = 0;
-      if (s < S && a.tab.seg_id[s] >= 0) {
-        off0 = a.tab.seg_off[s];
-        nt = (a.tab.seg_off[s + 1] - off0 + kShrinkRows - 1) / kShrinkRows;
-      }
-      const int inc = wave_incl_scan(nt);
-      const int o = run + inc - nt;
-      for (int j = 0; j < nt; ++j) {
-        if (o + j < a.tab.max_tiles) {
-          a.tab.tile_seg[o + j] = s;
-          a.tab.tile_row0[o + j] = off0 + j * kShrinkRows;
-        }
-      }
-      run += __shfl(inc, 63, 64);
-    }
-    if (lane == 0) a.tab.counts[1] = min(run, a.tab.max_tiles);
+    a.tab.counts[3] = s_nsmall;
   }
 
-  if (wave == 2) {
-    // 4c. small segments (adapter segments of at most kSmallRows tokens): E
-    // rows in segment order while they fit in kMaxSmallRows
-    int rows_run = 0, n_small = 0;
-    for (int base = 0; base < S; base += 64) {
-      const int s = base + lane;
-      int rows = 0;
-      if (s < S && a.tab.seg_id[s] >= 0) {
-        const int len = a.tab.seg_off[s + 1] - a.tab.seg_off[s];
-        if (len <= kSmallRows) rows = len;
-      }
-      const int inc = wave_incl_scan(rows);
-      const int e0 = rows_run + inc - rows;
-      const bool take = rows > 0 && e0 + rows <= kMaxSmallRows;
-      const uint64_t tk = __ballot(take);
-      if (s < S) a.tab.seg_e0[s] = take ? e0 : -1;
-      if (take) a.tab.small_seg[n_small + __popcll(tk & ((1ull << lane) - 1ull))] = s;
-      n_small += __popcll(tk);
-      rows_run += __shfl(inc, 63, 64);
-    }
-    if (lane == 0) a.tab.counts[3] = n_small;
-  }
-
-  // 4a. stable placement in blocks of kStageTok tokens whose buckets are
-  // staged in LDS by all waves; wave 0 then places the block, 64 at a time.
+  // 4. stable placement, in blocks of kStageTok tokens whose buckets are
+  // staged in LDS.  PW waves each take a contiguous share of a block:
+  // per-wave bucket counts, then for each bucket its running base plus the
+  // counts of the waves before, then each wave places its share 64 tokens
+  // at a time (one cursor update per distinct bucket among the 64).
   for (int blk0 = 0; blk0 < T; blk0 += kStageTok) {
     const int blk1 = min(T, blk0 + kStageTok);
+    const int share = (blk1 - blk0 + PW - 1) / PW;
     __syncthreads();  // the previous block is placed
     for (int t = blk0 + tid; t < blk1; t += kPlanThreads) s_bucket[t - blk0] = (uint16_t)(a.ids[t] + 1);
+    if (PW > 1)
+      for (int i = tid; i < PW * nb; i += kPlanThreads) cur[i] = 0;
     __syncthreads();
-    if (wave == 0) {
-      for (int base = blk0; base < blk1; base += 64) {
+    const int t0 = PW > 1 ? blk0 + wave * share : blk0;
+    const int t1 = PW > 1 ? min(blk1, t0 + share) : blk1;
+    int* mycur = PW > 1 ? cur + wave * nb : start;
+    if (PW > 1) {
+      if (wave < PW) {
+        for (int base = t0; base < t1; base += 64) {
+          const int t = base + lane;
+          const bool valid = t < t1;
+          const int b = valid ? (int)s_bucket[t - blk0] : -1;
+          uint64_t todo = __ballot(valid);
+          while (todo) {
+            const int ld = __builtin_ctzll(todo);  // wave-uniform
+            const int vb = __builtin_amdgcn_readlane(b, ld);
+            const uint64_t m = __ballot(b == vb) & todo;
+            if (lane == ld) mycur[vb] += __popcll(m);  // only this wave touches its row
+            todo &= ~m;
+          }
+        }
+      }
+      __syncthreads();
+      for (int b = tid; b < nb; b += kPlanThreads) {
+        int run = start[b];
+        for (int w = 0; w < PW; ++w) {
+          const int c = cur[w * nb + b];
+          cur[w * nb + b] = run;
+          run += c;
+        }
+        start[b] = run;
+      }
+      __syncthreads();
+    }
+    if (wave < PW) {
+      for (int base = t0; base < t1; base += 64) {
         const int t = base + lane;
-        const bool valid = t < blk1;
+        const bool valid = t < t1;
         const int b = valid ? (int)s_bucket[t - blk0] : -1;
         uint64_t todo = __ballot(valid);
         int leader = 0, rank = 0, cnt = 0;
@@ -182,7 +242,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
           todo &= ~m;
         }
         int first = 0;
-        if (valid && lane == leader) first = atomicAdd(&start[b], cnt);
+        if (valid && lane == leader) {
+          first = mycur[b];
+          mycur[b] = first + cnt;
+        }
         const int pos = __shfl(first, leader, 64) + rank;
         if (valid) {
           a.tab.perm[pos] = t;
@@ -192,28 +255,42 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       }
     }
   }
-
-  // 5. E row of every sorted position (-1 outside the small segments)
-  __syncthreads();
-  for (int p = tid; p < T; p += kPlanThreads) {
-    const int sg = a.tab.row_seg[p];
-    const int e0 = a.tab.seg_e0[sg];
-    a.tab.erow[p] = e0 >= 0 ? e0 + p - a.tab.seg_off[sg] : -1;
-  }
 }
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
-  const size_t lds = 2 * (size_t)(a.max_ids + 1) * sizeof(int);
+  const int nb = a.max_ids + 1;
+  const int pw = plan_place_waves(nb);
+  const size_t lds = (size_t)(2 + (pw > 1 ? pw : 0)) * nb * sizeof(int);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)plan_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+    // the most any nb needs: 2 (kMaxIds + 1) ints with pw = 1; with pw > 1,
+    // (2 + pw) nb <= 2 * 4097 + 16 * 1025 is smaller
+    hipError_t e = hipFuncSetAttribute((const void*)plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        2 * (kMaxIds + 1) * (int)sizeof(int));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), lds, s, a);
   return hipGetLastError();
+}
+
+int resident_blocks(const void* fn, int threads, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;  // (kernel, device) -> blocks
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find({fn, dev});
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 1;
+  }
+  const int n = std::max(1, per_cu * cus);
+  cache[{fn, dev}] = n;
+  return n;
 }
 
 // ---------------------------------------------------------------------------

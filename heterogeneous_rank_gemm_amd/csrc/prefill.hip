@@ -555,17 +555,24 @@ __global__ __launch_bounds__(256) void expand_small_kernel(GemmArgs a) {
   }
 }
 
-hipError_t launch_expand_small(const GemmArgs& a, hipStream_t s) {
-  // a fixed grid: at most kMaxSmallRows segments x ceil(N / 128) items
+template <int QC>
+static void launch_expand_small_cfg(const GemmArgs& a, hipStream_t s) {
+  // at most kMaxSmallRows segments x ceil(N / 128) items, walked by the
+  // blocks the chip holds at once
   const int items = kMaxSmallRows * ((a.N + 127) / 128);
-  const int grid = std::min((items + 3) / 4, 1024);
+  const int grid = std::min(resident_blocks(reinterpret_cast<const void*>(&expand_small_kernel<QC>), 256, 0),
+                            (items + 3) / 4);
+  hipLaunchKernelGGL(expand_small_kernel<QC>, dim3(grid), dim3(256), 0, s, a);
+}
+
+hipError_t launch_expand_small(const GemmArgs& a, hipStream_t s) {
   const int qc = a.u_ld / 16;
   if (qc <= 1)
-    hipLaunchKernelGGL(expand_small_kernel<1>, dim3(grid), dim3(256), 0, s, a);
+    launch_expand_small_cfg<1>(a, s);
   else if (qc == 2)
-    hipLaunchKernelGGL(expand_small_kernel<2>, dim3(grid), dim3(256), 0, s, a);
+    launch_expand_small_cfg<2>(a, s);
   else
-    hipLaunchKernelGGL(expand_small_kernel<4>, dim3(grid), dim3(256), 0, s, a);
+    launch_expand_small_cfg<4>(a, s);
   return hipGetLastError();
 }
 
