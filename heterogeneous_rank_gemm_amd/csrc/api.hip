@@ -44,7 +44,7 @@ struct lora_pool_s {
   uint16_t* v_lo = nullptr;          // [max_tokens][rpad] bf16 low part
   // decode-path workspace
   float* E = nullptr;                // [kMaxSmallRows][max d_out] small-segment expand rows
-  float* dec_part = nullptr;         // [ceil(max d_in / 1024)][64][max d_out] base partials
+  float* dec_part = nullptr;         // [ceil(max d_in / 1024)][64][max d_out rounded up to 64] base partials
   float* dec_upart = nullptr;        // [ceil(max d_in / 1024)][64][rpad] shrink partials
   std::vector<int32_t> h_id2slot, h_slot_rank;
   std::vector<float> h_slot_scale;
@@ -164,18 +164,13 @@ lora_status_t decode_apply(lora_pool_s* P, int32_t module, const lora_bf16_t* X,
   a.status = P->status;
   a.NT = ceil_div(N, hrg::kDecodeTileRows);
   a.KS = ceil_div(K, hrg::kDecodeChunk);
+  a.npad = a.NT * hrg::kDecodeTileRows;
   a.lora = lora ? 1 : 0;
-  if (lora) {
-    // A items: (adapter, 16-rank block); at most min(T, resident) adapters.
-    // They ride in the W-tile blocks (na waves each, 1, 2 or 4); the rest
-    // get extra blocks of A waves only.
-    const int loaded = P->max_adapters - (int)P->free_slots.size();
-    const int items = std::min(T, loaded) * (P->rpad / 16);
-    const int per_tile = ceil_div(items, a.NT);
-    a.na = per_tile <= 1 ? 1 : per_tile <= 2 ? 2 : 4;
-    a.a_tiles = ceil_div(std::max(0, items - a.NT * a.na), 4 + a.na);
-  }
-  return hrg::launch_decode(a, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+  // A items: (adapter, 16-rank block); at most min(T, resident) adapters
+  // (the launcher places them)
+  const int loaded = P->max_adapters - (int)P->free_slots.size();
+  const int items = lora ? std::min(T, loaded) * (P->rpad / 16) : 0;
+  return hrg::launch_decode(a, items, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
 }  // namespace
@@ -254,7 +249,8 @@ lora_status_t lora_pool_create(lora_pool_t* pool, int32_t max_adapters, int32_t 
   if (ok)
     ok = dmalloc(&P->E, (size_t)hrg::kMaxSmallRows * max_dout) == hipSuccess &&
          dmalloc(&P->dec_upart, ks_max * hrg::kDecodeMaxT * P->rpad) == hipSuccess &&
-         dmalloc(&P->dec_part, ks_max * hrg::kDecodeMaxT * max_dout) == hipSuccess;
+         dmalloc(&P->dec_part, ks_max * hrg::kDecodeMaxT * round_up((int)max_dout, hrg::kDecodeTileRows)) ==
+             hipSuccess;
   if (ok) ok = plan_alloc(P, &P->internal) == LORA_OK;
   if (!ok) {
     (void)hipGetLastError();

@@ -96,48 +96,46 @@ __device__ __forceinline__ void barrier_after(void) {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(N) : "memory");
 }
 
-// NA: A waves riding in each W-tile block (0 on the base-only path).
+// NA: A waves riding in each W block (0 on the base-only path).
+//
+// W blocks (the first np = nbc * KS): block b keeps K chunk c = b mod KS and
+// walks the column tiles bi, bi + nbc, ... (bi = b div KS), so its X chunk is
+// staged once however many tiles it takes.  Each W wave streams its 16 rows
+// of those tiles as a sequence of 512-deep halves through two register
+// buffers: the next half's loads are in flight while the current half's
+// MFMAs run (with 16 KB per wave and half in flight, the chip keeps about
+// 32 MB of reads outstanding, ample for the memory's latency).  Every load
+// is issued (past the last half a wave re-reads its last half, which is not
+// applied) and every partial store too (rows past N and tokens past T land
+// in the padding of `part`), so the loads' completion is counted exactly.
 template <int NA>
 __global__ __launch_bounds__(64 * (4 + NA)) void decode_main(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[64 * kXs];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g4 = lane >> 4, r16 = lane & 15;
-  const int T = a.T, N = a.N, K = a.K;
+  const int T = a.T, N = a.N, K = a.K, KS = a.KS;
+  const int nbc = a.np / KS;  // W blocks per K chunk
 
-  // Block order: the W tiles first, the hardware handing block b to XCD
-  // (b mod 8) -- each XCD takes a contiguous run of (tile, chunk) pairs so
-  // neighbouring tiles share its L2 -- then the blocks of A waves only.
-  const int G = a.NT * a.KS;
-  int tile, c;
-  bool w_block;
-  if ((int)blockIdx.x < G) {
-    w_block = true;
-    const int g = (int)blockIdx.x;
-    const int xcd = g % 8, qd = G / 8, rm = G % 8;
-    const int logical = xcd * qd + min(xcd, rm) + g / 8;
-    tile = logical / a.KS;
-    c = logical % a.KS;
-  } else {
-    w_block = false;
-    const int g = (int)blockIdx.x - G;
-    tile = g / a.KS;
-    c = g % a.KS;
+  int c, bi;
+  const bool w_block = (int)blockIdx.x < a.np;
+  if (w_block) {
+    c = (int)blockIdx.x % KS;
+    bi = (int)blockIdx.x / KS;
+  } else {  // blocks of A waves only
+    const int g = (int)blockIdx.x - a.np;
+    c = g % KS;
+    bi = g / KS;
   }
   const int k0 = c * kDecodeChunk, klen = min(K, k0 + kDecodeChunk) - k0;
+  const bool a_wave = !w_block || w >= 4;
 
-  // ---- this wave's 16 rows ----
+  // ---- an A wave's 16 rows ----
   const uint16_t* row = nullptr;  // row r16 of the block of 16, at k0
   bool row_ok = false;
-  int n0 = 0;                     // W wave: first column
-  int qb = 0;                     // A wave: rank block of the adapter
-  uint64_t members = 0;           // A wave: tokens of the adapter
-  const bool a_wave = !w_block || w >= 4;
-  if (!a_wave) {
-    n0 = tile * kDecodeTileRows + 16 * w;
-    row_ok = n0 + r16 < N;
-    row = a.W + (size_t)(row_ok ? n0 + r16 : 0) * K + k0;
-  } else {
+  int qb = 0;                     // rank block of the adapter
+  uint64_t members = 0;           // tokens of the adapter
+  if (a_wave) {
     // item = the item-th (adapter, 16-rank block) of the batch, adapters in
     // order of first occurrence.  Lane t holds token t's id.  A direct-mapped
     // pool keeps adapter id in slot id, so the page address follows from the
@@ -145,7 +143,7 @@ __global__ __launch_bounds__(64 * (4 + NA)) void decode_main(DecodeArgs a) {
     // rows past an adapter's rank are zero); otherwise one more round of
     // loads fetches each token's slot and rank.  Both load rounds go out
     // before the weight stream fills the memory queues.
-    const int item = w_block ? tile + a.NT * (w - 4) : a.NT * NA + (4 + NA) * tile + w;
+    const int item = w_block ? bi + nbc * (w - 4) : nbc * NA + (4 + NA) * bi + w;
     int id = -1, slot = -1, rank = 0, bad = 0;
     if (a.direct) {
       if (lane < T) id = a.ids[lane];
@@ -185,13 +183,9 @@ __global__ __launch_bounds__(64 * (4 + NA)) void decode_main(DecodeArgs a) {
     // with the W path (where it would also wait for the X DMA below)
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   }
-  const bool active = row != nullptr;  // an A wave past the last item has nothing to do
-  if (!active) row = a.X + k0;         // dummy in-bounds source, results discarded
 
   // ---- X chunk -> LDS by DMA: waves 0..3 copy tokens 16w .. 16w+15, two
-  // 1-KB pieces per token row.  Rows >= T and columns >= K read zeros.  (An
-  // A wave's lookups above have completed, so no wait for them lands between
-  // this DMA and the slice loads below.)
+  // 1-KB pieces per token row.  Rows >= T and columns >= K read zeros.
   if (w < 4) {
     const __amdgpu_buffer_rsrc_t rx =
         __builtin_amdgcn_make_buffer_rsrc((void*)a.X, (short)0, T * K * 2, 0x00020000);
@@ -199,48 +193,96 @@ __global__ __launch_bounds__(64 * (4 + NA)) void decode_main(DecodeArgs a) {
     for (int i = 0; i < 32; ++i) {
       const int r = 16 * w + (i >> 1), h = i & 1;
       const int k = k0 + 512 * h + 8 * lane;
-      const uint32_t off = (r < T && k < K) ? (uint32_t)(r * K + k) * 2u : kOobOff;
+      // rows >= T lie past the buffer's range (zeros); columns >= K are
+      // sent past it
+      const uint32_t off = k < K ? (uint32_t)(r * K + k) * 2u : kOobOff;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(xs + r * kXs + 512 * h), 16, off, 0, 0, 0);
     }
   }
 
-
-  // ---- the whole 16 x 1024 slice, issued at once ----
-  uint4 rw[kSteps];
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) rw[s] = ld16(row + min(32 * s + 8 * g4, klen - 8));
-  // the X DMA (issued before the slice) has landed in every wave
-  barrier_after<kSteps>();
-  if (!active) return;
-
-  const int nm = (T + 15) / 16;
   f32x4 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // acc[i] += X[16 i .. 16 i + 15, k .. k + 31] . W slice, for each step s
+  // of a register block of kHalf / 32 steps starting at kh
+  constexpr int kHalf = kDecodeChunk / 2, kHS = kHalf / 32;
+
+  if (!a_wave) {
+    const int ntile = (a.NT - bi + nbc - 1) / nbc;  // >= 1: the host keeps nbc <= NT
+    const int nhalf = 2 * ntile;
+    uint4 rw[2][kHS];
+    // one buffer resource over W: a half is one offset plus immediates, and
+    // reads past the end of W return zeros (reads past the chunk within W are
+    // masked below)
+    const __amdgpu_buffer_rsrc_t rws =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.W, (short)0, N * K * 2, 0x00020000);
+    auto load = [&](uint4 (&buf)[kHS], int s) __attribute__((always_inline)) {
+      const int sc = min(s, nhalf - 1);
+      // row r16 of this wave's 16 rows of tile sc / 2 (rows past N read row
+      // 0; their results land in the padding of `part`)
+      const int n = (bi + (sc >> 1) * nbc) * kDecodeTileRows + 16 * w + r16;
+      const int off = ((n < N ? n : 0) * K + k0 + kHalf * (sc & 1) + 8 * g4) * 2;
+#pragma unroll
+      for (int i = 0; i < kHS; ++i)
+        buf[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rws, off + 64 * i, 0, 0));
+    };
+    load(rw[0], 0);
+    // the X DMA (issued before these loads) has landed in every wave
+    barrier_after<kHS>();
+    // phase H of a tile: half H in rw[H]; the next half goes to rw[1 - H]
+    auto phase = [&](auto hc, int s) __attribute__((always_inline)) {
+      constexpr int H = decltype(hc)::value;
+      load(rw[1 - H], s + 1);
+#pragma unroll
+      for (int i = 0; i < kHS; ++i) {
+        const int k = kHalf * H + 32 * i + 8 * g4;
+        const bf16x8 wb = __builtin_bit_cast(bf16x8, keep_if(k < klen, rw[H][i]));
+        // W as the A operand: a lane's results are 4 consecutive columns of
+        // one token, stored as one 16-byte write
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb)
+          acc[tb] = mfma16(wb, lds_bf16x8(xs + (16 * tb + r16) * kXs + k), acc[tb]);
+        // at most four steps' X fragments in registers at a time
+        if (i % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (H == 1) {
+        // the tile's partial sums: acc[tb][e] is token 16 tb + r16, column
+        // n + e of this wave's 16
+        const int n = (bi + (s >> 1) * nbc) * kDecodeTileRows + 16 * w + 4 * g4;
+        float* pp = a.part + (size_t)c * 64 * a.npad + (size_t)r16 * a.npad + n;
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          *reinterpret_cast<float4*>(pp + (size_t)(16 * tb) * a.npad) =
+              make_float4(acc[tb][0], acc[tb][1], acc[tb][2], acc[tb][3]);
+          acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    };
+    for (int s = 0; s < nhalf; s += 2) {
+      phase(std::integral_constant<int, 0>{}, s);
+      phase(std::integral_constant<int, 1>{}, s + 1);
+    }
+    return;
+  }
+
+  // ---- an A wave: its whole 16 x 1024 slice, issued at once ----
+  const bool active = row != nullptr;  // an A wave past the last item has nothing to do
+  if (!active) row = a.X + k0;         // dummy in-bounds source, results discarded
+  uint4 rwa[kSteps];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) rwa[s] = ld16(row + min(32 * s + 8 * g4, klen - 8));
+  barrier_after<kSteps>();
+  if (!active) return;
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
     const int k = 32 * s + 8 * g4;
-    const bf16x8 wb = __builtin_bit_cast(bf16x8, keep_if(k < klen && row_ok, rw[s]));
+    const bf16x8 wb = __builtin_bit_cast(bf16x8, keep_if(k < klen && row_ok, rwa[s]));
     // all four 16-token row blocks: rows >= T hold zeros and are never stored
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = mfma16(lds_bf16x8(xs + (16 * i + r16) * kXs + k), wb, acc[i]);
   }
-
-  // ---- partial tile out: acc[i][e] is token 16 i + 4 g4 + e, row r16 of the block ----
-  if (!a_wave) {
-    if (row_ok) {
-      float* pp = a.part + (size_t)c * 64 * N + n0 + r16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i >= nm) continue;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * i + 4 * g4 + e;
-          if (t < T) pp[(size_t)t * N] = acc[i][e];
-        }
-      }
-    }
-  } else if (row_ok) {
+  if (row_ok) {
+    const int nm = (T + 15) / 16;
     float* up = a.upart + (size_t)c * 64 * a.u_ld + 16 * qb + r16;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -299,10 +341,10 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
     if (tid < 64) s_id[tid] = tid < T ? a.ids[tid] : -1;
     if (tid == 0) s_bad = 0;
   }
-  const float* pp = a.part + (size_t)min(t, T - 1) * N + min(n, N - 4);
+  const float* pp = a.part + (size_t)min(t, T - 1) * a.npad + min(n, N - 4);
   float4 pv[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) pv[j] = *reinterpret_cast<const float4*>(pp + (size_t)min(j, KS - 1) * 64 * N);
+  for (int j = 0; j < 4; ++j) pv[j] = *reinterpret_cast<const float4*>(pp + (size_t)min(j, KS - 1) * 64 * a.npad);
   float u[kVPer];
   uint4 bv[8];
   int slot = -1, rank = 0;
@@ -374,7 +416,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
     if (c0 > 0) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        pv[j] = *reinterpret_cast<const float4*>(pp + (size_t)min(c0 + j, KS - 1) * 64 * N);
+        pv[j] = *reinterpret_cast<const float4*>(pp + (size_t)min(c0 + j, KS - 1) * 64 * a.npad);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -421,8 +463,24 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
   *reinterpret_cast<uint2*>(a.out + (size_t)t * N + n) = make_uint2(o0, o1);
 }
 
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  const dim3 grid((a.NT + a.a_tiles) * a.KS);
+hipError_t launch_decode(const DecodeArgs& args, int items, hipStream_t s) {
+  DecodeArgs a = args;
+  // W blocks: every (tile, chunk) pair if the chip holds them at once, else
+  // as many whole sets of KS chunk blocks as it holds (one block per compute
+  // unit: the X chunk fills most of the LDS), each walking several tiles
+  const int resident = resident_blocks(reinterpret_cast<const void*>(&decode_main<0>), 256, 0);
+  a.np = std::min(a.NT * a.KS, std::max(1, resident / a.KS) * a.KS);
+  const int nbc = a.np / a.KS;
+  a.na = 0;
+  a.a_tiles = 0;
+  if (a.lora) {
+    // items ride in the W blocks (na waves each, 1, 2 or 4); the rest get
+    // extra blocks of A waves only
+    const int per_block = (items + nbc - 1) / nbc;
+    a.na = per_block <= 1 ? 1 : per_block <= 2 ? 2 : 4;
+    a.a_tiles = (std::max(0, items - nbc * a.na) + 3 + a.na) / (4 + a.na);
+  }
+  const dim3 grid(a.np + a.a_tiles * a.KS);
   switch (a.na) {
     case 0: hipLaunchKernelGGL(decode_main<0>, grid, dim3(256), 0, s, a); break;
     case 1: hipLaunchKernelGGL(decode_main<1>, grid, dim3(320), 0, s, a); break;

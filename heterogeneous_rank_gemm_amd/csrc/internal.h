@@ -120,7 +120,7 @@ struct DecodeArgs {
   const uint16_t* pages;
   size_t slot_stride;
   size_t a_off, b_off;
-  float* part;            // [KS][64][N]
+  float* part;            // [KS][64][npad]
   float* upart;           // [KS][64][u_ld]
   int32_t direct;         // pool keeps adapter id in slot id (max_ids <= max_adapters)
   int32_t max_slots;      // resident slots of the pool
@@ -129,7 +129,9 @@ struct DecodeArgs {
   int32_t* status;
   int32_t NT;             // W tiles (kDecodeTileRows rows each)
   int32_t KS;             // K chunks
-  int32_t na;             // A waves riding in each W-tile block: 0, 1, 2 or 4 (0: base-only)
+  int32_t np;             // W blocks: a multiple of KS, at most NT * KS (each walks NT / (np / KS) tiles)
+  int32_t npad;           // row length of part: NT * kDecodeTileRows
+  int32_t na;             // A waves riding in each W block: 0, 1, 2 or 4 (0: base-only)
   int32_t a_tiles;        // extra blocks of 4 + na A waves, per K chunk
   int32_t lora;
 };
@@ -161,7 +163,8 @@ hipError_t launch_prefill(const GemmArgs& a, bool lora, int shape, hipStream_t s
 // The E rows of the small segments (one launch, before the GEMM).
 hipError_t launch_expand_small(const GemmArgs& a, hipStream_t s);
 int prefill_choose(int T, int N);
-hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+// Picks the W blocks (np) and where the `items` A items go, then launches.
+hipError_t launch_decode(const DecodeArgs& a, int items, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 hipError_t launch_set_slot(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
                            int32_t id, int32_t slot, int32_t rank, float scale, hipStream_t s);
