@@ -80,6 +80,7 @@ struct GemmArgs {
   const uint16_t* W;      // [N][K]
   uint16_t* out;          // [T][N]
   int32_t T, N, K;
+  int32_t row0, row1;     // sorted rows [row0, row1) of this launch (set by launch_prefill)
   const int32_t* perm;    // sorted row -> token; nullptr = identity (base-only)
   // expand (unused by the base-only instantiation)
   const uint16_t* v_hi;   // [T_cap][u_ld] s * U, bf16 high part, sorted rows
@@ -157,8 +158,10 @@ int resident_blocks(const void* fn, int threads, size_t lds);
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 // Shrink partial planes, then the split reduction into V (two launches).
 hipError_t launch_shrink(const ShrinkArgs& a, int grid, int ksplit, int T, hipStream_t s);
-// shape < 0 picks the tile shape from (T, N); 0..3 force 256x256, 256x128,
-// 128x256, 128x128 (tokens x columns).  Every shape gives the same bits.
+// shape < 0 picks the tile shapes from (T, N): one shape for every row, or
+// 256x256 tiles over the first rows (whole 256-row tiles) and 128x128 tiles
+// over the rest, as two launches; 0..3 force 256x256, 256x128, 128x256,
+// 128x128 (tokens x columns) for every row.  Every shape gives the same bits.
 hipError_t launch_prefill(const GemmArgs& a, bool lora, int shape, hipStream_t s);
 // The E rows of the small segments (one launch, before the GEMM).
 hipError_t launch_expand_small(const GemmArgs& a, hipStream_t s);

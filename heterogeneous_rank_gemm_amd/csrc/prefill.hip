@@ -141,10 +141,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
     if (*a.status != 0) return;  // strict mode: a failed plan leaves out untouched
   }
   const int T = a.T, N = a.N, K = a.K;
-  const int tiles_m = (T + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  // this launch's rows: [row0, row1) of the sorted batch (row1 - row0 is a
+  // multiple of BM unless row1 = T)
+  const int tiles_m = (a.row1 - a.row0 + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = a.row0 + tm * BM, n0 = tn * BN;
   const int l = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wn = wid & 1, wm = wid >> 1;
@@ -578,7 +580,7 @@ hipError_t launch_expand_small(const GemmArgs& a, hipStream_t s) {
 
 template <int BM, int BN>
 static hipError_t launch_cfg(const GemmArgs& a, bool lora, hipStream_t s) {
-  const int tiles = ((a.T + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  const int tiles = ((a.row1 - a.row0 + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   if (!lora) {
     hipLaunchKernelGGL((prefill_kernel<BM, BN, false, 0>), dim3(tiles), dim3(256), 0, s, a);
   } else {
@@ -594,20 +596,23 @@ static hipError_t launch_cfg(const GemmArgs& a, bool lora, hipStream_t s) {
 }
 
 // Relative time of one tile (per unit of K) for each shape, measured on
-// MI355X; the launcher picks the shape with the least estimated time, counting
-// whole rounds of 256 tiles (one tile per compute unit).
+// MI355X; the launcher picks the shapes with the least estimated time,
+// counting whole rounds of 256 tiles (one tile per compute unit).
+struct Shape {
+  int bm, bn;
+  double cost;
+};
+static const Shape kShapes[] = {{256, 256, 1.00}, {256, 128, 0.56}, {128, 256, 0.56}, {128, 128, 0.32}};
+static double shape_time(int i, int rows, int N) {
+  const long tiles = (long)((rows + kShapes[i].bm - 1) / kShapes[i].bm) * ((N + kShapes[i].bn - 1) / kShapes[i].bn);
+  return (double)((tiles + 255) / 256) * kShapes[i].cost;
+}
+
 int prefill_choose(int T, int N) {
-  struct Shape {
-    int bm, bn;
-    double cost;
-  };
-  static const Shape shapes[] = {{256, 256, 1.00}, {256, 128, 0.56}, {128, 256, 0.56}, {128, 128, 0.32}};
   int best = 0;
   double best_t = 1e30;
   for (int i = 0; i < 4; ++i) {
-    const long tiles = (long)((T + shapes[i].bm - 1) / shapes[i].bm) * ((N + shapes[i].bn - 1) / shapes[i].bn);
-    const long rounds = (tiles + 255) / 256;
-    const double t = rounds * shapes[i].cost;
+    const double t = shape_time(i, T, N);
     if (t < best_t * 0.999) {
       best_t = t;
       best = i;
@@ -616,15 +621,48 @@ int prefill_choose(int T, int N) {
   return best;
 }
 
-hipError_t launch_prefill(const GemmArgs& a, bool lora, int shape, hipStream_t s) {
-  if (a.T <= 0) return hipSuccess;
-  if (shape < 0) shape = prefill_choose(a.T, a.N);
+static hipError_t launch_shape(const GemmArgs& a, bool lora, int shape, hipStream_t s) {
   switch (shape) {
     case 0: return launch_cfg<256, 256>(a, lora, s);
     case 1: return launch_cfg<256, 128>(a, lora, s);
     case 2: return launch_cfg<128, 256>(a, lora, s);
     default: return launch_cfg<128, 128>(a, lora, s);
   }
+}
+
+hipError_t launch_prefill(const GemmArgs& args, bool lora, int shape, hipStream_t s) {
+  if (args.T <= 0) return hipSuccess;
+  GemmArgs a = args;
+  a.row0 = 0;
+  a.row1 = a.T;
+  if (shape >= 0) return launch_shape(a, lora, shape, s);
+  // one shape for every row, or 256x256 tiles over the first rows (a whole
+  // number of 256-row tiles) and 128x128 tiles over the rest: a second,
+  // short round of small tiles instead of a mostly empty round of big ones
+  const int one = prefill_choose(a.T, a.N);
+  const double t_one = shape_time(one, a.T, a.N);
+  // (among equal estimates the most rows in big tiles: the small tiles then
+  // share the memory with fewer others)
+  int tm = 0;
+  double t_two = 1e30;
+  for (int r = 256; r < a.T; r += 256) {
+    const double t = shape_time(0, r, a.N) + shape_time(3, a.T - r, a.N) + 0.03;
+    if (t <= t_two * 1.001) {
+      t_two = std::min(t, t_two);
+      tm = r;
+    }
+  }
+  if (tm > 0) {
+    if (t_two < t_one * 0.999) {
+      a.row1 = tm;
+      hipError_t e = launch_shape(a, lora, 0, s);
+      if (e != hipSuccess) return e;
+      a.row0 = tm;
+      a.row1 = a.T;
+      return launch_shape(a, lora, 3, s);
+    }
+  }
+  return launch_shape(a, lora, one, s);
 }
 
 }  // namespace hrg
