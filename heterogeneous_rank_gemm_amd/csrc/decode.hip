@@ -104,10 +104,10 @@ __device__ __forceinline__ void barrier_after(void) {
 // of those tiles as a sequence of 512-deep halves through two register
 // buffers: the next half's loads are in flight while the current half's
 // MFMAs run (with 16 KB per wave and half in flight, the chip keeps about
-// 32 MB of reads outstanding, ample for the memory's latency).  Every load
-// is issued (past the last half a wave re-reads its last half, which is not
-// applied) and every partial store too (rows past N and tokens past T land
-// in the padding of `part`), so the loads' completion is counted exactly.
+// 32 MB of reads outstanding, ample for the memory's latency).  The loads
+// and partial stores follow a fixed pattern (rows past N and tokens past T
+// land in the padding of `part`), so the loads' completion is counted
+// exactly.
 template <int NA>
 __global__ __launch_bounds__(64 * (4 + NA)) void decode_main(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[64 * kXs];
@@ -229,10 +229,12 @@ __global__ __launch_bounds__(64 * (4 + NA)) void decode_main(DecodeArgs a) {
     load(rw[0], 0);
     // the X DMA (issued before these loads) has landed in every wave
     barrier_after<kHS>();
-    // phase H of a tile: half H in rw[H]; the next half goes to rw[1 - H]
-    auto phase = [&](auto hc, int s) __attribute__((always_inline)) {
+    // phase H of a tile: half H in rw[H]; the next half (if NEXT) goes to
+    // rw[1 - H]
+    auto phase = [&](auto hc, auto nc, int s) __attribute__((always_inline)) {
       constexpr int H = decltype(hc)::value;
-      load(rw[1 - H], s + 1);
+      constexpr bool NEXT = decltype(nc)::value;
+      if constexpr (NEXT) load(rw[1 - H], s + 1);
 #pragma unroll
       for (int i = 0; i < kHS; ++i) {
         const int k = kHalf * H + 32 * i + 8 * g4;
@@ -258,10 +260,15 @@ __global__ __launch_bounds__(64 * (4 + NA)) void decode_main(DecodeArgs a) {
         }
       }
     };
-    for (int s = 0; s < nhalf; s += 2) {
-      phase(std::integral_constant<int, 0>{}, s);
-      phase(std::integral_constant<int, 1>{}, s + 1);
+    // every tile but the last requests the next tile's first half during its
+    // second half; the last one requests nothing (a wave does not end with
+    // loads in flight)
+    for (int s = 0; s < nhalf - 2; s += 2) {
+      phase(std::integral_constant<int, 0>{}, std::true_type{}, s);
+      phase(std::integral_constant<int, 1>{}, std::true_type{}, s + 1);
     }
+    phase(std::integral_constant<int, 0>{}, std::true_type{}, nhalf - 2);
+    phase(std::integral_constant<int, 1>{}, std::false_type{}, nhalf - 1);
     return;
   }
 
