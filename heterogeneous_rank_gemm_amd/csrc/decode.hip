@@ -280,6 +280,34 @@ __global__ __launch_bounds__(64 * (4 + NA)) void decode_main(DecodeArgs a) {
   for (int s = 0; s < kSteps; ++s) rwa[s] = ld16(row + min(32 * s + 8 * g4, klen - 8));
   barrier_after<kSteps>();
   if (!active) return;
+  // An adapter with at most 16 tokens in the batch (the usual case at decode)
+  // needs one 16-token MFMA block, not four: lane r16 reads the X row of the
+  // adapter's r16-th token, a quarter of the MFMAs and LDS reads.
+  const int cnt = __popcll(members);
+  if (cnt <= 16) {
+    uint64_t m = members;  // X row of this lane: the r16-th member (row 0 past the last)
+    for (int i = 0; i < r16; ++i) m &= m - 1;
+    const int xr = m ? (int)__builtin_ctzll(m) : 0;
+    f32x4 acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+      const int k = 32 * s + 8 * g4;
+      const bf16x8 wb = __builtin_bit_cast(bf16x8, keep_if(k < klen && row_ok, rwa[s]));
+      acc1 = mfma16(lds_bf16x8(xs + xr * kXs + k), wb, acc1);
+    }
+    if (row_ok) {
+      // acc1[e] belongs to member 4 g4 + e
+      uint64_t mm = members;
+      for (int i = 0; i < 4 * g4; ++i) mm &= mm - 1;
+      float* up = a.upart + (size_t)c * 64 * a.u_ld + 16 * qb + r16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (mm) up[(size_t)__builtin_ctzll(mm) * a.u_ld] = acc1[e];
+        mm &= mm - 1;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) {
     const int k = 32 * s + 8 * g4;
