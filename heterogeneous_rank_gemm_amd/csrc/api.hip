@@ -83,8 +83,9 @@ lora_status_t plan_alloc(lora_pool_s* P, lora_plan_s** out) {
   const size_t Tc = (size_t)P->max_tokens;
   const int mt = max_tiles_for(P);
   // perm, inv, row_seg, erow (Tc each); seg_id, seg_slot, seg_rank, seg_scale,
-  // seg_e0 (Tc+1); seg_off (Tc+2); tile_seg, tile_row0 (mt); small_seg; counts (4)
-  const size_t n32 = 4 * Tc + 5 * (Tc + 1) + (Tc + 2) + 2 * (size_t)mt + hrg::kMaxSmallRows + 4;
+  // seg_e0 (Tc+1); seg_off (Tc+2); tile_info (4 mt, first: 16-byte aligned);
+  // small_seg; counts (4)
+  const size_t n32 = 4 * Tc + 5 * (Tc + 1) + (Tc + 2) + 4 * (size_t)mt + hrg::kMaxSmallRows + 4;
   lora_plan_s* pl = new (std::nothrow) lora_plan_s();
   if (!pl) return LORA_ERR_OOM;
   int32_t* blk = nullptr;
@@ -96,6 +97,7 @@ lora_status_t plan_alloc(lora_pool_s* P, lora_plan_s** out) {
   pl->block = blk;
   int32_t* c = blk;
   auto take = [&](size_t n) { int32_t* r = c; c += n; return r; };
+  pl->tab.tile_info = reinterpret_cast<int4*>(take(4 * (size_t)mt));
   pl->tab.perm = take(Tc);
   pl->tab.inv = take(Tc);
   pl->tab.row_seg = take(Tc);
@@ -104,8 +106,6 @@ lora_status_t plan_alloc(lora_pool_s* P, lora_plan_s** out) {
   pl->tab.seg_rank = take(Tc + 1);
   pl->tab.seg_scale = reinterpret_cast<float*>(take(Tc + 1));
   pl->tab.seg_off = take(Tc + 2);
-  pl->tab.tile_seg = take(mt);
-  pl->tab.tile_row0 = take(mt);
   pl->tab.erow = take(Tc);
   pl->tab.seg_e0 = take(Tc + 1);
   pl->tab.small_seg = take(hrg::kMaxSmallRows);
@@ -441,11 +441,9 @@ static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t
   sa.X = X;
   sa.K = K;
   sa.perm = pl->tab.perm;
-  sa.seg_off = pl->tab.seg_off;
   sa.seg_slot = pl->tab.seg_slot;
   sa.seg_rank = pl->tab.seg_rank;
-  sa.tile_seg = pl->tab.tile_seg;
-  sa.tile_row0 = pl->tab.tile_row0;
+  sa.tile_info = pl->tab.tile_info;
   sa.counts = pl->tab.counts;
   sa.seg_scale = pl->tab.seg_scale;
   sa.pages = P->pages;

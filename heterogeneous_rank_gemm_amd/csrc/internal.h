@@ -32,8 +32,7 @@ struct PlanTables {
   int32_t* seg_slot;   // [T_cap+1] pool slot (-1 for the base segment)
   int32_t* seg_rank;   // [T_cap+1] true rank (0 for the base segment)
   float* seg_scale;    // [T_cap+1] alpha / rank
-  int32_t* tile_seg;   // [max_tiles] shrink work tile -> segment
-  int32_t* tile_row0;  // [max_tiles] first sorted row of the tile
+  int4* tile_info;     // [max_tiles] shrink work tile: {first sorted row, rows, pool slot, rank}
   int32_t* seg_e0;     // [T_cap+1] first E row of a small segment, -1 otherwise
   int32_t* erow;       // [T_cap]   sorted position -> E row, -1 if not in a small segment
   int32_t* small_seg;  // [kMaxSmallRows] the small segments, in order
@@ -54,11 +53,9 @@ struct ShrinkArgs {
   const uint16_t* X;      // [T][K]
   int32_t K;
   const int32_t* perm;
-  const int32_t* seg_off;
   const int32_t* seg_slot;
   const int32_t* seg_rank;
-  const int32_t* tile_seg;
-  const int32_t* tile_row0;
+  const int4* tile_info;
   const int32_t* counts;
   const float* seg_scale;
   const uint16_t* pages;  // A^T page of (slot, module): pages + slot*slot_stride + a_off, [rmax][K]

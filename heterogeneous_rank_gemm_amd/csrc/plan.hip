@@ -84,6 +84,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     } else {
       if (id >= 0 && a.id_info[id].x < 0) atomicMax(&s_err, kStatusNotLoaded);
       atomicAdd(&start[id + 1], 1);
+      if (t < kStageTok) s_bucket[t] = (uint16_t)(id + 1);  // the first placement block, staged now
     }
   }
   __syncthreads();
@@ -118,26 +119,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   // adapter segment cut into runs of kShrinkRows sorted rows) and the small
   // segments (adapter segments of at most kSmallRows tokens; E rows in
   // segment order while they fit in kMaxSmallRows), placed by prefix sums
-  // over the threads' buckets
+  // over the threads' buckets.  The counts need only the bucket sizes; the
+  // id_info lookups and every table write come in the second pass.
   int v3[3] = {0, 0, 0};  // tiles, small rows, small segments
   for (int b = b0; b < b1; ++b) {
     const int nxt = (b + 1 < nb) ? start[b + 1] : T;
     const int len = nxt - start[b];
-    if (len > 0) {
-      const int s = segidx[b];
-      const int id = b - 1;
-      const int4 inf = id >= 0 ? a.id_info[id] : make_int4(-1, 0, 0, 0);
-      a.tab.seg_id[s] = id;
-      a.tab.seg_off[s] = start[b];
-      a.tab.seg_slot[s] = inf.x;
-      a.tab.seg_rank[s] = id >= 0 ? inf.y : 0;
-      a.tab.seg_scale[s] = id >= 0 ? __builtin_bit_cast(float, inf.z) : 0.f;
-      if (id >= 0) {
-        v3[0] += (len + kShrinkRows - 1) / kShrinkRows;
-        if (len <= kSmallRows) {
-          v3[1] += len;
-          v3[2] += 1;
-        }
+    if (len > 0 && b > 0) {
+      v3[0] += (len + kShrinkRows - 1) / kShrinkRows;
+      if (len <= kSmallRows) {
+        v3[1] += len;
+        v3[2] += 1;
       }
     }
   }
@@ -147,14 +139,21 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const int off = start[b], len = nxt - off;
     if (len <= 0) continue;
     const int s = segidx[b];
+    const int id = b - 1;
+    const int4 inf = id >= 0 ? a.id_info[id] : make_int4(-1, 0, 0, 0);
+    const int rank = id >= 0 ? inf.y : 0;
+    a.tab.seg_id[s] = id;
+    a.tab.seg_off[s] = off;
+    a.tab.seg_slot[s] = inf.x;
+    a.tab.seg_rank[s] = rank;
+    a.tab.seg_scale[s] = id >= 0 ? __builtin_bit_cast(float, inf.z) : 0.f;
     int e0 = -1;
-    if (b > 0) {
+    if (id >= 0) {
       const int nt = (len + kShrinkRows - 1) / kShrinkRows;
       for (int j = 0; j < nt; ++j) {
-        if (v3[0] + j < a.tab.max_tiles) {
-          a.tab.tile_seg[v3[0] + j] = s;
-          a.tab.tile_row0[v3[0] + j] = off + j * kShrinkRows;
-        }
+        if (v3[0] + j < a.tab.max_tiles)
+          a.tab.tile_info[v3[0] + j] =
+              make_int4(off + j * kShrinkRows, min(kShrinkRows, len - j * kShrinkRows), inf.x, rank);
       }
       v3[0] += nt;
       if (len <= kSmallRows) {
@@ -188,7 +187,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const int blk1 = min(T, blk0 + kStageTok);
     const int share = (blk1 - blk0 + PW - 1) / PW;
     __syncthreads();  // the previous block is placed
-    for (int t = blk0 + tid; t < blk1; t += kPlanThreads) s_bucket[t - blk0] = (uint16_t)(a.ids[t] + 1);
+    if (blk0 > 0)
+      for (int t = blk0 + tid; t < blk1; t += kPlanThreads) s_bucket[t - blk0] = (uint16_t)(a.ids[t] + 1);
     if (PW > 1)
       for (int i = tid; i < PW * nb; i += kPlanThreads) cur[i] = 0;
     __syncthreads();

@@ -29,14 +29,13 @@ __device__ __forceinline__ bf16x8 keep_bf(bool keep, uint4 v) {
 }
 
 // NQ: 16-rank blocks held per item (the pool's rank rounded up to 16, in
-// blocks; an adapter of lower rank masks the rest)
+// blocks; an adapter of lower rank masks the rest).
+// The next item's tile entry (index `next`) is requested into *tn with the
+// X loads, so waiting for it costs nothing.
 template <int NQ>
-__device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64 * kRedLd], int tile, int split) {
-  const int seg = a.tile_seg[tile];
-  const int row0 = a.tile_row0[tile];
-  const int rows = min(kShrinkRows, a.seg_off[seg + 1] - row0);
-  const int slot = a.seg_slot[seg];
-  const int rank = a.seg_rank[seg];
+__device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64 * kRedLd], int4 ti, int split,
+                                            int next, int4* tn) {
+  const int row0 = ti.x, rows = ti.y, slot = ti.z, rank = ti.w;
   const int nq = (rank + 15) / 16;  // 16-wide rank blocks actually computed
   const int nm = (rows + 15) / 16;  // 16-row blocks with at least one row
   const int K = a.K;
@@ -45,6 +44,31 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const uint16_t* Ap = a.pages + (size_t)slot * a.slot_stride + a.a_off;
 
+  // the A rows follow from the tile entry alone
+  const uint16_t* arow[NQ];
+  bool qv[NQ];
+#pragma unroll
+  for (int nb = 0; nb < NQ; ++nb) {
+    const int q = 16 * nb + (l & 15);
+    qv[nb] = q < rank;
+    arow[nb] = Ap + (size_t)(qv[nb] ? q : 0) * K;
+  }
+  const int koff = 8 * (l >> 4);
+  // 512-deep sub-chunks: wave w takes the 32-deep steps 32 w + 128 s of each;
+  // all of a sub-chunk's loads go out first (addresses clamped in bounds,
+  // values past the range masked), then its MFMAs.  The first sub-chunk's A
+  // loads go out before the token order is read.
+  uint4 av[4][NQ];
+  auto load_a = [&](int kb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int kc = min(kb + 128 * st + 32 * w + koff, K - 8);
+#pragma unroll
+      for (int nb = 0; nb < NQ; ++nb) av[st][nb] = ld16(arow[nb] + kc);
+    }
+  };
+  load_a(k0);
+  __builtin_amdgcn_sched_barrier(0);
   const uint16_t* xrow[4];
   bool rv[4];
 #pragma unroll
@@ -54,14 +78,6 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
     const int tok = a.perm[row0 + (rv[mb] ? p : 0)];
     xrow[mb] = a.X + (size_t)tok * K;
   }
-  const uint16_t* arow[NQ];
-  bool qv[NQ];
-#pragma unroll
-  for (int nb = 0; nb < NQ; ++nb) {
-    const int q = 16 * nb + (l & 15);
-    qv[nb] = q < rank;
-    arow[nb] = Ap + (size_t)(qv[nb] ? q : 0) * K;
-  }
 
   f32x4 acc[4][NQ];
 #pragma unroll
@@ -69,20 +85,16 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
 #pragma unroll
     for (int nb = 0; nb < NQ; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // 512-deep sub-chunks: wave w takes the 32-deep steps 32 w + 128 s of each;
-  // all of a sub-chunk's loads go out first (addresses clamped in bounds,
-  // values past the range masked), then its MFMAs
-  const int koff = 8 * (l >> 4);
   for (int kb = k0; kb < k1; kb += 512) {
-    uint4 xv[4][4], av[4][NQ];
+    if (kb > k0) load_a(kb);
+    uint4 xv[4][4];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int kc = min(kb + 128 * st + 32 * w + koff, K - 8);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) xv[st][mb] = ld16(xrow[mb] + kc);
-#pragma unroll
-      for (int nb = 0; nb < NQ; ++nb) av[st][nb] = ld16(arow[nb] + kc);
     }
+    if (kb == k0) *tn = a.tile_info[next];
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const bool kv = kb + 128 * st + 32 * w + koff < k1;  // a lane's 8 elements are all in or out
@@ -131,11 +143,19 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
 template <int NQ>
 __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
   __shared__ float red[4][64 * kRedLd];
-  if (*a.status != 0) return;
+  // the first item's tile entry is requested with the status and the count
+  // (the grid never exceeds max_tiles * nsplit items, so the read is in
+  // bounds; an entry past the count is never used), each next one while the
+  // current item runs
+  const int st = *a.status;
   const int nitems = a.counts[1] * a.nsplit;
+  int4 ti = a.tile_info[blockIdx.x / a.nsplit];
+  if (st != 0) return;
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    int4 tn;
     __syncthreads();  // the previous item is done with red
-    shrink_item<NQ>(a, red, item / a.nsplit, item % a.nsplit);
+    shrink_item<NQ>(a, red, ti, item % a.nsplit, min(item + (int)gridDim.x, nitems - 1) / a.nsplit, &tn);
+    ti = tn;
   }
 }
 
@@ -148,11 +168,20 @@ __global__ __launch_bounds__(256) void shrink_finalize_kernel(ShrinkArgs a, int 
   const int w = a.u_ld;
   for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < T * w; idx += gridDim.x * blockDim.x) {
     const int p = idx / w, q = idx % w;
-    const int sg = a.row_seg[p];
-    if (a.seg_slot[sg] < 0 || q >= ((a.seg_rank[sg] + 15) & ~15)) continue;
+    // the planes and the row's segment in one round, the segment's entry in
+    // the next; planes summed in split order
     const float* u0 = a.upart + (size_t)p * w + q;
-    float u = u0[0];
-    for (int sp = 1; sp < nsplit; ++sp) u += u0[(size_t)sp * a.split_stride];
+    const int sg = a.row_seg[p];
+    float u = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+      float pv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pv[j] = u0[(size_t)min(s0 + j, nsplit - 1) * a.split_stride];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (s0 + j < nsplit) u = (s0 + j == 0) ? pv[j] : u + pv[j];
+    }
+    if (a.seg_slot[sg] < 0 || q >= ((a.seg_rank[sg] + 15) & ~15)) continue;
     const float v = a.seg_scale[sg] * u;
     const __bf16 hi = (__bf16)v;
     const __bf16 lo = (__bf16)(v - (float)hi);
