@@ -83,9 +83,9 @@ lora_status_t plan_alloc(lora_pool_s* P, lora_plan_s** out) {
   const size_t Tc = (size_t)P->max_tokens;
   const int mt = max_tiles_for(P);
   // perm, inv, row_seg, erow (Tc each); seg_id, seg_slot, seg_rank, seg_scale,
-  // seg_e0 (Tc+1); seg_off (Tc+2); tile_info (4 mt, first: 16-byte aligned);
-  // small_seg; counts (4)
-  const size_t n32 = 4 * Tc + 5 * (Tc + 1) + (Tc + 2) + 4 * (size_t)mt + hrg::kMaxSmallRows + 4;
+  // seg_e0 (Tc+1); seg_off (Tc+2); tile_info (4 mt) and small_info
+  // (4 kMaxSmallRows), first: 16-byte aligned; counts (4)
+  const size_t n32 = 4 * Tc + 5 * (Tc + 1) + (Tc + 2) + 4 * (size_t)mt + 4 * (size_t)hrg::kMaxSmallRows + 4;
   lora_plan_s* pl = new (std::nothrow) lora_plan_s();
   if (!pl) return LORA_ERR_OOM;
   int32_t* blk = nullptr;
@@ -98,6 +98,7 @@ lora_status_t plan_alloc(lora_pool_s* P, lora_plan_s** out) {
   int32_t* c = blk;
   auto take = [&](size_t n) { int32_t* r = c; c += n; return r; };
   pl->tab.tile_info = reinterpret_cast<int4*>(take(4 * (size_t)mt));
+  pl->tab.small_info = reinterpret_cast<int4*>(take(4 * (size_t)hrg::kMaxSmallRows));
   pl->tab.perm = take(Tc);
   pl->tab.inv = take(Tc);
   pl->tab.row_seg = take(Tc);
@@ -108,7 +109,6 @@ lora_status_t plan_alloc(lora_pool_s* P, lora_plan_s** out) {
   pl->tab.seg_off = take(Tc + 2);
   pl->tab.erow = take(Tc);
   pl->tab.seg_e0 = take(Tc + 1);
-  pl->tab.small_seg = take(hrg::kMaxSmallRows);
   pl->tab.counts = take(4);
   pl->tab.max_tiles = mt;
   *out = pl;
@@ -473,7 +473,7 @@ static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t
   ga.b_off = P->b_off[module];
   ga.seg_e0 = pl->tab.seg_e0;
   ga.erow = pl->tab.erow;
-  ga.small_seg = pl->tab.small_seg;
+  ga.small_info = pl->tab.small_info;
   ga.counts = pl->tab.counts;
   ga.E = P->E;
   if (hrg::launch_expand_small(ga, stream) != hipSuccess) return LORA_ERR_HIP;

@@ -35,7 +35,8 @@ struct PlanTables {
   int4* tile_info;     // [max_tiles] shrink work tile: {first sorted row, rows, pool slot, rank}
   int32_t* seg_e0;     // [T_cap+1] first E row of a small segment, -1 otherwise
   int32_t* erow;       // [T_cap]   sorted position -> E row, -1 if not in a small segment
-  int32_t* small_seg;  // [kMaxSmallRows] the small segments, in order
+  int4* small_info;    // [kMaxSmallRows] the small segments in order: {first sorted row,
+                       //   rows | first E row << 8, pool slot, rank}
   int32_t* counts;     // [0] = S, [1] = number of shrink tiles, [2] = T, [3] = small segments
   int32_t max_tiles;
 };
@@ -95,7 +96,7 @@ struct GemmArgs {
   // small segments: their rows' s (U B) terms in fp32, E [kMaxSmallRows][N]
   const int32_t* seg_e0;
   const int32_t* erow;
-  const int32_t* small_seg;
+  const int4* small_info;
   const int32_t* counts;
   float* E;
 };

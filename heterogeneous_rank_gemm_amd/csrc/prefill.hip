@@ -501,21 +501,44 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
 // rows' accumulators from E, gives the bits it would give walking them.
 template <int QC>
 __global__ __launch_bounds__(256) void expand_small_kernel(GemmArgs a) {
-  if (*a.status != 0) return;  // strict mode: a failed plan leaves out untouched
   const int N = a.N, T = a.T;
   const int ng = (N + 127) / 128;
-  const int nitems = a.counts[3] * ng;
   const int l = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
-  for (int item = blockIdx.x * 4 + wid; item < nitems; item += gridDim.x * 4) {
-    const int s = a.small_seg[item / ng], g = item % ng;
-    const int off = a.seg_off[s], end = a.seg_off[s + 1];
-    const int nqc = (a.seg_rank[s] + 15) >> 4;
-    const int e0 = a.seg_e0[s];
-    const uint16_t* bt = a.pages + (size_t)a.seg_slot[s] * a.slot_stride + a.b_off;
+  // the status, the count and the first item's segment entry in one round
+  // (the grid holds at most kMaxSmallRows * ng items, so the entry is in
+  // bounds; one past the count is never used)
+  int item = blockIdx.x * 4 + wid;
+  const int st = *a.status;
+  const int nitems = a.counts[3] * ng;
+  int4 si = a.small_info[min(item / ng, kMaxSmallRows - 1)];
+  if (st != 0) return;  // strict mode: a failed plan leaves out untouched
+  for (; item < nitems; item += gridDim.x * 4) {
+    if (item != (int)(blockIdx.x * 4 + wid)) si = a.small_info[item / ng];
+    const int g = item % ng;
+    const int off = si.x, end = off + (si.y & 255), e0 = si.y >> 8;
+    const int nqc = (si.w + 15) >> 4;
+    const uint16_t* bt = a.pages + (size_t)si.z * a.slot_stride + a.b_off;
     for (int rb = off & ~31; rb < end; rb += 32) {
       const int p = rb + (l & 31);
       const uint32_t m = p >= off && p < end ? 0xffffffffu : 0u;
+      // every rank chunk's loads go out before the first MFMA
+      uint4 h[QC], o[QC];
+      bf16x8 bb[QC][4];
+#pragma unroll
+      for (int qc = 0; qc < QC; ++qc) {
+        if (qc < nqc) {
+          const size_t e = (size_t)min(p, T - 1) * a.u_ld + 16 * qc + 8 * (l >> 5);
+          h[qc] = ld16(a.v_hi + e);
+          o[qc] = ld16(a.v_lo + e);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int n = min(g * 128 + 32 * i + (l & 31), N - 1);
+            bb[qc][i] = __builtin_bit_cast(bf16x8, ld16(bt + ((size_t)qc * N + n) * 16 + 8 * (l >> 5)));
+          }
+        }
+      }
+      asm volatile("" ::: "memory");  // keep the loads ahead of every MFMA
       f32x16 acc[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -524,20 +547,13 @@ __global__ __launch_bounds__(256) void expand_small_kernel(GemmArgs a) {
 #pragma unroll
       for (int qc = 0; qc < QC; ++qc) {
         if (qc < nqc) {
-          const size_t e = (size_t)min(p, T - 1) * a.u_ld + 16 * qc + 8 * (l >> 5);
-          const uint4 h = ld16(a.v_hi + e), o = ld16(a.v_lo + e);
-          bf16x8 bb[4];
+          const uint4 hh = h[qc], oo = o[qc];
+          const bf16x8 mh = __builtin_bit_cast(bf16x8, make_uint4(hh.x & m, hh.y & m, hh.z & m, hh.w & m));
+          const bf16x8 ml = __builtin_bit_cast(bf16x8, make_uint4(oo.x & m, oo.y & m, oo.z & m, oo.w & m));
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int n = min(g * 128 + 32 * i + (l & 31), N - 1);
-            bb[i] = __builtin_bit_cast(bf16x8, ld16(bt + ((size_t)qc * N + n) * 16 + 8 * (l >> 5)));
-          }
-          const bf16x8 mh = __builtin_bit_cast(bf16x8, make_uint4(h.x & m, h.y & m, h.z & m, h.w & m));
-          const bf16x8 ml = __builtin_bit_cast(bf16x8, make_uint4(o.x & m, o.y & m, o.z & m, o.w & m));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[i] = mfma32(bb[i], mh, acc[i]);
-            acc[i] = mfma32(bb[i], ml, acc[i]);
+            acc[i] = mfma32(bb[qc][i], mh, acc[i]);
+            acc[i] = mfma32(bb[qc][i], ml, acc[i]);
           }
         }
       }
