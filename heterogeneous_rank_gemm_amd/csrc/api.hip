@@ -441,11 +441,8 @@ static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t
   sa.X = X;
   sa.K = K;
   sa.perm = pl->tab.perm;
-  sa.seg_slot = pl->tab.seg_slot;
-  sa.seg_rank = pl->tab.seg_rank;
   sa.tile_info = pl->tab.tile_info;
   sa.counts = pl->tab.counts;
-  sa.seg_scale = pl->tab.seg_scale;
   sa.pages = P->pages;
   sa.slot_stride = P->slot_elems;
   sa.a_off = P->a_off[module];
@@ -454,9 +451,6 @@ static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t
   sa.u_ld = P->rpad;
   sa.kchunk = kchunk;
   sa.nsplit = ksplit;
-  sa.row_seg = pl->tab.row_seg;
-  sa.v_hi = P->v_hi;
-  sa.v_lo = P->v_lo;
   sa.status = P->status;
   if (hrg::launch_shrink(sa, grid, ksplit, T, stream) != hipSuccess) return LORA_ERR_HIP;
   ga.perm = pl->tab.perm;
@@ -471,6 +465,10 @@ static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t
   ga.pages = P->pages;
   ga.slot_stride = P->slot_elems;
   ga.b_off = P->b_off[module];
+  ga.upart = P->upart;
+  ga.split_stride = P->split_stride;
+  ga.nsplit = ksplit;
+  ga.seg_scale = pl->tab.seg_scale;
   ga.seg_e0 = pl->tab.seg_e0;
   ga.erow = pl->tab.erow;
   ga.small_info = pl->tab.small_info;

@@ -36,7 +36,7 @@ struct PlanTables {
   int32_t* seg_e0;     // [T_cap+1] first E row of a small segment, -1 otherwise
   int32_t* erow;       // [T_cap]   sorted position -> E row, -1 if not in a small segment
   int4* small_info;    // [kMaxSmallRows] the small segments in order: {first sorted row,
-                       //   rows | first E row << 8, pool slot, rank}
+                       //   rows | first E row << 8 | rank << 20, pool slot, alpha / rank bits}
   int32_t* counts;     // [0] = S, [1] = number of shrink tiles, [2] = T, [3] = small segments
   int32_t max_tiles;
 };
@@ -54,11 +54,8 @@ struct ShrinkArgs {
   const uint16_t* X;      // [T][K]
   int32_t K;
   const int32_t* perm;
-  const int32_t* seg_slot;
-  const int32_t* seg_rank;
   const int4* tile_info;
   const int32_t* counts;
-  const float* seg_scale;
   const uint16_t* pages;  // A^T page of (slot, module): pages + slot*slot_stride + a_off, [rmax][K]
   size_t slot_stride;
   size_t a_off;
@@ -67,9 +64,6 @@ struct ShrinkArgs {
   int32_t u_ld;
   int32_t kchunk;         // K per split
   int32_t nsplit;         // splits (planes) per tile
-  const int32_t* row_seg;
-  uint16_t* v_hi;         // [T_cap][u_ld] bf16 high part of s * U (sorted rows)
-  uint16_t* v_lo;         // [T_cap][u_ld] bf16 low part, s * U - hi
   const int32_t* status;
 };
 
@@ -81,9 +75,14 @@ struct GemmArgs {
   int32_t row0, row1;     // sorted rows [row0, row1) of this launch (set by launch_prefill)
   const int32_t* perm;    // sorted row -> token; nullptr = identity (base-only)
   // expand (unused by the base-only instantiation)
-  const uint16_t* v_hi;   // [T_cap][u_ld] s * U, bf16 high part, sorted rows
-  const uint16_t* v_lo;   // [T_cap][u_ld] bf16 low part
+  uint16_t* v_hi;         // [T_cap][u_ld] s * U, bf16 high part, sorted rows
+  uint16_t* v_lo;         // [T_cap][u_ld] bf16 low part
   int32_t u_ld;
+  // the shrink's partial planes, summed into V by the small-segment launch
+  const float* upart;     // [nsplit][T_cap][u_ld]
+  size_t split_stride;
+  int32_t nsplit;
+  const float* seg_scale;
   const int32_t* row_seg;
   const int32_t* seg_id;
   const int32_t* seg_off;

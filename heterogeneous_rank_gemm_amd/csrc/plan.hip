@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       if (len <= kSmallRows) {
         if (v3[1] + len <= kMaxSmallRows) {
           e0 = v3[1];
-          a.tab.small_info[v3[2]] = make_int4(off, len | (e0 << 8), inf.x, rank);
+          a.tab.small_info[v3[2]] = make_int4(off, len | (e0 << 8) | (rank << 20), inf.x, inf.z);
           atomicMax(&s_nsmall, v3[2] + 1);
           for (int i = 0; i < len; ++i) a.tab.erow[off + i] = e0 + i;
         }

@@ -499,46 +499,120 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
 // lanes (rows of other segments masked to zero), the same MFMA, chunk order
 // and hi-then-lo order, starting from zero -- so the GEMM, starting those
 // rows' accumulators from E, gives the bits it would give walking them.
+// sum of the nsplit fp32 planes p[sp * stride] in split order, loads issued
+// eight at a time
+__device__ __forceinline__ float4 sum_planes4(const float* p, size_t stride, int nsplit) {
+  float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < nsplit; s0 += 8) {
+    float4 pv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pv[j] = *reinterpret_cast<const float4*>(p + (size_t)min(s0 + j, nsplit - 1) * stride);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (s0 + j >= nsplit) continue;
+      if (s0 + j == 0) {
+        u = pv[j];
+      } else {
+        u.x += pv[j].x;
+        u.y += pv[j].y;
+        u.z += pv[j].z;
+        u.w += pv[j].w;
+      }
+    }
+  }
+  return u;
+}
+
+// V = s U split into bf16 hi + lo (V ~= hi + lo to about 2^-16)
+__device__ __forceinline__ void split_hi_lo(float v, uint16_t& h, uint16_t& lo) {
+  const __bf16 hb = (__bf16)v;
+  h = __builtin_bit_cast(uint16_t, hb);
+  lo = __builtin_bit_cast(uint16_t, (__bf16)(v - (float)hb));
+}
+
+// One launch after the shrink, two kinds of blocks:
+//  * the first fin_blocks: V = s * (the shrink's planes summed in split
+//    order) as bf16 hi + lo, for every row of an adapter segment that the
+//    GEMM expands itself (not in E);
+//  * the rest: the small segments' s U B rows into E.  A block takes one
+//    small segment and four 128-column groups (one per wave); it forms the
+//    segment's V rows the same way, in LDS, while its B loads are in flight.
+// V's bits are the same whichever block forms them.
 template <int QC>
-__global__ __launch_bounds__(256) void expand_small_kernel(GemmArgs a) {
-  const int N = a.N, T = a.T;
-  const int ng = (N + 127) / 128;
-  const int l = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+__global__ __launch_bounds__(256) void expand_small_kernel(GemmArgs a, int fin_blocks) {
+  __shared__ __attribute__((aligned(16))) uint16_t vs[2][kSmallRows][kMaxRank];  // hi, lo
+  const int N = a.N, T = a.T, w = a.u_ld;
+  const int tid = threadIdx.x, l = tid & 63, wid = tid >> 6;
+  if ((int)blockIdx.x < fin_blocks) {
+    if (*a.status != 0) return;
+    for (int idx = blockIdx.x * 256 + tid; idx < T * (w / 4); idx += fin_blocks * 256) {
+      const int p = idx / (w / 4), q = 4 * (idx % (w / 4));
+      // the planes, the row's segment and E row in one round, the segment's
+      // entry in the next
+      const float4 u = sum_planes4(a.upart + (size_t)p * w + q, a.split_stride, a.nsplit);
+      const int sg = a.row_seg[p];
+      const int er = a.erow[p];
+      if (er >= 0 || a.seg_slot[sg] < 0 || q >= ((a.seg_rank[sg] + 15) & ~15)) continue;
+      const float sc = a.seg_scale[sg];
+      uint16_t h[4], lo[4];
+      split_hi_lo(sc * u.x, h[0], lo[0]);
+      split_hi_lo(sc * u.y, h[1], lo[1]);
+      split_hi_lo(sc * u.z, h[2], lo[2]);
+      split_hi_lo(sc * u.w, h[3], lo[3]);
+      *reinterpret_cast<uint2*>(a.v_hi + (size_t)p * w + q) =
+          make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+      *reinterpret_cast<uint2*>(a.v_lo + (size_t)p * w + q) =
+          make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+    }
+    return;
+  }
+  const int ng = (N + 127) / 128, ngb = (ng + 3) / 4;
+  const int eb = (int)gridDim.x - fin_blocks;
   // the status, the count and the first item's segment entry in one round
-  // (the grid holds at most kMaxSmallRows * ng items, so the entry is in
+  // (the grid holds at most kMaxSmallRows * ngb items, so the entry is in
   // bounds; one past the count is never used)
-  int item = blockIdx.x * 4 + wid;
+  int item = (int)blockIdx.x - fin_blocks;
   const int st = *a.status;
-  const int nitems = a.counts[3] * ng;
-  int4 si = a.small_info[min(item / ng, kMaxSmallRows - 1)];
+  const int nitems = a.counts[3] * ngb;
+  int4 si = a.small_info[min(item / ngb, kMaxSmallRows - 1)];
   if (st != 0) return;  // strict mode: a failed plan leaves out untouched
-  for (; item < nitems; item += gridDim.x * 4) {
-    if (item != (int)(blockIdx.x * 4 + wid)) si = a.small_info[item / ng];
-    const int g = item % ng;
-    const int off = si.x, end = off + (si.y & 255), e0 = si.y >> 8;
-    const int nqc = (si.w + 15) >> 4;
+  for (; item < nitems; item += eb) {
+    if (item != (int)blockIdx.x - fin_blocks) si = a.small_info[item / ngb];
+    const int g = min(4 * (item % ngb) + wid, ng - 1);  // a wave past the last group repeats it, no store
+    const bool gok = 4 * (item % ngb) + wid < ng;
+    const int off = si.x, len = si.y & 255, e0 = (si.y >> 8) & 0xfff, rank = si.y >> 20;
+    const int end = off + len;
+    const int nqc = (rank + 15) >> 4;
     const uint16_t* bt = a.pages + (size_t)si.z * a.slot_stride + a.b_off;
-    for (int rb = off & ~31; rb < end; rb += 32) {
-      const int p = rb + (l & 31);
-      const uint32_t m = p >= off && p < end ? 0xffffffffu : 0u;
-      // every rank chunk's loads go out before the first MFMA
-      uint4 h[QC], o[QC];
-      bf16x8 bb[QC][4];
+    // this wave's B rows, every rank chunk
+    bf16x8 bb[QC][4];
 #pragma unroll
-      for (int qc = 0; qc < QC; ++qc) {
-        if (qc < nqc) {
-          const size_t e = (size_t)min(p, T - 1) * a.u_ld + 16 * qc + 8 * (l >> 5);
-          h[qc] = ld16(a.v_hi + e);
-          o[qc] = ld16(a.v_lo + e);
+    for (int qc = 0; qc < QC; ++qc) {
+      if (qc < nqc) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int n = min(g * 128 + 32 * i + (l & 31), N - 1);
-            bb[qc][i] = __builtin_bit_cast(bf16x8, ld16(bt + ((size_t)qc * N + n) * 16 + 8 * (l >> 5)));
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int n = min(g * 128 + 32 * i + (l & 31), N - 1);
+          bb[qc][i] = __builtin_bit_cast(bf16x8, ld16(bt + ((size_t)qc * N + n) * 16 + 8 * (l >> 5)));
         }
       }
-      asm volatile("" ::: "memory");  // keep the loads ahead of every MFMA
+    }
+    // the segment's V rows: thread = (row, 4 ranks)
+    const int wq = nqc * 4;
+    if (tid < len * wq) {
+      const int r = tid / wq, q = 4 * (tid % wq);
+      const float4 u = sum_planes4(a.upart + (size_t)(off + r) * w + q, a.split_stride, a.nsplit);
+      const float sc = __builtin_bit_cast(float, si.w);
+      split_hi_lo(sc * u.x, vs[0][r][q], vs[1][r][q]);
+      split_hi_lo(sc * u.y, vs[0][r][q + 1], vs[1][r][q + 1]);
+      split_hi_lo(sc * u.z, vs[0][r][q + 2], vs[1][r][q + 2]);
+      split_hi_lo(sc * u.w, vs[0][r][q + 3], vs[1][r][q + 3]);
+    }
+    __syncthreads();
+    for (int rb = off & ~31; rb < end; rb += 32) {
+      const int p = rb + (l & 31);
+      const bool in = p >= off && p < end;
+      const uint32_t m = in ? 0xffffffffu : 0u;
+      const int pr = in ? p - off : 0;
       f32x16 acc[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -547,7 +621,8 @@ __global__ __launch_bounds__(256) void expand_small_kernel(GemmArgs a) {
 #pragma unroll
       for (int qc = 0; qc < QC; ++qc) {
         if (qc < nqc) {
-          const uint4 hh = h[qc], oo = o[qc];
+          const uint4 hh = *reinterpret_cast<const uint4*>(&vs[0][pr][16 * qc + 8 * (l >> 5)]);
+          const uint4 oo = *reinterpret_cast<const uint4*>(&vs[1][pr][16 * qc + 8 * (l >> 5)]);
           const bf16x8 mh = __builtin_bit_cast(bf16x8, make_uint4(hh.x & m, hh.y & m, hh.z & m, hh.w & m));
           const bf16x8 ml = __builtin_bit_cast(bf16x8, make_uint4(oo.x & m, oo.y & m, oo.z & m, oo.w & m));
 #pragma unroll
@@ -557,7 +632,7 @@ __global__ __launch_bounds__(256) void expand_small_kernel(GemmArgs a) {
           }
         }
       }
-      if (m) {
+      if (in && gok) {
         float* er = a.E + (size_t)(e0 + p - off) * N;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -570,17 +645,19 @@ __global__ __launch_bounds__(256) void expand_small_kernel(GemmArgs a) {
           }
       }
     }
+    __syncthreads();  // the next item rewrites vs
   }
 }
 
 template <int QC>
 static void launch_expand_small_cfg(const GemmArgs& a, hipStream_t s) {
-  // at most kMaxSmallRows segments x ceil(N / 128) items, walked by the
-  // blocks the chip holds at once
-  const int items = kMaxSmallRows * ((a.N + 127) / 128);
-  const int grid = std::min(resident_blocks(reinterpret_cast<const void*>(&expand_small_kernel<QC>), 256, 0),
-                            (items + 3) / 4);
-  hipLaunchKernelGGL(expand_small_kernel<QC>, dim3(grid), dim3(256), 0, s, a);
+  // V blocks: enough for about one 4-rank group per thread, at most 512;
+  // small-segment blocks: at most kMaxSmallRows segments x ceil(N / 512)
+  // items, at most 1024 blocks, each walking its share
+  const int fin = std::min((a.T * (a.u_ld / 4) + 255) / 256, 512);
+  const int items = kMaxSmallRows * (((a.N + 127) / 128 + 3) / 4);
+  const int eb = std::min(items, 1024);
+  hipLaunchKernelGGL(expand_small_kernel<QC>, dim3(fin + eb), dim3(256), 0, s, a, fin);
 }
 
 hipError_t launch_expand_small(const GemmArgs& a, hipStream_t s) {

@@ -8,10 +8,10 @@
 // once per tile and K-split; the 16x16x32 bf16 MFMA does the contraction.
 // Each of the 4 waves covers an interleaved quarter of the K range; the four
 // partial results are summed in a fixed order through LDS (deterministic),
-// and each K-split writes its own fp32 partial plane of U.  A second launch
-// sums the planes in split order (deterministic), scales by s = alpha/r and
-// writes V = s U as bf16 hi + lo parts (V ~= hi + lo to about 2^-16) for the
-// GEMM's expand.
+// and each K-split writes its own fp32 partial plane of U.  The small-segment
+// launch that follows sums the planes in split order (deterministic), scales
+// by s = alpha/r and forms V = s U as bf16 hi + lo parts (V ~= hi + lo to
+// about 2^-16) for the expand.
 #include <algorithm>
 
 #include "common.h"
@@ -159,37 +159,6 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
   }
 }
 
-// V = s * (sum of the partial planes in split order), written as bf16 hi + lo
-// for every sorted row of an adapter segment and q < 16 * ceil(rank / 16).
-// A separate launch: the kernel boundary orders the planes' writes before
-// these reads without a device-scope fence per block.
-__global__ __launch_bounds__(256) void shrink_finalize_kernel(ShrinkArgs a, int nsplit, int T) {
-  if (*a.status != 0) return;
-  const int w = a.u_ld;
-  for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < T * w; idx += gridDim.x * blockDim.x) {
-    const int p = idx / w, q = idx % w;
-    // the planes and the row's segment in one round, the segment's entry in
-    // the next; planes summed in split order
-    const float* u0 = a.upart + (size_t)p * w + q;
-    const int sg = a.row_seg[p];
-    float u = 0.f;
-    for (int s0 = 0; s0 < nsplit; s0 += 8) {
-      float pv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) pv[j] = u0[(size_t)min(s0 + j, nsplit - 1) * a.split_stride];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (s0 + j < nsplit) u = (s0 + j == 0) ? pv[j] : u + pv[j];
-    }
-    if (a.seg_slot[sg] < 0 || q >= ((a.seg_rank[sg] + 15) & ~15)) continue;
-    const float v = a.seg_scale[sg] * u;
-    const __bf16 hi = (__bf16)v;
-    const __bf16 lo = (__bf16)(v - (float)hi);
-    a.v_hi[(size_t)p * w + q] = __builtin_bit_cast(uint16_t, hi);
-    a.v_lo[(size_t)p * w + q] = __builtin_bit_cast(uint16_t, lo);
-  }
-}
-
 hipError_t launch_shrink(const ShrinkArgs& a, int grid, int ksplit, int T, hipStream_t s) {
   if (grid <= 0 || ksplit <= 0 || T <= 0) return hipSuccess;
   const int nq = a.u_ld / 16;
@@ -199,11 +168,6 @@ hipError_t launch_shrink(const ShrinkArgs& a, int grid, int ksplit, int T, hipSt
     hipLaunchKernelGGL(shrink_kernel<2>, dim3(grid), dim3(kShrinkThreads), 0, s, a);
   else
     hipLaunchKernelGGL(shrink_kernel<4>, dim3(grid), dim3(kShrinkThreads), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int n = T * a.u_ld;
-  const int fgrid = std::min((n + 255) / 256, 2048);
-  hipLaunchKernelGGL(shrink_finalize_kernel, dim3(fgrid), dim3(256), 0, s, a, ksplit, T);
   return hipGetLastError();
 }
 
