@@ -180,9 +180,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
 
   // 4. stable placement, in blocks of kStageTok tokens whose buckets are
   // staged in LDS.  PW waves each take a contiguous share of a block:
-  // per-wave bucket counts, then for each bucket its running base plus the
-  // counts of the waves before, then each wave places its share 64 tokens
-  // at a time (one cursor update per distinct bucket among the 64).
+  // per-wave bucket counts (LDS atomics), then for each bucket its running
+  // base plus the counts of the waves before, then each wave places its
+  // share 64 tokens at a time (one cursor update per distinct bucket among
+  // the 64, in token order).
   for (int blk0 = 0; blk0 < T; blk0 += kStageTok) {
     const int blk1 = min(T, blk0 + kStageTok);
     const int share = (blk1 - blk0 + PW - 1) / PW;
@@ -197,19 +198,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     int* mycur = PW > 1 ? cur + wave * nb : start;
     if (PW > 1) {
       if (wave < PW) {
-        for (int base = t0; base < t1; base += 64) {
-          const int t = base + lane;
-          const bool valid = t < t1;
-          const int b = valid ? (int)s_bucket[t - blk0] : -1;
-          uint64_t todo = __ballot(valid);
-          while (todo) {
-            const int ld = __builtin_ctzll(todo);  // wave-uniform
-            const int vb = __builtin_amdgcn_readlane(b, ld);
-            const uint64_t m = __ballot(b == vb) & todo;
-            if (lane == ld) mycur[vb] += __popcll(m);  // only this wave touches its row
-            todo &= ~m;
-          }
-        }
+        // counts only: the order of the LDS increments does not matter
+        for (int t = t0 + lane; t < t1; t += 64) atomicAdd(&mycur[s_bucket[t - blk0]], 1);
       }
       __syncthreads();
       for (int b = tid; b < nb; b += kPlanThreads) {
