@@ -57,6 +57,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   extern __shared__ int smem[];
   const int nb = a.max_ids + 1;
   const int PW = plan_place_waves(nb);
+  const int nbits = 32 - __builtin_clz((unsigned)nb);  // bits of a bucket number (nb >= 1)
   int* start = smem;
   int* segidx = smem + nb;
   int* cur = smem + 2 * nb;  // [PW][nb] when PW > 1
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   // per-wave bucket counts (LDS atomics), then for each bucket its running
   // base plus the counts of the waves before, then each wave places its
   // share 64 tokens at a time (one cursor update per distinct bucket among
-  // the 64, in token order).
+  // the 64; a token's rank among its bucket's lanes keeps token order).
   for (int blk0 = 0; blk0 < T; blk0 += kStageTok) {
     const int blk1 = min(T, blk0 + kStageTok);
     const int share = (blk1 - blk0 + PW - 1) / PW;
@@ -218,19 +219,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         const int t = base + lane;
         const bool valid = t < t1;
         const int b = valid ? (int)s_bucket[t - blk0] : -1;
-        uint64_t todo = __ballot(valid);
-        int leader = 0, rank = 0, cnt = 0;
-        while (todo) {
-          const int ld = __builtin_ctzll(todo);  // wave-uniform
-          const int vb = __builtin_amdgcn_readlane(b, ld);
-          const uint64_t m = __ballot(b == vb) & todo;
-          if ((m >> lane) & 1ull) {
-            leader = ld;
-            rank = __popcll(m & ((1ull << lane) - 1ull));
-            cnt = __popcll(m);
-          }
-          todo &= ~m;
+        // m = the lanes holding this lane's bucket: one ballot per bit of
+        // the bucket number, each lane keeping the lanes that agree with it
+        // on that bit
+        uint64_t m = __ballot(valid);
+        for (int k = 0; k < nbits; ++k) {
+          const bool bit = (b >> k) & 1;
+          const uint64_t on = __ballot(valid && bit);
+          m &= bit ? on : ~on;
         }
+        const int leader = valid ? __builtin_ctzll(m) : 0;  // the bucket's first lane
+        const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        const int cnt = __popcll(m);
         int first = 0;
         if (valid && lane == leader) {
           first = mycur[b];
