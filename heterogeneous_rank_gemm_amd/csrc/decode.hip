@@ -158,25 +158,32 @@ __global__ __launch_bounds__(64 * (4 + NA)) void decode_main(DecodeArgs a) {
       bad = ti.bad;
     }
     if (__ballot(bad != 0) == 0) {
-      uint64_t todo = __ballot(id >= 0);
-      int seen = 0;
-      while (todo) {
-        const int leader = __builtin_ctzll(todo);  // wave-uniform: readlane, not an LDS shuffle
-        const int v = __builtin_amdgcn_readlane(id, leader);
+      // m = the lanes holding this lane's adapter: one ballot per bit of the
+      // id, each lane keeping the lanes that agree with it on that bit
+      const bool v = id >= 0;
+      const int nbits = 32 - __builtin_clz((unsigned)max(max(a.max_ids, a.max_slots), 1));
+      uint64_t m = __ballot(v);
+      for (int k = 0; k < nbits; ++k) {
+        const bool bit = (id >> k) & 1;
+        const uint64_t on = __ballot(v && bit);
+        m &= bit ? on : ~on;
+      }
+      // an adapter's first lane owns ceil(rank / 16) consecutive items, the
+      // adapters in order of first occurrence (= lane order of first lanes)
+      const bool first = v && lane == (int)__builtin_ctzll(m);
+      const int nq = first ? (rank + 15) / 16 : 0;
+      const int incl = wave_incl_scan(nq);
+      const uint64_t hit = __ballot(first && item >= incl - nq && item < incl);
+      if (hit) {
+        const int leader = (int)__builtin_ctzll(hit);  // wave-uniform: readlane, not an LDS shuffle
         const int r = __builtin_amdgcn_readlane(rank, leader);
-        const uint64_t m = __ballot(id == v) & todo;
-        todo &= ~m;
-        const int nq = (r + 15) / 16;
-        if (item < seen + nq) {
-          const int sl = __builtin_amdgcn_readlane(slot, leader);
-          qb = item - seen;
-          members = m;
-          const int q = 16 * qb + r16;
-          row_ok = q < min(r, a.rmax);
-          row = a.pages + (size_t)sl * a.slot_stride + a.a_off + (size_t)(row_ok ? q : 0) * K + k0;
-          break;
-        }
-        seen += nq;
+        const int sl = __builtin_amdgcn_readlane(slot, leader);
+        qb = item - __builtin_amdgcn_readlane(incl - nq, leader);
+        members = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(m >> 32), leader) << 32) |
+                  (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)m, leader);
+        const int q = 16 * qb + r16;
+        row_ok = q < min(r, a.rmax);
+        row = a.pages + (size_t)sl * a.slot_stride + a.a_off + (size_t)(row_ok ? q : 0) * K + k0;
       }
     }
     // drain the lookups here, so that no wait for them is left to the merge
