@@ -297,3 +297,187 @@ def parity_metrics(out, Yref) -> Tuple[float, float, float]:
 # Tolerances on bf16 outputs with fp32 accumulation.
 MAX_REL_TOL = 1e-2   # max|out - Yref| <= 1e-2 * max|Yref|
 RELL1_TOL = 2e-3     # sum|out - Yref| / sum|Yref| <= 2e-3
+
+
+# --------------------------------------------------------------------------
+# host <-> device paging of the pool ([vLLM-ch7] "how vLLM implements
+# multi-LoRA", item 1: one device pool, adapters loaded on demand and swapped
+# in and out; "starting a multi-LoRA service": --max-loras adapters resident
+# on the GPU, --max-cpu-loras more kept in a CPU cache and swapped in on
+# demand; [icman] section 2.2: an adapter that is not loaded is read into
+# device memory, and when device memory runs short the least recently used
+# inactive adapter is swapped out; a preload list keeps the hottest few
+# resident)
+# --------------------------------------------------------------------------
+class PagedRegistry(Registry):
+    """The pool with a host cache in front of it.
+
+    Readings taken where the pages are silent:
+      * Capacity: ``max_adapters`` device slots, shared by adapters loaded
+        directly (never evicted) and host-cached adapters paged in.  The host
+        cache holds ``max_cpu`` adapters; a full host cache refuses a new one
+        (POOL_FULL) instead of forgetting an adapter.
+      * A prefetch names the ids of the next batch.  Every host-cached id in
+        it becomes addressable (paged in if it is not on the device); the
+        host-cached ids of the previous prefetch that are not named again
+        stop being addressable (strict mode then rejects them) but keep their
+        device copy as a cache.
+      * "Least recently used" counts prefetch calls: an id's last use is the
+        number of the last prefetch that named it.  The victim is the cached,
+        unpinned id not named by the current prefetch with the smallest
+        (last use, id).  Misses take a free slot first.
+      * Pinned ids (the preload list) are paged in when pinned, stay
+        addressable and are never evicted.  Pinning does not count as a use.
+      * If the misses of a prefetch outnumber the free slots plus the
+        evictable ids, the call fails with POOL_FULL and changes nothing.
+
+    ``self.adapters`` (the Registry's view) is always the addressable set, so
+    ``lora_linear`` and ``validate_ids`` apply strict mode to it unchanged.
+    """
+
+    def __init__(self, max_adapters: int, max_ids: int, max_rank: int,
+                 d_in: Sequence[int], d_out: Sequence[int], max_tokens: int, max_cpu: int):
+        super().__init__(max_adapters, max_ids, max_rank, d_in, d_out, max_tokens)
+        if not (1 <= max_cpu <= max_ids):
+            raise OracleError(INVALID_ARG, "host cache size")
+        self.max_cpu = max_cpu
+        self.host: Dict[int, Adapter] = {}     # the host cache
+        self.direct: Dict[int, Adapter] = {}   # loaded straight into the pool
+        self.cached: set = set()               # host-cached ids with a device copy
+        self.last_use: Dict[int, int] = {}
+        self.pinned: set = set()
+        self.calls = 0
+        self.named: set = set()                # host-cached ids of the last prefetch
+        self.loads_last_call: List[int] = []   # ids paged in by the last prefetch
+
+    # the Registry's addressable view
+    def _refresh(self) -> None:
+        view = dict(self.direct)
+        for i in self.cached:
+            if i in self.named or i in self.pinned:
+                view[i] = self.host[i]
+        self.adapters = view
+
+    def _slots_used(self) -> int:
+        return len(self.direct) + len(self.cached)
+
+    def load(self, adapter_id, rank, alpha, A, B) -> None:
+        if 0 <= adapter_id < self.max_ids and adapter_id in self.host:
+            raise OracleError(EXISTS, f"id {adapter_id} is in the host cache")
+        if 0 <= adapter_id < self.max_ids and 1 <= rank <= self.max_rank \
+                and adapter_id not in self.direct and self._slots_used() >= self.max_adapters:
+            raise OracleError(POOL_FULL, "no free slot")
+        saved = self.adapters
+        self.adapters = dict(self.direct)
+        try:
+            Registry.load(self, adapter_id, rank, alpha, A, B)
+            self.direct[adapter_id] = self.adapters[adapter_id]
+        finally:
+            self.adapters = saved
+        self._refresh()
+
+    def unload(self, adapter_id: int) -> None:
+        if not (0 <= adapter_id < self.max_ids):
+            raise OracleError(ID_RANGE, f"id {adapter_id}")
+        if adapter_id in self.direct:
+            del self.direct[adapter_id]
+        elif adapter_id in self.cached:
+            self.cached.discard(adapter_id)
+            self.pinned.discard(adapter_id)
+        else:
+            raise OracleError(NOT_LOADED, f"id {adapter_id}")
+        self._refresh()
+
+    def host_register(self, adapter_id: int, rank: int, alpha: float, A: Sequence, B: Sequence) -> None:
+        if not (0 <= adapter_id < self.max_ids):
+            raise OracleError(ID_RANGE, f"id {adapter_id}")
+        if not (1 <= rank <= self.max_rank):
+            raise OracleError(RANK, f"rank {rank}")
+        if adapter_id in self.host or adapter_id in self.direct:
+            raise OracleError(EXISTS, f"id {adapter_id}")
+        if len(self.host) >= self.max_cpu:
+            raise OracleError(POOL_FULL, "host cache full")
+        probe = Registry(1, self.max_ids, self.max_rank, self.d_in, self.d_out, self.max_tokens)
+        probe.load(adapter_id, rank, alpha, A, B)
+        self.host[adapter_id] = probe.adapters[adapter_id]
+
+    def host_unregister(self, adapter_id: int) -> None:
+        if not (0 <= adapter_id < self.max_ids):
+            raise OracleError(ID_RANGE, f"id {adapter_id}")
+        if adapter_id not in self.host:
+            raise OracleError(NOT_LOADED, f"id {adapter_id}")
+        del self.host[adapter_id]
+        self.cached.discard(adapter_id)
+        self.pinned.discard(adapter_id)
+        self.named.discard(adapter_id)
+        self.last_use.pop(adapter_id, None)
+        self._refresh()
+
+    def _victims(self, protect: set) -> List[int]:
+        """Evictable cached ids, least recently used first."""
+        c = [i for i in self.cached if i not in self.pinned and i not in protect]
+        return sorted(c, key=lambda i: (self.last_use.get(i, 0), i))
+
+    def pin(self, adapter_id: int, on: bool) -> None:
+        if not (0 <= adapter_id < self.max_ids):
+            raise OracleError(ID_RANGE, f"id {adapter_id}")
+        if adapter_id not in self.host:
+            raise OracleError(NOT_LOADED, f"id {adapter_id}")
+        if not on:
+            self.pinned.discard(adapter_id)
+            self._refresh()
+            return
+        if adapter_id not in self.cached:
+            if self._slots_used() >= self.max_adapters:
+                # never evict an id the current batch may address
+                victims = self._victims(protect=set(self.adapters))
+                if not victims:
+                    raise OracleError(POOL_FULL, "no evictable slot")
+                self.cached.discard(victims[0])
+            self.cached.add(adapter_id)
+        self.pinned.add(adapter_id)
+        self._refresh()
+
+    def prefetch(self, ids: Sequence[int]) -> List[int]:
+        """Make the ids of the next batch addressable; returns the ids paged in."""
+        ids = [int(i) for i in ids]
+        for i in ids:
+            if i < -1 or i >= self.max_ids:
+                raise OracleError(ID_RANGE, f"id {i}")
+        req: List[int] = []
+        for i in ids:
+            if i < 0 or i in self.direct:
+                continue
+            if i not in self.host:
+                raise OracleError(NOT_LOADED, f"id {i}")
+            if i not in req:
+                req.append(i)
+        misses = [i for i in req if i not in self.cached]
+        free = self.max_adapters - self._slots_used()
+        victims = self._victims(protect=set(req))
+        if len(misses) > free + len(victims):
+            raise OracleError(POOL_FULL, f"{len(misses)} misses, {free} free, {len(victims)} evictable")
+        self.calls += 1
+        for i in req:
+            self.last_use[i] = self.calls
+        for i in misses:
+            if free > 0:
+                free -= 1
+            else:
+                self.cached.discard(victims.pop(0))
+            self.cached.add(i)
+        self.named = set(req)
+        self.loads_last_call = misses
+        self._refresh()
+        return misses
+
+    def where(self, adapter_id: int) -> int:
+        """0 unknown, 1 host cache only, 2 cached on the device but not
+        addressable, 3 addressable."""
+        if adapter_id in self.adapters:
+            return 3
+        if adapter_id in self.cached:
+            return 2
+        if adapter_id in self.host:
+            return 1
+        return 0
