@@ -9,12 +9,16 @@ from . import _lora
 from ._lora import (LoraError, STATUS_NAMES, EXPORTED, lora_status_string, lora_pool_create,
                     lora_pool_destroy, lora_load_adapter, lora_unload_adapter, lora_pool_query,
                     lora_plan_create, lora_plan_destroy, lora_plan, lora_apply, lora_base_apply,
-                    lora_status, lora_debug_read_plan)
+                    lora_status, lora_debug_read_plan, lora_host_cache_create,
+                    lora_host_register, lora_host_unregister, lora_prefetch, lora_pin_adapter,
+                    lora_paging_query)
 from .pool import LoraPool
 
 __all__ = [
     "LoraError", "STATUS_NAMES", "EXPORTED", "LoraPool", "lora_status_string",
     "lora_pool_create", "lora_pool_destroy", "lora_load_adapter", "lora_unload_adapter",
     "lora_pool_query", "lora_plan_create", "lora_plan_destroy", "lora_plan", "lora_apply",
-    "lora_base_apply", "lora_status", "lora_debug_read_plan",
+    "lora_base_apply", "lora_status", "lora_debug_read_plan", "lora_host_cache_create",
+    "lora_host_register", "lora_host_unregister", "lora_prefetch", "lora_pin_adapter",
+    "lora_paging_query",
 ]

@@ -28,6 +28,8 @@ EXPORTED = (
     "lora_status_string", "lora_pool_create", "lora_pool_destroy", "lora_load_adapter",
     "lora_unload_adapter", "lora_pool_query", "lora_plan_create", "lora_plan_destroy",
     "lora_plan", "lora_apply", "lora_base_apply", "lora_status", "lora_debug_read_plan",
+    "lora_host_cache_create", "lora_host_register", "lora_host_unregister", "lora_prefetch",
+    "lora_pin_adapter", "lora_paging_query",
 )
 
 _vp = C.c_void_p
@@ -49,6 +51,12 @@ _sigs = {
     "lora_base_apply": [_vp, _i32, _vp, _i32, _vp, _vp, _vp],
     "lora_status": [_vp, _vp],
     "lora_debug_read_plan": [_vp, _vp, _P_i32, _P_i32, _P_i32, _P_i32, _P_i32, _P_i32, _vp],
+    "lora_host_cache_create": [_vp, _i32],
+    "lora_host_register": [_vp, _i32, _i32, C.c_float, C.POINTER(_vp), C.POINTER(_vp)],
+    "lora_host_unregister": [_vp, _i32, _vp],
+    "lora_prefetch": [_vp, _P_i32, _i32, _vp],
+    "lora_pin_adapter": [_vp, _i32, _i32, _vp],
+    "lora_paging_query": [_vp, _i32, _P_i32, _P_i32],
 }
 for _name, _args in _sigs.items():
     _f = getattr(_lib, _name)
@@ -175,3 +183,43 @@ def lora_debug_read_plan(pool: int, plan: Optional[int], max_tokens: int, stream
                                      C.byref(S), _stream(stream)), "lora_debug_read_plan")
     t, s = T.value, S.value
     return list(perm[:t]), list(inv[:t]), list(seg_id[:s]), list(seg_off[:s + 1])
+
+
+# ---------------------------------------------------------------------------
+# host <-> device paging
+# ---------------------------------------------------------------------------
+def lora_host_cache_create(pool: int, max_cpu_adapters: int) -> None:
+    _check(_lib.lora_host_cache_create(pool, max_cpu_adapters), "lora_host_cache_create")
+
+
+def lora_host_register(pool: int, adapter_id: int, rank: int, alpha: float, A: Sequence,
+                       B: Sequence) -> None:
+    n = len(A)
+    pa = (_vp * max(n, 1))(*[_ptr(a) for a in A])
+    pb = (_vp * max(n, 1))(*[_ptr(b) for b in B])
+    _check(_lib.lora_host_register(pool, adapter_id, rank, float(alpha), pa, pb),
+           "lora_host_register")
+
+
+def lora_host_unregister(pool: int, adapter_id: int, stream=None) -> None:
+    _check(_lib.lora_host_unregister(pool, adapter_id, _stream(stream)), "lora_host_unregister")
+
+
+def lora_prefetch(pool: int, ids: Sequence[int], stream=None) -> None:
+    """``ids``: the batch's adapter ids as a host sequence (list, numpy array)."""
+    vals = [int(i) for i in ids]
+    arr = (C.c_int32 * max(len(vals), 1))(*vals)
+    _check(_lib.lora_prefetch(pool, arr, len(vals), _stream(stream)), "lora_prefetch")
+
+
+def lora_pin_adapter(pool: int, adapter_id: int, pin: bool, stream=None) -> None:
+    _check(_lib.lora_pin_adapter(pool, adapter_id, 1 if pin else 0, _stream(stream)),
+           "lora_pin_adapter")
+
+
+def lora_paging_query(pool: int, adapter_id: int):
+    """(where, pinned): where 0 unknown, 1 host cache only, 2 device copy not
+    addressable, 3 addressable."""
+    w, p = C.c_int32(), C.c_int32()
+    _check(_lib.lora_paging_query(pool, adapter_id, C.byref(w), C.byref(p)), "lora_paging_query")
+    return w.value, p.value

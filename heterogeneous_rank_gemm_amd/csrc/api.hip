@@ -14,61 +14,17 @@
 
 #include "internal.h"
 #include "lora.h"
+#include "pool_state.h"
 
 static_assert(hrg::kStatusNotLoaded == LORA_ERR_NOT_LOADED, "status code mismatch");
 static_assert(hrg::kStatusIdRange == LORA_ERR_ID_RANGE, "status code mismatch");
-
-struct lora_plan_s {
-  hrg::PlanTables tab;
-  int32_t T = -1;
-  const int32_t* ids = nullptr;
-  void* block = nullptr;  // one allocation backing every table
-};
-
-struct lora_pool_s {
-  int device = 0;
-  int32_t max_adapters = 0, max_ids = 0, max_rank = 0, rpad = 0, n_modules = 0, max_tokens = 0;
-  std::vector<int32_t> d_in, d_out;
-  std::vector<size_t> a_off, b_off;  // element offsets of each module's pages inside a slot
-  size_t slot_elems = 0;
-  uint16_t* pages = nullptr;         // [max_adapters][slot_elems]
-  int32_t* id2slot = nullptr;        // [max_ids]
-  int32_t* slot_rank = nullptr;      // [max_adapters]
-  float* slot_scale = nullptr;       // [max_adapters]
-  int4* id_info = nullptr;           // [max_ids] {slot, rank, scale bits, 0}
-  int32_t* status = nullptr;         // sticky device status
-  uint16_t* staging = nullptr;       // one module's A or B as received
-  float* upart = nullptr;            // [kMaxSplits][max_tokens][rpad] shrink partial planes
-  size_t split_stride = 0;
-  uint16_t* v_hi = nullptr;          // [max_tokens][rpad] s * U, bf16 high part (sorted rows)
-  uint16_t* v_lo = nullptr;          // [max_tokens][rpad] bf16 low part
-  // decode-path workspace
-  float* E = nullptr;                // [kMaxSmallRows][max d_out] small-segment expand rows
-  float* dec_part = nullptr;         // [ceil(max d_in / 1024)][64][max d_out rounded up to 64] base partials
-  float* dec_upart = nullptr;        // [ceil(max d_in / 1024)][64][rpad] shrink partials
-  std::vector<int32_t> h_id2slot, h_slot_rank;
-  std::vector<float> h_slot_scale;
-  std::set<int32_t> free_slots;      // lowest free slot first
-  lora_plan_s* internal = nullptr;
-  std::set<lora_plan_s*> plans;
-};
 
 namespace {
 
 using hrg::ceil_div;
 using hrg::round_up;
 
-struct DeviceGuard {
-  int prev = -1;
-  explicit DeviceGuard(int dev) {
-    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
-    if (prev != dev) (void)hipSetDevice(dev);
-  }
-  ~DeviceGuard() {
-    int cur = -1;
-    if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
-  }
-};
+using hrg::DeviceGuard;
 
 template <typename T>
 hipError_t dmalloc(T** p, size_t n) {
@@ -294,6 +250,11 @@ lora_status_t lora_pool_destroy(lora_pool_t P) {
   (void)hipFree(P->dec_upart);
   (void)hipFree(P->dec_part);
   (void)hipFree(P->E);
+  if (P->hcache) (void)hipHostFree(P->hcache);
+  if (P->copy_stream) (void)hipStreamDestroy(P->copy_stream);
+  for (hipEvent_t e : P->call_ev)
+    if (e) (void)hipEventDestroy(e);
+  if (P->copy_ev) (void)hipEventDestroy(P->copy_ev);
   delete P;
   return LORA_OK;
 }
@@ -307,6 +268,7 @@ lora_status_t lora_load_adapter(lora_pool_t P, int32_t id, int32_t rank, float a
   if (id < 0 || id >= P->max_ids) return LORA_ERR_ID_RANGE;
   if (rank < 1 || rank > P->max_rank) return LORA_ERR_RANK;
   if (P->h_id2slot[id] >= 0) return LORA_ERR_EXISTS;
+  if (P->hcache && P->h_hslot[id] >= 0) return LORA_ERR_EXISTS;  // paged through the host cache
   if (P->free_slots.empty()) return LORA_ERR_POOL_FULL;
   DeviceGuard g(P->device);
   // a direct-mapped pool (max_ids <= max_adapters) keeps adapter id in slot id
@@ -342,6 +304,8 @@ lora_status_t lora_load_adapter(lora_pool_t P, int32_t id, int32_t rank, float a
 lora_status_t lora_unload_adapter(lora_pool_t P, int32_t id, hipStream_t stream) {
   if (!P) return LORA_ERR_INVALID_ARG;
   if (id < 0 || id >= P->max_ids) return LORA_ERR_ID_RANGE;
+  // a host-cached adapter gives up its device copy only (paging.hip)
+  if (P->hcache && P->h_hslot[id] >= 0) return hrg::paged_drop_device_copy(P, id, stream);
   const int32_t slot = P->h_id2slot[id];
   if (slot < 0) return LORA_ERR_NOT_LOADED;
   DeviceGuard g(P->device);

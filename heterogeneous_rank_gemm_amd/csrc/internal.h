@@ -169,5 +169,10 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 hipError_t launch_set_slot(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
                            int32_t id, int32_t slot, int32_t rank, float scale, hipStream_t s);
 hipError_t launch_clear_i32(int32_t* p, int32_t n, int32_t value, hipStream_t s);
+// Routing-table updates of several distinct ids, each {id, slot (-1: not
+// addressable), rank, scale bits}; launched in chunks of kSlotUpdatesPerLaunch.
+constexpr int kSlotUpdatesPerLaunch = 64;
+hipError_t launch_set_slots(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
+                            const int4* updates, int n, hipStream_t s);
 
 }  // namespace hrg

@@ -339,6 +339,41 @@ hipError_t launch_set_slot(int32_t* id2slot, int32_t* slot_rank, float* slot_sca
   return hipGetLastError();
 }
 
+// The same update for up to kSlotUpdatesPerLaunch distinct ids at once
+// (passed by value, so the host needs no staging buffer).
+struct SlotUpdates {
+  int4 u[kSlotUpdatesPerLaunch];  // {id, slot (-1: not addressable), rank, scale bits}
+  int32_t n;
+};
+
+__global__ void set_slots_kernel(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
+                                 SlotUpdates ups) {
+  const int i = threadIdx.x;
+  if (i < ups.n) {
+    const int4 e = ups.u[i];
+    if (e.y >= 0) {
+      slot_rank[e.y] = e.z;
+      slot_scale[e.y] = __builtin_bit_cast(float, e.w);
+    }
+    id2slot[e.x] = e.y;
+    id_info[e.x] = make_int4(e.y, e.y >= 0 ? e.z : 0, e.w, 0);
+  }
+}
+
+hipError_t launch_set_slots(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
+                            const int4* updates, int n, hipStream_t s) {
+  for (int i0 = 0; i0 < n; i0 += kSlotUpdatesPerLaunch) {
+    SlotUpdates ups{};
+    ups.n = std::min(kSlotUpdatesPerLaunch, n - i0);
+    for (int j = 0; j < ups.n; ++j) ups.u[j] = updates[i0 + j];
+    hipLaunchKernelGGL(set_slots_kernel, dim3(1), dim3(kSlotUpdatesPerLaunch), 0, s, id2slot, slot_rank,
+                       slot_scale, id_info, ups);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 __global__ void fill_i32_kernel(int32_t* p, int32_t n, int32_t v) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = v;
 }

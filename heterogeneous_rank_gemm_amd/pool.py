@@ -66,3 +66,22 @@ class LoraPool:
 
     def debug_read_plan(self, plan: Optional[int] = None, stream=None):
         return _lora.lora_debug_read_plan(self.handle, plan, self.max_tokens, stream)
+
+    # host <-> device paging
+    def host_cache_create(self, max_cpu_adapters: int):
+        _lora.lora_host_cache_create(self.handle, max_cpu_adapters)
+
+    def host_register(self, adapter_id: int, rank: int, alpha: float, A, B):
+        _lora.lora_host_register(self.handle, adapter_id, rank, alpha, A, B)
+
+    def host_unregister(self, adapter_id: int, stream=None):
+        _lora.lora_host_unregister(self.handle, adapter_id, stream)
+
+    def prefetch(self, ids, stream=None):
+        _lora.lora_prefetch(self.handle, ids, stream)
+
+    def pin(self, adapter_id: int, pin: bool = True, stream=None):
+        _lora.lora_pin_adapter(self.handle, adapter_id, pin, stream)
+
+    def paging_query(self, adapter_id: int):
+        return _lora.lora_paging_query(self.handle, adapter_id)

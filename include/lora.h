@@ -105,6 +105,7 @@ lora_status_t lora_pool_destroy(lora_pool_t pool);
  *          A[m], B[m] may point to host or device memory; they are copied
  *          before the call returns and may be freed afterwards.
  *
+ * EXISTS also if the id is in the pool's host cache (lora_host_register).
  * Slot choice: a pool with max_ids <= max_adapters is direct-mapped and
  * keeps adapter id in slot id (the decode kernels then address its pages
  * from the ids alone, without a round of slot-table loads); otherwise the
@@ -121,6 +122,8 @@ lora_status_t lora_load_adapter(lora_pool_t pool, int32_t id, int32_t rank, floa
  * API": unload frees the adapter's caches; [vLLM-ch7] unload endpoint).
  * Waits for `stream` first, so work already enqueued there never reads a
  * recycled page.  NOT_LOADED if the id is not resident, ID_RANGE if out of range.
+ * For an adapter in the host cache (lora_host_register) it drops the device
+ * copy only (NOT_LOADED if there is none); the host copy stays.
  */
 lora_status_t lora_unload_adapter(lora_pool_t pool, int32_t id, hipStream_t stream);
 
@@ -199,6 +202,86 @@ lora_status_t lora_status(lora_pool_t pool, hipStream_t stream);
 lora_status_t lora_debug_read_plan(lora_pool_t pool, lora_plan_t plan, int32_t* perm,
                                    int32_t* inv, int32_t* seg_id, int32_t* seg_off,
                                    int32_t* T_out, int32_t* S_out, hipStream_t stream);
+
+/*
+ * Host <-> device paging of the pool.  [vLLM-ch7] "how vLLM implements
+ * multi-LoRA" (item 1: adapters loaded on demand and swapped in and out of
+ * one device pool) and "starting a multi-LoRA service" (--max-loras on the
+ * GPU, --max-cpu-loras in a CPU cache swapped in on demand); [icman] 2.2 (a
+ * missing adapter is read into device memory, the least recently used
+ * inactive adapter is swapped out when memory runs short, a preload list
+ * keeps the hottest few resident) and 4.2 (cold loads are the latency cliff).
+ *
+ * lora_host_cache_create -- give the pool a host cache of up to
+ * max_cpu_adapters adapters (1..max_ids) in pinned host memory, kept in the
+ * device page layout, plus a copy stream of the pool's own.  Once per pool;
+ * INVALID_ARG on a second call, OOM if the pinned allocation fails.
+ * Memory: max_cpu_adapters x (the pool's per-slot page bytes) of host memory.
+ */
+lora_status_t lora_host_cache_create(lora_pool_t pool, int32_t max_cpu_adapters);
+
+/*
+ * lora_host_register -- copy an adapter into the host cache (not to the
+ * device).  Arguments as lora_load_adapter; A[m], B[m] may be host or device
+ * memory and may be freed when the call returns.  ID_RANGE, RANK, EXISTS (id
+ * already host-cached or loaded directly), POOL_FULL (host cache full; the
+ * caller unregisters, the library never forgets an adapter on its own),
+ * INVALID_ARG without a host cache.  Blocking; no stream work.
+ */
+lora_status_t lora_host_register(lora_pool_t pool, int32_t id, int32_t rank, float alpha,
+                                 const lora_bf16_t* const* A, const lora_bf16_t* const* B);
+
+/*
+ * lora_host_unregister -- forget a host-cached adapter, dropping its device
+ * copy too.  Synchronises `stream` and the copy stream.  NOT_LOADED if the id
+ * is not host-cached.
+ */
+lora_status_t lora_host_unregister(lora_pool_t pool, int32_t id, hipStream_t stream);
+
+/*
+ * lora_prefetch -- make the adapters of the next batch addressable.
+ *
+ *   ids  HOST array [n] of the batch's ids (repeats and -1 allowed)
+ *
+ * Every host-cached id named becomes addressable; host-cached ids named by
+ * the previous prefetch and not by this one stop being addressable (strict
+ * mode then rejects them in lora_apply) but keep their device copy as a
+ * cache.  Adapters loaded directly with lora_load_adapter are always
+ * addressable and never evicted.  A named id without a device copy takes a
+ * free slot, else the slot of the cached, unpinned, unnamed adapter with the
+ * smallest (number of the last prefetch that named it, id): least recently
+ * used.  The page copies run asynchronously on the pool's copy stream and
+ * overlap the work already on `stream`: a copy into an evicted adapter's slot
+ * waits only for the work enqueued before the first prefetch that stopped
+ * naming it; `stream` then waits for the copies and updates the routing table
+ * in order.  So a batch's applies must be enqueued after the prefetch that
+ * names its adapters and before the next prefetch call.
+ * Errors, with no side effects: ID_RANGE (an id outside [-1, max_ids); wins),
+ * NOT_LOADED (an id neither host-cached nor loaded), POOL_FULL (more misses
+ * than free plus evictable slots), INVALID_ARG (no host cache, ids NULL with
+ * n > 0, n < 0).  The host returns before the copies finish; the host cache
+ * is not modified while they run (unregister waits for them).
+ */
+lora_status_t lora_prefetch(lora_pool_t pool, const int32_t* ids, int32_t n, hipStream_t stream);
+
+/*
+ * lora_pin_adapter -- the preload list.  pin != 0 pages a host-cached adapter
+ * in now (free slot, else the least recently used adapter that is not
+ * addressable; POOL_FULL if there is none), makes it addressable and exempts
+ * it from eviction; synchronises `stream`.  pin == 0 returns it to the LRU
+ * with the recency of the latest prefetch; it stays addressable only if the
+ * last prefetch named it.  NOT_LOADED if not host-cached.
+ */
+lora_status_t lora_pin_adapter(lora_pool_t pool, int32_t id, int32_t pin, hipStream_t stream);
+
+/*
+ * lora_paging_query -- where an id is (host state, no device work):
+ *   *where  0 unknown, 1 host cache only, 2 device copy but not addressable,
+ *           3 addressable (host-cached and named or pinned, or loaded directly)
+ *   *pinned 1 if on the preload list
+ * Either pointer may be NULL.  ID_RANGE if the id is out of range.
+ */
+lora_status_t lora_paging_query(lora_pool_t pool, int32_t id, int32_t* where, int32_t* pinned);
 
 #ifdef __cplusplus
 }

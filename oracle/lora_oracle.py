@@ -327,7 +327,10 @@ class PagedRegistry(Registry):
         unpinned id not named by the current prefetch with the smallest
         (last use, id).  Misses take a free slot first.
       * Pinned ids (the preload list) are paged in when pinned, stay
-        addressable and are never evicted.  Pinning does not count as a use.
+        addressable and are never evicted.  Pinning does not count as a use;
+        unpinning gives the id the recency of the latest prefetch (it was in
+        use until then).  Pinning evicts only an id that is not addressable.
+      * Unloading a host-cached id drops its device copy only.
       * If the misses of a prefetch outnumber the free slots plus the
         evictable ids, the call fails with POOL_FULL and changes nothing.
 
@@ -362,18 +365,18 @@ class PagedRegistry(Registry):
         return len(self.direct) + len(self.cached)
 
     def load(self, adapter_id, rank, alpha, A, B) -> None:
-        if 0 <= adapter_id < self.max_ids and adapter_id in self.host:
-            raise OracleError(EXISTS, f"id {adapter_id} is in the host cache")
-        if 0 <= adapter_id < self.max_ids and 1 <= rank <= self.max_rank \
-                and adapter_id not in self.direct and self._slots_used() >= self.max_adapters:
+        """Load straight into the pool (never evicted)."""
+        if not (0 <= adapter_id < self.max_ids):
+            raise OracleError(ID_RANGE, f"id {adapter_id}")
+        if not (1 <= rank <= self.max_rank):
+            raise OracleError(RANK, f"rank {rank}")
+        if adapter_id in self.direct or adapter_id in self.host:
+            raise OracleError(EXISTS, f"id {adapter_id}")
+        if self._slots_used() >= self.max_adapters:
             raise OracleError(POOL_FULL, "no free slot")
-        saved = self.adapters
-        self.adapters = dict(self.direct)
-        try:
-            Registry.load(self, adapter_id, rank, alpha, A, B)
-            self.direct[adapter_id] = self.adapters[adapter_id]
-        finally:
-            self.adapters = saved
+        probe = Registry(1, self.max_ids, self.max_rank, self.d_in, self.d_out, self.max_tokens)
+        probe.load(adapter_id, rank, alpha, A, B)
+        self.direct[adapter_id] = probe.adapters[adapter_id]
         self._refresh()
 
     def unload(self, adapter_id: int) -> None:
@@ -384,6 +387,7 @@ class PagedRegistry(Registry):
         elif adapter_id in self.cached:
             self.cached.discard(adapter_id)
             self.pinned.discard(adapter_id)
+            self.named.discard(adapter_id)
         else:
             raise OracleError(NOT_LOADED, f"id {adapter_id}")
         self._refresh()
@@ -424,7 +428,10 @@ class PagedRegistry(Registry):
         if adapter_id not in self.host:
             raise OracleError(NOT_LOADED, f"id {adapter_id}")
         if not on:
-            self.pinned.discard(adapter_id)
+            if adapter_id in self.pinned:
+                # it was in use up to now: its recency is that of the latest call
+                self.pinned.discard(adapter_id)
+                self.last_use[adapter_id] = max(self.last_use.get(adapter_id, 0), self.calls)
             self._refresh()
             return
         if adapter_id not in self.cached:
