@@ -202,6 +202,94 @@ def graphed(fn, reps, torch, hrg):
 
 
 # ---------------------------------------------------------------------------
+# host <-> device paging (a separate measurement, not the contract line)
+# ---------------------------------------------------------------------------
+def paging_batches(wl: wk.Workload, n: int, mix: str, seed: int):
+    """`n` fresh batches of the workload's T ids over its adapters: "uniform"
+    (each id uniform) or "hot5" (5 hot adapters take 80 % of the tokens, the
+    rest uniform over the others)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for _ in range(n):
+        if mix == "uniform":
+            ids = g.integers(0, wl.n_adapters, size=wl.T)
+        else:
+            hot = g.random(wl.T) < 0.8
+            ids = np.where(hot, g.integers(0, 5, size=wl.T),
+                           g.integers(5, wl.n_adapters, size=wl.T))
+        out.append(ids.astype(np.int32))
+    return out
+
+
+def paging_bench(args, torch, hrg) -> dict:
+    """One linear of the decode workload served from a host cache holding
+    every adapter and a device pool of `slots` slots: each step is one
+    lora_prefetch of a fresh batch plus its lora_apply, timed against the same
+    batches with every adapter resident."""
+    wl = wk.WORKLOADS[args.workload]
+    if wl.T > DECODE_MAX_T or len(wl.modules) != 1:
+        raise SystemExit("--paging measures a one-linear decode workload (1 or 2)")
+    m = wl.modules[0]
+    ranks = wk.adapter_ranks(wl, wl.default_seed)
+    res = {"workload": wl.name, "slots": args.paging_slots, "host_cached": wl.n_adapters,
+           "mix": args.paging_mix, "steps": args.steps}
+    paged = hrg.LoraPool(args.paging_slots, wl.n_adapters, wl.max_rank, [m.d_in], [m.d_out], wl.T)
+    paged.host_cache_create(wl.n_adapters)
+    resident = hrg.LoraPool(wl.n_adapters, wl.n_adapters, wl.max_rank, [m.d_in], [m.d_out], wl.T)
+    for i in range(wl.n_adapters):
+        r = int(ranks[i])
+        a, b = wk.adapter_weights(wl, i, 0, r, wl.default_seed, "cuda")
+        paged.host_register(i, r, wk.adapter_alpha(wl, r), [a], [b])
+        resident.load_adapter(i, r, wk.adapter_alpha(wl, r), [a], [b])
+    if args.paging_mix == "hot5":
+        for i in range(5):
+            paged.pin(i, True)
+    X = wk.activation(wl, m.input_group, m.d_in, wl.default_seed, "cuda")
+    W = wk.base_weight(wl, 0, wl.default_seed, "cuda")
+    out = torch.empty((wl.T, m.d_out), dtype=torch.bfloat16, device="cuda")
+    n = args.warmup + args.steps
+    batches = paging_batches(wl, n, args.paging_mix, 7)
+    ids_dev = [torch.as_tensor(b, device="cuda") for b in batches]
+    ids_host = [b.tolist() for b in batches]
+
+    def run(pool, lo, hi, prefetch):
+        for k in range(lo, hi):
+            if prefetch:
+                pool.prefetch(ids_host[k])
+            hrg.lora_apply(pool.handle, 0, X, ids_dev[k], wl.T, W, out, None)
+
+    for pool, prefetch, key in ((paged, True, "paged"), (resident, False, "resident")):
+        run(pool, 0, args.warmup, prefetch)
+        torch.cuda.synchronize()
+        _, loads0, _ = paged.paging_stats()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        run(pool, args.warmup, n, prefetch)
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        res[f"{key}_us_per_step"] = round(e0.elapsed_time(e1) * 1e3 / args.steps, 2)
+        res[f"{key}_wall_us_per_step"] = round(wall * 1e6 / args.steps, 2)
+        if prefetch:
+            _, loads1, page_bytes = paged.paging_stats()
+            res["loads_per_step"] = round((loads1 - loads0) / args.steps, 2)
+            res["h2d_bytes_per_step"] = round((loads1 - loads0) * page_bytes / args.steps)
+    for pool in (paged, resident):
+        st = pool.status()
+        if st != "OK":
+            raise RuntimeError(f"device status {st}")
+    extra = (res["paged_us_per_step"] - res["resident_us_per_step"]) * 1e-6
+    res["h2d_GBps_over_extra_time"] = round(res["h2d_bytes_per_step"] / extra / 1e9, 2) \
+        if extra > 0 else None
+    res["distinct_per_batch"] = round(float(np.mean([len(set(b.tolist())) for b in batches])), 2)
+    paged.close()
+    resident.close()
+    return res
+
+
+# ---------------------------------------------------------------------------
 # CPU oracle baseline
 # ---------------------------------------------------------------------------
 def cpu_baseline(wl: wk.Workload, rep: Replica, seconds: float, torch):
@@ -267,6 +355,10 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (x steps), to scale "
                          "the rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--paging", action="store_true",
+                    help="measure host-cache paging instead (prints its own JSON line)")
+    ap.add_argument("--paging-slots", type=int, default=64, help="device slots of the paged pool")
+    ap.add_argument("--paging-mix", choices=["uniform", "hot5"], default="uniform")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
@@ -285,6 +377,10 @@ def main(argv=None) -> int:
                           "launches": args.steps}), flush=True)
         return 0
     import heterogeneous_rank_gemm_amd as hrg
+
+    if args.paging:
+        print(json.dumps({"paging": paging_bench(args, torch, hrg)}), flush=True)
+        return 0
 
     wl = wk.WORKLOADS[args.workload]
     R = 1 if wl.key == 5 else max(1, args.rotate)

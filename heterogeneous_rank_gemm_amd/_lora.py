@@ -29,7 +29,7 @@ EXPORTED = (
     "lora_unload_adapter", "lora_pool_query", "lora_plan_create", "lora_plan_destroy",
     "lora_plan", "lora_apply", "lora_base_apply", "lora_status", "lora_debug_read_plan",
     "lora_host_cache_create", "lora_host_register", "lora_host_unregister", "lora_prefetch",
-    "lora_pin_adapter", "lora_paging_query",
+    "lora_pin_adapter", "lora_paging_query", "lora_paging_stats",
 )
 
 _vp = C.c_void_p
@@ -57,6 +57,7 @@ _sigs = {
     "lora_prefetch": [_vp, _P_i32, _i32, _vp],
     "lora_pin_adapter": [_vp, _i32, _i32, _vp],
     "lora_paging_query": [_vp, _i32, _P_i32, _P_i32],
+    "lora_paging_stats": [_vp, C.POINTER(C.c_int64), C.POINTER(C.c_int64), C.POINTER(C.c_int64)],
 }
 for _name, _args in _sigs.items():
     _f = getattr(_lib, _name)
@@ -223,3 +224,10 @@ def lora_paging_query(pool: int, adapter_id: int):
     w, p = C.c_int32(), C.c_int32()
     _check(_lib.lora_paging_query(pool, adapter_id, C.byref(w), C.byref(p)), "lora_paging_query")
     return w.value, p.value
+
+
+def lora_paging_stats(pool: int):
+    """(prefetch calls, slots copied host -> device, bytes per slot copy)."""
+    a, b, c = C.c_int64(), C.c_int64(), C.c_int64()
+    _check(_lib.lora_paging_stats(pool, C.byref(a), C.byref(b), C.byref(c)), "lora_paging_stats")
+    return a.value, b.value, c.value

@@ -172,6 +172,12 @@ hipError_t launch_clear_i32(int32_t* p, int32_t n, int32_t value, hipStream_t s)
 // Routing-table updates of several distinct ids, each {id, slot (-1: not
 // addressable), rank, scale bits}; launched in chunks of kSlotUpdatesPerLaunch.
 constexpr int kSlotUpdatesPerLaunch = 64;
+// Page-in of host-cached adapters: one launch copies up to kPageMovesPerLaunch
+// whole slots, {host-cache slot, device slot} each, reading the pinned host
+// cache through its device mapping.  slot_vec = 16-byte vectors per slot.
+constexpr int kPageMovesPerLaunch = 64;
+hipError_t launch_page_in(const void* host_cache_dev, void* pages, const int2* moves, int n,
+                          size_t slot_vec, hipStream_t s);
 hipError_t launch_set_slots(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
                             const int4* updates, int n, hipStream_t s);
 

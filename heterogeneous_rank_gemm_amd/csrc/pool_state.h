@@ -49,6 +49,7 @@ struct lora_pool_s {
   std::set<lora_plan_s*> plans;
   // host cache and LRU paging (paging.hip); empty until lora_host_cache_create
   uint16_t* hcache = nullptr;        // pinned host [max_cpu][slot_elems], the device page layout
+  void* hcache_dev = nullptr;        // its device mapping (read by the page-in kernel)
   int32_t max_cpu = 0;
   std::vector<int32_t> h_hslot;      // [max_ids] host-cache slot of a registered id (-1: none)
   std::vector<int32_t> h_hrank;      // [max_ids] rank of a registered id
@@ -60,6 +61,7 @@ struct lora_pool_s {
   std::vector<uint8_t> pinned;       // [max_ids]
   std::vector<int32_t> named;        // registered ids named by the last prefetch
   int64_t calls = 0;                 // prefetch calls so far
+  int64_t pages_loaded = 0;          // host -> device slot copies so far (prefetch and pin)
   hipStream_t copy_stream = nullptr; // host -> device page copies
   hipEvent_t call_ev[hrg::kCallEvents] = {};  // recorded on the caller's stream as each prefetch starts
   hipEvent_t copy_ev = nullptr;      // the last prefetch's copies done

@@ -85,3 +85,6 @@ class LoraPool:
 
     def paging_query(self, adapter_id: int):
         return _lora.lora_paging_query(self.handle, adapter_id)
+
+    def paging_stats(self):
+        return _lora.lora_paging_stats(self.handle)

@@ -283,6 +283,15 @@ lora_status_t lora_pin_adapter(lora_pool_t pool, int32_t id, int32_t pin, hipStr
  */
 lora_status_t lora_paging_query(lora_pool_t pool, int32_t id, int32_t* where, int32_t* pinned);
 
+/*
+ * lora_paging_stats -- counters of the paging path (host state, no device
+ * work): prefetch calls so far, adapter slots copied host -> device so far
+ * (by prefetch and pin), and the bytes of one such copy (every module's pages
+ * of one slot, padded to max_rank).  Any pointer may be NULL.
+ */
+lora_status_t lora_paging_stats(lora_pool_t pool, int64_t* prefetches, int64_t* pages_loaded,
+                                int64_t* bytes_per_page);
+
 #ifdef __cplusplus
 }
 #endif
