@@ -40,6 +40,11 @@ What it computes (the readings taken where the pages are garbled):
     call fails and produces no output.
   * A rank above the configured maximum is refused ([vLLM-ch7] "starting a
     multi-LoRA service", --max-lora-rank; [icman] section 3.3).
+  * Target sets: an adapter adds its branch only on the linears it targets
+    ([icman] section 2.1: the low-rank branch is added on the target linear
+    layers; [vLLM-ch7] performance notes: adapters of one batch with
+    different target_modules send some sequences down a skip path).  A
+    module the adapter does not target is pure base for its tokens.
   * Grouping the batch by LoRA id ([LoRA-Land] section 2, "Grouped
     Multi-LoRA Execution") is read as a stable sort of token indices by
     (id ascending, original index ascending), -1 first, with the maximal
@@ -135,7 +140,17 @@ class Registry:
         if len(A) != self.n_modules or len(B) != self.n_modules:
             raise OracleError(INVALID_ARG, "one A and one B per module")
         As, Bs = [], []
+        if all(A[m] is None and B[m] is None for m in range(self.n_modules)):
+            raise OracleError(INVALID_ARG, "an adapter targets at least one module")
         for m in range(self.n_modules):
+            if A[m] is None and B[m] is None:
+                # the adapter does not target this module: tokens routed to it
+                # take the skip path there ([vLLM-ch7] performance notes)
+                As.append(None)
+                Bs.append(None)
+                continue
+            if A[m] is None or B[m] is None:
+                raise OracleError(INVALID_ARG, f"module {m}: A and B both given or both absent")
             a = _as_f64(A[m])
             b = _as_f64(B[m])
             if a.shape != (self.d_in[m], rank) or b.shape != (rank, self.d_out[m]):
@@ -254,6 +269,8 @@ def lora_linear(reg: Registry, module: int, X, ids, W) -> np.ndarray:
         if i < 0:
             continue                                # base only: no LoRA term
         ad = reg.adapters[i]
+        if ad.A[module] is None:
+            continue                                # not a target of this adapter
         u = Xf[t, :] @ ad.A[module]                 # shrink: d_in -> r
         Y[t, :] += ad.scale * (u @ ad.B[module])    # expand r -> d_out, scale, add
     return Y
@@ -275,6 +292,8 @@ def lora_linear_sampled(reg: Registry, module: int, X_rows, ids_rows, W_cols,
         if i < 0:
             continue
         ad = reg.adapters[i]
+        if ad.A[module] is None:
+            continue
         u = Xf[n, :] @ ad.A[module]
         Y[n, :] += ad.scale * (u @ ad.B[module][:, cols])
     return Y

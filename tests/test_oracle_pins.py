@@ -391,3 +391,41 @@ def test_parity_metrics_detect_a_dropped_delta():
     doubled = torch.as_tensor(2 * Y - Y0, dtype=torch.float32).to(torch.bfloat16)
     mx, rl1, _ = oracle.parity_metrics(doubled, Y)
     assert mx > oracle.MAX_REL_TOL or rl1 > oracle.RELL1_TOL
+
+
+def test_target_sets_skip_untargeted_modules():
+    """An adapter without pages for a module is pure base there ([vLLM-ch7]
+    performance notes, skip path): its rows equal X W^T exactly, and on the
+    modules it does target it equals the same adapter loaded with every
+    module (and the merged weight of the pinned brute force)."""
+    g = np.random.default_rng(5)
+    d_in, d_out, T = 6, 5, 7
+    full = Registry(3, 3, 4, [d_in] * 3, [d_out] * 3, T)
+    part = Registry(3, 3, 4, [d_in] * 3, [d_out] * 3, T)
+    As = [np.round(g.standard_normal((d_in, 3)) * 8) / 8 for _ in range(3)]
+    Bs = [np.round(g.standard_normal((3, d_out)) * 8) / 8 for _ in range(3)]
+    full.load(0, 3, 6.0, As, Bs)
+    part.load(0, 3, 6.0, [As[0], None, As[2]], [Bs[0], None, Bs[2]])
+    X = np.round(g.standard_normal((T, d_in)) * 4) / 4
+    W = np.round(g.standard_normal((d_out, d_in)) * 4) / 4
+    ids = np.array([0, -1, 0, 0, -1, 0, 0])
+    for m in (0, 2):
+        np.testing.assert_array_equal(oracle.lora_linear(part, m, X, ids, W),
+                                      oracle.lora_linear(full, m, X, ids, W))
+    np.testing.assert_array_equal(oracle.lora_linear(part, 1, X, ids, W), X @ W.T)
+    # the targeted module against the merged weight W + s (A B)^T, by loops
+    Wm = [[W[j][k] + 2.0 * sum(As[0][k][q] * Bs[0][q][j] for q in range(3)) for k in range(d_in)]
+          for j in range(d_out)]
+    Y = oracle.lora_linear(part, 0, X, ids, W)
+    for t in range(T):
+        if ids[t] < 0:
+            continue
+        for j in range(d_out):
+            ref = sum(X[t][k] * Wm[j][k] for k in range(d_in))
+            assert abs(Y[t, j] - ref) <= 1e-12 * (1 + abs(ref))
+    with pytest.raises(OracleError) as e:
+        part.load(1, 3, 6.0, [None] * 3, [None] * 3)
+    assert e.value.status == oracle.INVALID_ARG
+    with pytest.raises(OracleError) as e:
+        part.load(1, 3, 6.0, [As[0], None, As[2]], [Bs[0], Bs[1], Bs[2]])
+    assert e.value.status == oracle.INVALID_ARG
