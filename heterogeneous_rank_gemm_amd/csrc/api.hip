@@ -122,6 +122,7 @@ lora_status_t decode_apply(lora_pool_s* P, int32_t module, const lora_bf16_t* X,
   a.KS = ceil_div(K, hrg::kDecodeChunk);
   a.npad = a.NT * hrg::kDecodeTileRows;
   a.lora = lora ? 1 : 0;
+  a.module = module;
   // A items: (adapter, 16-rank block); at most min(T, resident) adapters
   // (the launcher places them)
   const int loaded = P->max_adapters - (int)P->free_slots.size();
@@ -214,6 +215,7 @@ lora_status_t lora_pool_create(lora_pool_t* pool, int32_t max_adapters, int32_t 
     return LORA_ERR_OOM;
   }
   P->h_id2slot.assign(max_ids, -1);
+  P->h_mask.assign(max_ids, 0);
   P->h_slot_rank.assign(max_adapters, 0);
   P->h_slot_scale.assign(max_adapters, 0.f);
   for (int32_t i = 0; i < max_adapters; ++i) P->free_slots.insert(i);
@@ -263,8 +265,10 @@ lora_status_t lora_load_adapter(lora_pool_t P, int32_t id, int32_t rank, float a
                                 const lora_bf16_t* const* A, const lora_bf16_t* const* B,
                                 hipStream_t stream) {
   if (!P || !A || !B) return LORA_ERR_INVALID_ARG;
-  for (int32_t m = 0; m < P->n_modules; ++m)
-    if (!A[m] || !B[m]) return LORA_ERR_INVALID_ARG;
+  int32_t mask = 0;
+  if (!hrg::target_mask(P->n_modules, reinterpret_cast<const void* const*>(A),
+                        reinterpret_cast<const void* const*>(B), &mask))
+    return LORA_ERR_INVALID_ARG;
   if (id < 0 || id >= P->max_ids) return LORA_ERR_ID_RANGE;
   if (rank < 1 || rank > P->max_rank) return LORA_ERR_RANK;
   if (P->h_id2slot[id] >= 0) return LORA_ERR_EXISTS;
@@ -277,6 +281,14 @@ lora_status_t lora_load_adapter(lora_pool_t P, int32_t id, int32_t rank, float a
   for (int32_t m = 0; m < P->n_modules; ++m) {
     const size_t na = (size_t)P->d_in[m] * rank, nb = (size_t)rank * P->d_out[m];
     hrg::PackArgs pa{};
+    if (!A[m]) {
+      // not a target of this adapter: zero pages (rank 0 reads no source)
+      pa = {P->staging, base + P->a_off[m], 0, P->max_rank, P->d_in[m], 0};
+      if (hrg::launch_pack(pa, stream) != hipSuccess) return LORA_ERR_HIP;
+      pa = {P->staging, base + P->b_off[m], 0, P->rpad, P->d_out[m], 1};
+      if (hrg::launch_pack(pa, stream) != hipSuccess) return LORA_ERR_HIP;
+      continue;
+    }
     if (hipMemcpyAsync(P->staging, A[m], na * 2, hipMemcpyDefault, stream) != hipSuccess)
       return (void)hipGetLastError(), LORA_ERR_HIP;
     pa = {P->staging, base + P->a_off[m], rank, P->max_rank, P->d_in[m], 0};
@@ -287,7 +299,7 @@ lora_status_t lora_load_adapter(lora_pool_t P, int32_t id, int32_t rank, float a
     if (hrg::launch_pack(pa, stream) != hipSuccess) return LORA_ERR_HIP;
   }
   const float scale = alpha / (float)rank;
-  if (hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, id, slot, rank, scale,
+  if (hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, id, slot, rank, scale, mask,
                            stream) !=
           hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess) {
@@ -296,6 +308,7 @@ lora_status_t lora_load_adapter(lora_pool_t P, int32_t id, int32_t rank, float a
   }
   P->free_slots.erase(slot);
   P->h_id2slot[id] = slot;
+  P->h_mask[id] = mask;
   P->h_slot_rank[slot] = rank;
   P->h_slot_scale[slot] = scale;
   return LORA_OK;
@@ -310,7 +323,7 @@ lora_status_t lora_unload_adapter(lora_pool_t P, int32_t id, hipStream_t stream)
   if (slot < 0) return LORA_ERR_NOT_LOADED;
   DeviceGuard g(P->device);
   if (hipStreamSynchronize(stream) != hipSuccess ||
-      hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, id, -1, 0, 0.f, stream) !=
+      hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, id, -1, 0, 0.f, 0, stream) !=
           hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess) {
     (void)hipGetLastError();

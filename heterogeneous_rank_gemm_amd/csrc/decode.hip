@@ -59,6 +59,10 @@ __device__ __forceinline__ uint4 keep_if(bool keep, uint4 v) {
 __device__ __forceinline__ float lo_f(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
 __device__ __forceinline__ float hi_f(uint32_t v) { return __builtin_bit_cast(float, v & 0xffff0000u); }
 
+// Whether an adapter with module mask `mask` targets linear `m` (modules >= 32
+// are always targeted).
+__device__ __forceinline__ bool targets(int mask, int m) { return m >= 32 || ((mask >> m) & 1); }
+
 // Token t's adapter lookup (lane t of a wave, t < 64): id, pool slot, true
 // rank and scale, or bad = the status code of an invalid id.  All lanes load
 // in parallel, so a wave pays one round of dependent loads, not one per token.
@@ -74,13 +78,14 @@ __device__ __forceinline__ TokInfo token_info(const DecodeArgs& a, int t) {
     if (id < -1 || id >= a.max_ids) {
       ti.bad = kStatusIdRange;
     } else if (id >= 0) {
-      const int4 e = a.id_info[id];  // {slot, rank, scale bits}: one load after ids
+      const int4 e = a.id_info[id];  // {slot, rank, scale bits, module mask}: one load after ids
       if (e.x < 0) {
         ti.bad = kStatusNotLoaded;
       } else {
         ti.id = id;
         ti.slot = e.x;
-        ti.rank = e.y;
+        // an adapter that does not target this linear has no rank here
+        ti.rank = targets(e.w, a.module) ? e.y : 0;
         ti.scale = __builtin_bit_cast(float, e.z);
       }
     }
@@ -414,6 +419,8 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
         if (e.x < 0) bad = kStatusNotLoaded;
       }
       if (bad) atomicMax(&s_bad, bad);
+      // a token whose adapter does not target this linear takes the base only
+      if (!bad && e.x >= 0 && !targets(e.w, a.module)) e = make_int4(-1, 0, 0, 0);
       if (tid >= t0 && tid < t0 + 16) s_info[tid - t0] = bad ? make_int4(-1, 0, 0, 0) : e;
     }
     // B^T page in 16-rank chunks [rpad/16][N][16]: the 4 columns' chunk is 64

@@ -45,7 +45,7 @@ struct PlanArgs {
   const int32_t* ids;
   int32_t T;
   int32_t max_ids;
-  const int4* id_info;     // [max_ids] {slot (-1: not resident), rank, scale bits, 0}
+  const int4* id_info;     // [max_ids] {slot (-1: not resident), rank, scale bits, module mask}
   int32_t* status;
   PlanTables tab;
 };
@@ -114,7 +114,7 @@ struct DecodeArgs {
   const int32_t* ids;     // [T]
   int32_t T, N, K;
   int32_t max_ids;
-  const int4* id_info;    // [max_ids] {slot (-1: not resident), rank, scale bits, 0}
+  const int4* id_info;    // [max_ids] {slot (-1: not resident), rank, scale bits, module mask}
   const uint16_t* pages;
   size_t slot_stride;
   size_t a_off, b_off;
@@ -132,6 +132,7 @@ struct DecodeArgs {
   int32_t na;             // A waves riding in each W block: 0, 1, 2 or 4 (0: base-only)
   int32_t a_tiles;        // extra blocks of 4 + na A waves, per K chunk
   int32_t lora;
+  int32_t module;         // index of the linear: an adapter whose id_info mask lacks it adds nothing
 };
 
 // Page layouts inside a slot (rows past the adapter's rank are zero):
@@ -166,8 +167,10 @@ int prefill_choose(int T, int N);
 // Picks the W blocks (np) and where the `items` A items go, then launches.
 hipError_t launch_decode(const DecodeArgs& a, int items, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
+// Routing-table update of one id; `mask` = the modules the adapter targets
+// (bit m: module m; modules >= 32 are always targeted), kept in id_info.w.
 hipError_t launch_set_slot(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
-                           int32_t id, int32_t slot, int32_t rank, float scale, hipStream_t s);
+                           int32_t id, int32_t slot, int32_t rank, float scale, int32_t mask, hipStream_t s);
 hipError_t launch_clear_i32(int32_t* p, int32_t n, int32_t value, hipStream_t s);
 // Routing-table updates of several distinct ids, each {id, slot (-1: not
 // addressable), rank, scale bits}; launched in chunks of kSlotUpdatesPerLaunch.
@@ -179,6 +182,6 @@ constexpr int kPageMovesPerLaunch = 64;
 hipError_t launch_page_in(const void* host_cache_dev, void* pages, const int2* moves, int n,
                           size_t slot_vec, hipStream_t s);
 hipError_t launch_set_slots(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
-                            const int4* updates, int n, hipStream_t s);
+                            const int4* updates, const int32_t* masks, int n, hipStream_t s);
 
 }  // namespace hrg

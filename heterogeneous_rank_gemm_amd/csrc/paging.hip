@@ -114,7 +114,7 @@ lora_status_t paged_drop_device_copy(lora_pool_s* P, int32_t id, hipStream_t str
   if (slot < 0) return LORA_ERR_NOT_LOADED;
   DeviceGuard g(P->device);
   if (hipStreamSynchronize(P->copy_stream) != hipSuccess || hipStreamSynchronize(stream) != hipSuccess ||
-      hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, id, -1, 0, 0.f, stream) !=
+      hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, id, -1, 0, 0.f, 0, stream) !=
           hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess)
     return hip_fail();
@@ -179,8 +179,10 @@ lora_status_t lora_host_cache_create(lora_pool_t P, int32_t max_cpu_adapters) {
 lora_status_t lora_host_register(lora_pool_t P, int32_t id, int32_t rank, float alpha,
                                  const lora_bf16_t* const* A, const lora_bf16_t* const* B) {
   if (!P || !P->hcache || !A || !B) return LORA_ERR_INVALID_ARG;
-  for (int32_t m = 0; m < P->n_modules; ++m)
-    if (!A[m] || !B[m]) return LORA_ERR_INVALID_ARG;
+  int32_t mask = 0;
+  if (!hrg::target_mask(P->n_modules, reinterpret_cast<const void* const*>(A),
+                        reinterpret_cast<const void* const*>(B), &mask))
+    return LORA_ERR_INVALID_ARG;
   if (id < 0 || id >= P->max_ids) return LORA_ERR_ID_RANGE;
   if (rank < 1 || rank > P->max_rank) return LORA_ERR_RANK;
   if (P->h_hslot[id] >= 0 || P->h_id2slot[id] >= 0) return LORA_ERR_EXISTS;
@@ -193,6 +195,7 @@ lora_status_t lora_host_register(lora_pool_t P, int32_t id, int32_t rank, float 
   std::vector<uint16_t> tmp;
   for (int32_t m = 0; m < P->n_modules; ++m) {
     const int32_t din = P->d_in[m], dout = P->d_out[m];
+    if (!A[m]) continue;  // not a target of this adapter: its pages stay zero
     // A (d_in x rank) -> rank-major A^T page [max_rank][d_in]; A may be host or device memory
     tmp.resize((size_t)din * rank);
     if (hipMemcpy(tmp.data(), A[m], tmp.size() * 2, hipMemcpyDefault) != hipSuccess) return hip_fail();
@@ -211,6 +214,7 @@ lora_status_t lora_host_register(lora_pool_t P, int32_t id, int32_t rank, float 
   P->h_hslot[id] = hs;
   P->h_hrank[id] = rank;
   P->h_hscale[id] = alpha / (float)rank;
+  P->h_mask[id] = mask;
   P->last_use[id] = 0;
   P->pinned[id] = 0;
   return LORA_OK;
@@ -249,7 +253,8 @@ lora_status_t lora_pin_adapter(lora_pool_t P, int32_t id, int32_t pin, hipStream
     P->last_use[id] = std::max<int64_t>(P->last_use[id], P->calls);
     if (!is_named(P, id) && P->h_id2slot[id] >= 0) {
       const int4 e = entry(P, id, -1);
-      if (hrg::launch_set_slots(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, &e, 1, stream) !=
+      const int32_t mk = 0;
+      if (hrg::launch_set_slots(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, &e, &mk, 1, stream) !=
           hipSuccess)
         return hip_fail();
       mirror(P, id, -1);
@@ -288,7 +293,8 @@ lora_status_t lora_pin_adapter(lora_pool_t P, int32_t id, int32_t pin, hipStream
   }
   if (P->h_id2slot[id] != slot) {
     const int4 e = entry(P, id, slot);
-    if (hrg::launch_set_slots(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, &e, 1, stream) !=
+    const int32_t mk = P->h_mask[id];
+    if (hrg::launch_set_slots(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, &e, &mk, 1, stream) !=
         hipSuccess)
       return hip_fail();
     mirror(P, id, slot);
@@ -367,19 +373,22 @@ lora_status_t lora_prefetch(lora_pool_t P, const int32_t* ids, int32_t n, hipStr
 
   // routing-table changes, in stream order after the copies
   std::vector<int4> ups;
+  std::vector<int32_t> masks;
   for (int32_t id : P->named)
     if (!inreq[id] && !P->pinned[id] && P->h_id2slot[id] >= 0) {
       ups.push_back(entry(P, id, -1));
+      masks.push_back(0);
       mirror(P, id, -1);
     }
   for (int32_t id : req)
     if (P->h_id2slot[id] != P->cached[id]) {
       ups.push_back(entry(P, id, P->cached[id]));
+      masks.push_back(P->h_mask[id]);
       mirror(P, id, P->cached[id]);
     }
   P->named = req;
   if (!ups.empty() && hrg::launch_set_slots(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, ups.data(),
-                                            (int)ups.size(), stream) != hipSuccess)
+                                            masks.data(), (int)ups.size(), stream) != hipSuccess)
     return hip_fail();
   return LORA_OK;
 }

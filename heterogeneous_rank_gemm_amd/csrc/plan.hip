@@ -321,21 +321,21 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
 // scale, and the packed per-id entry {slot, rank, scale} the decode kernels
 // read with one load.
 __global__ void set_slot_kernel(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
-                                int32_t id, int32_t slot, int32_t rank, float scale) {
+                                int32_t id, int32_t slot, int32_t rank, float scale, int32_t mask) {
   if (threadIdx.x == 0) {
     if (slot >= 0) {
       slot_rank[slot] = rank;
       slot_scale[slot] = scale;
     }
     id2slot[id] = slot;
-    id_info[id] = make_int4(slot, slot >= 0 ? rank : 0, __builtin_bit_cast(int, scale), 0);
+    id_info[id] = make_int4(slot, slot >= 0 ? rank : 0, __builtin_bit_cast(int, scale), slot >= 0 ? mask : 0);
   }
 }
 
 hipError_t launch_set_slot(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
-                           int32_t id, int32_t slot, int32_t rank, float scale, hipStream_t s) {
+                           int32_t id, int32_t slot, int32_t rank, float scale, int32_t mask, hipStream_t s) {
   hipLaunchKernelGGL(set_slot_kernel, dim3(1), dim3(64), 0, s, id2slot, slot_rank, slot_scale, id_info,
-                     id, slot, rank, scale);
+                     id, slot, rank, scale, mask);
   return hipGetLastError();
 }
 
@@ -343,6 +343,7 @@ hipError_t launch_set_slot(int32_t* id2slot, int32_t* slot_rank, float* slot_sca
 // (passed by value, so the host needs no staging buffer).
 struct SlotUpdates {
   int4 u[kSlotUpdatesPerLaunch];  // {id, slot (-1: not addressable), rank, scale bits}
+  int32_t mask[kSlotUpdatesPerLaunch];  // modules the adapter targets (bit m: module m)
   int32_t n;
 };
 
@@ -356,16 +357,19 @@ __global__ void set_slots_kernel(int32_t* id2slot, int32_t* slot_rank, float* sl
       slot_scale[e.y] = __builtin_bit_cast(float, e.w);
     }
     id2slot[e.x] = e.y;
-    id_info[e.x] = make_int4(e.y, e.y >= 0 ? e.z : 0, e.w, 0);
+    id_info[e.x] = make_int4(e.y, e.y >= 0 ? e.z : 0, e.w, e.y >= 0 ? ups.mask[i] : 0);
   }
 }
 
 hipError_t launch_set_slots(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
-                            const int4* updates, int n, hipStream_t s) {
+                            const int4* updates, const int32_t* masks, int n, hipStream_t s) {
   for (int i0 = 0; i0 < n; i0 += kSlotUpdatesPerLaunch) {
     SlotUpdates ups{};
     ups.n = std::min(kSlotUpdatesPerLaunch, n - i0);
-    for (int j = 0; j < ups.n; ++j) ups.u[j] = updates[i0 + j];
+    for (int j = 0; j < ups.n; ++j) {
+      ups.u[j] = updates[i0 + j];
+      ups.mask[j] = masks[i0 + j];
+    }
     hipLaunchKernelGGL(set_slots_kernel, dim3(1), dim3(kSlotUpdatesPerLaunch), 0, s, id2slot, slot_rank,
                        slot_scale, id_info, ups);
     const hipError_t e = hipGetLastError();

@@ -31,7 +31,7 @@ struct lora_pool_s {
   int32_t* id2slot = nullptr;        // [max_ids]
   int32_t* slot_rank = nullptr;      // [max_adapters]
   float* slot_scale = nullptr;       // [max_adapters]
-  int4* id_info = nullptr;           // [max_ids] {slot, rank, scale bits, 0}
+  int4* id_info = nullptr;           // [max_ids] {slot, rank, scale bits, module mask}
   int32_t* status = nullptr;         // sticky device status
   uint16_t* staging = nullptr;       // one module's A or B as received
   float* upart = nullptr;            // [kMaxSplits][max_tokens][rpad] shrink partial planes
@@ -43,6 +43,7 @@ struct lora_pool_s {
   float* dec_part = nullptr;         // [ceil(max d_in / 1024)][64][max d_out rounded up to 64] base partials
   float* dec_upart = nullptr;        // [ceil(max d_in / 1024)][64][rpad] shrink partials
   std::vector<int32_t> h_id2slot, h_slot_rank;
+  std::vector<int32_t> h_mask;       // [max_ids] modules a loaded or registered id targets (bit m)
   std::vector<float> h_slot_scale;
   std::set<int32_t> free_slots;      // lowest free slot first
   lora_plan_s* internal = nullptr;
@@ -68,6 +69,27 @@ struct lora_pool_s {
 };
 
 namespace hrg {
+
+// The module mask of an adapter given its A and B pointer arrays: bit m set
+// when module m has pages (modules >= 32 always count as targeted).  Returns
+// false if a module has only one of A, B, if no module is targeted, or if a
+// pool of more than 32 modules gets an adapter without some module.
+inline bool target_mask(int32_t n_modules, const void* const* A, const void* const* B, int32_t* mask) {
+  uint32_t m = 0xffffffffu;
+  int present = 0;
+  for (int32_t i = 0; i < n_modules; ++i) {
+    if (!A[i] != !B[i]) return false;
+    if (A[i]) {
+      ++present;
+    } else {
+      if (i >= 32) return false;
+      m &= ~(1u << i);
+    }
+  }
+  if (present == 0) return false;
+  *mask = (int32_t)m;
+  return true;
+}
 
 // Drops the device copy of host-cached adapter `id` (NOT_LOADED if it has
 // none); its host copy stays.  Synchronises `stream`.

@@ -104,6 +104,13 @@ lora_status_t lora_pool_destroy(lora_pool_t pool);
  *   B      host array [n_modules] of pointers, B[m] is r x d_out[m]
  *          A[m], B[m] may point to host or device memory; they are copied
  *          before the call returns and may be freed afterwards.
+ *          Target sets ([vLLM-ch7] performance notes: adapters with different
+ *          target_modules in one batch send some sequences down a skip path;
+ *          [icman] 2.1: the branch is added on the target linears only):
+ *          A[m] == B[m] == NULL means the adapter does not target module m,
+ *          and its tokens get exactly lora_base_apply's rows there.  One of
+ *          the two NULL, no module targeted, or an untargeted module in a
+ *          pool of more than 32 modules is INVALID_ARG.
  *
  * EXISTS also if the id is in the pool's host cache (lora_host_register).
  * Slot choice: a pool with max_ids <= max_adapters is direct-mapped and
@@ -222,8 +229,9 @@ lora_status_t lora_host_cache_create(lora_pool_t pool, int32_t max_cpu_adapters)
 
 /*
  * lora_host_register -- copy an adapter into the host cache (not to the
- * device).  Arguments as lora_load_adapter; A[m], B[m] may be host or device
- * memory and may be freed when the call returns.  ID_RANGE, RANK, EXISTS (id
+ * device).  Arguments as lora_load_adapter (NULL pairs: untargeted modules);
+ * A[m], B[m] may be host or device memory and may be freed when the call
+ * returns.  ID_RANGE, RANK, EXISTS (id
  * already host-cached or loaded directly), POOL_FULL (host cache full; the
  * caller unregisters, the library never forgets an adapter on its own),
  * INVALID_ARG without a host cache.  Blocking; no stream work.
