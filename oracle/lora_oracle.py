@@ -507,3 +507,42 @@ class PagedRegistry(Registry):
         if adapter_id in self.host:
             return 1
         return 0
+
+
+# --------------------------------------------------------------------------
+# INT4 base weight ([vLLM-ch7] performance notes: an AWQ-INT4 base with bf16
+# adapters).  Readings: group-wise asymmetric 4-bit weights along d_in, the
+# AWQ group size of 128, q and the zero point z in 0..15, a bf16 scale s per
+# (output row, group); the base GEMM works on the weight dequantized to the
+# compute dtype, i.e. W[n, k] = bf16((q[n, k] - z[n, g]) * s[n, g]), g = k // 128
+# (the product is exact in float64, then one round to nearest even).
+# --------------------------------------------------------------------------
+Q4_GROUP = 128
+
+
+def round_to_bf16(x) -> np.ndarray:
+    """Round float64 values that are exact in float32 to the nearest bf16
+    (ties to even); returns float64."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    assert np.array_equal(f.astype(np.float64), np.asarray(x, dtype=np.float64)), "not exact in f32"
+    b = f.view(np.uint32).astype(np.uint64)
+    lsb = (b >> np.uint64(16)) & np.uint64(1)
+    r = ((b + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) << np.uint64(16)
+    return (r.astype(np.uint32)).view(np.float32).astype(np.float64)
+
+
+def dequant_q4(q, z, s) -> np.ndarray:
+    """q: [N, K] integers 0..15; z: [N, K // 128] integers 0..15; s: [N, K // 128]
+    bf16 scales (bits or tensor).  Returns the dequantized weight [N, K]
+    (float64 holding bf16 values)."""
+    q = np.asarray(q, dtype=np.int64)
+    z = np.asarray(z, dtype=np.int64)
+    sf = _as_f64(s)
+    N, K = q.shape
+    if K % Q4_GROUP or z.shape != (N, K // Q4_GROUP) or sf.shape != z.shape:
+        raise OracleError(INVALID_ARG, "q4 shapes")
+    if q.min(initial=0) < 0 or q.max(initial=0) > 15 or z.min(initial=0) < 0 or z.max(initial=0) > 15:
+        raise OracleError(INVALID_ARG, "q4 values")
+    g = np.arange(K) // Q4_GROUP
+    exact = (q - z[:, g]).astype(np.float64) * sf[:, g]
+    return round_to_bf16(exact)

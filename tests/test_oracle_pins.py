@@ -429,3 +429,35 @@ def test_target_sets_skip_untargeted_modules():
     with pytest.raises(OracleError) as e:
         part.load(1, 3, 6.0, [As[0], None, As[2]], [Bs[0], Bs[1], Bs[2]])
     assert e.value.status == oracle.INVALID_ARG
+
+
+def test_round_to_bf16_matches_torch_rne():
+    """The oracle's bf16 rounding against torch's float32 -> bfloat16 cast (round
+    to nearest even), on random values, ties and values near powers of two."""
+    g = np.random.default_rng(9)
+    v = np.concatenate([g.standard_normal(4000).astype(np.float32) * 3,
+                        (np.arange(-300, 300, dtype=np.float32) + 0.5) * 2.0 ** -7,
+                        np.float32([1.00390625, 1.01171875, -1.00390625, 255.5, 0.0])])
+    ref = torch.as_tensor(v).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.round_to_bf16(v.astype(np.float64)), ref)
+
+
+def test_dequant_q4_against_elementwise_definition():
+    """W[n, k] = bf16((q - z) s) per 128-wide group, by plain loops over a
+    tiny weight, with groups that differ in zero point and scale."""
+    g = np.random.default_rng(4)
+    N, K = 3, 256
+    q = g.integers(0, 16, size=(N, K))
+    z = g.integers(0, 16, size=(N, K // 128))
+    s = _bf16(np.abs(g.standard_normal((N, K // 128))) * 0.01)
+    W = oracle.dequant_q4(q, z, s)
+    sf = _f(s)
+    for n in range(N):
+        for k in range(K):
+            exact = float((int(q[n, k]) - int(z[n, k // 128]))) * float(sf[n, k // 128])
+            assert W[n, k] == float(torch.tensor(exact, dtype=torch.float32).to(torch.bfloat16))
+    # a zero point equal to q gives exact zeros; scale 1 and z 0 give q itself
+    q2 = np.full((1, 128), 9)
+    assert not oracle.dequant_q4(q2, np.array([[9]]), _bf16([[0.5]])).any()
+    np.testing.assert_array_equal(oracle.dequant_q4(np.arange(128).reshape(1, 128) % 16, np.array([[0]]),
+                                                    _bf16([[1.0]]))[0], np.arange(128) % 16)
