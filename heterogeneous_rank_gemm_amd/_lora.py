@@ -29,7 +29,8 @@ EXPORTED = (
     "lora_unload_adapter", "lora_pool_query", "lora_plan_create", "lora_plan_destroy",
     "lora_plan", "lora_apply", "lora_base_apply", "lora_status", "lora_debug_read_plan",
     "lora_host_cache_create", "lora_host_register", "lora_host_unregister", "lora_prefetch",
-    "lora_pin_adapter", "lora_paging_query", "lora_paging_stats",
+    "lora_pin_adapter", "lora_paging_query", "lora_paging_stats", "lora_q4_pack", "lora_apply_q4",
+    "lora_base_apply_q4",
 )
 
 _vp = C.c_void_p
@@ -58,6 +59,9 @@ _sigs = {
     "lora_pin_adapter": [_vp, _i32, _i32, _vp],
     "lora_paging_query": [_vp, _i32, _P_i32, _P_i32],
     "lora_paging_stats": [_vp, C.POINTER(C.c_int64), C.POINTER(C.c_int64), C.POINTER(C.c_int64)],
+    "lora_q4_pack": [_vp, _vp, _vp, _i32, _i32, _vp, _vp],
+    "lora_apply_q4": [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp],
+    "lora_base_apply_q4": [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp],
 }
 for _name, _args in _sigs.items():
     _f = getattr(_lib, _name)
@@ -231,3 +235,41 @@ def lora_paging_stats(pool: int):
     a, b, c = C.c_int64(), C.c_int64(), C.c_int64()
     _check(_lib.lora_paging_stats(pool, C.byref(a), C.byref(b), C.byref(c)), "lora_paging_stats")
     return a.value, b.value, c.value
+
+
+# ---------------------------------------------------------------------------
+# INT4 base weight
+# ---------------------------------------------------------------------------
+def lora_q4_pack(q, z, s):
+    """Packs host arrays q [N, K] and z [N, K/128] (integers 0..15) and the bf16
+    scales s [N, K/128] (a bf16 tensor or uint16 bits) into the device layout;
+    returns numpy (Wq uint32 [N, K/8], Wsz uint32 [N, K/128]).  The packing runs
+    in the library."""
+    import numpy as np
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    z = np.ascontiguousarray(z, dtype=np.uint8)
+    try:
+        import torch
+        if isinstance(s, torch.Tensor):
+            s = s.detach().cpu().contiguous().view(torch.int16).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    s = np.ascontiguousarray(np.asarray(s).view(np.uint16))
+    N, K = q.shape
+    Wq = np.empty((N, K // 8), dtype=np.uint32)
+    Wsz = np.empty((N, max(K // 128, 1)), dtype=np.uint32)
+    _check(_lib.lora_q4_pack(q.ctypes.data, z.ctypes.data, s.ctypes.data, N, K, Wq.ctypes.data,
+                             Wsz.ctypes.data), "lora_q4_pack")
+    return Wq, Wsz
+
+
+def lora_apply_q4(pool: int, module: int, X, ids, T: int, Wq, Wsz, W_scratch, out,
+                  plan: Optional[int] = None, stream=None) -> None:
+    _check(_lib.lora_apply_q4(pool, module, _ptr(X), _ptr(ids), T, _ptr(Wq), _ptr(Wsz),
+                              _ptr(W_scratch), _ptr(out), plan, _stream(stream)), "lora_apply_q4")
+
+
+def lora_base_apply_q4(pool: int, module: int, X, T: int, Wq, Wsz, W_scratch, out,
+                       stream=None) -> None:
+    _check(_lib.lora_base_apply_q4(pool, module, _ptr(X), T, _ptr(Wq), _ptr(Wsz), _ptr(W_scratch),
+                                   _ptr(out), _stream(stream)), "lora_base_apply_q4")

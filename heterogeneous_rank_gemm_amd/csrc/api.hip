@@ -94,8 +94,8 @@ lora_status_t run_plan(lora_pool_s* P, const int32_t* ids, int32_t T, lora_plan_
 bool module_ok(const lora_pool_s* P, int32_t m) { return P && m >= 0 && m < P->n_modules; }
 
 lora_status_t decode_apply(lora_pool_s* P, int32_t module, const lora_bf16_t* X, const int32_t* ids,
-                           int32_t T, const lora_bf16_t* W, lora_bf16_t* out, bool lora,
-                           hipStream_t stream) {
+                           int32_t T, const lora_bf16_t* W, const uint32_t* Wq, const uint32_t* Wsz,
+                           lora_bf16_t* out, bool lora, hipStream_t stream) {
   const int K = P->d_in[module], N = P->d_out[module];
   hrg::DecodeArgs a{};
   a.X = X;
@@ -123,6 +123,8 @@ lora_status_t decode_apply(lora_pool_s* P, int32_t module, const lora_bf16_t* X,
   a.npad = a.NT * hrg::kDecodeTileRows;
   a.lora = lora ? 1 : 0;
   a.module = module;
+  a.Wq = Wq;
+  a.Wsz = Wsz;
   // A items: (adapter, 16-rank block); at most min(T, resident) adapters
   // (the launcher places them)
   const int loaded = P->max_adapters - (int)P->free_slots.size();
@@ -375,21 +377,32 @@ lora_status_t lora_plan(lora_pool_t P, const int32_t* ids, int32_t T, lora_plan_
   return run_plan(P, ids, T, plan, stream);
 }
 
+// The INT4 base weight (Wq, Wsz; W == nullptr) is dequantized in the decode
+// kernel's registers, or into the caller's `scratch` (d_out x d_in bf16)
+// before the batched path's GEMM.
 static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t* X,
                                 const int32_t* ids, int32_t T, const lora_bf16_t* W,
+                                const uint32_t* Wq, const uint32_t* Wsz, lora_bf16_t* scratch,
                                 lora_bf16_t* out, lora_plan_t plan, bool lora, hipStream_t stream) {
   if (!module_ok(P, module)) return LORA_ERR_INVALID_ARG;
   if (T < 0 || T > P->max_tokens) return LORA_ERR_INVALID_ARG;
+  const int K = P->d_in[module], N = P->d_out[module];
+  const bool q4 = Wq != nullptr || Wsz != nullptr;
+  if (q4 && (!Wq || !Wsz || K % hrg::kQ4Group != 0 || (T > hrg::kDecodeMaxT && !scratch)))
+    return LORA_ERR_INVALID_ARG;
   if (T == 0) return LORA_OK;
-  if (!X || !W || !out || (lora && !ids)) return LORA_ERR_INVALID_ARG;
+  if (!X || (!W && !q4) || !out || (lora && !ids)) return LORA_ERR_INVALID_ARG;
   if (plan) {
     if (!P->plans.count(plan) || plan->T != T || plan->ids != ids) return LORA_ERR_INVALID_ARG;
   }
   DeviceGuard g(P->device);
-  const int K = P->d_in[module], N = P->d_out[module];
-  if (T <= hrg::kDecodeMaxT) return decode_apply(P, module, X, ids, T, W, out, lora, stream);
+  if (T <= hrg::kDecodeMaxT) return decode_apply(P, module, X, ids, T, W, Wq, Wsz, out, lora, stream);
   // the batched path addresses X with 32-bit byte offsets
   if ((size_t)T * K * 2 > (size_t)INT32_MAX) return LORA_ERR_INVALID_ARG;
+  if (q4) {
+    if (hrg::launch_q4_dequant(Wq, Wsz, N, K, scratch, stream) != hipSuccess) return LORA_ERR_HIP;
+    W = scratch;
+  }
   hrg::GemmArgs ga{};
   ga.X = X;
   ga.W = W;
@@ -458,12 +471,50 @@ static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t
 lora_status_t lora_apply(lora_pool_t P, int32_t module, const lora_bf16_t* X, const int32_t* ids,
                          int32_t T, const lora_bf16_t* W, lora_bf16_t* out, lora_plan_t plan,
                          hipStream_t stream) {
-  return apply_impl(P, module, X, ids, T, W, out, plan, true, stream);
+  return apply_impl(P, module, X, ids, T, W, nullptr, nullptr, nullptr, out, plan, true, stream);
 }
 
 lora_status_t lora_base_apply(lora_pool_t P, int32_t module, const lora_bf16_t* X, int32_t T,
                               const lora_bf16_t* W, lora_bf16_t* out, hipStream_t stream) {
-  return apply_impl(P, module, X, nullptr, T, W, out, nullptr, false, stream);
+  return apply_impl(P, module, X, nullptr, T, W, nullptr, nullptr, nullptr, out, nullptr, false, stream);
+}
+
+lora_status_t lora_apply_q4(lora_pool_t P, int32_t module, const lora_bf16_t* X, const int32_t* ids,
+                            int32_t T, const uint32_t* Wq, const uint32_t* Wsz, lora_bf16_t* W_scratch,
+                            lora_bf16_t* out, lora_plan_t plan, hipStream_t stream) {
+  if (!Wq || !Wsz) return LORA_ERR_INVALID_ARG;
+  return apply_impl(P, module, X, ids, T, nullptr, Wq, Wsz, W_scratch, out, plan, true, stream);
+}
+
+lora_status_t lora_base_apply_q4(lora_pool_t P, int32_t module, const lora_bf16_t* X, int32_t T,
+                                 const uint32_t* Wq, const uint32_t* Wsz, lora_bf16_t* W_scratch,
+                                 lora_bf16_t* out, hipStream_t stream) {
+  if (!Wq || !Wsz) return LORA_ERR_INVALID_ARG;
+  return apply_impl(P, module, X, nullptr, T, nullptr, Wq, Wsz, W_scratch, out, nullptr, false, stream);
+}
+
+lora_status_t lora_q4_pack(const uint8_t* q, const uint8_t* z, const lora_bf16_t* s, int32_t N, int32_t K,
+                           uint32_t* Wq, uint32_t* Wsz) {
+  if (!q || !z || !s || !Wq || !Wsz || N < 1 || K < hrg::kQ4Group || K % hrg::kQ4Group != 0)
+    return LORA_ERR_INVALID_ARG;
+  const int KW = K / 8, KG = K / hrg::kQ4Group;
+  for (size_t i = 0; i < (size_t)N * K; ++i)
+    if (q[i] > 15) return LORA_ERR_INVALID_ARG;
+  for (size_t i = 0; i < (size_t)N * KG; ++i)
+    if (z[i] > 15) return LORA_ERR_INVALID_ARG;
+  for (int32_t n = 0; n < N; ++n) {
+    for (int g = 0; g < KG; ++g) {
+      Wsz[(size_t)n * KG + g] = (uint32_t)s[(size_t)n * KG + g] | ((uint32_t)z[(size_t)n * KG + g] << 16);
+      for (int p = 0; p < 16; ++p) {
+        const int j = p / 4, st = p % 4;
+        uint32_t w = 0;
+        for (int e = 0; e < 8; ++e)
+          w |= (uint32_t)q[(size_t)n * K + hrg::kQ4Group * g + 32 * st + 8 * j + e] << (4 * e);
+        Wq[(size_t)n * KW + 16 * g + p] = w;
+      }
+    }
+  }
+  return LORA_OK;
 }
 
 lora_status_t lora_status(lora_pool_t P, hipStream_t stream) {

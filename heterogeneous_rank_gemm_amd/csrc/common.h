@@ -49,6 +49,28 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Eight 4-bit weights of one 32-bit word (nibble e = bits 4e..4e+3) to bf16:
+// bf16((q - z) * s), given s and -z * s in fp32.  q * s and z * s are exact
+// in fp32 (a bf16 scale times a 4-bit integer), so the fma is exact and the
+// only rounding is the conversion to bf16 (to nearest even).
+__device__ __forceinline__ bf16x8 dequant_q4x8(uint32_t w, float s, float nzs) {
+  const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+  bf16x8 r;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    r[2 * b] = (__bf16)__builtin_fmaf((float)((lo >> (8 * b)) & 0xffu), s, nzs);
+    r[2 * b + 1] = (__bf16)__builtin_fmaf((float)((hi >> (8 * b)) & 0xffu), s, nzs);
+  }
+  return r;
+}
+
+// {scale, -zero * scale} of a packed group word (bf16 scale bits 0..15, zero
+// point bits 16..19).
+__device__ __forceinline__ float2 q4_group(uint32_t sz) {
+  const float s = __builtin_bit_cast(float, sz << 16);
+  return make_float2(s, -(float)((sz >> 16) & 15u) * s);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int l = __lane_id();

@@ -113,7 +113,9 @@ __device__ __forceinline__ void barrier_after(void) {
 // and partial stores follow a fixed pattern (rows past N and tokens past T
 // land in the padding of `part`), so the loads' completion is counted
 // exactly.
-template <int NA>
+// WQ: the base weight is INT4 (a.Wq, a.Wsz); each W wave loads a quarter of
+// the bytes and dequantizes its fragments in registers before the MFMAs.
+template <int NA, bool WQ>
 __global__ __launch_bounds__(64 * (4 + NA)) void decode_main(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[64 * kXs];
   const int lane = threadIdx.x & 63;
@@ -219,7 +221,81 @@ __global__ __launch_bounds__(64 * (4 + NA)) void decode_main(DecodeArgs a) {
   // of a register block of kHalf / 32 steps starting at kh
   constexpr int kHalf = kDecodeChunk / 2, kHS = kHalf / 32;
 
-  if (!a_wave) {
+  if constexpr (WQ) {
+    if (!a_wave) {
+      const int ntile = (a.NT - bi + nbc - 1) / nbc;  // >= 1: the host keeps nbc <= NT
+      const int nhalf = 2 * ntile;
+      constexpr int kHG = kHalf / kQ4Group;  // groups per half (4)
+      const int KW = K / 8, KG = K / kQ4Group;
+      uint4 rq[2][kHG];     // per group: the lane's 4 words, one per 32-deep step
+      uint32_t rz[2][kHG];  // per group: {bf16 scale, zero point}
+      // reads past the end of Wq / Wsz return zeros; groups past the chunk
+      // are masked below
+      const __amdgpu_buffer_rsrc_t rqs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)a.Wq, (short)0, N * KW * 4, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rzs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)a.Wsz, (short)0, N * KG * 4, 0x00020000);
+      auto load = [&](uint4 (&bq)[kHG], uint32_t (&bz)[kHG], int s) __attribute__((always_inline)) {
+        const int sc = min(s, nhalf - 1);
+        const int n = (bi + (sc >> 1) * nbc) * kDecodeTileRows + 16 * w + r16;
+        const int nn = n < N ? n : 0;
+        const int g0 = (k0 + kHalf * (sc & 1)) / kQ4Group;
+        const int offq = (nn * KW + 16 * g0 + 4 * g4) * 4;
+        const int offz = (nn * KG + g0) * 4;
+#pragma unroll
+        for (int gi = 0; gi < kHG; ++gi)
+          bq[gi] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rqs, offq + 64 * gi, 0, 0));
+        // the half's four group words as one load (kHG + 1 loads per half in all)
+        const uint4 zz = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rzs, offz, 0, 0));
+        bz[0] = zz.x;
+        bz[1] = zz.y;
+        bz[2] = zz.z;
+        bz[3] = zz.w;
+      };
+      static_assert(kHG == 4, "one 16-byte load of group words per half");
+      load(rq[0], rz[0], 0);
+      // the X DMA (issued before these kHG + 1 loads) has landed in every wave
+      barrier_after<kHG + 1>();
+      auto phase = [&](auto hc, auto nc, int s) __attribute__((always_inline)) {
+        constexpr int H = decltype(hc)::value;
+        constexpr bool NEXT = decltype(nc)::value;
+        if constexpr (NEXT) load(rq[1 - H], rz[1 - H], s + 1);
+#pragma unroll
+        for (int gi = 0; gi < kHG; ++gi) {
+          const float2 g = q4_group(rz[H][gi]);
+          const uint32_t words[4] = {rq[H][gi].x, rq[H][gi].y, rq[H][gi].z, rq[H][gi].w};
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            const int k = kHalf * H + kQ4Group * gi + 32 * st + 8 * g4;
+            const bf16x8 wb = __builtin_bit_cast(
+                bf16x8, keep_if(k < klen, __builtin_bit_cast(uint4, dequant_q4x8(words[st], g.x, g.y))));
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+              acc[tb] = mfma16(wb, lds_bf16x8(xs + (16 * tb + r16) * kXs + k), acc[tb]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (H == 1) {
+          const int n = (bi + (s >> 1) * nbc) * kDecodeTileRows + 16 * w + 4 * g4;
+          float* pp = a.part + (size_t)c * 64 * a.npad + (size_t)r16 * a.npad + n;
+#pragma unroll
+          for (int tb = 0; tb < 4; ++tb) {
+            *reinterpret_cast<float4*>(pp + (size_t)(16 * tb) * a.npad) =
+                make_float4(acc[tb][0], acc[tb][1], acc[tb][2], acc[tb][3]);
+            acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+      };
+      for (int s = 0; s < nhalf - 2; s += 2) {
+        phase(std::integral_constant<int, 0>{}, std::true_type{}, s);
+        phase(std::integral_constant<int, 1>{}, std::true_type{}, s + 1);
+      }
+      phase(std::integral_constant<int, 0>{}, std::true_type{}, nhalf - 2);
+      phase(std::integral_constant<int, 1>{}, std::false_type{}, nhalf - 1);
+      return;
+    }
+  }
+  if (!WQ && !a_wave) {
     const int ntile = (a.NT - bi + nbc - 1) / nbc;  // >= 1: the host keeps nbc <= NT
     const int nhalf = 2 * ntile;
     uint4 rw[2][kHS];
@@ -517,7 +593,7 @@ hipError_t launch_decode(const DecodeArgs& args, int items, hipStream_t s) {
   // W blocks: every (tile, chunk) pair if the chip holds them at once, else
   // as many whole sets of KS chunk blocks as it holds (one block per compute
   // unit: the X chunk fills most of the LDS), each walking several tiles
-  const int resident = resident_blocks(reinterpret_cast<const void*>(&decode_main<0>), 256, 0);
+  const int resident = resident_blocks(reinterpret_cast<const void*>(&decode_main<0, false>), 256, 0);
   a.np = std::min(a.NT * a.KS, std::max(1, resident / a.KS) * a.KS);
   const int nbc = a.np / a.KS;
   a.na = 0;
@@ -530,16 +606,51 @@ hipError_t launch_decode(const DecodeArgs& args, int items, hipStream_t s) {
     a.a_tiles = (std::max(0, items - nbc * a.na) + 3 + a.na) / (4 + a.na);
   }
   const dim3 grid(a.np + a.a_tiles * a.KS);
-  switch (a.na) {
-    case 0: hipLaunchKernelGGL(decode_main<0>, grid, dim3(256), 0, s, a); break;
-    case 1: hipLaunchKernelGGL(decode_main<1>, grid, dim3(320), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(decode_main<2>, grid, dim3(384), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(decode_main<4>, grid, dim3(512), 0, s, a); break;
-    default: return hipErrorInvalidValue;
+  if (a.Wq) {
+    switch (a.na) {
+      case 0: hipLaunchKernelGGL((decode_main<0, true>), grid, dim3(256), 0, s, a); break;
+      case 1: hipLaunchKernelGGL((decode_main<1, true>), grid, dim3(320), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((decode_main<2, true>), grid, dim3(384), 0, s, a); break;
+      case 4: hipLaunchKernelGGL((decode_main<4, true>), grid, dim3(512), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (a.na) {
+      case 0: hipLaunchKernelGGL((decode_main<0, false>), grid, dim3(256), 0, s, a); break;
+      case 1: hipLaunchKernelGGL((decode_main<1, false>), grid, dim3(320), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((decode_main<2, false>), grid, dim3(384), 0, s, a); break;
+      case 4: hipLaunchKernelGGL((decode_main<4, false>), grid, dim3(512), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine, dim3((a.N + 63) / 64, (a.T + 15) / 16), dim3(kCombThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// INT4 -> bf16 weight for the batched path: one thread per packed word (eight
+// weights, one 16-byte store).
+__global__ void q4_dequant_kernel(const uint32_t* __restrict__ Wq, const uint32_t* __restrict__ Wsz, int N,
+                                  int K, uint16_t* __restrict__ W) {
+  const int KW = K / 8, KG = K / kQ4Group;
+  const size_t total = (size_t)N * KW;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (size_t)gridDim.x * blockDim.x) {
+    const int n = (int)(i / KW), p = (int)(i % KW);
+    const int g = p / 16, j = (p % 16) / 4, st = p % 4;
+    const float2 gz = q4_group(Wsz[(size_t)n * KG + g]);
+    const bf16x8 v = dequant_q4x8(Wq[i], gz.x, gz.y);
+    *reinterpret_cast<uint4*>(W + (size_t)n * K + kQ4Group * g + 32 * st + 8 * j) = __builtin_bit_cast(uint4, v);
+  }
+}
+
+hipError_t launch_q4_dequant(const uint32_t* Wq, const uint32_t* Wsz, int N, int K, uint16_t* W,
+                             hipStream_t s) {
+  const size_t total = (size_t)N * (K / 8);
+  const int grid = (int)std::min<size_t>((total + 255) / 256, 8192);
+  hipLaunchKernelGGL(q4_dequant_kernel, dim3(grid), dim3(256), 0, s, Wq, Wsz, N, K, W);
   return hipGetLastError();
 }
 

@@ -133,7 +133,21 @@ struct DecodeArgs {
   int32_t a_tiles;        // extra blocks of 4 + na A waves, per K chunk
   int32_t lora;
   int32_t module;         // index of the linear: an adapter whose id_info mask lacks it adds nothing
+  // INT4 base weight instead of W (the W waves dequantize in registers)
+  const uint32_t* Wq;     // [N][K/8] packed 4-bit weights (layout below), or nullptr
+  const uint32_t* Wsz;    // [N][K/128] {bf16 scale, zero point << 16}
 };
+
+// INT4 base weight layout (group size kQ4Group along K; K % kQ4Group == 0).
+// Word p of group g of row n (Wq[n][16 g + p], p = 4 j + s) holds the eight
+// weights k = 128 g + 32 s + 8 j + e, e = 0..7, nibble e at bits 4e..4e+3: a
+// lane that supplies k in [8 j, 8 j + 8) of the MFMA's 32-deep steps reads
+// the four steps of a group as one 16-byte load.  Wsz[n][g] = bf16 scale bits
+// | zero point << 16.  The weight is bf16((q - z) * scale).
+constexpr int kQ4Group = 128;
+// Dequantizes an INT4 weight into a bf16 [N][K] buffer (one launch).
+hipError_t launch_q4_dequant(const uint32_t* Wq, const uint32_t* Wsz, int N, int K, uint16_t* W,
+                             hipStream_t s);
 
 // Page layouts inside a slot (rows past the adapter's rank are zero):
 //   A page: A^T, rank-major [rmax][d_in]          (pack mode 0, src d_in x rank)

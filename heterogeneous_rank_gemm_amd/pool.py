@@ -88,3 +88,14 @@ class LoraPool:
 
     def paging_stats(self):
         return _lora.lora_paging_stats(self.handle)
+
+    # INT4 base weight
+    def apply_q4(self, module: int, X, ids, Wq, Wsz, out, W_scratch=None, plan: Optional[int] = None,
+                 stream=None, T: Optional[int] = None):
+        T = X.shape[0] if T is None else T
+        _lora.lora_apply_q4(self.handle, module, X, ids, T, Wq, Wsz, W_scratch, out, plan, stream)
+
+    def base_apply_q4(self, module: int, X, Wq, Wsz, out, W_scratch=None, stream=None,
+                      T: Optional[int] = None):
+        T = X.shape[0] if T is None else T
+        _lora.lora_base_apply_q4(self.handle, module, X, T, Wq, Wsz, W_scratch, out, stream)

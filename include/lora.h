@@ -193,6 +193,43 @@ lora_status_t lora_base_apply(lora_pool_t pool, int32_t module, const lora_bf16_
                               const lora_bf16_t* W, lora_bf16_t* out, hipStream_t stream);
 
 /*
+ * INT4 base weight ([vLLM-ch7] performance notes: an AWQ-INT4 base with bf16
+ * adapters).  The frozen base weight is stored group-wise in 4 bits along
+ * d_in: groups of 128, q and the zero point z in 0..15, a bf16 scale s per
+ * (output row, group), and the GEMM uses W[n, k] = bf16((q - z) * s).  The
+ * adapters stay bf16.  d_in must be a multiple of 128.
+ *
+ * lora_q4_pack -- host-side packing into the device layout.
+ *   q    host uint8 [N][K], values 0..15 (row n = output feature)
+ *   z    host uint8 [N][K/128], values 0..15
+ *   s    host bf16 bits [N][K/128]
+ *   Wq   host out uint32 [N][K/8]: word 16 g + 4 j + st of row n holds the
+ *        weights k = 128 g + 32 st + 8 j + e, e = 0..7, in bits 4e..4e+3
+ *   Wsz  host out uint32 [N][K/128]: s bits | z << 16
+ * INVALID_ARG on a null pointer, K not a multiple of 128, or a value > 15.
+ */
+lora_status_t lora_q4_pack(const uint8_t* q, const uint8_t* z, const lora_bf16_t* s, int32_t N,
+                           int32_t K, uint32_t* Wq, uint32_t* Wsz);
+
+/*
+ * lora_apply_q4 / lora_base_apply_q4 -- lora_apply / lora_base_apply with the
+ * packed INT4 base weight (Wq, Wsz: caller-owned device buffers in the layout
+ * above, d_out x d_in of module `module`).  At T <= 64 the decode kernel
+ * dequantizes the weight in registers (a quarter of the bf16 weight's bytes);
+ * at larger T the call first dequantizes it into W_scratch (caller-owned
+ * device buffer of d_out x d_in bf16, required then, else may be NULL) and
+ * runs the bf16 GEMM on it.  Other arguments, errors and guarantees as
+ * lora_apply / lora_base_apply (id -1 rows equal lora_base_apply_q4's bit for
+ * bit).  INVALID_ARG if d_in % 128 != 0.
+ */
+lora_status_t lora_apply_q4(lora_pool_t pool, int32_t module, const lora_bf16_t* X, const int32_t* ids,
+                            int32_t T, const uint32_t* Wq, const uint32_t* Wsz, lora_bf16_t* W_scratch,
+                            lora_bf16_t* out, lora_plan_t plan, hipStream_t stream);
+lora_status_t lora_base_apply_q4(lora_pool_t pool, int32_t module, const lora_bf16_t* X, int32_t T,
+                                 const uint32_t* Wq, const uint32_t* Wsz, lora_bf16_t* W_scratch,
+                                 lora_bf16_t* out, hipStream_t stream);
+
+/*
  * lora_status -- synchronise `stream`, return the pool's sticky device
  * status (OK, NOT_LOADED or ID_RANGE; ID_RANGE wins if both occurred) and
  * clear it.

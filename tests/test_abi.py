@@ -88,3 +88,27 @@ def test_package_fails_loudly_without_library(tmp_path, monkeypatch):
     mod = importlib.util.module_from_spec(spec)
     with pytest.raises(ImportError):
         spec.loader.exec_module(mod)
+
+
+def test_q4_pack_layout():
+    """The host-side INT4 packer (no GPU call) writes the layout lora.h
+    documents: word 16 g + 4 j + st of a row holds k = 128 g + 32 st + 8 j + e
+    in nibble e; the group word is the bf16 scale bits | zero point << 16."""
+    import numpy as np
+    import heterogeneous_rank_gemm_amd as hrg
+    g = np.random.default_rng(0)
+    N, K = 3, 384
+    q = g.integers(0, 16, (N, K))
+    z = g.integers(0, 16, (N, K // 128))
+    s = g.integers(0, 65535, (N, K // 128)).astype(np.uint16)
+    Wq, Wsz = hrg.lora_q4_pack(q, z, s)
+    for n in range(N):
+        for k in range(K):
+            gg, st, j, e = k // 128, (k % 128) // 32, (k % 32) // 8, k % 8
+            assert (int(Wq[n, 16 * gg + 4 * j + st]) >> (4 * e)) & 15 == q[n, k]
+        for gg in range(K // 128):
+            assert int(Wsz[n, gg]) == int(s[n, gg]) | (int(z[n, gg]) << 16)
+    with pytest.raises(hrg.LoraError):
+        hrg.lora_q4_pack(np.full((1, 128), 16), np.zeros((1, 1)), np.zeros((1, 1), np.uint16))
+    with pytest.raises(hrg.LoraError):
+        hrg.lora_q4_pack(np.zeros((1, 200)), np.zeros((1, 1)), np.zeros((1, 1), np.uint16))
