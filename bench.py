@@ -47,9 +47,11 @@ METRIC = "LoRA-linear tokens/sec at 1 GPU; % overhead vs base-only GEMM; % roofl
 # ---------------------------------------------------------------------------
 # algorithmic work (bytes and flops that the definition must touch)
 # ---------------------------------------------------------------------------
-def base_bytes(T: int, d_in: int, d_out: int) -> int:
-    """W once, X once, out once (bf16)."""
-    return 2 * (d_in * d_out + T * d_in + T * d_out)
+def base_bytes(T: int, d_in: int, d_out: int, int4: bool = False) -> int:
+    """W once, X once, out once (bf16); an INT4 weight is half a byte per
+    weight plus one 4-byte group word per 128 weights."""
+    w = d_in * d_out // 2 + d_out * (d_in // 128) * 4 if int4 else 2 * d_in * d_out
+    return w + 2 * (T * d_in + T * d_out)
 
 
 def lora_bytes(ids: np.ndarray, ranks: np.ndarray, d_in: int, d_out: int) -> int:
@@ -68,12 +70,12 @@ def extra_flop_fraction(rank: int, d_in: int, d_out: int) -> float:
     return rank * (d_in + d_out) / (d_in * d_out)
 
 
-def step_work(wl: wk.Workload, ids: np.ndarray, ranks: np.ndarray):
+def step_work(wl: wk.Workload, ids: np.ndarray, ranks: np.ndarray, int4: bool = False):
     """(base bytes, lora bytes, flops, t_roof seconds) of one step."""
     bb = lb = fl = 0
     t_roof = 0.0
     for m in wl.modules:
-        b1 = base_bytes(ids.shape[0], m.d_in, m.d_out)
+        b1 = base_bytes(ids.shape[0], m.d_in, m.d_out, int4)
         l1 = lora_bytes(ids, ranks, m.d_in, m.d_out)
         f1 = flops(ids, ranks, m.d_in, m.d_out)
         bb += b1
@@ -86,10 +88,26 @@ def step_work(wl: wk.Workload, ids: np.ndarray, ranks: np.ndarray):
 # ---------------------------------------------------------------------------
 # GPU set-up
 # ---------------------------------------------------------------------------
+def q4_weight(wl: wk.Workload, module: int, seed: int, torch):
+    """A synthetic INT4 base weight of the module's shape in the device layout:
+    random 4-bit codes (every 32-bit word is eight valid codes), zero points in
+    4..11 and bf16 scales ~ |N(0.0045, 0.001)| (so the dequantized weight has a
+    standard deviation near 0.02, like the bf16 weights)."""
+    m = wl.modules[module]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wk.derive_seed(wl.key, seed, "q4", module) & 0x7FFFFFFF)
+    Wq = torch.randint(-2 ** 31, 2 ** 31 - 1, (m.d_out, m.d_in // 8), generator=g, device="cuda",
+                       dtype=torch.int64).to(torch.int32)
+    s = (torch.randn((m.d_out, m.d_in // 128), generator=g, device="cuda") * 0.001 + 0.0045).abs()
+    sbits = s.to(torch.bfloat16).view(torch.int16).to(torch.int32) & 0xFFFF
+    z = torch.randint(4, 12, (m.d_out, m.d_in // 128), generator=g, device="cuda", dtype=torch.int32)
+    return Wq, (sbits | (z << 16)).contiguous()
+
+
 class Replica:
     """One independent copy of the workload's resident state."""
 
-    def __init__(self, wl: wk.Workload, seed: int, torch, hrg):
+    def __init__(self, wl: wk.Workload, seed: int, torch, hrg, int4: bool = False):
         self.ids_np = wk.adapter_ids(wl, seed)
         self.ranks = wk.adapter_ranks(wl, seed)
         self.T = wl.T
@@ -110,7 +128,15 @@ class Replica:
         for m in mods:
             if m.input_group not in self.X:
                 self.X[m.input_group] = wk.activation(wl, m.input_group, m.d_in, seed, "cuda")
-        self.W = [wk.base_weight(wl, j, seed, "cuda") for j in range(len(mods))]
+        self.int4 = int4
+        if int4:
+            self.W = None
+            self.Wq = [q4_weight(wl, j, seed, torch) for j in range(len(mods))]
+            big = max(m.d_in * m.d_out for m in mods)
+            self.scratch = torch.empty(big, dtype=torch.bfloat16, device="cuda") \
+                if wl.T > DECODE_MAX_T else None
+        else:
+            self.W = [wk.base_weight(wl, j, seed, "cuda") for j in range(len(mods))]
         self.out = [torch.empty((wl.T, m.d_out), dtype=torch.bfloat16, device="cuda")
                     for m in mods]
         self.xin = [self.X[m.input_group] for m in mods]
@@ -124,28 +150,38 @@ class Replica:
 DECODE_MAX_T = 64
 
 
+def _apply(rep: Replica, hrg, j: int, plan):
+    if rep.int4:
+        hrg.lora_apply_q4(rep.pool.handle, j, rep.xin[j], rep.ids, rep.T, rep.Wq[j][0], rep.Wq[j][1],
+                          rep.scratch, rep.out[j], plan)
+    else:
+        hrg.lora_apply(rep.pool.handle, j, rep.xin[j], rep.ids, rep.T, rep.W[j], rep.out[j], plan)
+
+
 def lora_step(rep: Replica, hrg):
-    h = rep.pool.handle
     plan = None
     if rep.T > DECODE_MAX_T:
-        hrg.lora_plan(h, rep.ids, rep.T, rep.plan)
+        hrg.lora_plan(rep.pool.handle, rep.ids, rep.T, rep.plan)
         plan = rep.plan
-    for j in range(len(rep.W)):
-        hrg.lora_apply(h, j, rep.xin[j], rep.ids, rep.T, rep.W[j], rep.out[j], plan)
+    for j in range(len(rep.out)):
+        _apply(rep, hrg, j, plan)
 
 
 def apply_only(rep: Replica, hrg):
     """The step without its plan launch (identical to lora_step at decode)."""
-    h = rep.pool.handle
     plan = rep.plan if rep.T > DECODE_MAX_T else None
-    for j in range(len(rep.W)):
-        hrg.lora_apply(h, j, rep.xin[j], rep.ids, rep.T, rep.W[j], rep.out[j], plan)
+    for j in range(len(rep.out)):
+        _apply(rep, hrg, j, plan)
 
 
 def base_step(rep: Replica, hrg):
     h = rep.pool.handle
-    for j in range(len(rep.W)):
-        hrg.lora_base_apply(h, j, rep.xin[j], rep.T, rep.W[j], rep.out[j])
+    for j in range(len(rep.out)):
+        if rep.int4:
+            hrg.lora_base_apply_q4(h, j, rep.xin[j], rep.T, rep.Wq[j][0], rep.Wq[j][1], rep.scratch,
+                                   rep.out[j])
+        else:
+            hrg.lora_base_apply(h, j, rep.xin[j], rep.T, rep.W[j], rep.out[j])
 
 
 def measured_traffic(workload_name: str):
@@ -355,6 +391,8 @@ def main(argv=None) -> int:
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (x steps), to scale "
                          "the rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--int4", action="store_true",
+                    help="INT4 (group 128) base weights instead of bf16 (lora_apply_q4)")
     ap.add_argument("--paging", action="store_true",
                     help="measure host-cache paging instead (prints its own JSON line)")
     ap.add_argument("--paging-slots", type=int, default=64, help="device slots of the paged pool")
@@ -385,7 +423,7 @@ def main(argv=None) -> int:
     wl = wk.WORKLOADS[args.workload]
     R = 1 if wl.key == 5 else max(1, args.rotate)
     print(f"[bench] workload {wl.key} '{wl.name}', {R} replica(s)", file=sys.stderr, flush=True)
-    reps = [Replica(wl, wl.default_seed + 1000 * r if r else wl.default_seed, torch, hrg)
+    reps = [Replica(wl, wl.default_seed + 1000 * r if r else wl.default_seed, torch, hrg, args.int4)
             for r in range(R)]
     torch.cuda.synchronize()
     print("[bench] state resident; timing", file=sys.stderr, flush=True)
@@ -414,7 +452,7 @@ def main(argv=None) -> int:
         if st != "OK":
             raise RuntimeError(f"device status {st}")
 
-    works = [step_work(wl, rp.ids_np, rp.ranks) for rp in reps]
+    works = [step_work(wl, rp.ids_np, rp.ranks, args.int4) for rp in reps]
     bb = float(np.mean([w[0] for w in works]))
     lb = float(np.mean([w[1] for w in works]))
     fl = float(np.mean([w[2] for w in works]))
@@ -423,7 +461,7 @@ def main(argv=None) -> int:
     hbm_bound = (bb + lb) / (HBM_PEAK_GBS * 1e9) >= fl / (MFMA_BF16_PEAK_TFS * 1e12)
     if hbm_bound:
         achieved = (bb + lb) / n_launch / (t_apply / n_launch) / 1e9
-        traffic = measured_traffic(wl.name) if wl.T <= DECODE_MAX_T else None
+        traffic = measured_traffic(wl.name) if wl.T <= DECODE_MAX_T and not args.int4 else None
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": "lora_apply = decode_main + decode_combine" if wl.T <= DECODE_MAX_T
@@ -437,7 +475,7 @@ def main(argv=None) -> int:
                 "algorithmic_flops_per_apply": round(fl / n_launch)}
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.int4:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
         cpu = cpu_baseline(wl, reps[0], args.cpu_seconds, torch)
 
@@ -452,13 +490,14 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16 (int4 base weight)" if args.int4 else "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T,
                    "modules": [[m.d_in, m.d_out] for m in wl.modules[:7]],
                    "n_linears": len(wl.modules), "adapters": wl.n_adapters,
                    "ranks": list(wl.rank_choices), "max_rank": wl.max_rank,
-                   "replicas_rotated": R, "hipgraph": use_graph},
+                   "replicas_rotated": R, "hipgraph": use_graph,
+                   "base_weight": "int4-g128" if args.int4 else "bf16"},
         "lora_overhead_pct": round(100.0 * (t_step - t_base) / t_base, 2),
         "base_only_ms_per_step": round(t_base * 1e3, 5),
         "apply_ms_per_step": round(t_apply * 1e3, 5),

@@ -53,15 +53,24 @@ __device__ __forceinline__ int lane_id() { return __lane_id(); }
 // bf16((q - z) * s), given s and -z * s in fp32.  q * s and z * s are exact
 // in fp32 (a bf16 scale times a 4-bit integer), so the fma is exact and the
 // only rounding is the conversion to bf16 (to nearest even).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ bf16x8 dequant_q4x8(uint32_t w, float s, float nzs) {
-  const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
-  bf16x8 r;
+  uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
+  // opaque to the optimizer, so that byte b converts with one
+  // v_cvt_f32_ubyte<b> instead of a bit-field extract plus a conversion
+  asm volatile("" : "+v"(lo), "+v"(hi));
+  uint32_t p[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
-    r[2 * b] = (__bf16)__builtin_fmaf((float)((lo >> (8 * b)) & 0xffu), s, nzs);
-    r[2 * b + 1] = (__bf16)__builtin_fmaf((float)((hi >> (8 * b)) & 0xffu), s, nzs);
+    // elements 2b (nibble 2b, byte b of lo) and 2b + 1 (byte b of hi): one
+    // packed conversion
+    const f32x2_t v = {__builtin_fmaf((float)((lo >> (8 * b)) & 0xffu), s, nzs),
+                       __builtin_fmaf((float)((hi >> (8 * b)) & 0xffu), s, nzs)};
+    p[b] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
   }
-  return r;
+  return __builtin_bit_cast(bf16x8, make_uint4(p[0], p[1], p[2], p[3]));
 }
 
 // {scale, -zero * scale} of a packed group word (bf16 scale bits 0..15, zero

@@ -262,13 +262,17 @@ __global__ __launch_bounds__(64 * (4 + NA)) void decode_main(DecodeArgs a) {
         if constexpr (NEXT) load(rq[1 - H], rz[1 - H], s + 1);
 #pragma unroll
         for (int gi = 0; gi < kHG; ++gi) {
-          const float2 g = q4_group(rz[H][gi]);
+          // a group past the chunk (klen is a multiple of the group) gets
+          // scale 0 and offset 0: its weights dequantize to exact zeros
+          const bool in = kHalf * H + kQ4Group * gi < klen;
+          float2 g = q4_group(rz[H][gi]);
+          g.x = in ? g.x : 0.f;
+          g.y = in ? g.y : 0.f;
           const uint32_t words[4] = {rq[H][gi].x, rq[H][gi].y, rq[H][gi].z, rq[H][gi].w};
 #pragma unroll
           for (int st = 0; st < 4; ++st) {
             const int k = kHalf * H + kQ4Group * gi + 32 * st + 8 * g4;
-            const bf16x8 wb = __builtin_bit_cast(
-                bf16x8, keep_if(k < klen, __builtin_bit_cast(uint4, dequant_q4x8(words[st], g.x, g.y))));
+            const bf16x8 wb = dequant_q4x8(words[st], g.x, g.y);
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb)
               acc[tb] = mfma16(wb, lds_bf16x8(xs + (16 * tb + r16) * kXs + k), acc[tb]);
