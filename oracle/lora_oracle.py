@@ -164,6 +164,38 @@ class Registry:
             raise OracleError(NOT_LOADED, f"id {adapter_id}")
         del self.adapters[adapter_id]
 
+    def load_chain(self, chain_id: int, members: Sequence[int]) -> None:
+        """A chain of loaded adapters under a new id ([LoRA-Land] "technical
+        approach", item 3: LoRAs composed like a pipeline and applied in turn;
+        section "3. hot-plug API and composition": set_adaptive_chain).  At a
+        linear layer every member adds its own update, so the chain's term is
+        the sum of the members' terms.  The members are snapshotted: unloading
+        one later leaves the chain intact.  Limits: ids in range and loaded
+        (NOT_LOADED), no repeats and no chains as members (INVALID_ARG), the
+        members' 16-rank blocks fit the pool's max rank (RANK)."""
+        if not (0 <= chain_id < self.max_ids):
+            raise OracleError(ID_RANGE, f"id {chain_id}")
+        members = [int(i) for i in members]
+        if not members or len(set(members)) != len(members):
+            raise OracleError(INVALID_ARG, "members: at least one, no repeats")
+        for i in members:
+            if not (0 <= i < self.max_ids):
+                raise OracleError(ID_RANGE, f"member {i}")
+        for i in members:
+            if i not in self.adapters:
+                raise OracleError(NOT_LOADED, f"member {i}")
+            if isinstance(self.adapters[i], Chain):
+                raise OracleError(INVALID_ARG, f"member {i} is a chain")
+        ranks = [self.adapters[i].rank for i in members]
+        # each member but the last fills whole 16-rank blocks
+        if sum(16 * ((r + 15) // 16) for r in ranks[:-1]) + ranks[-1] > self.max_rank:
+            raise OracleError(RANK, f"chain ranks {ranks} exceed max rank {self.max_rank}")
+        if chain_id in self.adapters:
+            raise OracleError(EXISTS, f"id {chain_id}")
+        if len(self.adapters) >= self.max_adapters:
+            raise OracleError(POOL_FULL, "no free slot")
+        self.adapters[chain_id] = Chain([self.adapters[i] for i in members])
+
     def validate_ids(self, ids: np.ndarray) -> None:
         """Strict mode: every id is -1 or a loaded adapter; else the call fails.
         An out-of-range id is reported before an unloaded one."""
@@ -176,6 +208,32 @@ class Registry:
             i = int(ids[t])
             if i >= 0 and i not in self.adapters:
                 raise OracleError(NOT_LOADED, f"token {t} id {i}")
+
+
+class Chain:
+    """Several adapters on one id: the sum of their low-rank terms."""
+    __slots__ = ("members",)
+
+    def __init__(self, members: List[Adapter]):
+        self.members = list(members)
+
+
+def _lora_term(ad, module: int, x: np.ndarray, cols=None) -> Optional[np.ndarray]:
+    """s (x A) B of one adapter (x: one token row), the sum over a chain's
+    members, or None when nothing targets the module."""
+    if isinstance(ad, Chain):
+        terms = [t for t in (_lora_term(m, module, x, cols) for m in ad.members) if t is not None]
+        if not terms:
+            return None
+        acc = terms[0].copy()
+        for t in terms[1:]:
+            acc += t
+        return acc
+    if ad.A[module] is None:
+        return None                                 # not a target of this adapter
+    u = x @ ad.A[module]                            # shrink: d_in -> r
+    B = ad.B[module] if cols is None else ad.B[module][:, cols]
+    return ad.scale * (u @ B)                       # expand r -> d_out, scale
 
 
 def _as_f64(x) -> np.ndarray:
@@ -268,11 +326,9 @@ def lora_linear(reg: Registry, module: int, X, ids, W) -> np.ndarray:
         i = int(ids[t])
         if i < 0:
             continue                                # base only: no LoRA term
-        ad = reg.adapters[i]
-        if ad.A[module] is None:
-            continue                                # not a target of this adapter
-        u = Xf[t, :] @ ad.A[module]                 # shrink: d_in -> r
-        Y[t, :] += ad.scale * (u @ ad.B[module])    # expand r -> d_out, scale, add
+        term = _lora_term(reg.adapters[i], module, Xf[t, :])
+        if term is not None:                        # None: not a target of this adapter
+            Y[t, :] += term                         # added back onto the main path
     return Y
 
 
@@ -291,11 +347,9 @@ def lora_linear_sampled(reg: Registry, module: int, X_rows, ids_rows, W_cols,
         i = int(ids_rows[n])
         if i < 0:
             continue
-        ad = reg.adapters[i]
-        if ad.A[module] is None:
-            continue
-        u = Xf[n, :] @ ad.A[module]
-        Y[n, :] += ad.scale * (u @ ad.B[module][:, cols])
+        term = _lora_term(reg.adapters[i], module, Xf[n, :], cols)
+        if term is not None:
+            Y[n, :] += term
     return Y
 
 

@@ -461,3 +461,55 @@ def test_dequant_q4_against_elementwise_definition():
     assert not oracle.dequant_q4(q2, np.array([[9]]), _bf16([[0.5]])).any()
     np.testing.assert_array_equal(oracle.dequant_q4(np.arange(128).reshape(1, 128) % 16, np.array([[0]]),
                                                     _bf16([[1.0]]))[0], np.arange(128) % 16)
+
+
+def test_chain_is_the_sum_of_its_members():
+    """A chain ([LoRA-Land] set_adaptive_chain) adds each member's update: its
+    term equals the members' terms computed one adapter at a time, the merged
+    weight W + sum_c s_c (A_c B_c)^T by loops, and a chain of one adapter
+    equals that adapter."""
+    g = np.random.default_rng(8)
+    d_in, d_out, T = 6, 5, 6
+    reg = Registry(8, 8, 48, [d_in], [d_out], T)
+    params = {0: (3, 6.0), 1: (5, 7.5), 2: (16, 32.0)}
+    mats = {}
+    for i, (r, al) in params.items():
+        A = np.round(g.standard_normal((d_in, r)) * 8) / 8
+        B = np.round(g.standard_normal((r, d_out)) * 8) / 8
+        mats[i] = (A, B, al / r)
+        reg.load(i, r, al, [A], [B])
+    reg.load_chain(5, [0, 1, 2])
+    reg.load_chain(6, [2, 0])
+    reg.load_chain(7, [1])
+    X = np.round(g.standard_normal((T, d_in)) * 4) / 4
+    W = np.round(g.standard_normal((d_out, d_in)) * 4) / 4
+    Y0 = X @ W.T
+    single = {i: oracle.lora_linear(reg, 0, X, np.full(T, i), W) - Y0 for i in params}
+    Yc = oracle.lora_linear(reg, 0, X, np.full(T, 5), W)
+    np.testing.assert_allclose(Yc - Y0, single[0] + single[1] + single[2], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(oracle.lora_linear(reg, 0, X, np.full(T, 6), W) - Y0,
+                               single[2] + single[0], rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(oracle.lora_linear(reg, 0, X, np.full(T, 7), W),
+                                  oracle.lora_linear(reg, 0, X, np.full(T, 1), W))
+    Wm = [[W[j][k] + sum(mats[i][2] * sum(mats[i][0][k][q] * mats[i][1][q][j]
+                                           for q in range(params[i][0])) for i in (0, 1, 2))
+           for k in range(d_in)] for j in range(d_out)]
+    for t in range(T):
+        for j in range(d_out):
+            ref = sum(X[t][k] * Wm[j][k] for k in range(d_in))
+            assert abs(Yc[t, j] - ref) <= 1e-9 * (1 + abs(ref))
+    # the chain is a snapshot: unloading a member leaves it intact
+    reg.unload(0)
+    np.testing.assert_array_equal(oracle.lora_linear(reg, 0, X, np.full(T, 5), W), Yc)
+    for members, status in [([1, 1], oracle.INVALID_ARG), ([], oracle.INVALID_ARG),
+                            ([0, 1], oracle.NOT_LOADED), ([5, 1], oracle.INVALID_ARG),
+                            ([2, 2 + 0], oracle.INVALID_ARG), ([9], oracle.ID_RANGE)]:
+        with pytest.raises(OracleError) as e:
+            reg.load_chain(3, members)
+        assert e.value.status == status, members
+    reg.load(3, 16, 32.0, [np.ones((d_in, 16))], [np.ones((16, d_out))])
+    reg.load(0, 16, 32.0, [np.ones((d_in, 16))], [np.ones((16, d_out))])
+    with pytest.raises(OracleError) as e:
+        reg.load_chain(4, [2, 3, 0, 1])                       # 16 + 16 + 16 + 5 = 53 > 48
+    assert e.value.status == oracle.RANK
+    reg.load_chain(4, [2, 3, 1])                              # 16 + 16 + 5 = 37 fits
