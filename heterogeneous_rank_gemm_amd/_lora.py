@@ -30,7 +30,7 @@ EXPORTED = (
     "lora_plan", "lora_apply", "lora_base_apply", "lora_status", "lora_debug_read_plan",
     "lora_host_cache_create", "lora_host_register", "lora_host_unregister", "lora_prefetch",
     "lora_pin_adapter", "lora_paging_query", "lora_paging_stats", "lora_q4_pack", "lora_apply_q4",
-    "lora_base_apply_q4",
+    "lora_base_apply_q4", "lora_load_chain",
 )
 
 _vp = C.c_void_p
@@ -62,6 +62,7 @@ _sigs = {
     "lora_q4_pack": [_vp, _vp, _vp, _i32, _i32, _vp, _vp],
     "lora_apply_q4": [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp],
     "lora_base_apply_q4": [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp],
+    "lora_load_chain": [_vp, _i32, _i32, _P_i32, _vp],
 }
 for _name, _args in _sigs.items():
     _f = getattr(_lib, _name)
@@ -273,3 +274,9 @@ def lora_base_apply_q4(pool: int, module: int, X, T: int, Wq, Wsz, W_scratch, ou
                        stream=None) -> None:
     _check(_lib.lora_base_apply_q4(pool, module, _ptr(X), T, _ptr(Wq), _ptr(Wsz), _ptr(W_scratch),
                                    _ptr(out), _stream(stream)), "lora_base_apply_q4")
+
+
+def lora_load_chain(pool: int, chain_id: int, members: Sequence[int], stream=None) -> None:
+    vals = [int(i) for i in members]
+    arr = (C.c_int32 * max(len(vals), 1))(*vals)
+    _check(_lib.lora_load_chain(pool, chain_id, len(vals), arr, _stream(stream)), "lora_load_chain")

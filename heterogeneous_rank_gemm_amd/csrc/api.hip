@@ -41,7 +41,9 @@ lora_status_t plan_alloc(lora_pool_s* P, lora_plan_s** out) {
   // perm, inv, row_seg, erow (Tc each); seg_id, seg_slot, seg_rank, seg_scale,
   // seg_e0 (Tc+1); seg_off (Tc+2); tile_info (4 mt) and small_info
   // (4 kMaxSmallRows), first: 16-byte aligned; counts (4)
-  const size_t n32 = 4 * Tc + 5 * (Tc + 1) + (Tc + 2) + 4 * (size_t)mt + 4 * (size_t)hrg::kMaxSmallRows + 4;
+  // seg_bscale (4 (Tc+1)) and small_bscale (4 kMaxSmallRows), 16-byte aligned, after the int4 tables
+  const size_t n32 = 4 * Tc + 5 * (Tc + 1) + (Tc + 2) + 4 * (size_t)mt + 4 * (size_t)hrg::kMaxSmallRows +
+                     4 * (Tc + 1) + 4 * (size_t)hrg::kMaxSmallRows + 4;
   lora_plan_s* pl = new (std::nothrow) lora_plan_s();
   if (!pl) return LORA_ERR_OOM;
   int32_t* blk = nullptr;
@@ -55,6 +57,8 @@ lora_status_t plan_alloc(lora_pool_s* P, lora_plan_s** out) {
   auto take = [&](size_t n) { int32_t* r = c; c += n; return r; };
   pl->tab.tile_info = reinterpret_cast<int4*>(take(4 * (size_t)mt));
   pl->tab.small_info = reinterpret_cast<int4*>(take(4 * (size_t)hrg::kMaxSmallRows));
+  pl->tab.seg_bscale = reinterpret_cast<float4*>(take(4 * (Tc + 1)));
+  pl->tab.small_bscale = reinterpret_cast<float4*>(take(4 * (size_t)hrg::kMaxSmallRows));
   pl->tab.perm = take(Tc);
   pl->tab.inv = take(Tc);
   pl->tab.row_seg = take(Tc);
@@ -83,6 +87,7 @@ lora_status_t run_plan(lora_pool_s* P, const int32_t* ids, int32_t T, lora_plan_
   a.T = T;
   a.max_ids = P->max_ids;
   a.id_info = P->id_info;
+  a.id_bscale = P->id_bscale;
   a.status = P->status;
   a.tab = pl->tab;
   if (hrg::launch_plan(a, s) != hipSuccess) return LORA_ERR_HIP;
@@ -107,6 +112,7 @@ lora_status_t decode_apply(lora_pool_s* P, int32_t module, const lora_bf16_t* X,
   a.K = K;
   a.max_ids = P->max_ids;
   a.id_info = P->id_info;
+  a.id_bscale = P->id_bscale;
   a.pages = P->pages;
   a.slot_stride = P->slot_elems;
   a.a_off = P->a_off[module];
@@ -194,6 +200,7 @@ lora_status_t lora_pool_create(lora_pool_t* pool, int32_t max_adapters, int32_t 
             dmalloc(&P->slot_rank, max_adapters) == hipSuccess &&
             dmalloc(&P->slot_scale, max_adapters) == hipSuccess &&
             dmalloc(&P->id_info, max_ids) == hipSuccess &&
+            dmalloc(&P->id_bscale, max_ids) == hipSuccess &&
             dmalloc(&P->status, 4) == hipSuccess &&
             dmalloc(&P->staging, max_dim * max_rank) == hipSuccess &&
             dmalloc(&P->upart, (size_t)hrg::kMaxSplits * P->split_stride) == hipSuccess &&
@@ -218,11 +225,13 @@ lora_status_t lora_pool_create(lora_pool_t* pool, int32_t max_adapters, int32_t 
   }
   P->h_id2slot.assign(max_ids, -1);
   P->h_mask.assign(max_ids, 0);
+  P->h_chain.assign(max_ids, 0);
   P->h_slot_rank.assign(max_adapters, 0);
   P->h_slot_scale.assign(max_adapters, 0.f);
   for (int32_t i = 0; i < max_adapters; ++i) P->free_slots.insert(i);
   if (hrg::launch_clear_i32(P->id2slot, max_ids, -1, stream) != hipSuccess ||
       hrg::launch_clear_i32(reinterpret_cast<int32_t*>(P->id_info), 4 * max_ids, -1, stream) != hipSuccess ||
+      hrg::launch_clear_i32(reinterpret_cast<int32_t*>(P->id_bscale), 4 * max_ids, 0, stream) != hipSuccess ||
       hrg::launch_clear_i32(P->slot_rank, max_adapters, 0, stream) != hipSuccess ||
       hrg::launch_clear_i32(reinterpret_cast<int32_t*>(P->slot_scale), max_adapters, 0, stream) != hipSuccess ||
       hrg::launch_clear_i32(P->status, 4, 0, stream) != hipSuccess ||
@@ -246,6 +255,7 @@ lora_status_t lora_pool_destroy(lora_pool_t P) {
   (void)hipFree(P->slot_rank);
   (void)hipFree(P->slot_scale);
   (void)hipFree(P->id_info);
+  (void)hipFree(P->id_bscale);
   (void)hipFree(P->status);
   (void)hipFree(P->staging);
   (void)hipFree(P->upart);
@@ -301,8 +311,8 @@ lora_status_t lora_load_adapter(lora_pool_t P, int32_t id, int32_t rank, float a
     if (hrg::launch_pack(pa, stream) != hipSuccess) return LORA_ERR_HIP;
   }
   const float scale = alpha / (float)rank;
-  if (hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, id, slot, rank, scale, mask,
-                           stream) !=
+  if (hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, P->id_bscale, id, slot, rank,
+                           scale, mask, make_float4(scale, scale, scale, scale), stream) !=
           hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess) {
     (void)hipGetLastError();
@@ -325,16 +335,88 @@ lora_status_t lora_unload_adapter(lora_pool_t P, int32_t id, hipStream_t stream)
   if (slot < 0) return LORA_ERR_NOT_LOADED;
   DeviceGuard g(P->device);
   if (hipStreamSynchronize(stream) != hipSuccess ||
-      hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, id, -1, 0, 0.f, 0, stream) !=
-          hipSuccess ||
+      hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, P->id_bscale, id, -1, 0, 0.f, 0,
+                           make_float4(0.f, 0.f, 0.f, 0.f), stream) != hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess) {
     (void)hipGetLastError();
     return LORA_ERR_HIP;
   }
   P->h_id2slot[id] = -1;
+  P->h_chain[id] = 0;
   P->h_slot_rank[slot] = 0;
   P->h_slot_scale[slot] = 0.f;
   P->free_slots.insert(slot);
+  return LORA_OK;
+}
+
+lora_status_t lora_load_chain(lora_pool_t P, int32_t chain_id, int32_t n, const int32_t* members,
+                              hipStream_t stream) {
+  if (!P) return LORA_ERR_INVALID_ARG;
+  if (chain_id < 0 || chain_id >= P->max_ids) return LORA_ERR_ID_RANGE;
+  if (n < 1 || !members) return LORA_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i)
+    for (int32_t j = 0; j < i; ++j)
+      if (members[i] == members[j]) return LORA_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i)
+    if (members[i] < 0 || members[i] >= P->max_ids) return LORA_ERR_ID_RANGE;
+  for (int32_t i = 0; i < n; ++i) {
+    if (P->h_id2slot[members[i]] < 0) return LORA_ERR_NOT_LOADED;
+    if (P->h_chain[members[i]]) return LORA_ERR_INVALID_ARG;
+  }
+  // every member takes at least one 16-rank block, and max_rank <= 64
+  if (n > hrg::kMaxRank / 16) return LORA_ERR_RANK;
+  // member c takes the 16-rank blocks [blk[c], blk[c] + nb[c]) of the chain's pages
+  int32_t blk[4], nb[4], total = 0, rank = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t r = P->h_slot_rank[P->h_id2slot[members[i]]];
+    blk[i] = total;
+    nb[i] = (r + 15) / 16;
+    rank = 16 * total + r;
+    total += nb[i];
+  }
+  if (rank > P->max_rank) return LORA_ERR_RANK;
+  if (P->h_id2slot[chain_id] >= 0 || (P->hcache && P->h_hslot[chain_id] >= 0)) return LORA_ERR_EXISTS;
+  const bool direct = P->max_ids <= P->max_adapters;
+  if (direct ? !P->free_slots.count(chain_id) : P->free_slots.empty()) return LORA_ERR_POOL_FULL;
+  DeviceGuard g(P->device);
+  const int32_t slot = direct ? chain_id : *P->free_slots.begin();
+  uint16_t* base = P->pages + (size_t)slot * P->slot_elems;
+  float bs[4] = {0.f, 0.f, 0.f, 0.f};
+  int32_t mask = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t ms = P->h_id2slot[members[i]];
+    for (int32_t b = blk[i]; b < blk[i] + nb[i]; ++b) bs[b] = P->h_slot_scale[ms];
+    mask |= P->h_mask[members[i]];
+  }
+  for (int32_t m = 0; m < P->n_modules; ++m) {
+    // zero pages, then each member's rank blocks at its offset (rows past a
+    // member's rank are zero in its own pages)
+    hrg::PackArgs pa = {P->staging, base + P->a_off[m], 0, P->max_rank, P->d_in[m], 0};
+    if (hrg::launch_pack(pa, stream) != hipSuccess) return LORA_ERR_HIP;
+    pa = {P->staging, base + P->b_off[m], 0, P->rpad, P->d_out[m], 1};
+    if (hrg::launch_pack(pa, stream) != hipSuccess) return LORA_ERR_HIP;
+    for (int32_t i = 0; i < n; ++i) {
+      const uint16_t* mb = P->pages + (size_t)P->h_id2slot[members[i]] * P->slot_elems;
+      const size_t arows = (size_t)std::min(16 * nb[i], P->max_rank - 16 * blk[i]);
+      if (hipMemcpyAsync(base + P->a_off[m] + (size_t)16 * blk[i] * P->d_in[m], mb + P->a_off[m],
+                         arows * P->d_in[m] * 2, hipMemcpyDeviceToDevice, stream) != hipSuccess ||
+          hipMemcpyAsync(base + P->b_off[m] + (size_t)blk[i] * P->d_out[m] * 16, mb + P->b_off[m],
+                         (size_t)nb[i] * P->d_out[m] * 16 * 2, hipMemcpyDeviceToDevice, stream) != hipSuccess)
+        return (void)hipGetLastError(), LORA_ERR_HIP;
+    }
+  }
+  if (hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, P->id_bscale, chain_id, slot,
+                           rank, bs[0], mask, make_float4(bs[0], bs[1], bs[2], bs[3]), stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return LORA_ERR_HIP;
+  }
+  P->free_slots.erase(slot);
+  P->h_id2slot[chain_id] = slot;
+  P->h_slot_rank[slot] = rank;
+  P->h_slot_scale[slot] = bs[0];
+  P->h_mask[chain_id] = mask;
+  P->h_chain[chain_id] = 1;
   return LORA_OK;
 }
 
@@ -459,6 +541,8 @@ static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t
   ga.split_stride = P->split_stride;
   ga.nsplit = ksplit;
   ga.seg_scale = pl->tab.seg_scale;
+  ga.seg_bscale = pl->tab.seg_bscale;
+  ga.small_bscale = pl->tab.small_bscale;
   ga.seg_e0 = pl->tab.seg_e0;
   ga.erow = pl->tab.erow;
   ga.small_info = pl->tab.small_info;

@@ -80,6 +80,11 @@ __device__ __forceinline__ float2 q4_group(uint32_t sz) {
   return make_float2(s, -(float)((sz >> 16) & 15u) * s);
 }
 
+// Entry b (0..3) of a float4 without a register array (a select chain).
+__device__ __forceinline__ float pick4(float4 v, int b) {
+  return b == 0 ? v.x : b == 1 ? v.y : b == 2 ? v.z : v.w;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int l = __lane_id();

@@ -452,6 +452,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
   __shared__ float vsh[16][kMaxRank + 1];
   __shared__ int s_id[64];
   __shared__ int4 s_info[16];  // the block's tokens: {slot (-1: none), rank, scale bits, 0}
+  __shared__ float4 s_bsc[16];  // the block's tokens: scale of each 16-rank block
   __shared__ int s_bad;
   const int tid = threadIdx.x;
   const int T = a.T, N = a.N, KS = a.KS;
@@ -496,6 +497,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
         bad = kStatusIdRange;
       } else if (id >= 0) {
         e = a.id_info[id];  // {slot, rank, scale bits}
+        if (tid >= t0 && tid < t0 + 16) s_bsc[tid - t0] = a.id_bscale[id];  // same round
         if (e.x < 0) bad = kStatusNotLoaded;
       }
       if (bad) atomicMax(&s_bad, bad);
@@ -525,7 +527,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
       const int r = idx / kMaxRank, q = idx % kMaxRank;
       const int4 inf = s_info[r];
       const bool on = t0 + r < T && inf.x >= 0 && q < inf.y;
-      vsh[r][q] = on ? __builtin_bit_cast(float, inf.z) * u[e] : 0.f;
+      vsh[r][q] = on ? pick4(s_bsc[r], q >> 4) * u[e] : 0.f;
     }
     __syncthreads();  // vsh
     slot = s_info[tr].x;

@@ -37,6 +37,8 @@ struct PlanTables {
   int32_t* erow;       // [T_cap]   sorted position -> E row, -1 if not in a small segment
   int4* small_info;    // [kMaxSmallRows] the small segments in order: {first sorted row,
                        //   rows | first E row << 8 | rank << 20, pool slot, alpha / rank bits}
+  float4* seg_bscale;  // [T_cap+1] per-16-rank-block scales of each segment's adapter
+  float4* small_bscale;  // [kMaxSmallRows] the same for each small segment
   int32_t* counts;     // [0] = S, [1] = number of shrink tiles, [2] = T, [3] = small segments
   int32_t max_tiles;
 };
@@ -46,6 +48,7 @@ struct PlanArgs {
   int32_t T;
   int32_t max_ids;
   const int4* id_info;     // [max_ids] {slot (-1: not resident), rank, scale bits, module mask}
+  const float4* id_bscale; // [max_ids] scale of each 16-rank block (a chain's members differ)
   int32_t* status;
   PlanTables tab;
 };
@@ -83,6 +86,8 @@ struct GemmArgs {
   size_t split_stride;
   int32_t nsplit;
   const float* seg_scale;
+  const float4* seg_bscale;   // per-16-rank-block scales of each segment (V = s U per block)
+  const float4* small_bscale; // the same per small segment
   const int32_t* row_seg;
   const int32_t* seg_id;
   const int32_t* seg_off;
@@ -115,6 +120,7 @@ struct DecodeArgs {
   int32_t T, N, K;
   int32_t max_ids;
   const int4* id_info;    // [max_ids] {slot (-1: not resident), rank, scale bits, module mask}
+  const float4* id_bscale; // [max_ids] scale of each 16-rank block
   const uint16_t* pages;
   size_t slot_stride;
   size_t a_off, b_off;
@@ -183,8 +189,11 @@ hipError_t launch_decode(const DecodeArgs& a, int items, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 // Routing-table update of one id; `mask` = the modules the adapter targets
 // (bit m: module m; modules >= 32 are always targeted), kept in id_info.w.
+// `bscale`: the scale of each 16-rank block (all equal to `scale` but for
+// chains), kept in id_bscale.
 hipError_t launch_set_slot(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
-                           int32_t id, int32_t slot, int32_t rank, float scale, int32_t mask, hipStream_t s);
+                           float4* id_bscale, int32_t id, int32_t slot, int32_t rank, float scale,
+                           int32_t mask, float4 bscale, hipStream_t s);
 hipError_t launch_clear_i32(int32_t* p, int32_t n, int32_t value, hipStream_t s);
 // Routing-table updates of several distinct ids, each {id, slot (-1: not
 // addressable), rank, scale bits}; launched in chunks of kSlotUpdatesPerLaunch.
@@ -196,6 +205,7 @@ constexpr int kPageMovesPerLaunch = 64;
 hipError_t launch_page_in(const void* host_cache_dev, void* pages, const int2* moves, int n,
                           size_t slot_vec, hipStream_t s);
 hipError_t launch_set_slots(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
-                            const int4* updates, const int32_t* masks, int n, hipStream_t s);
+                            float4* id_bscale, const int4* updates, const int32_t* masks, int n,
+                            hipStream_t s);
 
 }  // namespace hrg

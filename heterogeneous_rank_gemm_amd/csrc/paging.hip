@@ -114,7 +114,8 @@ lora_status_t paged_drop_device_copy(lora_pool_s* P, int32_t id, hipStream_t str
   if (slot < 0) return LORA_ERR_NOT_LOADED;
   DeviceGuard g(P->device);
   if (hipStreamSynchronize(P->copy_stream) != hipSuccess || hipStreamSynchronize(stream) != hipSuccess ||
-      hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, id, -1, 0, 0.f, 0, stream) !=
+      hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, P->id_bscale, id, -1, 0, 0.f, 0,
+                           make_float4(0.f, 0.f, 0.f, 0.f), stream) !=
           hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess)
     return hip_fail();
@@ -254,7 +255,8 @@ lora_status_t lora_pin_adapter(lora_pool_t P, int32_t id, int32_t pin, hipStream
     if (!is_named(P, id) && P->h_id2slot[id] >= 0) {
       const int4 e = entry(P, id, -1);
       const int32_t mk = 0;
-      if (hrg::launch_set_slots(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, &e, &mk, 1, stream) !=
+      if (hrg::launch_set_slots(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, P->id_bscale, &e, &mk, 1,
+                                stream) !=
           hipSuccess)
         return hip_fail();
       mirror(P, id, -1);
@@ -294,7 +296,8 @@ lora_status_t lora_pin_adapter(lora_pool_t P, int32_t id, int32_t pin, hipStream
   if (P->h_id2slot[id] != slot) {
     const int4 e = entry(P, id, slot);
     const int32_t mk = P->h_mask[id];
-    if (hrg::launch_set_slots(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, &e, &mk, 1, stream) !=
+    if (hrg::launch_set_slots(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, P->id_bscale, &e, &mk, 1,
+                              stream) !=
         hipSuccess)
       return hip_fail();
     mirror(P, id, slot);
@@ -387,8 +390,8 @@ lora_status_t lora_prefetch(lora_pool_t P, const int32_t* ids, int32_t n, hipStr
       mirror(P, id, P->cached[id]);
     }
   P->named = req;
-  if (!ups.empty() && hrg::launch_set_slots(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, ups.data(),
-                                            masks.data(), (int)ups.size(), stream) != hipSuccess)
+  if (!ups.empty() && hrg::launch_set_slots(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, P->id_bscale,
+                                            ups.data(), masks.data(), (int)ups.size(), stream) != hipSuccess)
     return hip_fail();
   return LORA_OK;
 }

@@ -142,7 +142,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const int s = segidx[b];
     const int id = b - 1;
     const int4 inf = id >= 0 ? a.id_info[id] : make_int4(-1, 0, 0, 0);
+    const float4 bsc = id >= 0 ? a.id_bscale[id] : make_float4(0.f, 0.f, 0.f, 0.f);
     const int rank = id >= 0 ? inf.y : 0;
+    a.tab.seg_bscale[s] = bsc;
     a.tab.seg_id[s] = id;
     a.tab.seg_off[s] = off;
     a.tab.seg_slot[s] = inf.x;
@@ -161,6 +163,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
         if (v3[1] + len <= kMaxSmallRows) {
           e0 = v3[1];
           a.tab.small_info[v3[2]] = make_int4(off, len | (e0 << 8) | (rank << 20), inf.x, inf.z);
+          a.tab.small_bscale[v3[2]] = bsc;
           atomicMax(&s_nsmall, v3[2] + 1);
           for (int i = 0; i < len; ++i) a.tab.erow[off + i] = e0 + i;
         }
@@ -321,7 +324,8 @@ hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
 // scale, and the packed per-id entry {slot, rank, scale} the decode kernels
 // read with one load.
 __global__ void set_slot_kernel(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
-                                int32_t id, int32_t slot, int32_t rank, float scale, int32_t mask) {
+                                float4* id_bscale, int32_t id, int32_t slot, int32_t rank, float scale,
+                                int32_t mask, float4 bscale) {
   if (threadIdx.x == 0) {
     if (slot >= 0) {
       slot_rank[slot] = rank;
@@ -329,13 +333,15 @@ __global__ void set_slot_kernel(int32_t* id2slot, int32_t* slot_rank, float* slo
     }
     id2slot[id] = slot;
     id_info[id] = make_int4(slot, slot >= 0 ? rank : 0, __builtin_bit_cast(int, scale), slot >= 0 ? mask : 0);
+    id_bscale[id] = slot >= 0 ? bscale : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
 
 hipError_t launch_set_slot(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
-                           int32_t id, int32_t slot, int32_t rank, float scale, int32_t mask, hipStream_t s) {
+                           float4* id_bscale, int32_t id, int32_t slot, int32_t rank, float scale,
+                           int32_t mask, float4 bscale, hipStream_t s) {
   hipLaunchKernelGGL(set_slot_kernel, dim3(1), dim3(64), 0, s, id2slot, slot_rank, slot_scale, id_info,
-                     id, slot, rank, scale, mask);
+                     id_bscale, id, slot, rank, scale, mask, bscale);
   return hipGetLastError();
 }
 
@@ -348,7 +354,7 @@ struct SlotUpdates {
 };
 
 __global__ void set_slots_kernel(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
-                                 SlotUpdates ups) {
+                                 float4* id_bscale, SlotUpdates ups) {
   const int i = threadIdx.x;
   if (i < ups.n) {
     const int4 e = ups.u[i];
@@ -358,11 +364,15 @@ __global__ void set_slots_kernel(int32_t* id2slot, int32_t* slot_rank, float* sl
     }
     id2slot[e.x] = e.y;
     id_info[e.x] = make_int4(e.y, e.y >= 0 ? e.z : 0, e.w, e.y >= 0 ? ups.mask[i] : 0);
+    // host-cached adapters have one scale for every rank block
+    const float sc = e.y >= 0 ? __builtin_bit_cast(float, e.w) : 0.f;
+    id_bscale[e.x] = make_float4(sc, sc, sc, sc);
   }
 }
 
 hipError_t launch_set_slots(int32_t* id2slot, int32_t* slot_rank, float* slot_scale, int4* id_info,
-                            const int4* updates, const int32_t* masks, int n, hipStream_t s) {
+                            float4* id_bscale, const int4* updates, const int32_t* masks, int n,
+                            hipStream_t s) {
   for (int i0 = 0; i0 < n; i0 += kSlotUpdatesPerLaunch) {
     SlotUpdates ups{};
     ups.n = std::min(kSlotUpdatesPerLaunch, n - i0);
@@ -371,7 +381,7 @@ hipError_t launch_set_slots(int32_t* id2slot, int32_t* slot_rank, float* slot_sc
       ups.mask[j] = masks[i0 + j];
     }
     hipLaunchKernelGGL(set_slots_kernel, dim3(1), dim3(kSlotUpdatesPerLaunch), 0, s, id2slot, slot_rank,
-                       slot_scale, id_info, ups);
+                       slot_scale, id_info, id_bscale, ups);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

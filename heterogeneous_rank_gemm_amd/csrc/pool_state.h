@@ -32,6 +32,7 @@ struct lora_pool_s {
   int32_t* slot_rank = nullptr;      // [max_adapters]
   float* slot_scale = nullptr;       // [max_adapters]
   int4* id_info = nullptr;           // [max_ids] {slot, rank, scale bits, module mask}
+  float4* id_bscale = nullptr;       // [max_ids] scale of each 16-rank block (chains: per member)
   int32_t* status = nullptr;         // sticky device status
   uint16_t* staging = nullptr;       // one module's A or B as received
   float* upart = nullptr;            // [kMaxSplits][max_tokens][rpad] shrink partial planes
@@ -44,6 +45,7 @@ struct lora_pool_s {
   float* dec_upart = nullptr;        // [ceil(max d_in / 1024)][64][rpad] shrink partials
   std::vector<int32_t> h_id2slot, h_slot_rank;
   std::vector<int32_t> h_mask;       // [max_ids] modules a loaded or registered id targets (bit m)
+  std::vector<uint8_t> h_chain;      // [max_ids] the id is a chain (lora_load_chain)
   std::vector<float> h_slot_scale;
   std::set<int32_t> free_slots;      // lowest free slot first
   lora_plan_s* internal = nullptr;

@@ -553,7 +553,7 @@ __global__ __launch_bounds__(256) void expand_small_kernel(GemmArgs a, int fin_b
       const int sg = a.row_seg[p];
       const int er = a.erow[p];
       if (er >= 0 || a.seg_slot[sg] < 0 || q >= ((a.seg_rank[sg] + 15) & ~15)) continue;
-      const float sc = a.seg_scale[sg];
+      const float sc = pick4(a.seg_bscale[sg], q >> 4);  // the scale of q's 16-rank block
       uint16_t h[4], lo[4];
       split_hi_lo(sc * u.x, h[0], lo[0]);
       split_hi_lo(sc * u.y, h[1], lo[1]);
@@ -575,9 +575,13 @@ __global__ __launch_bounds__(256) void expand_small_kernel(GemmArgs a, int fin_b
   const int st = *a.status;
   const int nitems = a.counts[3] * ngb;
   int4 si = a.small_info[min(item / ngb, kMaxSmallRows - 1)];
+  float4 sb = a.small_bscale[min(item / ngb, kMaxSmallRows - 1)];
   if (st != 0) return;  // strict mode: a failed plan leaves out untouched
   for (; item < nitems; item += eb) {
-    if (item != (int)blockIdx.x - fin_blocks) si = a.small_info[item / ngb];
+    if (item != (int)blockIdx.x - fin_blocks) {
+      si = a.small_info[item / ngb];
+      sb = a.small_bscale[item / ngb];
+    }
     const int g = min(4 * (item % ngb) + wid, ng - 1);  // a wave past the last group repeats it, no store
     const bool gok = 4 * (item % ngb) + wid < ng;
     const int off = si.x, len = si.y & 255, e0 = (si.y >> 8) & 0xfff, rank = si.y >> 20;
@@ -601,7 +605,7 @@ __global__ __launch_bounds__(256) void expand_small_kernel(GemmArgs a, int fin_b
     if (tid < len * wq) {
       const int r = tid / wq, q = 4 * (tid % wq);
       const float4 u = sum_planes4(a.upart + (size_t)(off + r) * w + q, a.split_stride, a.nsplit);
-      const float sc = __builtin_bit_cast(float, si.w);
+      const float sc = pick4(sb, q >> 4);  // the scale of q's 16-rank block
       split_hi_lo(sc * u.x, vs[0][r][q], vs[1][r][q]);
       split_hi_lo(sc * u.y, vs[0][r][q + 1], vs[1][r][q + 1]);
       split_hi_lo(sc * u.z, vs[0][r][q + 2], vs[1][r][q + 2]);

@@ -99,3 +99,6 @@ class LoraPool:
                       T: Optional[int] = None):
         T = X.shape[0] if T is None else T
         _lora.lora_base_apply_q4(self.handle, module, X, T, Wq, Wsz, W_scratch, out, stream)
+
+    def load_chain(self, chain_id: int, members, stream=None):
+        _lora.lora_load_chain(self.handle, chain_id, members, stream)

@@ -134,6 +134,30 @@ lora_status_t lora_load_adapter(lora_pool_t pool, int32_t id, int32_t rank, floa
  */
 lora_status_t lora_unload_adapter(lora_pool_t pool, int32_t id, hipStream_t stream);
 
+/*
+ * lora_load_chain -- a chain of resident adapters under a new id ([LoRA-Land]
+ * "technical approach", item 3: several LoRAs composed like a pipeline and
+ * applied in turn; section "3. hot-plug API and composition":
+ * set_adaptive_chain).  At a linear layer each member adds its own update,
+ * so a token routed to the chain gets
+ *     out = bf16( X W^T + sum_c (alpha_c / r_c) (X A_c) B_c ),
+ * with one rounding.  The chain is a new adapter whose pages hold the
+ * members' pages side by side in whole 16-rank blocks (member c's blocks
+ * carry its scale); the members are copied (snapshotted), so unloading one
+ * later leaves the chain as it was.  Unload the chain with
+ * lora_unload_adapter.
+ *   members  host array [n], n >= 1, distinct resident ids that are not
+ *            chains (host-cached adapters must be addressable at the call)
+ * ID_RANGE (chain_id or a member out of range), INVALID_ARG (n, repeats, a
+ * chain as member), NOT_LOADED (a member not addressable), RANK (the blocks
+ * of all members but the last plus the last's rank exceed max_rank), EXISTS,
+ * POOL_FULL.  The chain's target set is the union of its members'.
+ * lora_pool_query reports the chain's rank as that total and its scale as the
+ * first member's.  Synchronises `stream`.
+ */
+lora_status_t lora_load_chain(lora_pool_t pool, int32_t chain_id, int32_t n, const int32_t* members,
+                              hipStream_t stream);
+
 /* Host-side lookup: slot, true rank and scale of a resident id (any out
  * pointer may be NULL).  NOT_LOADED / ID_RANGE as above. */
 lora_status_t lora_pool_query(lora_pool_t pool, int32_t id, int32_t* slot, int32_t* rank,
