@@ -406,7 +406,8 @@ lora_status_t lora_load_chain(lora_pool_t P, int32_t chain_id, int32_t n, const 
     }
   }
   if (hrg::launch_set_slot(P->id2slot, P->slot_rank, P->slot_scale, P->id_info, P->id_bscale, chain_id, slot,
-                           rank, bs[0], mask, make_float4(bs[0], bs[1], bs[2], bs[3]), stream) != hipSuccess ||
+                           rank | hrg::kChainRankFlag, bs[0], mask, make_float4(bs[0], bs[1], bs[2], bs[3]),
+                           stream) != hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess) {
     (void)hipGetLastError();
     return LORA_ERR_HIP;

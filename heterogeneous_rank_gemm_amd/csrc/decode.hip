@@ -85,7 +85,7 @@ __device__ __forceinline__ TokInfo token_info(const DecodeArgs& a, int t) {
         ti.id = id;
         ti.slot = e.x;
         // an adapter that does not target this linear has no rank here
-        ti.rank = targets(e.w, a.module) ? e.y : 0;
+        ti.rank = targets(e.w, a.module) ? (e.y & (kChainRankFlag - 1)) : 0;
         ti.scale = __builtin_bit_cast(float, e.z);
       }
     }
@@ -497,7 +497,12 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
         bad = kStatusIdRange;
       } else if (id >= 0) {
         e = a.id_info[id];  // {slot, rank, scale bits}
-        if (tid >= t0 && tid < t0 + 16) s_bsc[tid - t0] = a.id_bscale[id];  // same round
+        if (tid >= t0 && tid < t0 + 16) {
+          // a chain's blocks have their own scales (one more load, chains only)
+          const float sc = __builtin_bit_cast(float, e.z);
+          s_bsc[tid - t0] = (e.y & kChainRankFlag) ? a.id_bscale[id] : make_float4(sc, sc, sc, sc);
+        }
+        e.y &= kChainRankFlag - 1;
         if (e.x < 0) bad = kStatusNotLoaded;
       }
       if (bad) atomicMax(&s_bad, bad);

@@ -8,6 +8,10 @@ namespace hrg {
 
 constexpr int kMaxIds = 16384;       // plan histogram lives in LDS
 constexpr int kMaxRank = 64;
+// id_info.y = rank | kChainRankFlag for a chain: only then do the kernels
+// read id_bscale (the scale of each 16-rank block); a plain adapter's blocks
+// all use id_info.z.
+constexpr int kChainRankFlag = 1 << 16;
 constexpr int kShrinkRows = 64;      // rows per shrink work tile
 constexpr int kMaxSplits = 32;       // K-splits of the shrink
 // Segments of at most kSmallRows tokens are expanded by a separate launch into

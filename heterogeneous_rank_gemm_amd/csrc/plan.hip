@@ -142,8 +142,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     const int s = segidx[b];
     const int id = b - 1;
     const int4 inf = id >= 0 ? a.id_info[id] : make_int4(-1, 0, 0, 0);
-    const float4 bsc = id >= 0 ? a.id_bscale[id] : make_float4(0.f, 0.f, 0.f, 0.f);
-    const int rank = id >= 0 ? inf.y : 0;
+    const float sc0 = id >= 0 ? __builtin_bit_cast(float, inf.z) : 0.f;
+    // a chain's blocks have their own scales (one more load, chains only)
+    const float4 bsc = id >= 0 && (inf.y & kChainRankFlag) ? a.id_bscale[id] : make_float4(sc0, sc0, sc0, sc0);
+    const int rank = id >= 0 ? (inf.y & (kChainRankFlag - 1)) : 0;
     a.tab.seg_bscale[s] = bsc;
     a.tab.seg_id[s] = id;
     a.tab.seg_off[s] = off;
@@ -328,7 +330,7 @@ __global__ void set_slot_kernel(int32_t* id2slot, int32_t* slot_rank, float* slo
                                 int32_t mask, float4 bscale) {
   if (threadIdx.x == 0) {
     if (slot >= 0) {
-      slot_rank[slot] = rank;
+      slot_rank[slot] = rank & (kChainRankFlag - 1);
       slot_scale[slot] = scale;
     }
     id2slot[id] = slot;
