@@ -329,7 +329,9 @@ lora_status_t lora_host_unregister(lora_pool_t pool, int32_t id, hipStream_t str
  * NOT_LOADED (an id neither host-cached nor loaded), POOL_FULL (more misses
  * than free plus evictable slots), INVALID_ARG (no host cache, ids NULL with
  * n > 0, n < 0).  The host returns before the copies finish; the host cache
- * is not modified while they run (unregister waits for them).
+ * is not modified while they run (unregister waits for them).  The call
+ * changes host-side state, so it must not be captured into a hipGraph
+ * (capture the applies; call lora_prefetch before each replay instead).
  */
 lora_status_t lora_prefetch(lora_pool_t pool, const int32_t* ids, int32_t n, hipStream_t stream);
 
