@@ -326,6 +326,107 @@ def paging_bench(args, torch, hrg) -> dict:
 
 
 # ---------------------------------------------------------------------------
+# adapter chains and target sets (separate measurements, not the contract line)
+# ---------------------------------------------------------------------------
+def _event_time(fn, steps: int, warmup: int, torch) -> float:
+    """Seconds per call of fn() over `steps` calls between two synchronisations."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3 / steps
+
+
+def chains_bench(args, torch, hrg) -> dict:
+    """The q_proj decode linear with 200 rank-16 adapters plus 100 chains of two
+    of them (ids 200..299, rank 16 + 16): a batch over all 300 ids against a
+    batch over the 200 plain ids and the base-only call."""
+    wl = wk.WORKLOADS[2]
+    m = wl.modules[0]
+    n_ad, n_ch = wl.n_adapters, 100
+    pool = hrg.LoraPool(n_ad + n_ch, n_ad + n_ch, 32, [m.d_in], [m.d_out], wl.T)
+    for i in range(n_ad):
+        a, b = wk.adapter_weights(wl, i, 0, 16, wl.default_seed, "cuda")
+        pool.load_adapter(i, 16, 32.0, [a], [b])
+    g = np.random.Generator(np.random.PCG64(wk.derive_seed(wl.key, "chains")))
+    for c in range(n_ch):
+        pool.load_chain(n_ad + c, [int(x) for x in g.choice(n_ad, size=2, replace=False)])
+    X = wk.activation(wl, m.input_group, m.d_in, wl.default_seed, "cuda")
+    W = wk.base_weight(wl, 0, wl.default_seed, "cuda")
+    out = torch.empty((wl.T, m.d_out), dtype=torch.bfloat16, device="cuda")
+    ids_mixed = torch.as_tensor(g.integers(0, n_ad + n_ch, wl.T).astype(np.int32), device="cuda")
+    ids_plain = torch.as_tensor(g.integers(0, n_ad, wl.T).astype(np.int32), device="cuda")
+    res = {"workload": wl.name + "+100-chains-of-2", "T": wl.T, "steps": args.steps}
+    for key, ids in (("mixed_chain_batch", ids_mixed), ("plain_batch", ids_plain)):
+        t = _event_time(lambda: hrg.lora_apply(pool.handle, 0, X, ids, wl.T, W, out, None),
+                        args.steps, args.warmup, torch)
+        res[f"{key}_us"] = round(t * 1e6, 2)
+    res["chain_tokens"] = int((ids_mixed >= n_ad).sum())
+    t = _event_time(lambda: hrg.lora_base_apply(pool.handle, 0, X, wl.T, W, out),
+                    args.steps, args.warmup, torch)
+    res["base_only_us"] = round(t * 1e6, 2)
+    if pool.status() != "OK":
+        raise RuntimeError("device status")
+    pool.close()
+    return res
+
+
+def target_sets_bench(args, torch, hrg) -> dict:
+    """One Llama-2-7B decode layer (the seven linears of the 32-layer step,
+    T = 64, 200 rank-16 adapters, uniform ids): every adapter targeting all
+    seven linears, against even-numbered adapters targeting only q and v
+    (the others still all seven), in a direct-mapped and a slot-table pool."""
+    wl = wk.WORKLOADS[5]
+    mods = wl.modules[:7]
+    res = {"workload": "llama2-7b-decode-layer-T64-200xr16", "T": wl.T, "steps": args.steps}
+    X = {}
+    for mm in mods:
+        if mm.input_group not in X:
+            X[mm.input_group] = wk.activation(wl, mm.input_group, mm.d_in, wl.default_seed, "cuda")
+    W = [wk.base_weight(wl, j, wl.default_seed, "cuda") for j in range(7)]
+    out = [torch.empty((wl.T, mm.d_out), dtype=torch.bfloat16, device="cuda") for mm in mods]
+    ids = torch.as_tensor(wk.adapter_ids(wl, wl.default_seed), device="cuda")
+    # a direct-mapped pool (ids = slots) and a slot-table pool (max_ids > slots)
+    for key, qv_only, max_ids in (("all_seven", False, wl.n_adapters),
+                                  ("even_ids_q_v_only", True, wl.n_adapters),
+                                  ("all_seven_slot_table", False, 256),
+                                  ("even_ids_q_v_only_slot_table", True, 256)):
+        pool = hrg.LoraPool(wl.n_adapters, max_ids, 16, [mm.d_in for mm in mods],
+                            [mm.d_out for mm in mods], wl.T)
+        for i in range(wl.n_adapters):
+            A, B = [], []
+            for j in range(7):
+                if qv_only and i % 2 == 0 and j not in (0, 2):
+                    A.append(None)
+                    B.append(None)
+                    continue
+                a, b = wk.adapter_weights(wl, i, j, 16, wl.default_seed, "cuda")
+                A.append(a)
+                B.append(b)
+            pool.load_adapter(i, 16, 32.0, A, B)
+
+        def step():
+            for j in range(7):
+                hrg.lora_apply(pool.handle, j, X[mods[j].input_group], ids, wl.T, W[j], out[j], None)
+        res[f"{key}_layer_us"] = round(_event_time(step, args.steps, args.warmup, torch) * 1e6, 2)
+        if pool.status() != "OK":
+            raise RuntimeError("device status")
+        if key == "all_seven":
+            def base():
+                for j in range(7):
+                    hrg.lora_base_apply(pool.handle, j, X[mods[j].input_group], wl.T, W[j], out[j])
+            res["base_only_layer_us"] = round(_event_time(base, args.steps, args.warmup, torch) * 1e6, 2)
+        pool.close()
+    return res
+
+
+# ---------------------------------------------------------------------------
 # CPU oracle baseline
 # ---------------------------------------------------------------------------
 def cpu_baseline(wl: wk.Workload, rep: Replica, seconds: float, torch):
@@ -393,6 +494,10 @@ def main(argv=None) -> int:
                          "the rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--int4", action="store_true",
                     help="INT4 (group 128) base weights instead of bf16 (lora_apply_q4)")
+    ap.add_argument("--chains", action="store_true",
+                    help="measure adapter chains instead (prints its own JSON line)")
+    ap.add_argument("--target-sets", action="store_true",
+                    help="measure per-adapter target sets instead (prints its own JSON line)")
     ap.add_argument("--paging", action="store_true",
                     help="measure host-cache paging instead (prints its own JSON line)")
     ap.add_argument("--paging-slots", type=int, default=64, help="device slots of the paged pool")
@@ -418,6 +523,12 @@ def main(argv=None) -> int:
 
     if args.paging:
         print(json.dumps({"paging": paging_bench(args, torch, hrg)}), flush=True)
+        return 0
+    if args.chains:
+        print(json.dumps({"chains": chains_bench(args, torch, hrg)}), flush=True)
+        return 0
+    if args.target_sets:
+        print(json.dumps({"target_sets": target_sets_bench(args, torch, hrg)}), flush=True)
         return 0
 
     wl = wk.WORKLOADS[args.workload]
