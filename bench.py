@@ -504,7 +504,7 @@ def main(argv=None) -> int:
     ap.add_argument("--paging-mix", choices=["uniform", "hot5"], default="uniform")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); "
+        print(f"bench.py measures one GPU only (the library has no multi-GPU path); "
               f"got --gpus {args.gpus}", file=sys.stderr)
         return 2
 
