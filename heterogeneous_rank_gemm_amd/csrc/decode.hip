@@ -426,10 +426,10 @@ __global__ __launch_bounds__(64 * (4 + NA)) void decode_main(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // combine: block = 16 tokens x 64 columns, thread = (token, 4 columns).
 // Round 1 of loads depends on nothing: the ids, the chunk partials and the
-// shrink partials of the block's V.  Round 2: every token's {slot, rank,
-// scale} (each block checks the whole batch, strict mode) and, in a
-// direct-mapped pool, the thread's B rows.  Otherwise the B rows need the slot
-// and come in a third round.
+// shrink partials of the block's V, and in a direct-mapped pool the thread's
+// B rows (its token's id comes by a scalar load).  Round 2: every token's
+// {slot, rank, scale} (each block checks the whole batch, strict mode).
+// Otherwise the B rows need the slot and come in a third round.
 constexpr int kCombThreads = 256;
 constexpr int kVPer = 16 * kMaxRank / kCombThreads;  // V elements per thread
 
@@ -463,11 +463,12 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
   const bool mine = t < T && n < N;
 
   // ---- round 1 ----
-  int st = 0;
+  // (the ids for the whole-batch check are stored to LDS only after every
+  // other load of this round is out, so that no load waits for them)
+  int st = 0, idv = -1;
   if (a.lora) {
     st = *a.status;
-    if (tid < 64) s_id[tid] = tid < T ? a.ids[tid] : -1;
-    if (tid == 0) s_bad = 0;
+    if (tid < 64 && tid < T) idv = a.ids[tid];
   }
   const float* pp = a.part + (size_t)min(t, T - 1) * a.npad + min(n, N - 4);
   float4 pv[4];
@@ -478,14 +479,51 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
   int slot = -1, rank = 0;
   const uint16_t* Bp = nullptr;
   if (a.lora) {
-    // V[t][q] = (alpha / r) * sum of the shrink partials in chunk order
+    // this wave's four tokens' ids by wave-uniform (scalar) loads, so that a
+    // direct-mapped pool's B rows go out in this round, beside the partials,
+    // instead of after a round trip of vector loads
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int tw = t0 + 4 * wv;  // tr = 4 wv + (tr & 3)
+    const int i0 = tw < T ? a.ids[tw] : -1;
+    const int i1 = tw + 1 < T ? a.ids[tw + 1] : -1;
+    const int i2 = tw + 2 < T ? a.ids[tw + 2] : -1;
+    const int i3 = tw + 3 < T ? a.ids[tw + 3] : -1;
+    const int q4 = tr & 3;
+    const int my_id = q4 == 0 ? i0 : q4 == 1 ? i1 : q4 == 2 ? i2 : i3;
+    // B^T page in 16-rank chunks [rpad/16][N][16]: the 4 columns' chunk is 64
+    // contiguous values (ranks past the adapter's rank are zero)
+    if (a.direct && mine && my_id >= 0 && my_id < a.max_slots) {
+      Bp = a.pages + (size_t)my_id * a.slot_stride + a.b_off + (size_t)n * 16;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) bv[k] = *reinterpret_cast<const uint4*>(Bp + 8 * k);
+    }
+    // V[t][q] = (alpha / r) * sum of the shrink partials in chunk order; the
+    // loads of all kVPer entries go out together, four chunks at a time
+    const float* up[kVPer];
+    bool uq[kVPer];
 #pragma unroll
     for (int e = 0; e < kVPer; ++e) {
       const int idx = tid + kCombThreads * e;
       const int r = idx / kMaxRank, q = idx % kMaxRank;
-      const int tt = min(t0 + r, T - 1);
-      u[e] = q < a.u_ld ? sum_chunks(a.upart + (size_t)tt * a.u_ld + q, (size_t)64 * a.u_ld, KS) : 0.f;
+      uq[e] = q < a.u_ld;
+      up[e] = a.upart + (size_t)min(t0 + r, T - 1) * a.u_ld + (uq[e] ? q : 0);
+      u[e] = 0.f;
     }
+    const size_t ustr = (size_t)64 * a.u_ld;
+    for (int c0 = 0; c0 < KS; c0 += 4) {
+      float v[kVPer][4];
+#pragma unroll
+      for (int e = 0; e < kVPer; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[e][j] = up[e][(size_t)min(c0 + j, KS - 1) * ustr];
+#pragma unroll
+      for (int e = 0; e < kVPer; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (c0 + j < KS && uq[e]) u[e] += v[e][j];
+    }
+    if (tid < 64) s_id[tid] = idv;
+    if (tid == 0) s_bad = 0;
     __syncthreads();  // s_id
 
     // ---- round 2 ----
@@ -509,16 +547,6 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
       // a token whose adapter does not target this linear takes the base only
       if (!bad && e.x >= 0 && !targets(e.w, a.module)) e = make_int4(-1, 0, 0, 0);
       if (tid >= t0 && tid < t0 + 16) s_info[tid - t0] = bad ? make_int4(-1, 0, 0, 0) : e;
-    }
-    // B^T page in 16-rank chunks [rpad/16][N][16]: the 4 columns' chunk is 64
-    // contiguous values (ranks past the adapter's rank are zero)
-    if (a.direct && mine) {
-      const int id = s_id[t];
-      if (id >= 0 && id < a.max_slots) {
-        Bp = a.pages + (size_t)id * a.slot_stride + a.b_off + (size_t)n * 16;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) bv[k] = *reinterpret_cast<const uint4*>(Bp + 8 * k);
-      }
     }
     __syncthreads();  // s_bad, s_info
     if (s_bad) {
