@@ -143,6 +143,11 @@ __global__ __launch_bounds__(64 * (4 + NA)) void decode_main(DecodeArgs a) {
   int qb = 0;                     // rank block of the adapter
   uint64_t members = 0;           // tokens of the adapter
   if (a_wave) {
+    // In a W block the A waves copy no X: they join the block barrier first,
+    // so the W waves never wait there for these lookups (the X copy takes
+    // longer than the barrier wait it replaces; the A slices stay off the
+    // critical path).
+    if (w_block) __builtin_amdgcn_s_barrier();
     // item = the item-th (adapter, 16-rank block) of the batch, adapters in
     // order of first occurrence.  Lane t holds token t's id.  A direct-mapped
     // pool keeps adapter id in slot id, so the page address follows from the
@@ -370,7 +375,8 @@ __global__ __launch_bounds__(64 * (4 + NA)) void decode_main(DecodeArgs a) {
   uint4 rwa[kSteps];
 #pragma unroll
   for (int s = 0; s < kSteps; ++s) rwa[s] = ld16(row + min(32 * s + 8 * g4, klen - 8));
-  barrier_after<kSteps>();
+  // blocks of A waves only: waves 0..3 copied X, everyone waits for it here
+  if (!w_block) barrier_after<kSteps>();
   if (!active) return;
   // An adapter with at most 16 tokens in the batch (the usual case at decode)
   // needs one 16-token MFMA block, not four: lane r16 reads the X row of the
