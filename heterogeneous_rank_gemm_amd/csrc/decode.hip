@@ -456,7 +456,6 @@ __device__ __forceinline__ float sum_chunks(const float* p, size_t stride, int K
 
 __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
   __shared__ float vsh[16][kMaxRank + 1];
-  __shared__ int s_id[64];
   __shared__ int4 s_info[16];  // the block's tokens: {slot (-1: none), rank, scale bits, 0}
   __shared__ float4 s_bsc[16];  // the block's tokens: scale of each 16-rank block
   __shared__ int s_bad;
@@ -516,25 +515,19 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
       u[e] = 0.f;
     }
     const size_t ustr = (size_t)64 * a.u_ld;
-    for (int c0 = 0; c0 < KS; c0 += 4) {
-      float v[kVPer][4];
+    // the first four chunks' V partial loads go out now, the rest after the
+    // routing lookups
+    float v[kVPer][4];
 #pragma unroll
-      for (int e = 0; e < kVPer; ++e)
+    for (int e = 0; e < kVPer; ++e)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[e][j] = up[e][(size_t)min(c0 + j, KS - 1) * ustr];
-#pragma unroll
-      for (int e = 0; e < kVPer; ++e)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (c0 + j < KS && uq[e]) u[e] += v[e][j];
-    }
-    if (tid < 64) s_id[tid] = idv;
-    if (tid == 0) s_bad = 0;
-    __syncthreads();  // s_id
+      for (int j = 0; j < 4; ++j) v[e][j] = up[e][(size_t)min(j, KS - 1) * ustr];
 
-    // ---- round 2 ----
+    // ---- round 2: the whole batch's routing entries (strict mode), lane t
+    // from its own id register (wave 0 only), while round 1 is in flight ----
     if (tid < 64) {
-      const int id = s_id[tid];
+      if (tid == 0) s_bad = 0;  // before the wave's atomics, in program order
+      const int id = idv;
       int bad = 0;
       int4 e = make_int4(-1, 0, 0, 0);
       if (id < -1 || id >= a.max_ids) {
@@ -553,6 +546,19 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
       // a token whose adapter does not target this linear takes the base only
       if (!bad && e.x >= 0 && !targets(e.w, a.module)) e = make_int4(-1, 0, 0, 0);
       if (tid >= t0 && tid < t0 + 16) s_info[tid - t0] = bad ? make_int4(-1, 0, 0, 0) : e;
+    }
+    for (int c0 = 0; c0 < KS; c0 += 4) {
+      if (c0 > 0) {
+#pragma unroll
+        for (int e = 0; e < kVPer; ++e)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[e][j] = up[e][(size_t)min(c0 + j, KS - 1) * ustr];
+      }
+#pragma unroll
+      for (int e = 0; e < kVPer; ++e)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (c0 + j < KS && uq[e]) u[e] += v[e][j];
     }
     __syncthreads();  // s_bad, s_info
     if (s_bad) {
