@@ -143,11 +143,10 @@ __global__ __launch_bounds__(64 * (4 + NA)) void decode_main(DecodeArgs a) {
   int qb = 0;                     // rank block of the adapter
   uint64_t members = 0;           // tokens of the adapter
   if (a_wave) {
-    // In a W block the A waves copy no X: they join the block barrier first,
-    // so the W waves never wait there for these lookups (the X copy takes
-    // longer than the barrier wait it replaces; the A slices stay off the
-    // critical path).
-    if (w_block) __builtin_amdgcn_s_barrier();
+    // In a W block the A waves copy no X: they join the block barrier before
+    // their lookups, so the W waves never wait there for them (the X copy
+    // takes longer than the barrier wait it replaces; the A slices stay off
+    // the critical path).
     // item = the item-th (adapter, 16-rank block) of the batch, adapters in
     // order of first occurrence.  Lane t holds token t's id.  A direct-mapped
     // pool keeps adapter id in slot id, so the page address follows from the
@@ -159,10 +158,13 @@ __global__ __launch_bounds__(64 * (4 + NA)) void decode_main(DecodeArgs a) {
     int id = -1, slot = -1, rank = 0, bad = 0;
     if (a.direct) {
       if (lane < T) id = a.ids[lane];
+      // the id load stays in flight across the barrier
+      if (w_block) __builtin_amdgcn_s_barrier();
       if (id >= a.max_slots || id < -1) bad = 1;  // the combine launch rejects the batch
       slot = id;
       rank = a.u_ld;
     } else {
+      if (w_block) __builtin_amdgcn_s_barrier();
       const TokInfo ti = token_info(a, lane);
       id = ti.id;
       slot = ti.slot;
