@@ -28,13 +28,25 @@ __device__ __forceinline__ bf16x8 keep_bf(bool keep, uint4 v) {
   return __builtin_bit_cast(bf16x8, make_uint4(v.x & m, v.y & m, v.z & m, v.w & m));
 }
 
+// The tokens of a tile's rows this lane gathers: row 16 mb + (lane & 15).
+__device__ __forceinline__ void tile_tokens(const ShrinkArgs& a, int4 ti, int (&tok)[4]) {
+  const int l = threadIdx.x & 63;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int p = 16 * mb + (l & 15);
+    tok[mb] = a.perm[ti.x + (p < ti.y ? p : 0)];
+  }
+}
+
 // NQ: 16-rank blocks held per item (the pool's rank rounded up to 16, in
 // blocks; an adapter of lower rank masks the rest).
-// The next item's tile entry (index `next`) is requested into *tn with the
-// X loads, so waiting for it costs nothing.
+// `tok` holds this item's gathered tokens (requested during the previous
+// item), so the A and X loads go out together.  The next item's tile entry
+// (index `next`) is requested into *tn with them and its tokens into tokn
+// once it lands, so neither lookup costs a round of its own.
 template <int NQ>
 __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64 * kRedLd], int4 ti, int split,
-                                            int next, int4* tn) {
+                                            int next, const int (&tok)[4], int4* tn, int (&tokn)[4]) {
   const int row0 = ti.x, rows = ti.y, slot = ti.z, rank = ti.w;
   const int nq = (rank + 15) / 16;  // 16-wide rank blocks actually computed
   const int nm = (rows + 15) / 16;  // 16-row blocks with at least one row
@@ -68,15 +80,13 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
     }
   };
   load_a(k0);
-  __builtin_amdgcn_sched_barrier(0);
   const uint16_t* xrow[4];
   bool rv[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     const int p = 16 * mb + (l & 15);
     rv[mb] = p < rows;
-    const int tok = a.perm[row0 + (rv[mb] ? p : 0)];
-    xrow[mb] = a.X + (size_t)tok * K;
+    xrow[mb] = a.X + (size_t)tok[mb] * K;
   }
 
   f32x4 acc[4][NQ];
@@ -94,7 +104,10 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) xv[st][mb] = ld16(xrow[mb] + kc);
     }
-    if (kb == k0) *tn = a.tile_info[next];
+    if (kb == k0) {
+      *tn = a.tile_info[next];
+      tile_tokens(a, *tn, tokn);  // waits for the entry only; lands during the MFMAs
+    }
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const bool kv = kb + 128 * st + 32 * w + koff < k1;  // a lane's 8 elements are all in or out
@@ -150,12 +163,18 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
   const int st = *a.status;
   const int nitems = a.counts[1] * a.nsplit;
   int4 ti = a.tile_info[blockIdx.x / a.nsplit];
-  if (st != 0) return;
+  if (st != 0 || (int)blockIdx.x >= nitems) return;
+  int tok[4];
+  tile_tokens(a, ti, tok);
   for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
     int4 tn;
+    int tokn[4];
     __syncthreads();  // the previous item is done with red
-    shrink_item<NQ>(a, red, ti, item % a.nsplit, min(item + (int)gridDim.x, nitems - 1) / a.nsplit, &tn);
+    shrink_item<NQ>(a, red, ti, item % a.nsplit, min(item + (int)gridDim.x, nitems - 1) / a.nsplit, tok, &tn,
+                    tokn);
     ti = tn;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) tok[mb] = tokn[mb];
   }
 }
 
