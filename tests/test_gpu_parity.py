@@ -122,6 +122,37 @@ def test_plan_2000_distinct():
     pool.close()
 
 
+# the largest batches and id ranges the plan takes: placement over several
+# LDS-staged blocks of 8192 tokens (T > 8192), and each cursor layout (16, 8,
+# 4 or 1 placement waves for pools of up to 1024, 2048, 4096 or 16384 ids)
+PLAN_LIMITS = [(8969, 48), (9000, 1500), (12000, 3000), (4096, 16384), (1, 16384)]
+
+
+@pytest.mark.parametrize("T,max_ids", PLAN_LIMITS)
+def test_plan_size_limits_bit_exact(T, max_ids):
+    _say(f"[plan] T={T} max_ids={max_ids}")
+    from heterogeneous_rank_gemm_amd import LoraPool
+    g = np.random.default_rng(T + max_ids)
+    # half uniform over every id (and -1), half on five hot ids: long runs
+    # beside single-token segments
+    hot = g.choice(max_ids, size=5, replace=False)
+    ids_np = np.where(g.random(T) < 0.5, g.integers(-1, max_ids, T), g.choice(hot, T)).astype(np.int32)
+    used = sorted(set(int(i) for i in ids_np if i >= 0))
+    pool = LoraPool(max(len(used), 1), max_ids, 8, [64], [64], T)
+    A = torch.zeros((64, 8), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")
+    for i in used:
+        pool.load_adapter(i, 8, 16.0, [A], [B])
+    plan = pool.plan_create()
+    pool.plan(torch.as_tensor(ids_np, device="cuda"), T, plan)
+    got = pool.debug_read_plan(plan)
+    want = oracle.plan(ids_np, max_ids)
+    for g_, w in zip(got, want):
+        assert g_ == w.tolist()
+    assert pool.status() == "OK"
+    pool.close()
+
+
 # --------------------------------------------------------------------------
 # values: small ragged shapes that span several tiles
 # --------------------------------------------------------------------------
@@ -138,6 +169,7 @@ RAGGED = [
     (130, 1032, 200, (8, 16, 32, 64), 64, -1),
     (257, 264, 1160, (4, 64, 17), 64, -1),
     (333, 4104, 136, (16,), 16, 0),
+    (9000, 72, 136, (16, 5, 64), 64, -1),  # above one 8192-token placement block
 ]
 
 
