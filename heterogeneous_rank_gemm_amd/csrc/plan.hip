@@ -4,6 +4,7 @@
 // id" is the "Grouped Multi-LoRA Execution" of the LoRA-Land post (section
 // "2. multi-LoRA batch scheduling"); ids are validated here in strict mode
 // (icman report section 4.1: reject, never silently serve the base).
+#include <atomic>
 #include <map>
 #include <mutex>
 
@@ -256,14 +257,20 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
   const int nb = a.max_ids + 1;
   const int pw = plan_place_waves(nb);
   const size_t lds = (size_t)(2 + (pw > 1 ? pw : 0)) * nb * sizeof(int);
-  static bool attr_set = false;
-  if (!attr_set) {
+  // the dynamic LDS limit, raised once per device (setting it twice from
+  // racing threads is harmless)
+  static std::atomic<uint64_t> attr_devices{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev < 64 ? 1ull << dev : 0;
+  if (bit == 0 || (attr_devices.load(std::memory_order_acquire) & bit) == 0) {
     // the most any nb needs: 2 (kMaxIds + 1) ints with pw = 1; with pw > 1,
-    // (2 + pw) nb <= 2 * 4097 + 16 * 1025 is smaller
-    hipError_t e = hipFuncSetAttribute((const void*)plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       2 * (kMaxIds + 1) * (int)sizeof(int));
+    // (2 + pw) nb <= 6 * 4096 ints is less
+    e = hipFuncSetAttribute((const void*)plan_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            2 * (kMaxIds + 1) * (int)sizeof(int));
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_devices.fetch_or(bit, std::memory_order_release);
   }
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), lds, s, a);
   return hipGetLastError();

@@ -32,6 +32,9 @@
  *   - Work is enqueued on the caller's stream; calls on one pool must be
  *     ordered on one stream (they share the pool's workspace).  Calls that
  *     overlap on different streams race.
+ *   - A pool's host-side state is not locked: calls on one pool (and its
+ *     plans) come from one host thread at a time; different pools may be
+ *     driven from different threads.
  *   - d_in and d_out must be multiples of 8 (16-byte rows of bf16).
  */
 #ifndef HRG_LORA_H
