@@ -539,7 +539,7 @@ __device__ __forceinline__ void split_hi_lo(float v, uint16_t& h, uint16_t& lo) 
 //    segment's V rows the same way, in LDS, while its B loads are in flight.
 // V's bits are the same whichever block forms them.
 template <int QC>
-__global__ __launch_bounds__(256) void expand_small_kernel(GemmArgs a, int fin_blocks) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void expand_small_kernel(GemmArgs a, int fin_blocks) {
   __shared__ __attribute__((aligned(16))) uint16_t vs[2][kSmallRows][kMaxRank];  // hi, lo
   const int N = a.N, T = a.T, w = a.u_ld;
   const int tid = threadIdx.x, l = tid & 63, wid = tid >> 6;
@@ -588,18 +588,18 @@ __global__ __launch_bounds__(256) void expand_small_kernel(GemmArgs a, int fin_b
     const int end = off + len;
     const int nqc = (rank + 15) >> 4;
     const uint16_t* bt = a.pages + (size_t)si.z * a.slot_stride + a.b_off;
-    // this wave's B rows, every rank chunk
-    bf16x8 bb[QC][4];
+    // this wave's B rows one 16-rank chunk at a time (the first goes out
+    // before V is formed): 16 registers for B instead of 16 QC, so that every
+    // item of the launch fits on the chip at once
+    bf16x8 bb[4];
+    auto load_b = [&](int qc) __attribute__((always_inline)) {
 #pragma unroll
-    for (int qc = 0; qc < QC; ++qc) {
-      if (qc < nqc) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = min(g * 128 + 32 * i + (l & 31), N - 1);
-          bb[qc][i] = __builtin_bit_cast(bf16x8, ld16(bt + ((size_t)qc * N + n) * 16 + 8 * (l >> 5)));
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int n = min(g * 128 + 32 * i + (l & 31), N - 1);
+        bb[i] = __builtin_bit_cast(bf16x8, ld16(bt + ((size_t)qc * N + n) * 16 + 8 * (l >> 5)));
       }
-    }
+    };
+    load_b(0);
     // the segment's V rows: thread = (row, 4 ranks)
     const int wq = nqc * 4;
     if (tid < len * wq) {
@@ -622,18 +622,17 @@ __global__ __launch_bounds__(256) void expand_small_kernel(GemmArgs a, int fin_b
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+      // rank chunks in order, hi then lo (the GEMM walker's order)
+      for (int qc = 0; qc < nqc; ++qc) {
+        if (qc > 0 || rb != (off & ~31)) load_b(qc);  // chunk 0 of the first row block is loaded
+        const uint4 hh = *reinterpret_cast<const uint4*>(&vs[0][pr][16 * qc + 8 * (l >> 5)]);
+        const uint4 oo = *reinterpret_cast<const uint4*>(&vs[1][pr][16 * qc + 8 * (l >> 5)]);
+        const bf16x8 mh = __builtin_bit_cast(bf16x8, make_uint4(hh.x & m, hh.y & m, hh.z & m, hh.w & m));
+        const bf16x8 ml = __builtin_bit_cast(bf16x8, make_uint4(oo.x & m, oo.y & m, oo.z & m, oo.w & m));
 #pragma unroll
-      for (int qc = 0; qc < QC; ++qc) {
-        if (qc < nqc) {
-          const uint4 hh = *reinterpret_cast<const uint4*>(&vs[0][pr][16 * qc + 8 * (l >> 5)]);
-          const uint4 oo = *reinterpret_cast<const uint4*>(&vs[1][pr][16 * qc + 8 * (l >> 5)]);
-          const bf16x8 mh = __builtin_bit_cast(bf16x8, make_uint4(hh.x & m, hh.y & m, hh.z & m, hh.w & m));
-          const bf16x8 ml = __builtin_bit_cast(bf16x8, make_uint4(oo.x & m, oo.y & m, oo.z & m, oo.w & m));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[i] = mfma32(bb[qc][i], mh, acc[i]);
-            acc[i] = mfma32(bb[qc][i], ml, acc[i]);
-          }
+        for (int i = 0; i < 4; ++i) {
+          acc[i] = mfma32(bb[i], mh, acc[i]);
+          acc[i] = mfma32(bb[i], ml, acc[i]);
         }
       }
       if (in && gok) {
