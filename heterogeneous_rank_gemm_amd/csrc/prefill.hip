@@ -137,9 +137,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t w3[NS > 3 ? BN * kBK : 8];
   __shared__ __attribute__((aligned(16))) uint16_t x3[NS > 3 ? BM * kBK : 8];
 
-  if constexpr (LORA) {
-    if (*a.status != 0) return;  // strict mode: a failed plan leaves out untouched
-  }
+  // the plan's status is requested with the token order below (one round
+  // of loads) and checked before anything is issued on either
+  int st = 0;
+  if constexpr (LORA) st = *a.status;
   const int T = a.T, N = a.N, K = a.K;
   // this launch's rows: [row0, row1) of the sorted batch (row1 - row0 is a
   // multiple of BM unless row1 = T)
@@ -167,11 +168,35 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
     const int row = 8 * (wid * NWB + i) + (l >> 3);
     woff[i] = row < wrows ? (uint32_t)(row * K + (c0 ^ (i & 1)) * 8) * 2u : kOob;
   }
+  // the token order: every load issued (rows past T read row T - 1, then
+  // point past the operand), so one wait covers them all; the base-only
+  // kernel takes rows in order
 #pragma unroll
   for (int i = 0; i < NXB; ++i) {
     const int p = m0 + 8 * (wid * NXB + i) + (l >> 3);
-    const int tok = p < T ? (a.perm ? a.perm[p] : p) : 0;
-    xoff[i] = p < T ? (uint32_t)(tok * K + (c0 ^ (i & 1)) * 8) * 2u : kOob;
+    int tok;
+    if constexpr (LORA) tok = a.perm[min(p, T - 1)];
+    else tok = p;
+    // a row past T: the offset's top bit puts it past the operand (a mask
+    // rather than a select, so the load is not moved under a branch)
+    xoff[i] = (uint32_t)(tok * K + (c0 ^ (i & 1)) * 8) * 2u | (p < T ? 0u : kOob);
+  }
+  // the output rows of this lane's 32-row blocks, requested in the same
+  // round and held from here (the empty asm keeps the loads from sinking
+  // to the stores, one wait each)
+  int otok[FM];
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    const int p = m0 + wm * (BM / 2) + 32 * j + (l & 31);
+    if constexpr (LORA) otok[j] = a.perm[min(p, T - 1)];
+    else otok[j] = p;
+  }
+  if constexpr (LORA) {
+#pragma unroll
+    for (int j = 0; j < FM; ++j) asm volatile("" : "+v"(otok[j]));
+  }
+  if constexpr (LORA) {
+    if (st != 0) return;  // strict mode: a failed plan leaves out untouched
   }
   auto issue = [&](uint16_t* ws, uint16_t* xs, int k0) __attribute__((always_inline)) {
     dma_issue<NWB, NXB>(rw, rx, ws, xs, woff, xoff, wid, c0, K, k0);
@@ -472,8 +497,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
   for (int j = 0; j < FM; ++j) {
     const int p = m0 + wm * (BM / 2) + 32 * j + (l & 31);
     if (p >= T) continue;
-    const int tok = a.perm ? a.perm[p] : p;
-    uint16_t* orow = a.out + (size_t)tok * N;
+    uint16_t* orow = a.out + (size_t)otok[j] * N;
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
 #pragma unroll
