@@ -182,8 +182,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
     xoff[i] = (uint32_t)(tok * K + (c0 ^ (i & 1)) * 8) * 2u | (p < T ? 0u : kOob);
   }
   // the output rows of this lane's 32-row blocks, requested in the same
-  // round and held from here (the empty asm keeps the loads from sinking
-  // to the stores, one wait each)
+  // round and held from there (an empty asm below keeps the loads from
+  // sinking to the stores, one wait each)
   int otok[FM];
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
@@ -191,9 +191,20 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
     if constexpr (LORA) otok[j] = a.perm[min(p, T - 1)];
     else otok[j] = p;
   }
+  // also in that round: each 32-row block's E rows and its first and last
+  // rows' segments (the expand below starts from them; any load issued
+  // after the K-step DMA would wait for all of it)
+  int erj[FM], rs0[FM], rs1[FM];
   if constexpr (LORA) {
 #pragma unroll
-    for (int j = 0; j < FM; ++j) asm volatile("" : "+v"(otok[j]));
+    for (int j = 0; j < FM; ++j) {
+      const int rb = m0 + wm * (BM / 2) + 32 * j;
+      erj[j] = a.erow[min(rb + (l & 31), T - 1)];
+      rs0[j] = a.row_seg[min(rb, T - 1)];
+      rs1[j] = a.row_seg[min(rb + 31, T - 1)];
+    }
+#pragma unroll
+    for (int j = 0; j < FM; ++j) asm volatile("" : "+v"(otok[j]), "+v"(erj[j]), "+v"(rs0[j]), "+v"(rs1[j]));
   }
   if constexpr (LORA) {
     if (st != 0) return;  // strict mode: a failed plan leaves out untouched
@@ -210,8 +221,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // DMA of the first NS-1 K-steps; it goes out before the expand, so its
-  // latency and the expand's page loads overlap
+  // DMA of the first NS-1 K-steps; it goes out after the E rows' loads
+  // (which then never wait for it) and before the expand's page loads, so
+  // their latencies overlap
   auto prologue = [&]() __attribute__((always_inline)) {
     for_each_stage<NS>([&](auto sc) __attribute__((always_inline)) {
       constexpr int S = decltype(sc)::value;
@@ -222,34 +234,38 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
       }
     });
   };
-  prologue();
-
   if constexpr (LORA) {
     // ---- rows of small segments start from their fp32 E rows (the same
-    // MFMA chain as below, run by the small-segment launch)
+    // MFMA chain as below, run by the small-segment launch).  A block with
+    // any such row loads for all its lanes, through the buffer range check:
+    // a lane of another row, or a column past N, reads zeros (what its
+    // accumulator holds), so no load waits behind a branch.
+    const __amdgpu_buffer_rsrc_t re =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.E, (short)0, kMaxSmallRows * N * 4, 0x00020000);
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
       const int p = m0 + wm * (BM / 2) + 32 * j + (l & 31);
-      const int er = p < T ? a.erow[p] : -1;
-      if (er >= 0) {
-        const float* erow = a.E + (size_t)er * N;
+      const int er = p < T ? erj[j] : -1;
+      if (__ballot(er >= 0) == 0) continue;  // wave-uniform
 #pragma unroll
-        for (int i = 0; i < FN; ++i) {
+      for (int i = 0; i < FN; ++i) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int col = n0 + wn * (BN / 2) + 32 * i + 8 * q + 4 * (l >> 5);
-            if (col < N) {
-              const float4 v = *reinterpret_cast<const float4*>(erow + col);
-              acc[i][j][4 * q + 0] = v.x;
-              acc[i][j][4 * q + 1] = v.y;
-              acc[i][j][4 * q + 2] = v.z;
-              acc[i][j][4 * q + 3] = v.w;
-            }
-          }
+        for (int q = 0; q < 4; ++q) {
+          const int col = n0 + wn * (BN / 2) + 32 * i + 8 * q + 4 * (l >> 5);
+          const uint32_t off = er >= 0 && col < N ? (uint32_t)(er * N + col) * 4u : kOob;
+          const float4 v = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(re, off, 0, 0));
+          acc[i][j][4 * q + 0] = v.x;
+          acc[i][j][4 * q + 1] = v.y;
+          acc[i][j][4 * q + 2] = v.z;
+          acc[i][j][4 * q + 3] = v.w;
         }
       }
     }
 
+  }
+  prologue();
+
+  if constexpr (LORA) {
     // ---- expand first: acc = s_i * (U_t B_i) for every token of a (not
     // small) adapter segment.  V = s U arrives from the shrink as bf16 hi +
     // lo parts (V ~= hi + lo to about 2^-16); the B page is stored transposed
@@ -296,8 +312,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
             vl[j][qc] = zero_bf16x8();
           }
         }
-        const int sg = act ? a.row_seg[rb] : 0;
-        const int sl = act ? a.row_seg[min(rb + 31, T - 1)] : -1;
+        const int sg = act ? rs0[g * JG + j] : 0;
+        const int sl = act ? rs1[g * JG + j] : -1;
         const int sx = sg + (l & 31);
         const bool mine = sx <= sl && l < 32;
         const int sc = min(sx, max(sl, 0));
