@@ -68,14 +68,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   __shared__ uint16_t s_bucket[kStageTok];  // id + 1 of the tokens of one placement block
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int T = a.T;
-  if (*a.status != 0) return;  // a sticky error is pending: leave the tables alone
+  // a sticky error pending leaves the tables alone; the status is checked
+  // once the ids are in (until then only LDS is written)
+  const int st = *a.status;
 
   if (tid == 0) {
     s_err = 0;
     s_nsmall = 0;
   }
   for (int b = tid; b < nb; b += kPlanThreads) start[b] = 0;
-  for (int p = tid; p < T; p += kPlanThreads) a.tab.erow[p] = -1;
   __syncthreads();
 
   // 1. validate every id and count tokens per bucket
@@ -89,11 +90,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
       if (t < kStageTok) s_bucket[t] = (uint16_t)(id + 1);  // the first placement block, staged now
     }
   }
+  if (st != 0) return;
   __syncthreads();
   if (s_err != 0) {
     if (tid == 0) atomicMax(a.status, s_err);
     return;
   }
+  // E rows: none until the small segments below claim theirs (the barrier
+  // after the scans orders these stores before those)
+  for (int p = tid; p < T; p += kPlanThreads) a.tab.erow[p] = -1;
 
   // 2. exclusive scans: counts -> bucket start offsets, non-empty -> segment index
   const int per = (nb + kPlanThreads - 1) / kPlanThreads;
