@@ -278,11 +278,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
     // Every ring load is issued (an item past a walker's last reads a valid
     // page and is not applied), so the loads' completion is counted exactly.
     constexpr int QB = QC < 2 ? QC : 2;  // rank chunks per work item
+    constexpr int kBudget = FN >= 4 ? 96 : 198;  // 256-column tiles keep 256 accumulators live
     // ring of D items in flight per walker: deeper where the tile leaves
-    // registers free (one block per compute unit)
-    constexpr int D = (FN * QB <= 4 && FM <= 2) ? 4 : 2;
+    // registers free (one block per compute unit), but never at the cost of
+    // running the walkers one after another (each group is its own chain of
+    // dependent loads)
+    constexpr int kPerWalker4 = 4 * QB * FN * 4 + QC * 8 + 6;
+    constexpr int D = (FN * QB <= 4 && FM <= 2 && kPerWalker4 * FM <= kBudget) ? 4 : 2;
     constexpr int kPerWalker = D * QB * FN * 4 + QC * 8 + 6;
-    constexpr int kBudget = FN >= 4 ? 54 : 198;  // 256-column tiles keep 256 accumulators live
     // walkers per group: the expand's registers (V, D B buffers) stay
     // within a budget
     constexpr int JG = kPerWalker * FM <= kBudget ? FM : (kPerWalker * 2 <= kBudget ? 2 : 1);
