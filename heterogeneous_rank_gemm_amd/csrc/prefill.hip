@@ -205,6 +205,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < FM; ++j) asm volatile("" : "+v"(otok[j]), "+v"(erj[j]), "+v"(rs0[j]), "+v"(rs1[j]));
+#pragma unroll
+    for (int i = 0; i < NXB; ++i) asm volatile("" : "+v"(xoff[i]));  // formed here, not beside the DMA
   }
   if constexpr (LORA) {
     if (st != 0) return;  // strict mode: a failed plan leaves out untouched
@@ -221,9 +223,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // DMA of the first NS-1 K-steps; it goes out after the E rows' loads
-  // (which then never wait for it) and before the expand's page loads, so
-  // their latencies overlap
+  // DMA of the first NS-1 K-steps; with LoRA it goes out after the E rows'
+  // and the first walkers' table loads (which then never wait for it) and
+  // before the expand's page loads, so their latencies overlap
   auto prologue = [&]() __attribute__((always_inline)) {
     for_each_stage<NS>([&](auto sc) __attribute__((always_inline)) {
       constexpr int S = decltype(sc)::value;
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
     }
 
   }
-  prologue();
+  if constexpr (!LORA) prologue();
 
   if constexpr (LORA) {
     // ---- expand first: acc = s_i * (U_t B_i) for every token of a (not
@@ -298,6 +300,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
       // lane i (mod 32): the block's i-th segment -- first row, end, slot,
       // number of items, first item
       int s_off[JG], s_end[JG], s_slot[JG], s_nqc[JG], s_it0[JG], s_nit[JG];
+      int s_rk[JG], s_id[JG], s_e0[JG];
+      bool s_mine[JG];
 #pragma unroll
       for (int j = 0; j < JG; ++j) {
         const int rb = m0 + wm * (BM / 2) + 32 * (g * JG + j);  // first sorted row of block g*JG+j
@@ -323,8 +327,18 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
         s_off[j] = a.seg_off[sc];
         s_end[j] = a.seg_off[sc + 1];
         s_slot[j] = a.seg_slot[sc];
-        s_nqc[j] = (a.seg_rank[sc] + 15) >> 4;
-        const bool big = mine && a.seg_id[sc] >= 0 && a.seg_e0[sc] < 0;
+        s_rk[j] = a.seg_rank[sc];
+        s_id[j] = a.seg_id[sc];
+        s_e0[j] = a.seg_e0[sc];
+        s_mine[j] = mine;
+      }
+      // the K-step DMA goes out behind the first walkers' loads: vmcnt
+      // counts in issue order, so waiting for these does not wait for it
+      if (g == 0) prologue();
+#pragma unroll
+      for (int j = 0; j < JG; ++j) {
+        s_nqc[j] = (s_rk[j] + 15) >> 4;
+        const bool big = s_mine[j] && s_id[j] >= 0 && s_e0[j] < 0;
         s_nit[j] = big ? (s_nqc[j] + QB - 1) / QB : 0;
         const int inc = wave_incl_scan(s_nit[j]);
         s_it0[j] = inc - s_nit[j];
