@@ -1,22 +1,26 @@
 """Benchmark of the heterogeneous-batch LoRA linear on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5]
 
 A step is one pass of the whole hot path over one batch: the grouping plan
-of the batch's adapter ids, then the LoRA linear of every module of the
-workload (shrink, base GEMM with the fused expand, single bf16 rounding).
-The default workload is the Llama-2-7B q_proj decode batch: 4096 -> 4096,
-64 tokens, 200 resident rank-16 adapters, ids uniform over the 200.
+of the batch's adapter ids (built in-kernel at decode), then the LoRA linear
+of every module of the workload (shrink, base GEMM, expand, single bf16
+rounding).  Linears that read the same X run as one lora_apply_group call.
+The default workload is the largest single-GPU one: a full decode step of a
+32-layer Llama-2-7B-shaped stack (224 linears, 64 tokens, 200 resident
+rank-16 adapters), replayed as one captured hipGraph.
 
-Timing: hip events on the stream the library launches on, K steps between
-two device synchronisations.  Inputs (X, W, ids, the adapter pool) are
-resident in HBM; R independent copies are rotated so the 256 MB
-Infinity Cache cannot hold the working set.
+Timing: hip events on the stream the library launches on, one pair per step
+over K steps between two device synchronisations; the median step is
+reported (the mean beside it).  Inputs (X, W, ids, the adapter pool) are
+resident in HBM; workloads whose state fits the 256 MB Infinity Cache rotate
+R independent copies (cold numbers) and are also timed on one copy (warm,
+labelled as such).
 
 Printed: ONE JSON line with tokens/s, the LoRA overhead against the
-library's own base-only GEMM, the roofline of the dominant launch (the
-apply with a prebuilt plan) and the CPU oracle's throughput on a bounded
-sample of the same workload.
+library's own base-only path, the roofline of the dominant launch pair
+(decode_main + decode_combine, or shrink + GEMM at large T) and the CPU
+oracle's throughput on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -35,10 +39,9 @@ if ROOT not in sys.path:
 import workloads as wk  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
-# Measured HBM traffic per apply, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
-# (scaled by a plain copy of known size); valid only for the kernel source it
-# was measured on.
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "decode_llama2-7b-q_proj-T64_pmc_traffic.md")
+# Measured HBM traffic per step comes from rocprofv3 FETCH_SIZE / WRITE_SIZE
+# runs (scaled by a plain copy of known size), valid only for the kernel
+# source it was measured on.
 KERNEL_SOURCE = os.path.join(ROOT, "heterogeneous_rank_gemm_amd", "csrc", "decode.hip")
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "LoRA-linear tokens/sec at 1 GPU; % overhead vs base-only GEMM; % roofline"
@@ -140,22 +143,50 @@ class Replica:
         self.out = [torch.empty((wl.T, m.d_out), dtype=torch.bfloat16, device="cuda")
                     for m in mods]
         self.xin = [self.X[m.input_group] for m in mods]
+        self.groups = input_groups(wl)
         self.plan = self.pool.plan_create()
         self.pool.plan(self.ids, self.T, self.plan)
 
 
-# Up to 64 tokens (decode) one lora_apply launch groups the batch itself, so a
+def input_groups(wl: wk.Workload):
+    """The workload's linears in call order, those that read one X together
+    (at most 8 per group, in order of first appearance): for a Llama layer
+    [q, k, v, gate, up], [o], [down]."""
+    groups, where = [], {}
+    for j, m in enumerate(wl.modules):
+        k = where.get(m.input_group)
+        if k is None or len(groups[k]) == 8:
+            where[m.input_group] = len(groups)
+            groups.append([j])
+        else:
+            groups[k].append(j)
+    return groups
+
+
+# Up to 64 tokens (decode) one launch pair groups the batch itself, so a
 # step is just the applies; larger batches build one plan per step and every
 # linear of the step reuses it.
 DECODE_MAX_T = 64
 
 
-def _apply(rep: Replica, hrg, j: int, plan):
+def _apply_group(rep: Replica, hrg, g, plan):
     if rep.int4:
-        hrg.lora_apply_q4(rep.pool.handle, j, rep.xin[j], rep.ids, rep.T, rep.Wq[j][0], rep.Wq[j][1],
-                          rep.scratch, rep.out[j], plan)
+        for j in g:
+            hrg.lora_apply_q4(rep.pool.handle, j, rep.xin[j], rep.ids, rep.T, rep.Wq[j][0], rep.Wq[j][1],
+                              rep.scratch, rep.out[j], plan)
     else:
-        hrg.lora_apply(rep.pool.handle, j, rep.xin[j], rep.ids, rep.T, rep.W[j], rep.out[j], plan)
+        hrg.lora_apply_group(rep.pool.handle, g, rep.xin[g[0]], rep.ids, rep.T, [rep.W[j] for j in g],
+                             [rep.out[j] for j in g], plan)
+
+
+def _base_group(rep: Replica, hrg, g):
+    if rep.int4:
+        for j in g:
+            hrg.lora_base_apply_q4(rep.pool.handle, j, rep.xin[j], rep.T, rep.Wq[j][0], rep.Wq[j][1],
+                                   rep.scratch, rep.out[j])
+    else:
+        hrg.lora_base_apply_group(rep.pool.handle, g, rep.xin[g[0]], rep.T, [rep.W[j] for j in g],
+                                  [rep.out[j] for j in g])
 
 
 def lora_step(rep: Replica, hrg):
@@ -163,56 +194,91 @@ def lora_step(rep: Replica, hrg):
     if rep.T > DECODE_MAX_T:
         hrg.lora_plan(rep.pool.handle, rep.ids, rep.T, rep.plan)
         plan = rep.plan
-    for j in range(len(rep.out)):
-        _apply(rep, hrg, j, plan)
+    for g in rep.groups:
+        _apply_group(rep, hrg, g, plan)
 
 
 def apply_only(rep: Replica, hrg):
     """The step without its plan launch (identical to lora_step at decode)."""
     plan = rep.plan if rep.T > DECODE_MAX_T else None
-    for j in range(len(rep.out)):
-        _apply(rep, hrg, j, plan)
+    for g in rep.groups:
+        _apply_group(rep, hrg, g, plan)
 
 
 def base_step(rep: Replica, hrg):
-    h = rep.pool.handle
+    for g in rep.groups:
+        _base_group(rep, hrg, g)
+
+
+def per_linear_step(rep: Replica, hrg):
+    """The step as one lora_apply per linear (no grouping of shared inputs)."""
+    plan = None
+    if rep.T > DECODE_MAX_T:
+        hrg.lora_plan(rep.pool.handle, rep.ids, rep.T, rep.plan)
+        plan = rep.plan
     for j in range(len(rep.out)):
         if rep.int4:
-            hrg.lora_base_apply_q4(h, j, rep.xin[j], rep.T, rep.Wq[j][0], rep.Wq[j][1], rep.scratch,
-                                   rep.out[j])
+            _apply_group(rep, hrg, [j], plan)
         else:
-            hrg.lora_base_apply(h, j, rep.xin[j], rep.T, rep.W[j], rep.out[j])
+            hrg.lora_apply(rep.pool.handle, j, rep.xin[j], rep.ids, rep.T, rep.W[j], rep.out[j], plan)
 
 
 def measured_traffic(workload_name: str):
-    """HBM bytes per apply recorded for this workload, if the decode kernel
-    source is unchanged since the counters were taken; else None."""
+    """HBM bytes per step recorded for this workload by rocprofv3 FETCH_SIZE +
+    WRITE_SIZE runs (profiles/*_pmc_traffic.md), if the decode kernel source
+    is unchanged since the counters were taken; else None."""
+    import glob
     import hashlib
     import re
     try:
-        text = open(TRAFFIC_SUMMARY).read()
         src_hash = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
     except OSError:
         return None
-    m = re.search(r"traffic_bytes_per_apply:\s*(\d+)\s+workload:\s*(\S+)\s+source_sha256:\s*([0-9a-f]+)", text)
-    if not m or m.group(2) != workload_name or m.group(3) != src_hash:
-        return None
-    return int(m.group(1))
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*_pmc_traffic.md"))):
+        text = open(path).read()
+        m = re.search(r"traffic_bytes_per_step:\s*(\d+)\s+workload:\s*(\S+)\s+source_sha256:\s*([0-9a-f]+)",
+                      text)
+        if m and m.group(2) == workload_name and m.group(3) == src_hash:
+            return int(m.group(1))
+    return None
 
 
-def time_steps(fn, reps, steps: int, warmup: int, torch, hrg) -> float:
-    """Average seconds per step over `steps` steps, rotating replicas."""
+def time_steps(fn, reps, steps: int, warmup: int, torch, hrg):
+    """Per-step seconds over `steps` steps (rotating replicas), each step
+    between two events on the current stream; returns (median, mean)."""
     for i in range(warmup):
         fn(reps[i % len(reps)], hrg)
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
     for i in range(steps):
         fn(reps[i % len(reps)], hrg)
-    e1.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e-3 / steps
+    t = np.array([ev[i].elapsed_time(ev[i + 1]) * 1e-3 for i in range(steps)])
+    return float(np.median(t)), float(t.mean())
+
+
+def time_launches(rep, hrg, torch, rounds: int = 5):
+    """Mean seconds of each grouped apply of the step, called eagerly with an
+    event pair around every call (the launch pair decode_main +
+    decode_combine at decode); returns the list per group."""
+    plan = rep.plan if rep.T > DECODE_MAX_T else None
+    if plan is not None:
+        hrg.lora_plan(rep.pool.handle, rep.ids, rep.T, rep.plan)
+    for g in rep.groups:          # warm
+        _apply_group(rep, hrg, g, plan)
+    torch.cuda.synchronize()
+    acc = np.zeros(len(rep.groups))
+    for _ in range(rounds):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(rep.groups))]
+        for k, g in enumerate(rep.groups):
+            ev[2 * k].record()
+            _apply_group(rep, hrg, g, plan)
+            ev[2 * k + 1].record()
+        torch.cuda.synchronize()
+        acc += np.array([ev[2 * k].elapsed_time(ev[2 * k + 1]) * 1e-3 for k in range(len(rep.groups))])
+    return list(acc / rounds)
 
 
 def capture(fn, rep, torch, hrg):
@@ -429,69 +495,164 @@ def target_sets_bench(args, torch, hrg) -> dict:
 # ---------------------------------------------------------------------------
 # CPU oracle baseline
 # ---------------------------------------------------------------------------
-def cpu_baseline(wl: wk.Workload, rep: Replica, seconds: float, torch):
-    """The oracle timed on the host over a bounded sample: the linears of the
-    first layer (all of them for one-layer workloads), repeated for about
-    `seconds`, scaled to whole steps."""
-    import oracle
+def host_info() -> dict:
+    """nproc, the threads this process may run on, and the CPU model name."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"nproc": os.cpu_count(), "affinity": affinity, "cpu_model": model}
+
+
+def _blas_threads() -> int:
     try:
         import threadpoolctl
-        threads = max(int(i.get("num_threads", 1)) for i in threadpoolctl.threadpool_info()) \
-            if threadpoolctl.threadpool_info() else 1
+        info = threadpoolctl.threadpool_info()
+        return max(int(i.get("num_threads", 1)) for i in info) if info else 1
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    n_sample = min(7, len(wl.modules))
+        return os.cpu_count() or 1
+
+
+def _oracle_rate(wl: wk.Workload, ids_np, ranks, X, W, n_sample: int, seconds: float, seed: int):
+    """Linears per second of the oracle over the first n_sample linears of
+    `wl` (X, W: host tensors per linear), run for about `seconds`.  The
+    adapters are drawn on the GPU, as the library's were, and copied back."""
+    import oracle
     mods = wl.modules[:n_sample]
     reg = oracle.Registry(wl.n_adapters, wl.n_adapters, wl.max_rank, [m.d_in for m in mods],
                           [m.d_out for m in mods], wl.T)
-    # the oracle sees the same bf16 bits as the GPU (regenerated on the device, copied back)
-    used = wk.distinct_adapters(rep.ids_np)
-    for i in used:
-        r = int(rep.ranks[i])
+    for i in wk.distinct_adapters(ids_np):
+        r = int(ranks[i])
         A, B = [], []
         for j in range(n_sample):
-            a, b = wk.adapter_weights(wl, i, j, r, wl.default_seed, "cuda")
+            a, b = wk.adapter_weights(wl, i, j, r, seed, "cuda")
             A.append(a.cpu())
             B.append(b.cpu())
         reg.load(i, r, wk.adapter_alpha(wl, r), A, B)
-    X = [x.cpu() for x in rep.xin[:n_sample]]
-    W = [w.cpu() for w in rep.W[:n_sample]]
     n_lin = 0
     t0 = time.perf_counter()
     while True:
         j = n_lin % n_sample
-        oracle.lora_linear(reg, j, X[j], rep.ids_np, W[j])
+        oracle.lora_linear(reg, j, X[j], ids_np, W[j])
         n_lin += 1
         el = time.perf_counter() - t0
-        if el >= seconds and n_lin % n_sample == 0:
+        if (el >= seconds and n_lin % n_sample == 0) or el >= 4 * seconds:
             break
-        if el >= 4 * seconds:
-            break
-    # seconds per sampled layer -> seconds per step of len(wl.modules) linears
+    return n_lin, el
+
+
+def cpu_baseline(wl: wk.Workload, rep: Replica, seconds: float, torch):
+    """The oracle (float64 numpy, the base product through numpy's BLAS) timed
+    on the host over a bounded sample: the linears of the first layer (all of
+    them for one-layer workloads), repeated for about `seconds`, scaled to
+    whole steps; plus the toy workload on one core."""
+    n_sample = min(7, len(wl.modules))
+    # the oracle sees the same bf16 bits as the GPU (copies of the replica's)
+    X = [x.cpu() for x in rep.xin[:n_sample]]
+    W = [w.cpu() for w in rep.W[:n_sample]]
+    threads = _blas_threads()
+    n_lin, el = _oracle_rate(wl, rep.ids_np, rep.ranks, X, W, n_sample, seconds, wl.default_seed)
     t_step = el / (n_lin / n_sample) * (len(wl.modules) / n_sample)
-    return {"value": wl.T / t_step, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_lin} linears ({n_lin / n_sample:.2f} passes over the first {n_sample} "
-                      f"of the {len(wl.modules)} linears of workload '{wl.name}', {wl.T} tokens) "
-                      f"in {el:.1f} s, float64 numpy; scaled to a whole step"}
+    out = {"value": round(wl.T / t_step, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n_lin} linears ({n_lin / n_sample:.2f} passes over the first {n_sample} "
+                     f"of the {len(wl.modules)} linears of workload '{wl.name}', {wl.T} tokens) "
+                     f"in {el:.1f} s, float64 numpy on {threads} BLAS threads; scaled to a whole step"}
+    out.update(host_info())
+    # one core, the toy workload (1024 -> 1024, 64 tokens, 4 rank-8 adapters)
+    try:
+        import threadpoolctl
+        w1 = wk.WORKLOADS[1]
+        ids1, ranks1 = wk.adapter_ids(w1), wk.adapter_ranks(w1)
+        X1 = [wk.activation(w1, w1.modules[0].input_group, w1.modules[0].d_in, device="cuda").cpu()]
+        W1 = [wk.base_weight(w1, 0, device="cuda").cpu()]
+        with threadpoolctl.threadpool_limits(1):
+            n1, el1 = _oracle_rate(w1, ids1, ranks1, X1, W1, 1, 2.0, w1.default_seed)
+        out["one_core_toy"] = {"value": round(w1.T * n1 / el1, 1), "unit": "tokens/s",
+                               "workload": w1.name, "linears": n1, "seconds": round(el1, 2)}
+    except Exception as e:  # pragma: no cover
+        out["one_core_toy"] = f"unavailable: {e}"
+    return out
+
+
+# ---------------------------------------------------------------------------
+# chip peaks (measured denominators printed beside the published ones)
+# ---------------------------------------------------------------------------
+def peaks(torch, steps: int = 20) -> dict:
+    """A streaming read of a 4 GiB device buffer and a register-resident bf16
+    MFMA loop, both timed with events over `steps` launches."""
+    import ctypes as C
+    import heterogeneous_rank_gemm_amd as hrg
+    lib = C.CDLL(hrg._lora.LIB_PATH)
+    lib.hrg_probe_read.argtypes = [C.c_void_p, C.c_size_t, C.c_void_p, C.c_int, C.c_void_p]
+    lib.hrg_probe_mfma.argtypes = [C.c_int, C.c_void_p, C.c_int, C.c_void_p]
+    s = torch.cuda.current_stream().cuda_stream
+    n = 4 << 30
+    buf = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    res = {"cus": cus}
+    best = 0.0
+    for blocks in (cus * 4, cus * 8, cus * 16):
+        sink = torch.zeros(blocks * 4, dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            assert lib.hrg_probe_read(buf.data_ptr(), n, sink.data_ptr(), blocks, s) == 0
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            lib.hrg_probe_read(buf.data_ptr(), n, sink.data_ptr(), blocks, s)
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = n * steps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        res[f"read_GBps_{blocks}_blocks"] = round(gbs, 1)
+        best = max(best, gbs)
+    res["hbm_read_GBps"] = round(best, 1)
+    res["hbm_spec_GBps"] = HBM_PEAK_GBS
+    del buf
+    iters, blocks = 4096, cus * 8
+    sink = torch.zeros(blocks * 256, dtype=torch.float32, device="cuda")
+    lib.hrg_probe_mfma(iters, sink.data_ptr(), blocks, s)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        lib.hrg_probe_mfma(iters, sink.data_ptr(), blocks, s)
+    e1.record()
+    torch.cuda.synchronize()
+    flop = blocks * 4 * iters * 4 * 32768.0 * steps
+    res["mfma_bf16_TFLOPs"] = round(flop / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    res["mfma_bf16_spec_TFLOPs"] = MFMA_BF16_PEAK_TFS
+    return res
 
 
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=sorted(wk.WORKLOADS))
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=5, choices=sorted(wk.WORKLOADS))
     ap.add_argument("--rotate", type=int, default=8, help="independent copies of the state")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", choices=["auto", "on", "off"], default="auto",
                     help="replay each step as one captured hipGraph (auto: for multi-linear "
                          "decode steps)")
-    ap.add_argument("--phase", choices=["all", "lora", "base"], default="all",
-                    help="time only the LoRA apply or only the base-only GEMM (for profiling)")
+    ap.add_argument("--phase", choices=["all", "lora", "base", "linear"], default="all",
+                    help="time only the LoRA step, the base-only step or the per-linear step "
+                         "(for profiling)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (x steps), to scale "
                          "the rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--peaks", action="store_true",
+                    help="measure the chip's streaming-read GB/s and bf16 MFMA TFLOP/s instead")
     ap.add_argument("--int4", action="store_true",
                     help="INT4 (group 128) base weights instead of bf16 (lora_apply_q4)")
     ap.add_argument("--chains", action="store_true",
@@ -521,6 +682,9 @@ def main(argv=None) -> int:
         return 0
     import heterogeneous_rank_gemm_amd as hrg
 
+    if args.peaks:
+        print(json.dumps({"peaks": peaks(torch)}), flush=True)
+        return 0
     if args.paging:
         print(json.dumps({"paging": paging_bench(args, torch, hrg)}), flush=True)
         return 0
@@ -541,23 +705,33 @@ def main(argv=None) -> int:
 
     use_graph = args.graph == "on" or (args.graph == "auto" and wl.T <= DECODE_MAX_T
                                        and len(wl.modules) > 1)
-    f_lora, f_apply, f_base = lora_step, apply_only, base_step
+    f_lora, f_apply, f_base, f_lin = lora_step, apply_only, base_step, per_linear_step
     if use_graph:
         print("[bench] capturing the steps as hipGraphs", file=sys.stderr, flush=True)
         f_lora = graphed(lora_step, reps, torch, hrg)
         f_apply = f_lora if wl.T <= DECODE_MAX_T else graphed(apply_only, reps, torch, hrg)
         f_base = graphed(base_step, reps, torch, hrg)
-    if args.phase == "lora":
-        t_step = time_steps(f_lora, reps, args.steps, args.warmup, torch, hrg)
-        print(json.dumps({"phase": "lora", "ms_per_step": t_step * 1e3}), flush=True)
+        if args.phase in ("all", "linear") and len(wl.modules) > 1:
+            f_lin = graphed(per_linear_step, reps, torch, hrg)
+    if args.phase != "all":
+        fn = {"lora": f_lora, "base": f_base, "linear": f_lin}[args.phase]
+        t_med, t_mean = time_steps(fn, reps, args.steps, args.warmup, torch, hrg)
+        print(json.dumps({"phase": args.phase, "ms_per_step": t_med * 1e3, "mean_ms": t_mean * 1e3}),
+              flush=True)
         return 0
-    if args.phase == "base":
-        t_base = time_steps(f_base, reps, args.steps, args.warmup, torch, hrg)
-        print(json.dumps({"phase": "base", "ms_per_step": t_base * 1e3}), flush=True)
-        return 0
-    t_step = time_steps(f_lora, reps, args.steps, args.warmup, torch, hrg)
-    t_apply = time_steps(f_apply, reps, args.steps, args.warmup, torch, hrg)
-    t_base = time_steps(f_base, reps, args.steps, args.warmup, torch, hrg)
+    t_step, t_step_mean = time_steps(f_lora, reps, args.steps, args.warmup, torch, hrg)
+    t_apply, _ = time_steps(f_apply, reps, args.steps, args.warmup, torch, hrg)
+    t_base, t_base_mean = time_steps(f_base, reps, args.steps, args.warmup, torch, hrg)
+    t_lin = None
+    if len(wl.modules) > 1 and len(reps[0].groups) < len(wl.modules):
+        t_lin, _ = time_steps(f_lin, reps, args.steps, args.warmup, torch, hrg)
+    warm = None
+    if R > 1:
+        # one copy, so the Infinity Cache holds what it can (labelled warm)
+        w_step, _ = time_steps(f_lora, reps[:1], args.steps, args.warmup, torch, hrg)
+        w_base, _ = time_steps(f_base, reps[:1], args.steps, args.warmup, torch, hrg)
+        warm = {"ms_per_step": round(w_step * 1e3, 5), "base_only_ms_per_step": round(w_base * 1e3, 5)}
+    t_groups = time_launches(reps[0], hrg, torch)
     for rp in reps:
         st = rp.pool.status()
         if st != "OK":
@@ -568,22 +742,30 @@ def main(argv=None) -> int:
     lb = float(np.mean([w[1] for w in works]))
     fl = float(np.mean([w[2] for w in works]))
     t_roof = float(np.mean([w[3] for w in works]))
-    n_launch = len(wl.modules)
     hbm_bound = (bb + lb) / (HBM_PEAK_GBS * 1e9) >= fl / (MFMA_BF16_PEAK_TFS * 1e12)
+    # the dominant launch pair, measured live: every grouped apply of one
+    # step, each between its own events (eager), its algorithmic work over
+    # the sum of their durations
+    b0, l0, f0, _ = works[0]
+    n_calls = len(reps[0].groups)
+    t_calls = float(np.sum(t_groups))
+    decode = wl.T <= DECODE_MAX_T
+    kernel = ("decode_main + decode_combine: one launch pair per lora_apply_group call, "
+              f"{n_calls} calls per step" if decode else
+              "shrink_kernel + expand_small_kernel + prefill_kernel per linear, plan_kernel per step")
     if hbm_bound:
-        achieved = (bb + lb) / n_launch / (t_apply / n_launch) / 1e9
-        traffic = measured_traffic(wl.name) if wl.T <= DECODE_MAX_T and not args.int4 else None
+        achieved = (b0 + l0) / t_calls / 1e9
+        traffic = measured_traffic(wl.name) if decode and not args.int4 else None
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "lora_apply = decode_main + decode_combine" if wl.T <= DECODE_MAX_T
-                else "lora_apply = shrink_kernel + gemm_kernel",
-                "algorithmic_bytes_per_apply": round((bb + lb) / n_launch)}
+                "kernel": kernel, "algorithmic_bytes_per_step": round(b0 + l0),
+                "launch_seconds_per_step": t_calls, "calls_per_step": n_calls}
     else:
-        achieved = fl / n_launch / (t_apply / n_launch) / 1e12
+        achieved = f0 / t_calls / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4),
-                "traffic": None, "kernel": "lora_apply = shrink_kernel + gemm_kernel",
-                "algorithmic_flops_per_apply": round(fl / n_launch)}
+                "traffic": None, "kernel": kernel, "algorithmic_flops_per_step": round(f0),
+                "launch_seconds_per_step": t_calls, "calls_per_step": n_calls}
 
     cpu = None
     if not args.no_cpu_baseline and not args.int4:
@@ -608,13 +790,19 @@ def main(argv=None) -> int:
                    "n_linears": len(wl.modules), "adapters": wl.n_adapters,
                    "ranks": list(wl.rank_choices), "max_rank": wl.max_rank,
                    "replicas_rotated": R, "hipgraph": use_graph,
+                   "calls_per_step": n_calls,
                    "base_weight": "int4-g128" if args.int4 else "bf16"},
+        "timing": f"median of {args.steps} steps (event pair per step) after {args.warmup} warm-up steps",
+        "mean_ms_per_step": round(t_step_mean * 1e3, 5),
         "lora_overhead_pct": round(100.0 * (t_step - t_base) / t_base, 2),
         "base_only_ms_per_step": round(t_base * 1e3, 5),
         "apply_ms_per_step": round(t_apply * 1e3, 5),
+        "per_linear_ms_per_step": round(t_lin * 1e3, 5) if t_lin else None,
+        "warm": warm,
         "step_roofline_frac": round(t_roof / t_step, 4),
         "algorithmic": {"base_bytes": bb, "lora_bytes": lb, "flops": fl,
-                        "t_roof_us": round(t_roof * 1e6, 3)},
+                        "t_roof_us": round(t_roof * 1e6, 3),
+                        "lora_overhead_floor_pct": round(100.0 * lb / bb, 2) if hbm_bound else None},
         "roofline": roof,
         "cpu_baseline": cpu,
     }

@@ -12,7 +12,7 @@ from ._lora import (LoraError, STATUS_NAMES, EXPORTED, lora_status_string, lora_
                     lora_status, lora_debug_read_plan, lora_host_cache_create,
                     lora_host_register, lora_host_unregister, lora_prefetch, lora_pin_adapter,
                     lora_paging_query, lora_paging_stats, lora_q4_pack, lora_apply_q4,
-                    lora_base_apply_q4, lora_load_chain)
+                    lora_base_apply_q4, lora_load_chain, lora_apply_group, lora_base_apply_group)
 from .pool import LoraPool
 
 __all__ = [
@@ -22,5 +22,5 @@ __all__ = [
     "lora_base_apply", "lora_status", "lora_debug_read_plan", "lora_host_cache_create",
     "lora_host_register", "lora_host_unregister", "lora_prefetch", "lora_pin_adapter",
     "lora_paging_query", "lora_paging_stats", "lora_q4_pack", "lora_apply_q4", "lora_base_apply_q4",
-    "lora_load_chain",
+    "lora_load_chain", "lora_apply_group", "lora_base_apply_group",
 ]

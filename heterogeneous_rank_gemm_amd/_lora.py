@@ -30,7 +30,7 @@ EXPORTED = (
     "lora_plan", "lora_apply", "lora_base_apply", "lora_status", "lora_debug_read_plan",
     "lora_host_cache_create", "lora_host_register", "lora_host_unregister", "lora_prefetch",
     "lora_pin_adapter", "lora_paging_query", "lora_paging_stats", "lora_q4_pack", "lora_apply_q4",
-    "lora_base_apply_q4", "lora_load_chain",
+    "lora_base_apply_q4", "lora_load_chain", "lora_apply_group", "lora_base_apply_group",
 )
 
 _vp = C.c_void_p
@@ -63,6 +63,8 @@ _sigs = {
     "lora_apply_q4": [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp],
     "lora_base_apply_q4": [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _vp],
     "lora_load_chain": [_vp, _i32, _i32, _P_i32, _vp],
+    "lora_apply_group": [_vp, _i32, _P_i32, _vp, _vp, _i32, C.POINTER(_vp), C.POINTER(_vp), _vp, _vp],
+    "lora_base_apply_group": [_vp, _i32, _P_i32, _vp, _i32, C.POINTER(_vp), C.POINTER(_vp), _vp],
 }
 for _name, _args in _sigs.items():
     _f = getattr(_lib, _name)
@@ -163,6 +165,28 @@ def lora_apply(pool: int, module: int, X, ids, T: int, W, out, plan: Optional[in
                stream=None) -> None:
     _check(_lib.lora_apply(pool, module, _ptr(X), _ptr(ids), T, _ptr(W), _ptr(out), plan,
                            _stream(stream)), "lora_apply")
+
+
+def _group_arrays(modules: Sequence[int], W: Sequence, out: Sequence):
+    n = len(modules)
+    mods = (C.c_int32 * max(n, 1))(*[int(m) for m in modules])
+    pw = (_vp * max(n, 1))(*[_ptr(w) for w in W])
+    po = (_vp * max(n, 1))(*[_ptr(o) for o in out])
+    return n, mods, pw, po
+
+
+def lora_apply_group(pool: int, modules: Sequence[int], X, ids, T: int, W: Sequence, out: Sequence,
+                     plan: Optional[int] = None, stream=None) -> None:
+    n, mods, pw, po = _group_arrays(modules, W, out)
+    _check(_lib.lora_apply_group(pool, n, mods, _ptr(X), _ptr(ids), T, pw, po, plan, _stream(stream)),
+           "lora_apply_group")
+
+
+def lora_base_apply_group(pool: int, modules: Sequence[int], X, T: int, W: Sequence, out: Sequence,
+                          stream=None) -> None:
+    n, mods, pw, po = _group_arrays(modules, W, out)
+    _check(_lib.lora_base_apply_group(pool, n, mods, _ptr(X), T, pw, po, _stream(stream)),
+           "lora_base_apply_group")
 
 
 def lora_base_apply(pool: int, module: int, X, T: int, W, out, stream=None) -> None:

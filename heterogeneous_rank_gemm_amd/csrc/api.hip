@@ -98,44 +98,78 @@ lora_status_t run_plan(lora_pool_s* P, const int32_t* ids, int32_t T, lora_plan_
 
 bool module_ok(const lora_pool_s* P, int32_t m) { return P && m >= 0 && m < P->n_modules; }
 
-lora_status_t decode_apply(lora_pool_s* P, int32_t module, const lora_bf16_t* X, const int32_t* ids,
-                           int32_t T, const lora_bf16_t* W, const uint32_t* Wq, const uint32_t* Wsz,
-                           lora_bf16_t* out, bool lora, hipStream_t stream) {
-  const int K = P->d_in[module], N = P->d_out[module];
+// The decode path (T <= kDecodeMaxT) for a group of n linears that read the
+// same X (one launch pair; a single linear is a group of one).
+lora_status_t decode_group(lora_pool_s* P, int32_t n, const int32_t* modules, const lora_bf16_t* X,
+                           const int32_t* ids, int32_t T, const lora_bf16_t* const* W,
+                           const uint32_t* const* Wq, const uint32_t* const* Wsz, lora_bf16_t* const* out,
+                           bool lora, float* part, float* upart, hipStream_t stream) {
+  const int K = P->d_in[modules[0]];
   hrg::DecodeArgs a{};
   a.X = X;
-  a.W = W;
-  a.out = out;
   a.ids = ids;
   a.T = T;
-  a.N = N;
   a.K = K;
+  a.KS = ceil_div(K, hrg::kDecodeChunk);
+  a.n_mod = n;
+  a.wq = Wq ? 1 : 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t m = modules[i], N = P->d_out[m];
+    a.W[i] = W ? W[i] : nullptr;
+    a.Wq[i] = Wq ? Wq[i] : nullptr;
+    a.Wsz[i] = Wsz ? Wsz[i] : nullptr;
+    a.out[i] = out[i];
+    a.N[i] = N;
+    a.module[i] = m;
+    a.a_off[i] = P->a_off[m];
+    a.b_off[i] = P->b_off[m];
+    a.u0[i + 1] = a.u0[i] + ceil_div(N, 16);
+    a.n0[i + 1] = a.n0[i] + round_up(N, 16);
+    a.ct0[i + 1] = a.ct0[i] + ceil_div(N, hrg::kDecodeTileRows);
+  }
+  for (int32_t i = n + 1; i <= hrg::kMaxGroup; ++i) {
+    a.u0[i] = a.u0[n];
+    a.n0[i] = a.n0[n];
+    a.ct0[i] = a.ct0[n];
+  }
+  a.npad = a.n0[n];
   a.max_ids = P->max_ids;
   a.id_info = P->id_info;
   a.id_bscale = P->id_bscale;
   a.pages = P->pages;
   a.slot_stride = P->slot_elems;
-  a.a_off = P->a_off[module];
-  a.b_off = P->b_off[module];
-  a.part = P->dec_part;
-  a.upart = P->dec_upart;
+  a.part = part;
+  a.upart = upart;
   a.direct = P->max_ids <= P->max_adapters ? 1 : 0;
   a.max_slots = P->max_adapters;
   a.rmax = P->max_rank;
   a.u_ld = P->rpad;
   a.status = P->status;
-  a.NT = ceil_div(N, hrg::kDecodeTileRows);
-  a.KS = ceil_div(K, hrg::kDecodeChunk);
-  a.npad = a.NT * hrg::kDecodeTileRows;
   a.lora = lora ? 1 : 0;
-  a.module = module;
-  a.Wq = Wq;
-  a.Wsz = Wsz;
-  // A items: (adapter, 16-rank block); at most min(T, resident) adapters
-  // (the launcher places them)
-  const int loaded = P->max_adapters - (int)P->free_slots.size();
-  const int items = lora ? std::min(T, loaded) * (P->rpad / 16) : 0;
-  return hrg::launch_decode(a, items, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+  // A items: (adapter, 16-rank block); a batch holds at most min(T, slots,
+  // ids) distinct adapters.  Sized from the pool's capacity, never from how
+  // many adapters are resident now: a captured graph replays this launch
+  // after later loads and prefetches, and items the grid does not hold would
+  // be skipped.  The kernel walks only the batch's own items.
+  const int items_cap = std::min(T, std::min(P->max_adapters, P->max_ids)) * (P->rpad / 16);
+  return hrg::launch_decode(a, items_cap, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+// Floats of the decode partial planes a group of up to kMaxGroup linears
+// with one d_in needs: KS chunks x 64 tokens x the columns (each linear's
+// rounded up to 16) of its largest members.
+size_t decode_part_floats(const std::vector<int32_t>& d_in, const std::vector<int32_t>& d_out) {
+  size_t best = 0;
+  for (size_t i = 0; i < d_in.size(); ++i) {
+    std::vector<int32_t> cols;
+    for (size_t j = 0; j < d_in.size(); ++j)
+      if (d_in[j] == d_in[i]) cols.push_back(round_up(d_out[j], 16));
+    std::sort(cols.rbegin(), cols.rend());
+    size_t sum = 0;
+    for (size_t j = 0; j < cols.size() && j < (size_t)hrg::kMaxGroup; ++j) sum += cols[j];
+    best = std::max(best, (size_t)ceil_div(d_in[i], hrg::kDecodeChunk) * hrg::kDecodeMaxT * sum);
+  }
+  return best;
 }
 
 }  // namespace
@@ -167,6 +201,8 @@ lora_status_t lora_pool_create(lora_pool_t* pool, int32_t max_adapters, int32_t 
   for (int32_t m = 0; m < n_modules; ++m) {
     if (d_in[m] < 8 || d_in[m] > 65536 || d_in[m] % 8) return LORA_ERR_INVALID_ARG;
     if (d_out[m] < 8 || d_out[m] > 65536 || d_out[m] % 8) return LORA_ERR_INVALID_ARG;
+    // the decode kernels address a base weight with 32-bit byte offsets
+    if ((int64_t)d_in[m] * d_out[m] * 2 > (int64_t)INT32_MAX) return LORA_ERR_INVALID_ARG;
   }
   lora_pool_s* P = new (std::nothrow) lora_pool_s();
   if (!P) return LORA_ERR_OOM;
@@ -214,9 +250,8 @@ lora_status_t lora_pool_create(lora_pool_t* pool, int32_t max_adapters, int32_t 
   const size_t ks_max = (max_din + hrg::kDecodeChunk - 1) / hrg::kDecodeChunk;
   if (ok)
     ok = dmalloc(&P->E, (size_t)hrg::kMaxSmallRows * max_dout) == hipSuccess &&
-         dmalloc(&P->dec_upart, ks_max * hrg::kDecodeMaxT * P->rpad) == hipSuccess &&
-         dmalloc(&P->dec_part, ks_max * hrg::kDecodeMaxT * round_up((int)max_dout, hrg::kDecodeTileRows)) ==
-             hipSuccess;
+         dmalloc(&P->dec_upart, ks_max * hrg::kMaxGroup * hrg::kDecodeMaxT * P->rpad) == hipSuccess &&
+         dmalloc(&P->dec_part, decode_part_floats(P->d_in, P->d_out)) == hipSuccess;
   if (ok) ok = plan_alloc(P, &P->internal) == LORA_OK;
   if (!ok) {
     (void)hipGetLastError();
@@ -460,32 +495,13 @@ lora_status_t lora_plan(lora_pool_t P, const int32_t* ids, int32_t T, lora_plan_
   return run_plan(P, ids, T, plan, stream);
 }
 
-// The INT4 base weight (Wq, Wsz; W == nullptr) is dequantized in the decode
-// kernel's registers, or into the caller's `scratch` (d_out x d_in bf16)
-// before the batched path's GEMM.
-static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t* X,
-                                const int32_t* ids, int32_t T, const lora_bf16_t* W,
-                                const uint32_t* Wq, const uint32_t* Wsz, lora_bf16_t* scratch,
-                                lora_bf16_t* out, lora_plan_t plan, bool lora, hipStream_t stream) {
-  if (!module_ok(P, module)) return LORA_ERR_INVALID_ARG;
-  if (T < 0 || T > P->max_tokens) return LORA_ERR_INVALID_ARG;
+// The batched path (T > kDecodeMaxT) of one linear: the shrink, the
+// small-segment expand and the GEMM with the fused expand, on a plan `pl`
+// already built for the batch (lora), or the plain GEMM (base only).
+static lora_status_t batched_apply(lora_pool_s* P, int32_t module, const lora_bf16_t* X, int32_t T,
+                                   const lora_bf16_t* W, lora_bf16_t* out, lora_plan_s* pl, bool lora,
+                                   hipStream_t stream) {
   const int K = P->d_in[module], N = P->d_out[module];
-  const bool q4 = Wq != nullptr || Wsz != nullptr;
-  if (q4 && (!Wq || !Wsz || K % hrg::kQ4Group != 0 || (T > hrg::kDecodeMaxT && !scratch)))
-    return LORA_ERR_INVALID_ARG;
-  if (T == 0) return LORA_OK;
-  if (!X || (!W && !q4) || !out || (lora && !ids)) return LORA_ERR_INVALID_ARG;
-  if (plan) {
-    if (!P->plans.count(plan) || plan->T != T || plan->ids != ids) return LORA_ERR_INVALID_ARG;
-  }
-  DeviceGuard g(P->device);
-  if (T <= hrg::kDecodeMaxT) return decode_apply(P, module, X, ids, T, W, Wq, Wsz, out, lora, stream);
-  // the batched path addresses X with 32-bit byte offsets
-  if ((size_t)T * K * 2 > (size_t)INT32_MAX) return LORA_ERR_INVALID_ARG;
-  if (q4) {
-    if (hrg::launch_q4_dequant(Wq, Wsz, N, K, scratch, stream) != hipSuccess) return LORA_ERR_HIP;
-    W = scratch;
-  }
   hrg::GemmArgs ga{};
   ga.X = X;
   ga.W = W;
@@ -497,12 +513,6 @@ static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t
   if (!lora) {
     ga.perm = nullptr;
     return hrg::launch_prefill(ga, false, -1, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
-  }
-  lora_plan_s* pl = plan;
-  if (!pl) {
-    pl = P->internal;
-    lora_status_t st = run_plan(P, ids, T, pl, stream);
-    if (st != LORA_OK) return st;
   }
   // shrink: a fixed grid walks the plan's (tile, K-split) items; K splits of
   // at least 512 (at most kMaxSplits planes)
@@ -553,29 +563,110 @@ static lora_status_t apply_impl(lora_pool_t P, int32_t module, const lora_bf16_t
   return hrg::launch_prefill(ga, true, -1, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
 }
 
+// Host checks shared by every apply entry point (no side effects on error):
+// n distinct linears of one d_in, sizes, pointers, the plan, INT4 rules.
+static lora_status_t check_apply(lora_pool_t P, int32_t n, const int32_t* modules, const lora_bf16_t* X,
+                                 const int32_t* ids, int32_t T, const lora_bf16_t* const* W,
+                                 const uint32_t* const* Wq, const uint32_t* const* Wsz,
+                                 lora_bf16_t* scratch, lora_bf16_t* const* out, lora_plan_t plan,
+                                 bool lora) {
+  if (!P || n < 1 || n > hrg::kMaxGroup || !modules || !out) return LORA_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i) {
+    if (!module_ok(P, modules[i])) return LORA_ERR_INVALID_ARG;
+    if (P->d_in[modules[i]] != P->d_in[modules[0]]) return LORA_ERR_INVALID_ARG;
+    for (int32_t j = 0; j < i; ++j)
+      if (modules[j] == modules[i]) return LORA_ERR_INVALID_ARG;
+  }
+  if (T < 0 || T > P->max_tokens) return LORA_ERR_INVALID_ARG;
+  const int K = P->d_in[modules[0]];
+  const bool q4 = Wq != nullptr || Wsz != nullptr;
+  if (q4 && (!Wq || !Wsz || K % hrg::kQ4Group != 0 || (T > hrg::kDecodeMaxT && !scratch)))
+    return LORA_ERR_INVALID_ARG;
+  if (T == 0) return LORA_OK;
+  if (!X || (!W && !q4) || (lora && !ids)) return LORA_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i) {
+    if (!out[i]) return LORA_ERR_INVALID_ARG;
+    if (q4 ? (!Wq[i] || !Wsz[i]) : !W[i]) return LORA_ERR_INVALID_ARG;
+  }
+  if (plan) {
+    if (!P->plans.count(plan) || plan->T != T || plan->ids != ids) return LORA_ERR_INVALID_ARG;
+  }
+  // the batched path addresses X with 32-bit byte offsets
+  if (T > hrg::kDecodeMaxT && (size_t)T * K * 2 > (size_t)INT32_MAX) return LORA_ERR_INVALID_ARG;
+  return LORA_OK;
+}
+
+// The INT4 base weight (Wq, Wsz; W == nullptr) is dequantized in the decode
+// kernel's registers, or into the caller's `scratch` (d_out x d_in bf16)
+// before each linear's GEMM on the batched path.
+static lora_status_t apply_impl(lora_pool_t P, int32_t n, const int32_t* modules, const lora_bf16_t* X,
+                                const int32_t* ids, int32_t T, const lora_bf16_t* const* W,
+                                const uint32_t* const* Wq, const uint32_t* const* Wsz,
+                                lora_bf16_t* scratch, lora_bf16_t* const* out, lora_plan_t plan, bool lora,
+                                hipStream_t stream) {
+  const lora_status_t st = check_apply(P, n, modules, X, ids, T, W, Wq, Wsz, scratch, out, plan, lora);
+  if (st != LORA_OK || T == 0) return st;
+  DeviceGuard g(P->device);
+  if (T <= hrg::kDecodeMaxT)
+    return decode_group(P, n, modules, X, ids, T, W, Wq, Wsz, out, lora, P->dec_part, P->dec_upart, stream);
+  lora_plan_s* pl = plan;
+  if (lora && !pl) {
+    // one plan serves every linear of the call
+    pl = P->internal;
+    const lora_status_t s2 = run_plan(P, ids, T, pl, stream);
+    if (s2 != LORA_OK) return s2;
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t m = modules[i];
+    const lora_bf16_t* Wi = W ? W[i] : nullptr;
+    if (Wq) {
+      if (hrg::launch_q4_dequant(Wq[i], Wsz[i], P->d_out[m], P->d_in[m], scratch, stream) != hipSuccess)
+        return LORA_ERR_HIP;
+      Wi = scratch;
+    }
+    const lora_status_t s3 = batched_apply(P, m, X, T, Wi, out[i], pl, lora, stream);
+    if (s3 != LORA_OK) return s3;
+  }
+  return LORA_OK;
+}
+
 lora_status_t lora_apply(lora_pool_t P, int32_t module, const lora_bf16_t* X, const int32_t* ids,
                          int32_t T, const lora_bf16_t* W, lora_bf16_t* out, lora_plan_t plan,
                          hipStream_t stream) {
-  return apply_impl(P, module, X, ids, T, W, nullptr, nullptr, nullptr, out, plan, true, stream);
+  return apply_impl(P, 1, &module, X, ids, T, &W, nullptr, nullptr, nullptr, &out, plan, true, stream);
 }
 
 lora_status_t lora_base_apply(lora_pool_t P, int32_t module, const lora_bf16_t* X, int32_t T,
                               const lora_bf16_t* W, lora_bf16_t* out, hipStream_t stream) {
-  return apply_impl(P, module, X, nullptr, T, W, nullptr, nullptr, nullptr, out, nullptr, false, stream);
+  return apply_impl(P, 1, &module, X, nullptr, T, &W, nullptr, nullptr, nullptr, &out, nullptr, false, stream);
+}
+
+lora_status_t lora_apply_group(lora_pool_t P, int32_t n, const int32_t* modules, const lora_bf16_t* X,
+                               const int32_t* ids, int32_t T, const lora_bf16_t* const* W,
+                               lora_bf16_t* const* out, lora_plan_t plan, hipStream_t stream) {
+  if (!W) return LORA_ERR_INVALID_ARG;
+  return apply_impl(P, n, modules, X, ids, T, W, nullptr, nullptr, nullptr, out, plan, true, stream);
+}
+
+lora_status_t lora_base_apply_group(lora_pool_t P, int32_t n, const int32_t* modules, const lora_bf16_t* X,
+                                    int32_t T, const lora_bf16_t* const* W, lora_bf16_t* const* out,
+                                    hipStream_t stream) {
+  if (!W) return LORA_ERR_INVALID_ARG;
+  return apply_impl(P, n, modules, X, nullptr, T, W, nullptr, nullptr, nullptr, out, nullptr, false, stream);
 }
 
 lora_status_t lora_apply_q4(lora_pool_t P, int32_t module, const lora_bf16_t* X, const int32_t* ids,
                             int32_t T, const uint32_t* Wq, const uint32_t* Wsz, lora_bf16_t* W_scratch,
                             lora_bf16_t* out, lora_plan_t plan, hipStream_t stream) {
   if (!Wq || !Wsz) return LORA_ERR_INVALID_ARG;
-  return apply_impl(P, module, X, ids, T, nullptr, Wq, Wsz, W_scratch, out, plan, true, stream);
+  return apply_impl(P, 1, &module, X, ids, T, nullptr, &Wq, &Wsz, W_scratch, &out, plan, true, stream);
 }
 
 lora_status_t lora_base_apply_q4(lora_pool_t P, int32_t module, const lora_bf16_t* X, int32_t T,
                                  const uint32_t* Wq, const uint32_t* Wsz, lora_bf16_t* W_scratch,
                                  lora_bf16_t* out, hipStream_t stream) {
   if (!Wq || !Wsz) return LORA_ERR_INVALID_ARG;
-  return apply_impl(P, module, X, nullptr, T, nullptr, Wq, Wsz, W_scratch, out, nullptr, false, stream);
+  return apply_impl(P, 1, &module, X, nullptr, T, nullptr, &Wq, &Wsz, W_scratch, &out, nullptr, false, stream);
 }
 
 lora_status_t lora_q4_pack(const uint8_t* q, const uint8_t* z, const lora_bf16_t* s, int32_t N, int32_t K,

@@ -1,39 +1,40 @@
 // Decode-shaped LoRA linear (T <= 64 tokens): two launches, no inter-block
-// waiting.
+// waiting, for a group of up to kMaxGroup linears that read the same X (the
+// q/k/v and gate/up projections of a transformer layer read one hidden
+// state; a single linear is a group of one).
 //
 // At decode the linear is bound by bytes: W once, plus the A and B pages of
 // every distinct adapter in the batch.  X is small (T x K), but every column
-// tile needs all of it, so it is staged once per K chunk in LDS and never
-// re-read from L2 per 16 columns.
+// of W needs all of it, so it is staged once per K chunk in LDS and never
+// re-read from L2 per 16 columns.  A group shares that staging: one launch
+// streams every linear's W rows against the one X chunk, where separate
+// launches would each stage X again and each pay a ramp and a tail.
 //
-// Launch 1 (decode_main): a grid of (column tile, 1024-deep K chunk) blocks.
-// Each block's first four waves copy X[:, chunk] (64 x 1024 bf16, 132 KB with
-// row padding) into LDS by direct DMA and own 16 rows of W each; every wave
-// loads its whole 16 x 1024 slice into registers up front (32 KB in flight per
-// wave) and runs bf16 MFMA 16x16x32 against the X chunk as the slice lands.
-// Two kinds of waves:
-//   * W waves (the first four of a block): 16 rows of the base weight; the
-//     fp32 partial sums go to part[chunk][t][n].
-//   * A waves (the rest): one item (adapter, 16 ranks) each, i.e. 16 rows of
-//     an adapter's A^T page.  The wave groups the batch by adapter id
+// Launch 1 (decode_main): blocks of WPB waves, each block keeping one
+// 1024-deep K chunk of X (64 x 1024 bf16, 132 KB with row padding) in LDS,
+// copied by direct DMA.  The chunk's work is a list of 16-row units:
+//   * W units: 16 rows of one linear's base weight; the fp32 partial sums go
+//     to part[chunk][t][column];
+//   * A units: one (adapter, 16-rank block) item on one linear, i.e. 16 rows
+//     of the adapter's A^T page.  The batch is grouped by adapter id
 //     (LoRA-Land post, section "2. multi-LoRA batch scheduling": Grouped
 //     Multi-LoRA Execution), so each adapter's page is streamed once per
 //     chunk; the partial shrink U_c[t, q] = X[t, chunk] . A[chunk, q] is kept
-//     for the adapter's own tokens in upart[chunk][t][q].
-// Riding in the W tiles' blocks, the A items add no second round of blocks.
-// Items past what those waves hold go to extra blocks of A waves only.  The
-// A waves' id loads go out before the weight stream fills the memory
-// queues; a load issued behind that stream waits for most of it, so every
-// further dependent round costs several microseconds.  A direct-mapped pool
-// (adapter id in slot id) therefore needs no slot-table round at all.
+//     for the adapter's own tokens in upart[chunk][linear][t][q].
+// The W units come first and the A units last; wave i of a chunk takes units
+// i, i + NWc, i + 2 NWc, ... (NWc waves per chunk), so every wave streams
+// about the same number of bytes and no adapter work is left to a second
+// round of blocks.  A unit is two 512-deep halves through two register
+// buffers: the next half's loads are in flight while the current half's MFMAs
+// run.
 // Launch 2 (decode_combine), one thread per (token, 4 columns):
-//     V[t, q]   = (alpha/r) * sum_chunks upart[c][t][q]
+//     V[t, q]   = (alpha/r) * sum_chunks upart[c][linear][t][q]
 //     out[t, n] = bf16( sum_chunks part[c][t][n]  +  sum_q V[t, q] B_i[q, n] )
 //   chunks added in order, the expand in fp32, a single rounding (icman
 //   report, section 2.1: the low-rank branch is added back to the main path).
 //   Rows with id -1 get no LoRA term at all.
 //
-// The base-only entry runs the same launches without A waves and without the
+// The base-only entry runs the same launches without A units and without the
 // expand, so id -1 rows match it bit for bit.  Every combine block validates
 // all the ids the same way (strict mode, icman report section 4.1): on an
 // invalid batch nothing is written to `out`.
@@ -42,14 +43,15 @@
 
 namespace hrg {
 
-constexpr int kSteps = kDecodeChunk / 32;  // MFMA K steps per chunk (32)
+constexpr int kHalf = kDecodeChunk / 2;    // K of one register block (a "half")
+constexpr int kHS = kHalf / 32;            // MFMA K steps per half (16)
 constexpr int kXs = kDecodeChunk + 8;      // LDS row of the X chunk (16-byte pad)
+constexpr int kXPieces = 2 * 64;           // 1-KB DMA pieces of an X chunk
 constexpr uint32_t kOobOff = 0x80000000u;  // buffer offset past every operand
-static_assert(4 * 16 == kDecodeTileRows, "tile rows");
+constexpr int kBufFlags = 0x00020000;      // buffer resource word 3 (raw, dword data)
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 // v if keep, else zero -- with a mask, so the compiler never selects between
 // addresses (which would push register arrays to scratch memory)
 __device__ __forceinline__ uint4 keep_if(bool keep, uint4 v) {
@@ -63,398 +65,418 @@ __device__ __forceinline__ float hi_f(uint32_t v) { return __builtin_bit_cast(fl
 // are always targeted).
 __device__ __forceinline__ bool targets(int mask, int m) { return m >= 32 || ((mask >> m) & 1); }
 
-// Token t's adapter lookup (lane t of a wave, t < 64): id, pool slot, true
-// rank and scale, or bad = the status code of an invalid id.  All lanes load
-// in parallel, so a wave pays one round of dependent loads, not one per token.
-struct TokInfo {
-  int id = -1, slot = -1, rank = 0, bad = 0;
-  float scale = 0.f;
-};
-
-__device__ __forceinline__ TokInfo token_info(const DecodeArgs& a, int t) {
-  TokInfo ti;
-  if (t < a.T) {
-    const int id = a.ids[t];
-    if (id < -1 || id >= a.max_ids) {
-      ti.bad = kStatusIdRange;
-    } else if (id >= 0) {
-      const int4 e = a.id_info[id];  // {slot, rank, scale bits, module mask}: one load after ids
-      if (e.x < 0) {
-        ti.bad = kStatusNotLoaded;
-      } else {
-        ti.id = id;
-        ti.slot = e.x;
-        // an adapter that does not target this linear has no rank here
-        ti.rank = targets(e.w, a.module) ? (e.y & (kChainRankFlag - 1)) : 0;
-        ti.scale = __builtin_bit_cast(float, e.z);
-      }
-    }
-  }
-  return ti;
+// The kernel's argument block in the kernarg segment (constant memory).  The
+// per-linear tables are read through it with a wave-uniform index: one scalar
+// load each, where indexing the by-value argument with a variable would copy
+// the whole table to scratch memory.
+typedef const __attribute__((address_space(4))) DecodeArgs* KArgs;
+__device__ __forceinline__ KArgs kargs() {
+  return (KArgs)__builtin_amdgcn_kernarg_segment_ptr();
 }
+
+// A buffer resource over [p, p + bytes) whose words the compiler knows to be
+// wave-uniform (p and bytes must be): without the readfirstlanes it may keep
+// an address computed by vector instructions in VGPRs and then wrap every
+// load in a loop over the distinct values.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* p, int bytes) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
+                                           __builtin_amdgcn_readfirstlane(bytes), kBufFlags);
+}
+
+// The linear of the group whose range [p[m], p[m+1]) holds x (p[0] = 0; the
+// host fills p[i] = p[n] for i > n).
+__device__ __forceinline__ int group_of(const int32_t (&p)[kMaxGroup + 1], int x) {
+  // (constant indices: no scratch copy)
+  int m = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i) m += x >= p[i] ? 1 : 0;
+  return m;
+}
+
+// One 16-row unit of a wave's walk: where its rows come from (needed until
+// its second half is requested) and where its results go (needed until its
+// store).  Every field is wave-uniform but the offsets.
+struct UnitSrc {
+  __amdgpu_buffer_rsrc_t rs;  // rows of the unit's source: a W, Wq or A page
+  __amdgpu_buffer_rsrc_t rz;  // INT4 W units: the linear's group words (Wsz)
+  uint32_t off;               // this lane's byte offset at the chunk start (kOobOff: no row)
+  uint32_t offz;              // INT4 W units: the lane's group-word offset
+};
+struct UnitDst {
+  int kind;                   // 0: W rows, 1: A rows
+  int m;                      // linear of the group
+  int col;                    // W: first column in `part`; A: first rank (16 x rank block)
+  uint64_t members;           // A: the adapter's tokens
+};
 
 // Waits until at most N of this wave's vector-memory operations are
 // outstanding and every LDS access has completed, then joins the workgroup
-// barrier.  (__syncthreads() would wait for all of them.)
+// barrier (__syncthreads() would wait for all of them).  Exact only where
+// the N youngest operations are known: here they are N explicit 16-byte
+// buffer loads (nothing the compiler can merge or split) that the scheduling
+// fences keep after the X copy and before the wait.
 template <int N>
 __device__ __forceinline__ void barrier_after(void) {
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-// NA: A waves riding in each W block (0 on the base-only path).
-//
-// W blocks (the first np = nbc * KS): block b keeps K chunk c = b mod KS and
-// walks the column tiles bi, bi + nbc, ... (bi = b div KS), so its X chunk is
-// staged once however many tiles it takes.  Each W wave streams its 16 rows
-// of those tiles as a sequence of 512-deep halves through two register
-// buffers: the next half's loads are in flight while the current half's
-// MFMAs run (with 16 KB per wave and half in flight, the chip keeps about
-// 32 MB of reads outstanding, ample for the memory's latency).  The loads
-// and partial stores follow a fixed pattern (rows past N and tokens past T
-// land in the padding of `part`), so the loads' completion is counted
-// exactly.
-// WQ: the base weight is INT4 (a.Wq, a.Wsz); each W wave loads a quarter of
+// The walk: WPB waves per block, all alike.
+// WQ: the base weights are INT4 (a.Wq, a.Wsz); a W unit loads a quarter of
 // the bytes and dequantizes its fragments in registers before the MFMAs.
-template <int NA, bool WQ>
-__global__ __launch_bounds__(64 * (4 + NA)) void decode_main(DecodeArgs a) {
+template <int WPB, bool WQ>
+__global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[64 * kXs];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g4 = lane >> 4, r16 = lane & 15;
-  const int T = a.T, N = a.N, K = a.K, KS = a.KS;
-  const int nbc = a.np / KS;  // W blocks per K chunk
-
-  int c, bi;
-  const bool w_block = (int)blockIdx.x < a.np;
-  if (w_block) {
-    c = (int)blockIdx.x % KS;
-    bi = (int)blockIdx.x / KS;
-  } else {  // blocks of A waves only
-    const int g = (int)blockIdx.x - a.np;
-    c = g % KS;
-    bi = g / KS;
-  }
+  const int T = a.T, K = a.K, KS = a.KS, n_mod = a.n_mod;
+  const int c = (int)blockIdx.x % KS, bi = (int)blockIdx.x / KS;
   const int k0 = c * kDecodeChunk, klen = min(K, k0 + kDecodeChunk) - k0;
-  const bool a_wave = !w_block || w >= 4;
+  const int wi = bi * WPB + w;  // this wave among the chunk's NWc waves
+  const int NWc = a.NWc;
+  const int NUW = a.u0[kMaxGroup];  // W units of the group (16 rows each)
+  const KArgs ka = kargs();
+  // the wave's units are wi, wi + NWc, ...: first its W units, then its A units
+  const int nw = wi < NUW ? (NUW - wi + NWc - 1) / NWc : 0;
 
-  // ---- an A wave's 16 rows ----
-  const uint16_t* row = nullptr;  // row r16 of the block of 16, at k0
-  bool row_ok = false;
-  int qb = 0;                     // rank block of the adapter
-  uint64_t members = 0;           // tokens of the adapter
-  if (a_wave) {
-    // In a W block the A waves copy no X: they join the block barrier before
-    // their lookups, so the W waves never wait there for them (the X copy
-    // takes longer than the barrier wait it replaces; the A slices stay off
-    // the critical path).
-    // item = the item-th (adapter, 16-rank block) of the batch, adapters in
-    // order of first occurrence.  Lane t holds token t's id.  A direct-mapped
-    // pool keeps adapter id in slot id, so the page address follows from the
-    // ids alone (every rank block up to the pool's padded rank is an item;
-    // rows past an adapter's rank are zero); otherwise one more round of
-    // loads fetches each token's slot and rank.  Both load rounds go out
-    // before the weight stream fills the memory queues.
-    const int item = w_block ? bi + nbc * (w - 4) : nbc * NA + (4 + NA) * bi + w;
-    int id = -1, slot = -1, rank = 0, bad = 0;
-    if (a.direct) {
-      if (lane < T) id = a.ids[lane];
-      // the id load stays in flight across the barrier
-      if (w_block) __builtin_amdgcn_s_barrier();
-      if (id >= a.max_slots || id < -1) bad = 1;  // the combine launch rejects the batch
-      slot = id;
-      rank = a.u_ld;
-    } else {
-      if (w_block) __builtin_amdgcn_s_barrier();
-      const TokInfo ti = token_info(a, lane);
-      id = ti.id;
-      slot = ti.slot;
-      rank = ti.rank;
-      bad = ti.bad;
-    }
-    if (__ballot(bad != 0) == 0) {
-      // m = the lanes holding this lane's adapter: one ballot per bit of the
-      // id, each lane keeping the lanes that agree with it on that bit
-      const bool v = id >= 0;
-      const int nbits = 32 - __builtin_clz((unsigned)max(max(a.max_ids, a.max_slots), 1));
-      uint64_t m = __ballot(v);
-      for (int k = 0; k < nbits; ++k) {
-        const bool bit = (id >> k) & 1;
-        const uint64_t on = __ballot(v && bit);
-        m &= bit ? on : ~on;
-      }
-      // an adapter's first lane owns ceil(rank / 16) consecutive items, the
-      // adapters in order of first occurrence (= lane order of first lanes)
-      const bool first = v && lane == (int)__builtin_ctzll(m);
-      const int nq = first ? (rank + 15) / 16 : 0;
-      const int incl = wave_incl_scan(nq);
-      const uint64_t hit = __ballot(first && item >= incl - nq && item < incl);
-      if (hit) {
-        const int leader = (int)__builtin_ctzll(hit);  // wave-uniform: readlane, not an LDS shuffle
-        const int r = __builtin_amdgcn_readlane(rank, leader);
-        const int sl = __builtin_amdgcn_readlane(slot, leader);
-        qb = item - __builtin_amdgcn_readlane(incl - nq, leader);
-        members = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(m >> 32), leader) << 32) |
-                  (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)m, leader);
-        const int q = 16 * qb + r16;
-        row_ok = q < min(r, a.rmax);
-        row = a.pages + (size_t)sl * a.slot_stride + a.a_off + (size_t)(row_ok ? q : 0) * K + k0;
-      }
-    }
-    // drain the lookups here, so that no wait for them is left to the merge
-    // with the W path (where it would also wait for the X DMA below)
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-  }
+  // ---- round 0: the token ids (lane t), before anything else ----
+  int id = -1;
+  if (a.lora && lane < T) id = a.ids[lane];
 
-  // ---- X chunk -> LDS by DMA: waves 0..3 copy tokens 16w .. 16w+15, two
-  // 1-KB pieces per token row.  Rows >= T and columns >= K read zeros.
-  if (w < 4) {
-    const __amdgpu_buffer_rsrc_t rx =
-        __builtin_amdgcn_make_buffer_rsrc((void*)a.X, (short)0, T * K * 2, 0x00020000);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int r = 16 * w + (i >> 1), h = i & 1;
+  // ---- X chunk -> LDS by DMA: the block's waves share the 128 pieces (two
+  // 1-KB pieces per token row).  Rows >= T and columns >= K read zeros. ----
+  {
+    const __amdgpu_buffer_rsrc_t rx = uniform_rsrc(a.X, T * K * 2);
+    for (int i = w; i < kXPieces; i += WPB) {
+      const int r = i >> 1, h = i & 1;
       const int k = k0 + 512 * h + 8 * lane;
-      // rows >= T lie past the buffer's range (zeros); columns >= K are
-      // sent past it
+      // rows >= T lie past the buffer's range (zeros); columns >= K are sent past it
       const uint32_t off = k < K ? (uint32_t)(r * K + k) * 2u : kOobOff;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(xs + r * kXs + 512 * h), 16, off, 0, 0, 0);
     }
   }
 
+  // a W unit's rows: row r16 of the 16, at the chunk start
+  auto w_unit = [&](int u, UnitSrc& sr, UnitDst& ds) __attribute__((always_inline)) {
+    const int m = group_of(a.u0, u);
+    const int N = ka->N[m];
+    const int row0 = (u - ka->u0[m]) * 16;
+    const int row = row0 + r16;
+    ds.kind = 0;
+    ds.m = m;
+    ds.col = ka->n0[m] + row0;
+    ds.members = 0;
+    if constexpr (WQ) {
+      const int KW = K / 8, KG = K / kQ4Group;
+      sr.rs = uniform_rsrc(ka->Wq[m], N * KW * 4);
+      sr.rz = uniform_rsrc(ka->Wsz[m], N * KG * 4);
+      sr.off = row < N ? (uint32_t)(row * KW + 16 * (k0 / kQ4Group) + 4 * g4) * 4u : kOobOff;
+      sr.offz = row < N ? (uint32_t)(row * KG + k0 / kQ4Group) * 4u : kOobOff;
+    } else {
+      sr.rs = uniform_rsrc(ka->W[m], N * K * 2);
+      sr.rz = sr.rs;
+      sr.off = row < N ? (uint32_t)(row * K + k0 + 8 * g4) * 2u : kOobOff;
+      sr.offz = 0;
+    }
+  };
+  // Register buffers of two halves: bf16 rows (W or A units) take 16 loads of
+  // 16 bytes per lane per half; INT4 W units 4 of codes and 1 of group words.
+  constexpr int kQL = 5;
+  uint4 buf[2][kHS];            // bf16 halves (every unit, or the A units with WQ)
+  uint4 qbuf[2][WQ ? kQL : 1];  // INT4 W halves (WQ only)
+  auto load_b = [&](uint4 (&b)[kHS], const UnitSrc& sr, auto hc) __attribute__((always_inline)) {
+    constexpr int H = decltype(hc)::value;
+#pragma unroll
+    for (int i = 0; i < kHS; ++i)
+      b[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(sr.rs, sr.off + 2 * kHalf * H + 64 * i, 0, 0));
+  };
+  auto load_q = [&](uint4 (&b)[WQ ? kQL : 1], const UnitSrc& sr, auto hc) __attribute__((always_inline)) {
+    if constexpr (WQ) {
+      constexpr int H = decltype(hc)::value;
+      // four groups of 128: the lane's four words of each (one per 32-deep
+      // step) as one 16-byte load, then the half's four group words
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi)
+        b[gi] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(sr.rs, sr.off + 256 * H + 64 * gi, 0, 0));
+      b[4] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(sr.rz, sr.offz + 16 * H, 0, 0));
+    }
+  };
+  const auto H0 = std::integral_constant<int, 0>{};
+  const auto H1 = std::integral_constant<int, 1>{};
+
+  // ---- the first half of the wave's first W unit goes out after the X copy;
+  // the barrier waits for the copy (and the ids before it), not for it ----
+  UnitSrc csrc;
+  UnitDst cdst;
+  if (nw > 0) {
+    w_unit(wi, csrc, cdst);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (WQ) {
+      load_q(qbuf[0], csrc, H0);
+      barrier_after<kQL>();
+    } else {
+      load_b(buf[0], csrc, H0);
+      barrier_after<kHS>();
+    }
+  } else {
+    barrier_after<0>();
+  }
+
+  // ---- routing entries: a slot-table pool needs one more round after the
+  // ids; it goes out now and is first needed by the grouping, after the W units ----
+  int slot = id, rank = a.u_ld, mask = -1, bad = 0;
+  if (a.lora) {
+    if (a.direct) {
+      // a direct-mapped pool keeps adapter id in slot id: the pages follow
+      // from the ids alone (every rank block up to the padded rank is an
+      // item; rows past an adapter's rank are zero)
+      if (id >= a.max_slots || id < -1) bad = 1;  // the combine launch rejects the batch
+    } else {
+      slot = -1;
+      rank = 0;
+      if (id < -1 || id >= a.max_ids) {
+        bad = 1;
+      } else if (id >= 0) {
+        const int4 e = a.id_info[id];  // {slot, rank, scale bits, module mask}
+        if (e.x < 0) bad = 1;
+        slot = e.x;
+        rank = e.y & (kChainRankFlag - 1);
+        mask = e.w;
+      }
+    }
+  }
+
+  // ---- grouping (done when the first A unit is due): the batch's adapters
+  // in order of first occurrence, each owning ceil(rank / 16) consecutive
+  // items; the A units are item-major over the linears, so the active ones
+  // follow the W units without a gap ----
+  bool first = false;
+  int nq = 0, incl = 0, nu = nw;
+  uint64_t grp = 0;  // the lanes holding this lane's adapter
+  auto group = [&]() __attribute__((always_inline)) {
+    int n_items = 0;
+    if (a.lora && __ballot(bad != 0) == 0) {
+      // one ballot per bit of the id, each lane keeping the lanes that agree
+      // with it on that bit
+      const bool v = id >= 0;
+      const int nbits = 32 - __builtin_clz((unsigned)max(max(a.max_ids, a.max_slots), 1));
+      grp = __ballot(v);
+      for (int k = 0; k < nbits; ++k) {
+        const bool bit = (id >> k) & 1;
+        const uint64_t on = __ballot(v && bit);
+        grp &= bit ? on : ~on;
+      }
+      first = v && lane == (int)__builtin_ctzll(grp);
+      nq = first ? (rank + 15) / 16 : 0;
+      incl = wave_incl_scan(nq);
+      n_items = __builtin_amdgcn_readlane(incl, 63);
+    }
+    const int NU = NUW + n_mod * n_items;
+    nu = wi < NU ? (NU - wi + NWc - 1) / NWc : 0;
+  };
+  // an A unit's rows: rank block qb of the item's adapter on linear m
+  auto a_unit = [&](int v, UnitSrc& sr, UnitDst& ds) __attribute__((always_inline)) {
+    const int m = v % n_mod, item = v / n_mod;
+    const uint64_t hit = __ballot(first && item >= incl - nq && item < incl);
+    const int leader = (int)__builtin_ctzll(hit);  // wave-uniform: readlane, not an LDS shuffle
+    const int sl = __builtin_amdgcn_readlane(slot, leader);
+    const int r = __builtin_amdgcn_readlane(rank, leader);
+    const int mk = __builtin_amdgcn_readlane(mask, leader);
+    const int qb = item - __builtin_amdgcn_readlane(incl - nq, leader);
+    ds.kind = 1;
+    ds.m = m;
+    ds.col = 16 * qb;
+    ds.members = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(grp >> 32), leader) << 32) |
+                 (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)grp, leader);
+    const int q = 16 * qb + r16;
+    // an adapter that does not target this linear streams nothing here
+    const bool ok = q < min(r, a.rmax) && targets(mk, ka->module[m]);
+    const uint16_t* page = a.pages + (size_t)sl * a.slot_stride + ka->a_off[m];
+    sr.rs = uniform_rsrc(page, a.rmax * K * 2);
+    sr.rz = sr.rs;
+    sr.off = ok ? (uint32_t)(q * K + k0 + 8 * g4) * 2u : kOobOff;
+    sr.offz = 0;
+  };
+  // a unit past the wave's last: no row, no bytes (the loads that a loop
+  // issues unconditionally for it return zeros without touching memory)
+  auto none = [&](UnitSrc& sr, UnitDst& ds) __attribute__((always_inline)) {
+    sr.rs = uniform_rsrc(a.X, 0);
+    sr.rz = sr.rs;
+    sr.off = kOobOff;
+    sr.offz = kOobOff;
+    ds.kind = -1;
+    ds.m = 0;
+    ds.col = 0;
+    ds.members = 0;
+  };
+  // the unit after the last W unit: the first A unit, or none
+  auto after_w = [&](int j, UnitSrc& sr, UnitDst& ds) __attribute__((always_inline)) {
+    group();
+    if (j < nu)
+      a_unit(wi + j * NWc - NUW, sr, ds);
+    else
+      none(sr, ds);
+  };
+
   f32x4 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // acc[i] += X[16 i .. 16 i + 15, k .. k + 31] . W slice, for each step s
-  // of a register block of kHalf / 32 steps starting at kh
-  constexpr int kHalf = kDecodeChunk / 2, kHS = kHalf / 32;
-
-  if constexpr (WQ) {
-    if (!a_wave) {
-      const int ntile = (a.NT - bi + nbc - 1) / nbc;  // >= 1: the host keeps nbc <= NT
-      const int nhalf = 2 * ntile;
-      constexpr int kHG = kHalf / kQ4Group;  // groups per half (4)
-      const int KW = K / 8, KG = K / kQ4Group;
-      uint4 rq[2][kHG];     // per group: the lane's 4 words, one per 32-deep step
-      uint32_t rz[2][kHG];  // per group: {bf16 scale, zero point}
-      // reads past the end of Wq / Wsz return zeros; groups past the chunk
-      // are masked below
-      const __amdgpu_buffer_rsrc_t rqs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)a.Wq, (short)0, N * KW * 4, 0x00020000);
-      const __amdgpu_buffer_rsrc_t rzs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)a.Wsz, (short)0, N * KG * 4, 0x00020000);
-      auto load = [&](uint4 (&bq)[kHG], uint32_t (&bz)[kHG], int s) __attribute__((always_inline)) {
-        const int sc = min(s, nhalf - 1);
-        const int n = (bi + (sc >> 1) * nbc) * kDecodeTileRows + 16 * w + r16;
-        const int nn = n < N ? n : 0;
-        const int g0 = (k0 + kHalf * (sc & 1)) / kQ4Group;
-        const int offq = (nn * KW + 16 * g0 + 4 * g4) * 4;
-        const int offz = (nn * KG + g0) * 4;
+  // acc[tb] += (16 rows x 32) . X[16 tb .. 16 tb + 15, k .. k + 31]^T over the
+  // half's 16 steps; the unit's rows are the MFMA's A operand, so a lane ends
+  // with 4 consecutive rows (columns of the output, or ranks) of one token.
+  // The X fragments of step i + 1 are read from LDS while step i's MFMAs run.
+  auto compute_b = [&](const uint4 (&b)[kHS], auto hc) __attribute__((always_inline)) {
+    constexpr int H = decltype(hc)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    // the chunk's depth, opaque here: the 16 lane masks of the K tail are
+    // formed where they are used instead of being hoisted out of the walk
+    // (32 live 64-bit masks would spill the scalar registers)
+    int kl = klen;
+    asm volatile("" : "+s"(kl));
+    bf16x8 xf[2][4];
 #pragma unroll
-        for (int gi = 0; gi < kHG; ++gi)
-          bq[gi] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rqs, offq + 64 * gi, 0, 0));
-        // the half's four group words as one load (kHG + 1 loads per half in all)
-        const uint4 zz = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rzs, offz, 0, 0));
-        bz[0] = zz.x;
-        bz[1] = zz.y;
-        bz[2] = zz.z;
-        bz[3] = zz.w;
-      };
-      static_assert(kHG == 4, "one 16-byte load of group words per half");
-      load(rq[0], rz[0], 0);
-      // the X DMA (issued before these kHG + 1 loads) has landed in every wave
-      barrier_after<kHG + 1>();
-      auto phase = [&](auto hc, auto nc, int s) __attribute__((always_inline)) {
-        constexpr int H = decltype(hc)::value;
-        constexpr bool NEXT = decltype(nc)::value;
-        if constexpr (NEXT) load(rq[1 - H], rz[1 - H], s + 1);
+    for (int tb = 0; tb < 4; ++tb) xf[0][tb] = lds_bf16x8(xs + (16 * tb + r16) * kXs + kHalf * H + 8 * g4);
 #pragma unroll
-        for (int gi = 0; gi < kHG; ++gi) {
-          // a group past the chunk (klen is a multiple of the group) gets
-          // scale 0 and offset 0: its weights dequantize to exact zeros
-          const bool in = kHalf * H + kQ4Group * gi < klen;
-          float2 g = q4_group(rz[H][gi]);
-          g.x = in ? g.x : 0.f;
-          g.y = in ? g.y : 0.f;
-          const uint32_t words[4] = {rq[H][gi].x, rq[H][gi].y, rq[H][gi].z, rq[H][gi].w};
+    for (int i = 0; i < kHS; ++i) {
+      const int k = kHalf * H + 32 * i + 8 * g4;
+      if (i + 1 < kHS) {
 #pragma unroll
-          for (int st = 0; st < 4; ++st) {
-            const int k = kHalf * H + kQ4Group * gi + 32 * st + 8 * g4;
-            const bf16x8 wb = dequant_q4x8(words[st], g.x, g.y);
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-              acc[tb] = mfma16(wb, lds_bf16x8(xs + (16 * tb + r16) * kXs + k), acc[tb]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if constexpr (H == 1) {
-          const int n = (bi + (s >> 1) * nbc) * kDecodeTileRows + 16 * w + 4 * g4;
-          float* pp = a.part + (size_t)c * 64 * a.npad + (size_t)r16 * a.npad + n;
-#pragma unroll
-          for (int tb = 0; tb < 4; ++tb) {
-            *reinterpret_cast<float4*>(pp + (size_t)(16 * tb) * a.npad) =
-                make_float4(acc[tb][0], acc[tb][1], acc[tb][2], acc[tb][3]);
-            acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
-        }
-      };
-      for (int s = 0; s < nhalf - 2; s += 2) {
-        phase(std::integral_constant<int, 0>{}, std::true_type{}, s);
-        phase(std::integral_constant<int, 1>{}, std::true_type{}, s + 1);
+        for (int tb = 0; tb < 4; ++tb) xf[(i + 1) & 1][tb] = lds_bf16x8(xs + (16 * tb + r16) * kXs + k + 32);
       }
-      phase(std::integral_constant<int, 0>{}, std::true_type{}, nhalf - 2);
-      phase(std::integral_constant<int, 1>{}, std::false_type{}, nhalf - 1);
-      return;
-    }
-  }
-  if (!WQ && !a_wave) {
-    const int ntile = (a.NT - bi + nbc - 1) / nbc;  // >= 1: the host keeps nbc <= NT
-    const int nhalf = 2 * ntile;
-    uint4 rw[2][kHS];
-    // one buffer resource over W: a half is one offset plus immediates, and
-    // reads past the end of W return zeros (reads past the chunk within W are
-    // masked below)
-    const __amdgpu_buffer_rsrc_t rws =
-        __builtin_amdgcn_make_buffer_rsrc((void*)a.W, (short)0, N * K * 2, 0x00020000);
-    auto load = [&](uint4 (&buf)[kHS], int s) __attribute__((always_inline)) {
-      const int sc = min(s, nhalf - 1);
-      // row r16 of this wave's 16 rows of tile sc / 2 (rows past N read row
-      // 0; their results land in the padding of `part`)
-      const int n = (bi + (sc >> 1) * nbc) * kDecodeTileRows + 16 * w + r16;
-      const int off = ((n < N ? n : 0) * K + k0 + kHalf * (sc & 1) + 8 * g4) * 2;
+      const bf16x8 wb = __builtin_bit_cast(bf16x8, keep_if(k < kl, b[i]));
 #pragma unroll
-      for (int i = 0; i < kHS; ++i)
-        buf[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rws, off + 64 * i, 0, 0));
-    };
-    load(rw[0], 0);
-    // the X DMA (issued before these loads) has landed in every wave
-    barrier_after<kHS>();
-    // phase H of a tile: half H in rw[H]; the next half (if NEXT) goes to
-    // rw[1 - H]
-    auto phase = [&](auto hc, auto nc, int s) __attribute__((always_inline)) {
+      for (int tb = 0; tb < 4; ++tb) acc[tb] = mfma16(wb, xf[i & 1][tb], acc[tb]);
+    }
+    // order: step 0's reads, then each step's MFMAs with the next step's reads between them
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i + 1 < kHS; ++i) {
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto compute_q = [&](const uint4 (&b)[WQ ? kQL : 1], auto hc) __attribute__((always_inline)) {
+    if constexpr (WQ) {
       constexpr int H = decltype(hc)::value;
-      constexpr bool NEXT = decltype(nc)::value;
-      if constexpr (NEXT) load(rw[1 - H], s + 1);
+      const uint4 zz = b[4];
+      const uint32_t gw[4] = {zz.x, zz.y, zz.z, zz.w};
 #pragma unroll
-      for (int i = 0; i < kHS; ++i) {
-        const int k = kHalf * H + 32 * i + 8 * g4;
-        const bf16x8 wb = __builtin_bit_cast(bf16x8, keep_if(k < klen, rw[H][i]));
-        // W as the A operand: a lane's results are 4 consecutive columns of
-        // one token, stored as one 16-byte write
+      for (int gi = 0; gi < 4; ++gi) {
+        // a group past the chunk (klen is a multiple of the group) gets
+        // scale 0 and offset 0: its weights dequantize to exact zeros
+        const bool in = kHalf * H + kQ4Group * gi < klen;
+        float2 g = q4_group(gw[gi]);
+        g.x = in ? g.x : 0.f;
+        g.y = in ? g.y : 0.f;
+        const uint32_t words[4] = {b[gi].x, b[gi].y, b[gi].z, b[gi].w};
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb)
-          acc[tb] = mfma16(wb, lds_bf16x8(xs + (16 * tb + r16) * kXs + k), acc[tb]);
-        // at most four steps' X fragments in registers at a time
-        if (i % 4 == 3) __builtin_amdgcn_sched_barrier(0);
-      }
-      if constexpr (H == 1) {
-        // the tile's partial sums: acc[tb][e] is token 16 tb + r16, column
-        // n + e of this wave's 16
-        const int n = (bi + (s >> 1) * nbc) * kDecodeTileRows + 16 * w + 4 * g4;
-        float* pp = a.part + (size_t)c * 64 * a.npad + (size_t)r16 * a.npad + n;
+        for (int st = 0; st < 4; ++st) {
+          const int k = kHalf * H + kQ4Group * gi + 32 * st + 8 * g4;
+          const bf16x8 wb = dequant_q4x8(words[st], g.x, g.y);
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          *reinterpret_cast<float4*>(pp + (size_t)(16 * tb) * a.npad) =
-              make_float4(acc[tb][0], acc[tb][1], acc[tb][2], acc[tb][3]);
-          acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int tb = 0; tb < 4; ++tb)
+            acc[tb] = mfma16(wb, lds_bf16x8(xs + (16 * tb + r16) * kXs + k), acc[tb]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
-    };
-    // every tile but the last requests the next tile's first half during its
-    // second half; the last one requests nothing (a wave does not end with
-    // loads in flight)
-    for (int s = 0; s < nhalf - 2; s += 2) {
-      phase(std::integral_constant<int, 0>{}, std::true_type{}, s);
-      phase(std::integral_constant<int, 1>{}, std::true_type{}, s + 1);
     }
-    phase(std::integral_constant<int, 0>{}, std::true_type{}, nhalf - 2);
-    phase(std::integral_constant<int, 1>{}, std::false_type{}, nhalf - 1);
-    return;
-  }
+  };
+  // acc[tb][e]: token 16 tb + r16, row 4 g4 + e of the unit
+  auto store = [&](const UnitDst& d) __attribute__((always_inline)) {
+    if (d.kind == 0) {
+      // rows past the linear's N land in its padding columns of `part`
+      float* pp = a.part + (size_t)c * 64 * a.npad + (size_t)r16 * a.npad + d.col + 4 * g4;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+        *reinterpret_cast<float4*>(pp + (size_t)(16 * tb) * a.npad) =
+            make_float4(acc[tb][0], acc[tb][1], acc[tb][2], acc[tb][3]);
+    } else if (d.kind == 1) {
+      float* up = a.upart + ((size_t)(c * n_mod + d.m) * 64 + r16) * a.u_ld + d.col + 4 * g4;
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+        if ((d.members >> (16 * tb + r16)) & 1ull)
+          *reinterpret_cast<float4*>(up + (size_t)(16 * tb) * a.u_ld) =
+              make_float4(acc[tb][0], acc[tb][1], acc[tb][2], acc[tb][3]);
+    }
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
 
-  // ---- an A wave: its whole 16 x 1024 slice, issued at once ----
-  const bool active = row != nullptr;  // an A wave past the last item has nothing to do
-  if (!active) row = a.X + k0;         // dummy in-bounds source, results discarded
-  uint4 rwa[kSteps];
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) rwa[s] = ld16(row + min(32 * s + 8 * g4, klen - 8));
-  // blocks of A waves only: waves 0..3 copied X, everyone waits for it here
-  if (!w_block) barrier_after<kSteps>();
-  if (!active) return;
-  // An adapter with at most 16 tokens in the batch (the usual case at decode)
-  // needs one 16-token MFMA block, not four: lane r16 reads the X row of the
-  // adapter's r16-th token, a quarter of the MFMAs and LDS reads.
-  const int cnt = __popcll(members);
-  if (cnt <= 16) {
-    uint64_t m = members;  // X row of this lane: the r16-th member (row 0 past the last)
-    for (int i = 0; i < r16; ++i) m &= m - 1;
-    const int xr = m ? (int)__builtin_ctzll(m) : 0;
-    f32x4 acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-      const int k = 32 * s + 8 * g4;
-      const bf16x8 wb = __builtin_bit_cast(bf16x8, keep_if(k < klen && row_ok, rwa[s]));
-      acc1 = mfma16(lds_bf16x8(xs + xr * kXs + k), wb, acc1);
-    }
-    if (row_ok) {
-      // acc1[e] belongs to member 4 g4 + e
-      uint64_t mm = members;
-      for (int i = 0; i < 4 * g4; ++i) mm &= mm - 1;
-      float* up = a.upart + (size_t)c * 64 * a.u_ld + 16 * qb + r16;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (mm) up[(size_t)__builtin_ctzll(mm) * a.u_ld] = acc1[e];
-        mm &= mm - 1;
+  // Unit j's first half is in flight when its step starts; its second half
+  // is requested before its first half's MFMAs, the next unit's first half
+  // before its second half's.  Every load is issued unconditionally (past the
+  // wave's last unit, rows of no bytes), so the compiler counts each wait
+  // exactly.  W units first (INT4 or bf16), then the A units (bf16 pages).
+  int j = 0;
+  for (; j < nw; ++j) {
+    UnitDst ndst;
+    if constexpr (WQ) {
+      load_q(qbuf[1], csrc, H1);
+      compute_q(qbuf[0], H0);
+      if (j + 1 < nw) {
+        w_unit(wi + (j + 1) * NWc, csrc, ndst);
+        load_q(qbuf[0], csrc, H0);
+        compute_q(qbuf[1], H1);
+      } else {
+        compute_q(qbuf[1], H1);
+        after_w(j + 1, csrc, ndst);
+        load_b(buf[0], csrc, H0);
       }
+    } else {
+      load_b(buf[1], csrc, H1);
+      compute_b(buf[0], H0);
+      if (j + 1 < nw)
+        w_unit(wi + (j + 1) * NWc, csrc, ndst);
+      else
+        after_w(j + 1, csrc, ndst);
+      load_b(buf[0], csrc, H0);
+      compute_b(buf[1], H1);
     }
-    return;
+    store(cdst);
+    cdst = ndst;
   }
-#pragma unroll
-  for (int s = 0; s < kSteps; ++s) {
-    const int k = 32 * s + 8 * g4;
-    const bf16x8 wb = __builtin_bit_cast(bf16x8, keep_if(k < klen && row_ok, rwa[s]));
-    // all four 16-token row blocks: rows >= T hold zeros and are never stored
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = mfma16(lds_bf16x8(xs + (16 * i + r16) * kXs + k), wb, acc[i]);
+  if (nw == 0) {
+    group();
+    if (nu == 0) return;  // nothing in flight: the barrier waited for every load
+    a_unit(wi - NUW, csrc, cdst);
+    load_b(buf[0], csrc, H0);
   }
-  if (row_ok) {
-    const int nm = (T + 15) / 16;
-    float* up = a.upart + (size_t)c * 64 * a.u_ld + 16 * qb + r16;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i >= nm) continue;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int t = 16 * i + 4 * g4 + e;
-        if ((members >> t) & 1ull) up[(size_t)t * a.u_ld] = acc[i][e];
-      }
-    }
+  for (; j < nu; ++j) {
+    load_b(buf[1], csrc, H1);
+    compute_b(buf[0], H0);
+    UnitDst ndst;
+    if (j + 1 < nu)
+      a_unit(wi + (j + 1) * NWc - NUW, csrc, ndst);
+    else
+      none(csrc, ndst);
+    load_b(buf[0], csrc, H0);
+    compute_b(buf[1], H1);
+    store(cdst);
+    cdst = ndst;
   }
+  // the last (empty) request has returned before the wave ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // ---------------------------------------------------------------------------
-// combine: block = 16 tokens x 64 columns, thread = (token, 4 columns).
-// Round 1 of loads depends on nothing: the ids, the chunk partials and the
-// shrink partials of the block's V, and in a direct-mapped pool the thread's
-// B rows (its token's id comes by a scalar load).  Round 2: every token's
-// {slot, rank, scale} (each block checks the whole batch, strict mode).
-// Otherwise the B rows need the slot and come in a third round.
+// combine: block = 16 tokens x 64 columns of one linear, thread = (token, 4
+// columns).  Round 1 of loads depends on nothing: the ids, the chunk partials
+// and the shrink partials of the block's V, and in a direct-mapped pool the
+// thread's B rows (its token's id comes by a scalar load).  Round 2: every
+// token's {slot, rank, scale} (each block checks the whole batch, strict
+// mode).  Otherwise the B rows need the slot and come in a third round.
 constexpr int kCombThreads = 256;
 constexpr int kVPer = 16 * kMaxRank / kCombThreads;  // V elements per thread
-
-// sum over the KS chunk planes p[c * stride], c = 0, 1, ... in order; loads
-// issued four at a time
-__device__ __forceinline__ float sum_chunks(const float* p, size_t stride, int KS) {
-  float s = 0.f;
-  for (int c0 = 0; c0 < KS; c0 += 4) {
-    float v[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = p[(size_t)min(c0 + j, KS - 1) * stride];
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (c0 + j < KS) s += v[j];
-  }
-  return s;
-}
 
 __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
   __shared__ float vsh[16][kMaxRank + 1];
@@ -462,12 +484,16 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
   __shared__ float4 s_bsc[16];  // the block's tokens: scale of each 16-rank block
   __shared__ int s_bad;
   const int tid = threadIdx.x;
-  const int T = a.T, N = a.N, KS = a.KS;
+  const int T = a.T, KS = a.KS;
+  const KArgs ka = kargs();
+  const int mg = group_of(a.ct0, (int)blockIdx.x);  // the block's linear
+  const int N = ka->N[mg];
   const int t0 = blockIdx.y * 16;
   const int tr = tid >> 4, quad = tid & 15;
   const int t = t0 + tr;
-  const int n = blockIdx.x * 64 + quad * 4;
+  const int n = ((int)blockIdx.x - ka->ct0[mg]) * 64 + quad * 4;
   const bool mine = t < T && n < N;
+  const size_t pstr = (size_t)64 * a.npad;  // one chunk plane of `part`
 
   // ---- round 1 ----
   // (the ids for the whole-batch check are stored to LDS only after every
@@ -477,14 +503,15 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
     st = *a.status;
     if (tid < 64 && tid < T) idv = a.ids[tid];
   }
-  const float* pp = a.part + (size_t)min(t, T - 1) * a.npad + min(n, N - 4);
+  const float* pp = a.part + (size_t)min(t, T - 1) * a.npad + ka->n0[mg] + min(n, N - 4);
   float4 pv[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) pv[j] = *reinterpret_cast<const float4*>(pp + (size_t)min(j, KS - 1) * 64 * a.npad);
+  for (int j = 0; j < 4; ++j) pv[j] = *reinterpret_cast<const float4*>(pp + (size_t)min(j, KS - 1) * pstr);
   float u[kVPer];
   uint4 bv[8];
   int slot = -1, rank = 0;
   const uint16_t* Bp = nullptr;
+  const size_t b_off = ka->b_off[mg];
   if (a.lora) {
     // this wave's four tokens' ids by wave-uniform (scalar) loads, so that a
     // direct-mapped pool's B rows go out in this round, beside the partials,
@@ -500,7 +527,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
     // B^T page in 16-rank chunks [rpad/16][N][16]: the 4 columns' chunk is 64
     // contiguous values (ranks past the adapter's rank are zero)
     if (a.direct && mine && my_id >= 0 && my_id < a.max_slots) {
-      Bp = a.pages + (size_t)my_id * a.slot_stride + a.b_off + (size_t)n * 16;
+      Bp = a.pages + (size_t)my_id * a.slot_stride + b_off + (size_t)n * 16;
 #pragma unroll
       for (int k = 0; k < 8; ++k) bv[k] = *reinterpret_cast<const uint4*>(Bp + 8 * k);
     }
@@ -513,10 +540,10 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
       const int idx = tid + kCombThreads * e;
       const int r = idx / kMaxRank, q = idx % kMaxRank;
       uq[e] = q < a.u_ld;
-      up[e] = a.upart + (size_t)min(t0 + r, T - 1) * a.u_ld + (uq[e] ? q : 0);
+      up[e] = a.upart + ((size_t)mg * 64 + min(t0 + r, T - 1)) * a.u_ld + (uq[e] ? q : 0);
       u[e] = 0.f;
     }
-    const size_t ustr = (size_t)64 * a.u_ld;
+    const size_t ustr = (size_t)a.n_mod * 64 * a.u_ld;  // one chunk plane of upart
     // the first four chunks' V partial loads go out now, the rest after the
     // routing lookups
     float v[kVPer][4];
@@ -546,7 +573,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
       }
       if (bad) atomicMax(&s_bad, bad);
       // a token whose adapter does not target this linear takes the base only
-      if (!bad && e.x >= 0 && !targets(e.w, a.module)) e = make_int4(-1, 0, 0, 0);
+      if (!bad && e.x >= 0 && !targets(e.w, ka->module[mg])) e = make_int4(-1, 0, 0, 0);
       if (tid >= t0 && tid < t0 + 16) s_info[tid - t0] = bad ? make_int4(-1, 0, 0, 0) : e;
     }
     for (int c0 = 0; c0 < KS; c0 += 4) {
@@ -583,7 +610,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
   if (!mine) return;
   if (slot >= 0 && !a.direct) {
     // ---- round 3 (pool not direct-mapped) ----
-    Bp = a.pages + (size_t)slot * a.slot_stride + a.b_off + (size_t)n * 16;
+    Bp = a.pages + (size_t)slot * a.slot_stride + b_off + (size_t)n * 16;
 #pragma unroll
     for (int k = 0; k < 8; ++k) bv[k] = *reinterpret_cast<const uint4*>(Bp + 8 * k);
   }
@@ -594,7 +621,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
     if (c0 > 0) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        pv[j] = *reinterpret_cast<const float4*>(pp + (size_t)min(c0 + j, KS - 1) * 64 * a.npad);
+        pv[j] = *reinterpret_cast<const float4*>(pp + (size_t)min(c0 + j, KS - 1) * pstr);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -638,47 +665,58 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
   }
   const uint32_t o0 = (uint32_t)f32_to_bf16_bits(s.x) | ((uint32_t)f32_to_bf16_bits(s.y) << 16);
   const uint32_t o1 = (uint32_t)f32_to_bf16_bits(s.z) | ((uint32_t)f32_to_bf16_bits(s.w) << 16);
-  *reinterpret_cast<uint2*>(a.out + (size_t)t * N + n) = make_uint2(o0, o1);
+  *reinterpret_cast<uint2*>(ka->out[mg] + (size_t)t * N + n) = make_uint2(o0, o1);
 }
 
-hipError_t launch_decode(const DecodeArgs& args, int items, hipStream_t s) {
+template <bool WQ>
+hipError_t launch_main(const DecodeArgs& a, int wpb, int grid, hipStream_t s) {
+  switch (wpb) {
+    case 4: hipLaunchKernelGGL((decode_main<4, WQ>), dim3(grid), dim3(256), 0, s, a); break;
+    case 5: hipLaunchKernelGGL((decode_main<5, WQ>), dim3(grid), dim3(320), 0, s, a); break;
+    case 6: hipLaunchKernelGGL((decode_main<6, WQ>), dim3(grid), dim3(384), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((decode_main<8, WQ>), dim3(grid), dim3(512), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <bool WQ>
+int main_resident(int wpb) {
+  switch (wpb) {
+    case 4: return resident_blocks(reinterpret_cast<const void*>(&decode_main<4, WQ>), 256, 0);
+    case 5: return resident_blocks(reinterpret_cast<const void*>(&decode_main<5, WQ>), 320, 0);
+    case 6: return resident_blocks(reinterpret_cast<const void*>(&decode_main<6, WQ>), 384, 0);
+    case 8: return resident_blocks(reinterpret_cast<const void*>(&decode_main<8, WQ>), 512, 0);
+  }
+  return 1;
+}
+
+hipError_t launch_decode(const DecodeArgs& args, int items_cap, hipStream_t s) {
   DecodeArgs a = args;
-  // W blocks: every (tile, chunk) pair if the chip holds them at once, else
-  // as many whole sets of KS chunk blocks as it holds (one block per compute
-  // unit: the X chunk fills most of the LDS), each walking several tiles
-  const int resident = resident_blocks(reinterpret_cast<const void*>(&decode_main<0, false>), 256, 0);
-  a.np = std::min(a.NT * a.KS, std::max(1, resident / a.KS) * a.KS);
-  const int nbc = a.np / a.KS;
-  a.na = 0;
-  a.a_tiles = 0;
-  if (a.lora) {
-    // items ride in the W blocks (na waves each, 1, 2 or 4); the rest get
-    // extra blocks of A waves only
-    const int per_block = (items + nbc - 1) / nbc;
-    a.na = per_block <= 1 ? 1 : per_block <= 2 ? 2 : 4;
-    a.a_tiles = (std::max(0, items - nbc * a.na) + 3 + a.na) / (4 + a.na);
-  }
-  const dim3 grid(a.np + a.a_tiles * a.KS);
-  if (a.Wq) {
-    switch (a.na) {
-      case 0: hipLaunchKernelGGL((decode_main<0, true>), grid, dim3(256), 0, s, a); break;
-      case 1: hipLaunchKernelGGL((decode_main<1, true>), grid, dim3(320), 0, s, a); break;
-      case 2: hipLaunchKernelGGL((decode_main<2, true>), grid, dim3(384), 0, s, a); break;
-      case 4: hipLaunchKernelGGL((decode_main<4, true>), grid, dim3(512), 0, s, a); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    switch (a.na) {
-      case 0: hipLaunchKernelGGL((decode_main<0, false>), grid, dim3(256), 0, s, a); break;
-      case 1: hipLaunchKernelGGL((decode_main<1, false>), grid, dim3(320), 0, s, a); break;
-      case 2: hipLaunchKernelGGL((decode_main<2, false>), grid, dim3(384), 0, s, a); break;
-      case 4: hipLaunchKernelGGL((decode_main<4, false>), grid, dim3(512), 0, s, a); break;
-      default: return hipErrorInvalidValue;
+  // units per K chunk the grid must hold: every W unit plus every A item the
+  // batch could have on every linear
+  const int units = a.u0[kMaxGroup] + (a.lora ? a.n_mod * items_cap : 0);
+  // waves per block: the shape whose busiest wave has the fewest units (one
+  // block per compute unit: the X chunk fills most of the LDS); a tie keeps
+  // fewer waves
+  int best_w = 4, best_nbc = 1, best_max = INT32_MAX;
+  for (int wpb : {4, 5, 6, 8}) {
+    // the INT4 walk holds both kinds of buffers: one wave per SIMD
+    if (a.wq && wpb != 4) continue;
+    const int resident = a.wq ? main_resident<true>(wpb) : main_resident<false>(wpb);
+    const int nbc = std::max(1, std::min(resident / a.KS, ceil_div(units, wpb)));
+    const int mx = ceil_div(units, nbc * wpb);
+    if (mx < best_max) {
+      best_max = mx;
+      best_w = wpb;
+      best_nbc = nbc;
     }
   }
-  hipError_t e = hipGetLastError();
+  a.NWc = best_nbc * best_w;
+  const int grid = best_nbc * a.KS;
+  const hipError_t e = a.wq ? launch_main<true>(a, best_w, grid, s) : launch_main<false>(a, best_w, grid, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine, dim3((a.N + 63) / 64, (a.T + 15) / 16), dim3(kCombThreads), 0, s, a);
+  hipLaunchKernelGGL(decode_combine, dim3(a.ct0[kMaxGroup], (a.T + 15) / 16), dim3(kCombThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -110,42 +110,46 @@ struct GemmArgs {
 };
 
 // Decode path (T <= kDecodeMaxT): launch 1 computes the K-chunk partials of
-// the base GEMM (W tiles) and of the shrink (A tiles), launch 2 combines them
-// with the expand.  Workspace: part [KS][64][N] and upart [KS][64][u_ld] (fp32).
+// the base GEMM (W rows) and of the shrink (A rows) of a group of linears that
+// read the same X, launch 2 combines them with the expand.  Workspace: part
+// [KS][64][npad] and upart [KS][n_mod][64][u_ld] (fp32).
 constexpr int kDecodeMaxT = 64;
-constexpr int kDecodeTileRows = 64;   // W rows per block (4 waves x 16)
+constexpr int kDecodeTileRows = 64;   // combine columns per block
 constexpr int kDecodeChunk = 1024;    // K per block
+constexpr int kMaxGroup = 8;          // linears of one grouped decode launch
 
 struct DecodeArgs {
-  const uint16_t* X;      // [T][K]
-  const uint16_t* W;      // [N][K]
-  uint16_t* out;          // [T][N]
+  const uint16_t* X;      // [T][K], shared by every linear of the group
   const int32_t* ids;     // [T]
-  int32_t T, N, K;
+  int32_t T, K, KS;       // KS = ceil(K / kDecodeChunk)
+  int32_t n_mod;          // linears in the group, 1..kMaxGroup
+  // per linear of the group (entries >= n_mod unused)
+  const uint16_t* W[kMaxGroup];    // [N][K] bf16 base weight, or
+  const uint32_t* Wq[kMaxGroup];   // [N][K/8] packed INT4 weight (layout below)
+  const uint32_t* Wsz[kMaxGroup];  // [N][K/128] {bf16 scale, zero point << 16}
+  uint16_t* out[kMaxGroup];        // [T][N]
+  int32_t N[kMaxGroup];
+  int32_t module[kMaxGroup];       // pool module index (target mask bit)
+  size_t a_off[kMaxGroup], b_off[kMaxGroup];  // the module's pages inside a slot
+  int32_t u0[kMaxGroup + 1];   // first 16-row W unit of each linear; u0[n_mod] = W units
+  int32_t n0[kMaxGroup + 1];   // first column of each linear in `part` (multiples of 16)
+  int32_t ct0[kMaxGroup + 1];  // first 64-column combine tile of each linear
   int32_t max_ids;
   const int4* id_info;    // [max_ids] {slot (-1: not resident), rank, scale bits, module mask}
   const float4* id_bscale; // [max_ids] scale of each 16-rank block
   const uint16_t* pages;
   size_t slot_stride;
-  size_t a_off, b_off;
   float* part;            // [KS][64][npad]
-  float* upart;           // [KS][64][u_ld]
+  float* upart;           // [KS][n_mod][64][u_ld]
+  int32_t npad;           // n0[n_mod]
   int32_t direct;         // pool keeps adapter id in slot id (max_ids <= max_adapters)
   int32_t max_slots;      // resident slots of the pool
   int32_t rmax;           // rows of an A page (the pool's max rank)
-  int32_t u_ld;
+  int32_t u_ld;           // the pool's rank rounded up to 16
   int32_t* status;
-  int32_t NT;             // W tiles (kDecodeTileRows rows each)
-  int32_t KS;             // K chunks
-  int32_t np;             // W blocks: a multiple of KS, at most NT * KS (each walks NT / (np / KS) tiles)
-  int32_t npad;           // row length of part: NT * kDecodeTileRows
-  int32_t na;             // A waves riding in each W block: 0, 1, 2 or 4 (0: base-only)
-  int32_t a_tiles;        // extra blocks of 4 + na A waves, per K chunk
+  int32_t NWc;            // waves per K chunk (set by launch_decode)
   int32_t lora;
-  int32_t module;         // index of the linear: an adapter whose id_info mask lacks it adds nothing
-  // INT4 base weight instead of W (the W waves dequantize in registers)
-  const uint32_t* Wq;     // [N][K/8] packed 4-bit weights (layout below), or nullptr
-  const uint32_t* Wsz;    // [N][K/128] {bf16 scale, zero point << 16}
+  int32_t wq;             // INT4 base weights (Wq, Wsz) instead of W
 };
 
 // INT4 base weight layout (group size kQ4Group along K; K % kQ4Group == 0).
@@ -188,8 +192,10 @@ hipError_t launch_prefill(const GemmArgs& a, bool lora, int shape, hipStream_t s
 // The E rows of the small segments (one launch, before the GEMM).
 hipError_t launch_expand_small(const GemmArgs& a, hipStream_t s);
 int prefill_choose(int T, int N);
-// Picks the W blocks (np) and where the `items` A items go, then launches.
-hipError_t launch_decode(const DecodeArgs& a, int items, hipStream_t s);
+// Picks the waves per block and the blocks per K chunk for the group's W
+// units plus `items_cap` A items per linear (the most a batch can hold), then
+// launches both kernels.
+hipError_t launch_decode(const DecodeArgs& a, int items_cap, hipStream_t s);
 hipError_t launch_pack(const PackArgs& a, hipStream_t s);
 // Routing-table update of one id; `mask` = the modules the adapter targets
 // (bit m: module m; modules >= 32 are always targeted), kept in id_info.w.

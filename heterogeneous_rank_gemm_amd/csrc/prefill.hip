@@ -103,9 +103,15 @@ __device__ __forceinline__ void dma_issue(__amdgpu_buffer_rsrc_t rw, __amdgpu_bu
 // older ones -- the next stage's DMA -- have landed in LDS) and every LDS
 // access has completed, then joins the workgroup barrier.  Unlike
 // __syncthreads() it does not wait for the DMA of the stages further ahead.
+// The count holds because every vector-memory instruction of the main loop
+// is one of the DMA builtins (16 bytes per lane each: nothing to merge); the
+// scheduling fences keep the compiler from moving any other memory
+// instruction across the wait.
 template <int N>
 __device__ __forceinline__ void barrier_after_dma() {
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // Calls f(integral_constant<int, S>) for S = 0 .. NS-1, in order.

@@ -79,7 +79,9 @@ const char* lora_status_string(lora_status_t s);
  *                 ([vLLM-ch7] "performance notes": mixed ranks are aligned
  *                 to the largest); 1..64 (--max-lora-rank 64)
  *   n_modules     number of LoRA-augmented linears served by the pool
- *   d_in, d_out   host arrays [n_modules]; multiples of 8, 8..65536
+ *   d_in, d_out   host arrays [n_modules]; multiples of 8, 8..65536, and
+ *                 d_in * d_out * 2 <= 2^31 - 1 (a base weight under 2 GiB:
+ *                 the decode kernels address it with 32-bit byte offsets)
  *   max_tokens    largest T accepted by lora_apply / lora_plan; 1..65536
  *   stream        stream used to initialise the device tables
  *
@@ -154,7 +156,10 @@ lora_status_t lora_unload_adapter(lora_pool_t pool, int32_t id, hipStream_t stre
  * ID_RANGE (chain_id or a member out of range), INVALID_ARG (n, repeats, a
  * chain as member), NOT_LOADED (a member not addressable), RANK (the blocks
  * of all members but the last plus the last's rank exceed max_rank), EXISTS,
- * POOL_FULL.  The chain's target set is the union of its members'.
+ * POOL_FULL.  The RANK rule is this library's page layout, stricter than the
+ * pages' (a chain is one adapter of rank sum_c r_c <= max rank): every member
+ * but the last takes whole 16-rank blocks, so ranks 5 + 5 + 5 need 37 page
+ * rows, not 15.  The chain's target set is the union of its members'.
  * lora_pool_query reports the chain's rank as that total and its scale as the
  * first member's.  Synchronises `stream`.
  */
@@ -218,6 +223,31 @@ lora_status_t lora_apply(lora_pool_t pool, int32_t module, const lora_bf16_t* X,
  */
 lora_status_t lora_base_apply(lora_pool_t pool, int32_t module, const lora_bf16_t* X, int32_t T,
                               const lora_bf16_t* W, lora_bf16_t* out, hipStream_t stream);
+
+/*
+ * lora_apply_group / lora_base_apply_group -- lora_apply / lora_base_apply
+ * for n linears that read the same X, in one call ([LoRA-Land] section "2.
+ * multi-LoRA batch scheduling": one forward serves the whole grouped batch;
+ * the q/k/v and gate/up projections of a layer read one hidden state).
+ *
+ *   n        1..8 linears
+ *   modules  host int32[n]: distinct pool modules with one d_in
+ *   W        host array [n] of device pointers, W[i] is d_out[modules[i]] x d_in
+ *   out      host array [n] of device pointers, out[i] is T x d_out[modules[i]]
+ *   X, ids, T, plan, stream as lora_apply
+ *
+ * Each out[i] is exactly what lora_apply (lora_base_apply) on module
+ * modules[i] writes, bit for bit.  At T <= 64 the group runs as one launch
+ * pair that stages X once for all n linears; at larger T one plan serves the
+ * n linears in turn.  Errors as lora_apply, plus INVALID_ARG for n outside
+ * 1..8, a repeated module or modules of different d_in.
+ */
+lora_status_t lora_apply_group(lora_pool_t pool, int32_t n, const int32_t* modules, const lora_bf16_t* X,
+                               const int32_t* ids, int32_t T, const lora_bf16_t* const* W,
+                               lora_bf16_t* const* out, lora_plan_t plan, hipStream_t stream);
+lora_status_t lora_base_apply_group(lora_pool_t pool, int32_t n, const int32_t* modules, const lora_bf16_t* X,
+                                    int32_t T, const lora_bf16_t* const* W, lora_bf16_t* const* out,
+                                    hipStream_t stream);
 
 /*
  * INT4 base weight ([vLLM-ch7] performance notes: an AWQ-INT4 base with bf16

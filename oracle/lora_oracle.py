@@ -171,8 +171,10 @@ class Registry:
         linear layer every member adds its own update, so the chain's term is
         the sum of the members' terms.  The members are snapshotted: unloading
         one later leaves the chain intact.  Limits: ids in range and loaded
-        (NOT_LOADED), no repeats and no chains as members (INVALID_ARG), the
-        members' 16-rank blocks fit the pool's max rank (RANK)."""
+        (NOT_LOADED), no repeats and no chains as members (INVALID_ARG), and
+        the chain, an adapter of rank sum_c r_c, within the pool's max rank
+        (RANK; [vLLM-ch7] "starting a multi-LoRA service", --max-lora-rank;
+        [icman] section 3.3)."""
         if not (0 <= chain_id < self.max_ids):
             raise OracleError(ID_RANGE, f"id {chain_id}")
         members = [int(i) for i in members]
@@ -187,8 +189,7 @@ class Registry:
             if isinstance(self.adapters[i], Chain):
                 raise OracleError(INVALID_ARG, f"member {i} is a chain")
         ranks = [self.adapters[i].rank for i in members]
-        # each member but the last fills whole 16-rank blocks
-        if sum(16 * ((r + 15) // 16) for r in ranks[:-1]) + ranks[-1] > self.max_rank:
+        if sum(ranks) > self.max_rank:
             raise OracleError(RANK, f"chain ranks {ranks} exceed max rank {self.max_rank}")
         if chain_id in self.adapters:
             raise OracleError(EXISTS, f"id {chain_id}")

@@ -49,6 +49,7 @@ def _raw():
     (dict(max_rank=0), 1), (dict(max_rank=65), 1), (dict(max_ids=0), 1),
     (dict(max_ids=16385), 1), (dict(max_adapters=0), 1), (dict(max_tokens=0), 1),
     (dict(d_in=[1020]), 1), (dict(d_out=[4]), 1), (dict(n_modules=0), 1),
+    (dict(d_in=[65536], d_out=[16384]), 1),       # a 2 GiB base weight
 ])
 def test_pool_create_rejects_bad_arguments_on_host(kw, code):
     args = dict(max_adapters=4, max_ids=4, max_rank=8, d_in=[64], d_out=[64], max_tokens=64,
@@ -112,3 +113,29 @@ def test_q4_pack_layout():
         hrg.lora_q4_pack(np.full((1, 128), 16), np.zeros((1, 1)), np.zeros((1, 1), np.uint16))
     with pytest.raises(hrg.LoraError):
         hrg.lora_q4_pack(np.zeros((1, 200)), np.zeros((1, 1)), np.zeros((1, 1), np.uint16))
+
+
+def test_wrapper_rejects_bad_tensors_before_the_library():
+    """The Python wrapper checks dtype, layout, shape and device before it
+    passes raw addresses on (an int64 id tensor or a transposed view would
+    otherwise be read as something else)."""
+    import torch
+    from heterogeneous_rank_gemm_amd import LoraError
+    from heterogeneous_rank_gemm_amd.pool import check_tensor
+    good = torch.zeros((8, 64), dtype=torch.bfloat16)
+    check_tensor(good, "X", torch.bfloat16, 64, 8, "t", need_cuda=False)
+    cases = [
+        (torch.zeros((8, 64), dtype=torch.float32), torch.bfloat16, 64, 8),   # dtype
+        (torch.zeros((64, 8), dtype=torch.bfloat16).t(), torch.bfloat16, 64, 8),  # not contiguous
+        (torch.zeros((4, 64), dtype=torch.bfloat16), torch.bfloat16, 64, 8),   # too few rows
+        (torch.zeros((8, 32), dtype=torch.bfloat16), torch.bfloat16, 64, 8),   # wrong width
+        (torch.zeros(8, dtype=torch.int64), torch.int32, None, 8),            # int64 ids
+        (torch.zeros((8, 1), dtype=torch.int32), torch.int32, None, 8),       # ids not 1-D
+    ]
+    for t, dt, cols, rows in cases:
+        with pytest.raises(LoraError) as e:
+            check_tensor(t, "x", dt, cols, rows, "t", need_cuda=False)
+        assert e.value.status == "INVALID_ARG"
+    with pytest.raises(LoraError) as e:                                       # host tensor
+        check_tensor(good, "X", torch.bfloat16, 64, 8, "t")
+    assert e.value.status == "INVALID_ARG"

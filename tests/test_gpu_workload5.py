@@ -2,11 +2,15 @@
 stack (7 LoRA-augmented linears per layer, 224 in all), 64 tokens, 200
 resident rank-16 adapters in one pool of 224 modules.
 
-The step is captured as one hipGraph (the library records kernel launches
-only) and replayed several times with eager work in between; every replay
-must reproduce the eager outputs bit for bit.  Parity against the oracle is
-checked on sampled rows of every linear of layers 0, 15 and 31, and the
-base-only step's id-free rows against the oracle's base product."""
+A layer runs as three calls: one lora_apply_group over the five linears that
+read the hidden state h (q, k, v, gate, up), then o and down.  Checked:
+  * every row of every one of the 224 linears against the oracle (a registry
+    of one layer at a time, so the host holds one layer's adapters);
+  * the per-linear step (224 lora_apply calls) equals the grouped step bit
+    for bit;
+  * the step captured as one hipGraph and replayed several times, with eager
+    work in between, reproduces the eager outputs bit for bit;
+  * the base-only step likewise, and against the oracle's base product."""
 from __future__ import annotations
 
 import sys
@@ -20,8 +24,9 @@ pytestmark = pytest.mark.gpu
 import oracle  # noqa: E402
 import workloads as wk  # noqa: E402
 
-LAYERS = (0, 15, 31)
-ROWS = np.array([0, 1, 17, 31, 32, 47, 62, 63])
+# positions within a layer: the h-fed linears, then o, then down
+LAYER_GROUPS = ((0, 1, 2, 4, 5), (3,), (6,))
+LAYERS = 32
 
 
 def _say(*a):
@@ -33,25 +38,32 @@ def _say(*a):
 def case5():
     from gpu_helpers import Case
     wl = wk.WORKLOADS[5]
-    sampled = [7 * L + k for L in LAYERS for k in range(7)]
     _say("[workload 5] loading 200 adapters x 224 modules")
-    c = Case(wl, oracle_modules=sampled)
-    c.sampled = sampled
+    c = Case(wl, oracle_modules=[0])
     c.outs = [c.out_buf(j) for j in range(len(c.modules))]
     yield c
     c.close()
 
 
-def _step(c, lora=True):
-    for j in range(len(c.modules)):
-        if lora:
-            c.pool.apply(j, c.x_for(j), c.ids, c.W[j], c.outs[j])
-        else:
-            c.pool.base_apply(j, c.x_for(j), c.W[j], c.outs[j])
-
-
-def _snapshot(c):
-    return [o.clone() for o in c.outs]
+def _step(c, lora=True, grouped=True, outs=None):
+    outs = c.outs if outs is None else outs
+    for L in range(LAYERS):
+        for grp in LAYER_GROUPS:
+            mods = [7 * L + k for k in grp]
+            X = c.x_for(mods[0])
+            if grouped:
+                W = [c.W[m] for m in mods]
+                O = [outs[m] for m in mods]
+                if lora:
+                    c.pool.apply_group(mods, X, c.ids, W, O)
+                else:
+                    c.pool.base_apply_group(mods, X, W, O)
+            else:
+                for m in mods:
+                    if lora:
+                        c.pool.apply(m, X, c.ids, c.W[m], outs[m])
+                    else:
+                        c.pool.base_apply(m, X, c.W[m], outs[m])
 
 
 def _capture(c, lora):
@@ -68,17 +80,52 @@ def _capture(c, lora):
     return g
 
 
-def test_workload5_eager_step_parity_sampled_layers(case5):
+def _layer_registry(c, L):
+    """The oracle's registry for layer L's seven linears, holding the adapters
+    the batch uses (the same bf16 bits the library got, regenerated)."""
+    wl = c.wl
+    mods = [wl.modules[7 * L + k] for k in range(7)]
+    reg = oracle.Registry(wl.n_adapters, wl.n_adapters, wl.max_rank, [m.d_in for m in mods],
+                          [m.d_out for m in mods], wl.T)
+    for i in sorted(c.used):
+        r = int(c.ranks[i])
+        A, B = [], []
+        for k in range(7):
+            a, b = wk.adapter_weights(wl, i, 7 * L + k, r, c.seed, "cuda")
+            A.append(a.cpu())
+            B.append(b.cpu())
+        reg.load(i, r, wk.adapter_alpha(wl, r), A, B)
+    return reg
+
+
+def test_workload5_grouped_step_full_parity(case5):
     c = case5
-    _say("[workload 5] eager step, parity on layers 0, 15, 31")
+    _say("[workload 5] grouped eager step, parity on all 64 rows of all 224 linears")
     _step(c, lora=True)
     torch.cuda.synchronize()
     assert c.pool.status() == "OK"
-    for j in c.sampled:
-        out = c.outs[j][torch.as_tensor(ROWS, device="cuda")].cpu()
-        from gpu_helpers import assert_parity
-        mx, rl1, _ = assert_parity(out, c.oracle(j, rows=ROWS), f"module {c.wl.modules[j].name}")
-        _say(f"  {c.wl.modules[j].name}: max {mx:.3e} relL1 {rl1:.3e}")
+    from gpu_helpers import assert_parity
+    for L in range(LAYERS):
+        reg = _layer_registry(c, L)
+        worst = 0.0
+        for k in range(7):
+            j = 7 * L + k
+            ref = oracle.lora_linear(reg, k, c.x_for(j).cpu(), c.ids_np, c.W[j].cpu())
+            mx, rl1, _ = assert_parity(c.outs[j].cpu(), ref, f"module {c.wl.modules[j].name}")
+            worst = max(worst, rl1)
+        _say(f"  layer {L}: worst relL1 {worst:.3e}")
+
+
+def test_workload5_per_linear_step_equals_grouped(case5):
+    c = case5
+    _say("[workload 5] per-linear step against the grouped step")
+    _step(c, lora=True)
+    other = [torch.empty_like(o) for o in c.outs]
+    _step(c, lora=True, grouped=False, outs=other)
+    torch.cuda.synchronize()
+    assert c.pool.status() == "OK"
+    for j in range(len(c.outs)):
+        assert torch.equal(other[j], c.outs[j]), f"module {j}"
 
 
 def test_workload5_graph_replays_match_eager(case5):
@@ -86,7 +133,7 @@ def test_workload5_graph_replays_match_eager(case5):
     _say("[workload 5] eager reference step")
     _step(c, lora=True)
     torch.cuda.synchronize()
-    ref = _snapshot(c)
+    ref = [o.clone() for o in c.outs]
     _say("[workload 5] capture and replay")
     g = _capture(c, lora=True)
     for rep in range(3):
@@ -105,15 +152,14 @@ def test_workload5_base_step_graph(case5):
     _say("[workload 5] base-only step as a graph")
     _step(c, lora=False)
     torch.cuda.synchronize()
-    ref = _snapshot(c)
+    ref = [o.clone() for o in c.outs]
     g = _capture(c, lora=False)
     g.replay()
     torch.cuda.synchronize()
     for j in range(len(c.outs)):
         assert torch.equal(c.outs[j], ref[j])
-    # the base-only product against the oracle's, on the sampled rows of layer 0
+    # the base-only product against the oracle's, every row of layers 0 and 31
     from gpu_helpers import assert_parity
-    for j in c.sampled[:7]:
-        X = c.x_for(j).cpu()[torch.as_tensor(ROWS)]
-        Yb = oracle.base_linear(X, c.W[j].cpu())
-        assert_parity(ref[j][torch.as_tensor(ROWS, device="cuda")].cpu(), Yb, f"base {j}")
+    for j in list(range(7)) + list(range(7 * 31, 7 * 32)):
+        Yb = oracle.base_linear(c.x_for(j).cpu(), c.W[j].cpu())
+        assert_parity(ref[j].cpu(), Yb, f"base {j}")

@@ -513,3 +513,31 @@ def test_chain_is_the_sum_of_its_members():
         reg.load_chain(4, [2, 3, 0, 1])                       # 16 + 16 + 16 + 5 = 53 > 48
     assert e.value.status == oracle.RANK
     reg.load_chain(4, [2, 3, 1])                              # 16 + 16 + 5 = 37 fits
+
+
+def test_chain_rank_is_the_sum_of_member_ranks():
+    """A chain is one adapter of rank sum_c r_c, refused only above the pool's
+    max rank ([vLLM-ch7] "starting a multi-LoRA service", --max-lora-rank;
+    [icman] section 3.3).  Pinned where a block-padded rule would differ:
+    three rank-5 adapters (15) fit a max rank of 16, a fourth (20) does not,
+    and a sum of exactly the max rank fits; the accepted chain's term is the
+    members' terms added."""
+    g = np.random.default_rng(21)
+    d_in, d_out, T = 7, 4, 5
+    reg = Registry(12, 12, 16, [d_in], [d_out], T)
+    mats = {}
+    for i, r in enumerate([5, 5, 5, 5, 11, 1]):
+        A = np.round(g.standard_normal((d_in, r)) * 8) / 8
+        B = np.round(g.standard_normal((r, d_out)) * 8) / 8
+        mats[i] = (A, B)
+        reg.load(i, r, 2.0 * r, [A], [B])
+    reg.load_chain(6, [0, 1, 2])                               # 5 + 5 + 5 = 15 <= 16
+    reg.load_chain(7, [4, 0])                                  # 11 + 5 = 16 == max rank
+    for members in ([0, 1, 2, 3], [4, 0, 5], [4, 1, 2]):       # 20, 17, 21 > 16
+        with pytest.raises(OracleError) as e:
+            reg.load_chain(8, members)
+        assert e.value.status == oracle.RANK, members
+    X = np.round(g.standard_normal((T, d_in)) * 4) / 4
+    W = np.round(g.standard_normal((d_out, d_in)) * 4) / 4
+    ref = X @ W.T + sum(2.0 * (X @ mats[i][0]) @ mats[i][1] for i in (0, 1, 2))
+    np.testing.assert_allclose(oracle.lora_linear(reg, 0, X, np.full(T, 6), W), ref, rtol=0, atol=1e-12)
