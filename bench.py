@@ -110,7 +110,7 @@ def q4_weight(wl: wk.Workload, module: int, seed: int, torch):
 class Replica:
     """One independent copy of the workload's resident state."""
 
-    def __init__(self, wl: wk.Workload, seed: int, torch, hrg, int4: bool = False):
+    def __init__(self, wl: wk.Workload, seed: int, torch, hrg, int4: bool = False, packed: bool = True):
         self.ids_np = wk.adapter_ids(wl, seed)
         self.ranks = wk.adapter_ranks(wl, seed)
         self.T = wl.T
@@ -140,6 +140,10 @@ class Replica:
                 if wl.T > DECODE_MAX_T else None
         else:
             self.W = [wk.base_weight(wl, j, seed, "cuda") for j in range(len(mods))]
+        # decode batches stream the base weights in the decode kernels' fragment
+        # tiles (packed once, like a model's weights at load time)
+        self.Wp = [self.pool.pack_weight(w) for w in self.W] \
+            if packed and not int4 and wl.T <= DECODE_MAX_T else None
         self.out = [torch.empty((wl.T, m.d_out), dtype=torch.bfloat16, device="cuda")
                     for m in mods]
         self.xin = [self.X[m.input_group] for m in mods]
@@ -170,7 +174,10 @@ DECODE_MAX_T = 64
 
 
 def _apply_group(rep: Replica, hrg, g, plan):
-    if rep.int4:
+    if rep.Wp is not None:
+        hrg.lora_apply_group_packed(rep.pool.handle, g, rep.xin[g[0]], rep.ids, rep.T, [rep.Wp[j] for j in g],
+                                    [rep.out[j] for j in g])
+    elif rep.int4:
         for j in g:
             hrg.lora_apply_q4(rep.pool.handle, j, rep.xin[j], rep.ids, rep.T, rep.Wq[j][0], rep.Wq[j][1],
                               rep.scratch, rep.out[j], plan)
@@ -180,7 +187,10 @@ def _apply_group(rep: Replica, hrg, g, plan):
 
 
 def _base_group(rep: Replica, hrg, g):
-    if rep.int4:
+    if rep.Wp is not None:
+        hrg.lora_base_apply_group_packed(rep.pool.handle, g, rep.xin[g[0]], rep.T, [rep.Wp[j] for j in g],
+                                         [rep.out[j] for j in g])
+    elif rep.int4:
         for j in g:
             hrg.lora_base_apply_q4(rep.pool.handle, j, rep.xin[j], rep.T, rep.Wq[j][0], rep.Wq[j][1],
                                    rep.scratch, rep.out[j])
@@ -653,6 +663,9 @@ def main(argv=None) -> int:
                          "the rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     ap.add_argument("--peaks", action="store_true",
                     help="measure the chip's streaming-read GB/s and bf16 MFMA TFLOP/s instead")
+    ap.add_argument("--layout", choices=["packed", "row"], default="packed",
+                    help="decode batches: base weights in fragment tiles (lora_pack_weight) or "
+                         "row-major")
     ap.add_argument("--int4", action="store_true",
                     help="INT4 (group 128) base weights instead of bf16 (lora_apply_q4)")
     ap.add_argument("--chains", action="store_true",
@@ -698,8 +711,8 @@ def main(argv=None) -> int:
     wl = wk.WORKLOADS[args.workload]
     R = 1 if wl.key == 5 else max(1, args.rotate)
     print(f"[bench] workload {wl.key} '{wl.name}', {R} replica(s)", file=sys.stderr, flush=True)
-    reps = [Replica(wl, wl.default_seed + 1000 * r if r else wl.default_seed, torch, hrg, args.int4)
-            for r in range(R)]
+    reps = [Replica(wl, wl.default_seed + 1000 * r if r else wl.default_seed, torch, hrg, args.int4,
+                    args.layout == "packed") for r in range(R)]
     torch.cuda.synchronize()
     print("[bench] state resident; timing", file=sys.stderr, flush=True)
 
@@ -750,7 +763,7 @@ def main(argv=None) -> int:
     n_calls = len(reps[0].groups)
     t_calls = float(np.sum(t_groups))
     decode = wl.T <= DECODE_MAX_T
-    kernel = ("decode_main + decode_combine: one launch pair per lora_apply_group call, "
+    kernel = ("decode_main + decode_combine: one launch pair per grouped apply, "
               f"{n_calls} calls per step" if decode else
               "shrink_kernel + expand_small_kernel + prefill_kernel per linear, plan_kernel per step")
     if hbm_bound:
@@ -791,13 +804,14 @@ def main(argv=None) -> int:
                    "ranks": list(wl.rank_choices), "max_rank": wl.max_rank,
                    "replicas_rotated": R, "hipgraph": use_graph,
                    "calls_per_step": n_calls,
-                   "base_weight": "int4-g128" if args.int4 else "bf16"},
+                   "base_weight": "int4-g128" if args.int4 else
+                   ("bf16, fragment tiles" if reps[0].Wp is not None else "bf16, row-major")},
         "timing": f"median of {args.steps} steps (event pair per step) after {args.warmup} warm-up steps",
         "mean_ms_per_step": round(t_step_mean * 1e3, 5),
         "lora_overhead_pct": round(100.0 * (t_step - t_base) / t_base, 2),
         "base_only_ms_per_step": round(t_base * 1e3, 5),
         "apply_ms_per_step": round(t_apply * 1e3, 5),
-        "per_linear_ms_per_step": round(t_lin * 1e3, 5) if t_lin else None,
+        "per_linear_row_major_ms_per_step": round(t_lin * 1e3, 5) if t_lin else None,
         "warm": warm,
         "step_roofline_frac": round(t_roof / t_step, 4),
         "algorithmic": {"base_bytes": bb, "lora_bytes": lb, "flops": fl,

@@ -31,6 +31,8 @@ EXPORTED = (
     "lora_host_cache_create", "lora_host_register", "lora_host_unregister", "lora_prefetch",
     "lora_pin_adapter", "lora_paging_query", "lora_paging_stats", "lora_q4_pack", "lora_apply_q4",
     "lora_base_apply_q4", "lora_load_chain", "lora_apply_group", "lora_base_apply_group",
+    "lora_packed_weight_elems", "lora_pack_weight", "lora_apply_group_packed",
+    "lora_base_apply_group_packed",
 )
 
 _vp = C.c_void_p
@@ -65,6 +67,10 @@ _sigs = {
     "lora_load_chain": [_vp, _i32, _i32, _P_i32, _vp],
     "lora_apply_group": [_vp, _i32, _P_i32, _vp, _vp, _i32, C.POINTER(_vp), C.POINTER(_vp), _vp, _vp],
     "lora_base_apply_group": [_vp, _i32, _P_i32, _vp, _i32, C.POINTER(_vp), C.POINTER(_vp), _vp],
+    "lora_packed_weight_elems": [_i32, _i32, C.POINTER(C.c_int64)],
+    "lora_pack_weight": [_vp, _i32, _i32, _vp, _vp],
+    "lora_apply_group_packed": [_vp, _i32, _P_i32, _vp, _vp, _i32, C.POINTER(_vp), C.POINTER(_vp), _vp],
+    "lora_base_apply_group_packed": [_vp, _i32, _P_i32, _vp, _i32, C.POINTER(_vp), C.POINTER(_vp), _vp],
 }
 for _name, _args in _sigs.items():
     _f = getattr(_lib, _name)
@@ -187,6 +193,30 @@ def lora_base_apply_group(pool: int, modules: Sequence[int], X, T: int, W: Seque
     n, mods, pw, po = _group_arrays(modules, W, out)
     _check(_lib.lora_base_apply_group(pool, n, mods, _ptr(X), T, pw, po, _stream(stream)),
            "lora_base_apply_group")
+
+
+def lora_packed_weight_elems(N: int, K: int) -> int:
+    n = C.c_int64()
+    _check(_lib.lora_packed_weight_elems(N, K, C.byref(n)), "lora_packed_weight_elems")
+    return n.value
+
+
+def lora_pack_weight(W, N: int, K: int, Wp, stream=None) -> None:
+    _check(_lib.lora_pack_weight(_ptr(W), N, K, _ptr(Wp), _stream(stream)), "lora_pack_weight")
+
+
+def lora_apply_group_packed(pool: int, modules: Sequence[int], X, ids, T: int, Wp: Sequence,
+                            out: Sequence, stream=None) -> None:
+    n, mods, pw, po = _group_arrays(modules, Wp, out)
+    _check(_lib.lora_apply_group_packed(pool, n, mods, _ptr(X), _ptr(ids), T, pw, po, _stream(stream)),
+           "lora_apply_group_packed")
+
+
+def lora_base_apply_group_packed(pool: int, modules: Sequence[int], X, T: int, Wp: Sequence,
+                                 out: Sequence, stream=None) -> None:
+    n, mods, pw, po = _group_arrays(modules, Wp, out)
+    _check(_lib.lora_base_apply_group_packed(pool, n, mods, _ptr(X), T, pw, po, _stream(stream)),
+           "lora_base_apply_group_packed")
 
 
 def lora_base_apply(pool: int, module: int, X, T: int, W, out, stream=None) -> None:

@@ -103,7 +103,7 @@ bool module_ok(const lora_pool_s* P, int32_t m) { return P && m >= 0 && m < P->n
 lora_status_t decode_group(lora_pool_s* P, int32_t n, const int32_t* modules, const lora_bf16_t* X,
                            const int32_t* ids, int32_t T, const lora_bf16_t* const* W,
                            const uint32_t* const* Wq, const uint32_t* const* Wsz, lora_bf16_t* const* out,
-                           bool lora, float* part, float* upart, hipStream_t stream) {
+                           bool lora, bool wpacked, float* part, float* upart, hipStream_t stream) {
   const int K = P->d_in[modules[0]];
   hrg::DecodeArgs a{};
   a.X = X;
@@ -113,6 +113,7 @@ lora_status_t decode_group(lora_pool_s* P, int32_t n, const int32_t* modules, co
   a.KS = ceil_div(K, hrg::kDecodeChunk);
   a.n_mod = n;
   a.wq = Wq ? 1 : 0;
+  a.wpacked = wpacked ? 1 : 0;
   for (int32_t i = 0; i < n; ++i) {
     const int32_t m = modules[i], N = P->d_out[m];
     a.W[i] = W ? W[i] : nullptr;
@@ -222,7 +223,7 @@ lora_status_t lora_pool_create(lora_pool_t* pool, int32_t max_adapters, int32_t 
   size_t off = 0, max_dim = 0;
   for (int32_t m = 0; m < n_modules; ++m) {
     P->a_off.push_back(off);
-    off += (size_t)max_rank * d_in[m];
+    off += hrg::frag_elems(P->rpad, d_in[m]);  // A^T in fragment tiles
     P->b_off.push_back(off);
     off += (size_t)P->rpad * d_out[m];  // B^T in 16-rank chunks
     max_dim = std::max<size_t>(max_dim, std::max(d_in[m], d_out[m]));
@@ -330,7 +331,7 @@ lora_status_t lora_load_adapter(lora_pool_t P, int32_t id, int32_t rank, float a
     hrg::PackArgs pa{};
     if (!A[m]) {
       // not a target of this adapter: zero pages (rank 0 reads no source)
-      pa = {P->staging, base + P->a_off[m], 0, P->max_rank, P->d_in[m], 0};
+      pa = {P->staging, base + P->a_off[m], 0, P->rpad, P->d_in[m], 0};
       if (hrg::launch_pack(pa, stream) != hipSuccess) return LORA_ERR_HIP;
       pa = {P->staging, base + P->b_off[m], 0, P->rpad, P->d_out[m], 1};
       if (hrg::launch_pack(pa, stream) != hipSuccess) return LORA_ERR_HIP;
@@ -338,7 +339,7 @@ lora_status_t lora_load_adapter(lora_pool_t P, int32_t id, int32_t rank, float a
     }
     if (hipMemcpyAsync(P->staging, A[m], na * 2, hipMemcpyDefault, stream) != hipSuccess)
       return (void)hipGetLastError(), LORA_ERR_HIP;
-    pa = {P->staging, base + P->a_off[m], rank, P->max_rank, P->d_in[m], 0};
+    pa = {P->staging, base + P->a_off[m], rank, P->rpad, P->d_in[m], 0};
     if (hrg::launch_pack(pa, stream) != hipSuccess) return LORA_ERR_HIP;
     if (hipMemcpyAsync(P->staging, B[m], nb * 2, hipMemcpyDefault, stream) != hipSuccess)
       return (void)hipGetLastError(), LORA_ERR_HIP;
@@ -426,15 +427,24 @@ lora_status_t lora_load_chain(lora_pool_t P, int32_t chain_id, int32_t n, const 
   for (int32_t m = 0; m < P->n_modules; ++m) {
     // zero pages, then each member's rank blocks at its offset (rows past a
     // member's rank are zero in its own pages)
-    hrg::PackArgs pa = {P->staging, base + P->a_off[m], 0, P->max_rank, P->d_in[m], 0};
+    hrg::PackArgs pa = {P->staging, base + P->a_off[m], 0, P->rpad, P->d_in[m], 0};
     if (hrg::launch_pack(pa, stream) != hipSuccess) return LORA_ERR_HIP;
     pa = {P->staging, base + P->b_off[m], 0, P->rpad, P->d_out[m], 1};
     if (hrg::launch_pack(pa, stream) != hipSuccess) return LORA_ERR_HIP;
     for (int32_t i = 0; i < n; ++i) {
       const uint16_t* mb = P->pages + (size_t)P->h_id2slot[members[i]] * P->slot_elems;
-      const size_t arows = (size_t)std::min(16 * nb[i], P->max_rank - 16 * blk[i]);
-      if (hipMemcpyAsync(base + P->a_off[m] + (size_t)16 * blk[i] * P->d_in[m], mb + P->a_off[m],
-                         arows * P->d_in[m] * 2, hipMemcpyDeviceToDevice, stream) != hipSuccess ||
+      // member block b (16 ranks) -> chain block blk[i] + b: in fragment
+      // tiles a block's steps of one 1024-deep column block are contiguous
+      const int32_t din = P->d_in[m], k32 = (din + 31) / 32;
+      bool ok = true;
+      for (int32_t b = 0; b < nb[i] && ok; ++b)
+        for (int32_t s0 = 0; s0 < k32 && ok; s0 += hrg::kFragChunk / 32) {
+          const size_t steps = (size_t)std::min(hrg::kFragChunk / 32, k32 - s0);
+          ok = hipMemcpyAsync(base + P->a_off[m] + hrg::frag_tile(blk[i] + b, s0, P->rpad, din) * 512,
+                              mb + P->a_off[m] + hrg::frag_tile(b, s0, P->rpad, din) * 512, steps * 1024,
+                              hipMemcpyDeviceToDevice, stream) == hipSuccess;
+        }
+      if (!ok ||
           hipMemcpyAsync(base + P->b_off[m] + (size_t)blk[i] * P->d_out[m] * 16, mb + P->b_off[m],
                          (size_t)nb[i] * P->d_out[m] * 16 * 2, hipMemcpyDeviceToDevice, stream) != hipSuccess)
         return (void)hipGetLastError(), LORA_ERR_HIP;
@@ -603,12 +613,15 @@ static lora_status_t apply_impl(lora_pool_t P, int32_t n, const int32_t* modules
                                 const int32_t* ids, int32_t T, const lora_bf16_t* const* W,
                                 const uint32_t* const* Wq, const uint32_t* const* Wsz,
                                 lora_bf16_t* scratch, lora_bf16_t* const* out, lora_plan_t plan, bool lora,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool wpacked = false) {
   const lora_status_t st = check_apply(P, n, modules, X, ids, T, W, Wq, Wsz, scratch, out, plan, lora);
   if (st != LORA_OK || T == 0) return st;
+  // fragment-tiled weights are the decode kernels' layout only
+  if (wpacked && T > hrg::kDecodeMaxT) return LORA_ERR_INVALID_ARG;
   DeviceGuard g(P->device);
   if (T <= hrg::kDecodeMaxT)
-    return decode_group(P, n, modules, X, ids, T, W, Wq, Wsz, out, lora, P->dec_part, P->dec_upart, stream);
+    return decode_group(P, n, modules, X, ids, T, W, Wq, Wsz, out, lora, wpacked, P->dec_part, P->dec_upart,
+                        stream);
   lora_plan_s* pl = plan;
   if (lora && !pl) {
     // one plan serves every linear of the call
@@ -653,6 +666,34 @@ lora_status_t lora_base_apply_group(lora_pool_t P, int32_t n, const int32_t* mod
                                     hipStream_t stream) {
   if (!W) return LORA_ERR_INVALID_ARG;
   return apply_impl(P, n, modules, X, nullptr, T, W, nullptr, nullptr, nullptr, out, nullptr, false, stream);
+}
+
+lora_status_t lora_pack_weight(const lora_bf16_t* W, int32_t N, int32_t K, lora_bf16_t* Wp, hipStream_t stream) {
+  if (!W || !Wp || N < 8 || K < 8 || N > 65536 || K > 65536 || N % 8 || K % 8) return LORA_ERR_INVALID_ARG;
+  if ((int64_t)hrg::frag_elems(N, K) * 2 > (int64_t)INT32_MAX) return LORA_ERR_INVALID_ARG;
+  hrg::PackArgs pa = {W, Wp, N, N, K, 2};
+  return hrg::launch_pack(pa, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+lora_status_t lora_packed_weight_elems(int32_t N, int32_t K, int64_t* elems) {
+  if (!elems || N < 1 || K < 1) return LORA_ERR_INVALID_ARG;
+  *elems = (int64_t)hrg::frag_elems(N, K);
+  return LORA_OK;
+}
+
+lora_status_t lora_apply_group_packed(lora_pool_t P, int32_t n, const int32_t* modules, const lora_bf16_t* X,
+                                      const int32_t* ids, int32_t T, const lora_bf16_t* const* Wp,
+                                      lora_bf16_t* const* out, hipStream_t stream) {
+  if (!Wp) return LORA_ERR_INVALID_ARG;
+  return apply_impl(P, n, modules, X, ids, T, Wp, nullptr, nullptr, nullptr, out, nullptr, true, stream, true);
+}
+
+lora_status_t lora_base_apply_group_packed(lora_pool_t P, int32_t n, const int32_t* modules,
+                                           const lora_bf16_t* X, int32_t T, const lora_bf16_t* const* Wp,
+                                           lora_bf16_t* const* out, hipStream_t stream) {
+  if (!Wp) return LORA_ERR_INVALID_ARG;
+  return apply_impl(P, n, modules, X, nullptr, T, Wp, nullptr, nullptr, nullptr, out, nullptr, false, stream,
+                    true);
 }
 
 lora_status_t lora_apply_q4(lora_pool_t P, int32_t module, const lora_bf16_t* X, const int32_t* ids,

@@ -45,6 +45,7 @@ namespace hrg {
 
 constexpr int kHalf = kDecodeChunk / 2;    // K of one register block (a "half")
 constexpr int kHS = kHalf / 32;            // MFMA K steps per half (16)
+constexpr int kQS = 8;                     // MFMA K steps per quarter of a chunk
 constexpr int kXs = kDecodeChunk + 8;      // LDS row of the X chunk (16-byte pad)
 constexpr int kXPieces = 2 * 64;           // 1-KB DMA pieces of an X chunk
 constexpr uint32_t kOobOff = 0x80000000u;  // buffer offset past every operand
@@ -104,6 +105,9 @@ struct UnitSrc {
   __amdgpu_buffer_rsrc_t rz;  // INT4 W units: the linear's group words (Wsz)
   uint32_t off;               // this lane's byte offset at the chunk start (kOobOff: no row)
   uint32_t offz;              // INT4 W units: the lane's group-word offset
+  int istep;                  // bytes from one 32-deep step to the next: 64 in a
+                              // row-major W, 1024 in fragment tiles (wave-uniform;
+                              // the loads take it as their scalar offset)
 };
 struct UnitDst {
   int kind;                   // 0: W rows, 1: A rows
@@ -177,11 +181,22 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
       sr.rz = uniform_rsrc(ka->Wsz[m], N * KG * 4);
       sr.off = row < N ? (uint32_t)(row * KW + 16 * (k0 / kQ4Group) + 4 * g4) * 4u : kOobOff;
       sr.offz = row < N ? (uint32_t)(row * KG + k0 / kQ4Group) * 4u : kOobOff;
+      sr.istep = 0;
+    } else if (a.wpacked) {
+      // fragment tiles: the unit's 16 rows are row group u - u0[m]; its
+      // tiles of the chunk are one contiguous 32 KB (1 KB per 32-deep
+      // step, this lane's 16 bytes at 16 lane)
+      sr.rs = uniform_rsrc(ka->W[m], (int)frag_elems(N, K) * 2);
+      sr.rz = sr.rs;
+      sr.off = (uint32_t)((frag_tile(u - ka->u0[m], k0 / 32, N, K) * 64 + lane) * 16);
+      sr.offz = 0;
+      sr.istep = 1024;
     } else {
       sr.rs = uniform_rsrc(ka->W[m], N * K * 2);
       sr.rz = sr.rs;
       sr.off = row < N ? (uint32_t)(row * K + k0 + 8 * g4) * 2u : kOobOff;
       sr.offz = 0;
+      sr.istep = 64;
     }
   };
   // Register buffers of two halves: bf16 rows (W or A units) take 16 loads of
@@ -193,7 +208,19 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
     constexpr int H = decltype(hc)::value;
 #pragma unroll
     for (int i = 0; i < kHS; ++i)
-      b[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(sr.rs, sr.off + 2 * kHalf * H + 64 * i, 0, 0));
+      b[i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                     sr.rs, sr.off, __builtin_amdgcn_readfirstlane((kHS * H + i) * sr.istep), 0));
+  };
+  // the bf16 walk's ring: four quarters of 8 steps (256 deep, 8 KB per wave)
+  uint4 rq[4][kQS];
+  auto load_r = [&](uint4 (&b)[kQS], const UnitSrc& sr, auto qc) __attribute__((always_inline)) {
+    constexpr int Q = decltype(qc)::value;
+#pragma unroll
+    for (int i = 0; i < kQS; ++i)
+      b[i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                     sr.rs, sr.off, __builtin_amdgcn_readfirstlane((kQS * Q + i) * sr.istep), 0));
   };
   auto load_q = [&](uint4 (&b)[WQ ? kQL : 1], const UnitSrc& sr, auto hc) __attribute__((always_inline)) {
     if constexpr (WQ) {
@@ -213,6 +240,10 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
   // the barrier waits for the copy (and the ids before it), not for it ----
   UnitSrc csrc;
   UnitDst cdst;
+  const auto Q0 = std::integral_constant<int, 0>{};
+  const auto Q1 = std::integral_constant<int, 1>{};
+  const auto Q2 = std::integral_constant<int, 2>{};
+  const auto Q3 = std::integral_constant<int, 3>{};
   if (nw > 0) {
     w_unit(wi, csrc, cdst);
     __builtin_amdgcn_sched_barrier(0);
@@ -220,8 +251,11 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
       load_q(qbuf[0], csrc, H0);
       barrier_after<kQL>();
     } else {
-      load_b(buf[0], csrc, H0);
-      barrier_after<kHS>();
+      // three quarters in flight before the walk starts
+      load_r(rq[0], csrc, Q0);
+      load_r(rq[1], csrc, Q1);
+      load_r(rq[2], csrc, Q2);
+      barrier_after<3 * kQS>();
     }
   } else {
     barrier_after<0>();
@@ -293,14 +327,16 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
     ds.col = 16 * qb;
     ds.members = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(grp >> 32), leader) << 32) |
                  (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)grp, leader);
-    const int q = 16 * qb + r16;
+    // the page holds A^T in fragment tiles: rank block qb's tiles of the
+    // chunk are one contiguous 32 KB (ranks past the adapter's are zero);
     // an adapter that does not target this linear streams nothing here
-    const bool ok = q < min(r, a.rmax) && targets(mk, ka->module[m]);
+    const bool ok = 16 * qb < min(r, a.rmax) && targets(mk, ka->module[m]);
     const uint16_t* page = a.pages + (size_t)sl * a.slot_stride + ka->a_off[m];
-    sr.rs = uniform_rsrc(page, a.rmax * K * 2);
+    sr.rs = uniform_rsrc(page, (int)frag_elems(a.u_ld, K) * 2);
     sr.rz = sr.rs;
-    sr.off = ok ? (uint32_t)(q * K + k0 + 8 * g4) * 2u : kOobOff;
+    sr.off = ok ? (uint32_t)((frag_tile(qb, k0 / 32, a.u_ld, K) * 64 + lane) * 16) : kOobOff;
     sr.offz = 0;
+    sr.istep = 1024;
   };
   // a unit past the wave's last: no row, no bytes (the loads that a loop
   // issues unconditionally for it return zeros without touching memory)
@@ -309,6 +345,7 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
     sr.rz = sr.rs;
     sr.off = kOobOff;
     sr.offz = kOobOff;
+    sr.istep = 0;
     ds.kind = -1;
     ds.m = 0;
     ds.col = 0;
@@ -356,6 +393,37 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int i = 0; i + 1 < kHS; ++i) {
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto compute_r = [&](const uint4 (&b)[kQS], auto qc) __attribute__((always_inline)) {
+    constexpr int Q = decltype(qc)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    int kl = klen;  // opaque: the tail masks are formed where used (see compute_b)
+    asm volatile("" : "+s"(kl));
+    bf16x8 xf[2][4];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) xf[0][tb] = lds_bf16x8(xs + (16 * tb + r16) * kXs + 32 * kQS * Q + 8 * g4);
+#pragma unroll
+    for (int i = 0; i < kQS; ++i) {
+      const int k = 32 * kQS * Q + 32 * i + 8 * g4;
+      if (i + 1 < kQS) {
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) xf[(i + 1) & 1][tb] = lds_bf16x8(xs + (16 * tb + r16) * kXs + k + 32);
+      }
+      const bf16x8 wb = __builtin_bit_cast(bf16x8, keep_if(k < kl, b[i]));
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) acc[tb] = mfma16(wb, xf[i & 1][tb], acc[tb]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i + 1 < kQS; ++i) {
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -417,10 +485,12 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
   // before its second half's.  Every load is issued unconditionally (past the
   // wave's last unit, rows of no bytes), so the compiler counts each wait
   // exactly.  W units first (INT4 or bf16), then the A units (bf16 pages).
-  int j = 0;
-  for (; j < nw; ++j) {
-    UnitDst ndst;
-    if constexpr (WQ) {
+  if constexpr (WQ) {
+    int j = 0;
+    // W units (INT4, two halves through two register buffers), then the A
+    // units (bf16 pages, likewise)
+    for (; j < nw; ++j) {
+      UnitDst ndst;
       load_q(qbuf[1], csrc, H1);
       compute_q(qbuf[0], H0);
       if (j + 1 < nw) {
@@ -432,37 +502,62 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
         after_w(j + 1, csrc, ndst);
         load_b(buf[0], csrc, H0);
       }
-    } else {
+      store(cdst);
+      cdst = ndst;
+    }
+    if (nw == 0) {
+      group();
+      if (nu == 0) return;  // nothing in flight: the barrier waited for every load
+      a_unit(wi - NUW, csrc, cdst);
+      load_b(buf[0], csrc, H0);
+    }
+    for (; j < nu; ++j) {
       load_b(buf[1], csrc, H1);
       compute_b(buf[0], H0);
-      if (j + 1 < nw)
-        w_unit(wi + (j + 1) * NWc, csrc, ndst);
+      UnitDst ndst;
+      if (j + 1 < nu)
+        a_unit(wi + (j + 1) * NWc - NUW, csrc, ndst);
       else
-        after_w(j + 1, csrc, ndst);
+        none(csrc, ndst);
       load_b(buf[0], csrc, H0);
       compute_b(buf[1], H1);
+      store(cdst);
+      cdst = ndst;
     }
-    store(cdst);
-    cdst = ndst;
-  }
-  if (nw == 0) {
-    group();
-    if (nu == 0) return;  // nothing in flight: the barrier waited for every load
-    a_unit(wi - NUW, csrc, cdst);
-    load_b(buf[0], csrc, H0);
-  }
-  for (; j < nu; ++j) {
-    load_b(buf[1], csrc, H1);
-    compute_b(buf[0], H0);
-    UnitDst ndst;
-    if (j + 1 < nu)
-      a_unit(wi + (j + 1) * NWc - NUW, csrc, ndst);
-    else
-      none(csrc, ndst);
-    load_b(buf[0], csrc, H0);
-    compute_b(buf[1], H1);
-    store(cdst);
-    cdst = ndst;
+  } else {
+    // bf16: a ring of four quarters; while one quarter's MFMAs run the next
+    // three are in flight (24 KB per wave), W units first, then A units
+    if (nw == 0) {
+      group();
+      if (nu == 0) return;  // nothing in flight: the barrier waited for every load
+      a_unit(wi - NUW, csrc, cdst);
+      load_r(rq[0], csrc, Q0);
+      load_r(rq[1], csrc, Q1);
+      load_r(rq[2], csrc, Q2);
+    }
+    for (int j = 0; j < nu; ++j) {
+      UnitSrc nsrc;
+      UnitDst ndst;
+      load_r(rq[3], csrc, Q3);
+      compute_r(rq[0], Q0);
+      if (j + 1 < nw)
+        w_unit(wi + (j + 1) * NWc, nsrc, ndst);
+      else if (j + 1 == nw)
+        after_w(j + 1, nsrc, ndst);  // groups the batch; nu may grow
+      else if (j + 1 < nu)
+        a_unit(wi + (j + 1) * NWc - NUW, nsrc, ndst);
+      else
+        none(nsrc, ndst);
+      load_r(rq[0], nsrc, Q0);
+      compute_r(rq[1], Q1);
+      load_r(rq[1], nsrc, Q1);
+      compute_r(rq[2], Q2);
+      load_r(rq[2], nsrc, Q2);
+      compute_r(rq[3], Q3);
+      store(cdst);
+      csrc = nsrc;
+      cdst = ndst;
+    }
   }
   // the last (empty) request has returned before the wave ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -674,7 +769,6 @@ hipError_t launch_main(const DecodeArgs& a, int wpb, int grid, hipStream_t s) {
     case 4: hipLaunchKernelGGL((decode_main<4, WQ>), dim3(grid), dim3(256), 0, s, a); break;
     case 5: hipLaunchKernelGGL((decode_main<5, WQ>), dim3(grid), dim3(320), 0, s, a); break;
     case 6: hipLaunchKernelGGL((decode_main<6, WQ>), dim3(grid), dim3(384), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((decode_main<8, WQ>), dim3(grid), dim3(512), 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -686,7 +780,6 @@ int main_resident(int wpb) {
     case 4: return resident_blocks(reinterpret_cast<const void*>(&decode_main<4, WQ>), 256, 0);
     case 5: return resident_blocks(reinterpret_cast<const void*>(&decode_main<5, WQ>), 320, 0);
     case 6: return resident_blocks(reinterpret_cast<const void*>(&decode_main<6, WQ>), 384, 0);
-    case 8: return resident_blocks(reinterpret_cast<const void*>(&decode_main<8, WQ>), 512, 0);
   }
   return 1;
 }
@@ -696,18 +789,25 @@ hipError_t launch_decode(const DecodeArgs& args, int items_cap, hipStream_t s) {
   // units per K chunk the grid must hold: every W unit plus every A item the
   // batch could have on every linear
   const int units = a.u0[kMaxGroup] + (a.lora ? a.n_mod * items_cap : 0);
-  // waves per block: the shape whose busiest wave has the fewest units (one
-  // block per compute unit: the X chunk fills most of the LDS); a tie keeps
-  // fewer waves
-  int best_w = 4, best_nbc = 1, best_max = INT32_MAX;
-  for (int wpb : {4, 5, 6, 8}) {
+  // waves per block: the shape whose waves are busiest on average relative
+  // to the busiest one (the launch lasts as long as its busiest wave, and the
+  // compute units' share of the bandwidth does not depend on how many waves
+  // split it); one block per compute unit (the X chunk fills most of the
+  // LDS); a tie keeps fewer waves
+  int best_w = 4, best_nbc = 1;
+  double best_eff = -1.0;
+  // (at most six waves: with two halves of 16 KB in flight per wave, more
+  // outstanding reads per compute unit lower the stream rate -- measured
+  // 6.0 TB/s at 128 KB per compute unit, 5.4 at 256 KB)
+  for (int wpb : {4, 5, 6}) {
     // the INT4 walk holds both kinds of buffers: one wave per SIMD
     if (a.wq && wpb != 4) continue;
     const int resident = a.wq ? main_resident<true>(wpb) : main_resident<false>(wpb);
     const int nbc = std::max(1, std::min(resident / a.KS, ceil_div(units, wpb)));
     const int mx = ceil_div(units, nbc * wpb);
-    if (mx < best_max) {
-      best_max = mx;
+    const double eff = (double)units / ((double)nbc * wpb * mx);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
       best_w = wpb;
       best_nbc = nbc;
     }

@@ -23,8 +23,35 @@ constexpr int kMaxSmallRows = 512;
 constexpr int kStatusNotLoaded = 6;
 constexpr int kStatusIdRange = 7;
 
-inline int round_up(int x, int m) { return (x + m - 1) / m * m; }
-inline int ceil_div(int x, int m) { return (x + m - 1) / m; }
+inline __host__ __device__ int round_up(int x, int m) { return (x + m - 1) / m * m; }
+inline __host__ __device__ int ceil_div(int x, int m) { return (x + m - 1) / m; }
+
+// Fragment tiles (the "packed" layout) of a rows x cols bf16 matrix M: tiles
+// of 16 rows by 32 columns, 1 KB each.  Inside a tile the 16 bytes of lane
+// l = 16 j + r hold M[16 g + r][32 s + 8 j .. 32 s + 8 j + 7], exactly the
+// operand a lane supplies to one 16x16x32 bf16 MFMA step, so a wave loads a
+// tile with one contiguous 1-KB instruction.  Tiles are ordered by 1024-deep
+// column block, then row group, then step: a decode unit (16 rows of one
+// 1024-deep K chunk) is one contiguous 32 KB.  Measured on MI355X by pure
+// reads in the decode walk's order: the row-major layout (every 16-byte
+// operand load touching 16 rows) 4.6 TB/s, tiles ordered row group first
+// 4.7 TB/s (the waves of a chunk meet on a few memory channels), this order
+// 6.0-6.2 TB/s with 64-128 KB in flight per compute unit.  Rows and columns
+// are zero-padded to multiples of 16 and 32.
+constexpr int kFragChunk = 1024;  // columns of a tile block (the decode K chunk)
+inline __host__ __device__ size_t frag_elems(int rows, int cols) {
+  return (size_t)round_up(rows, 16) * round_up(cols, 32);
+}
+// 1-KB tile index of (row group g, step s) in a rows x cols matrix
+inline __host__ __device__ size_t frag_tile(int g, int s, int rows, int cols) {
+  const int k32 = (cols + 31) / 32, ng = (rows + 15) / 16;
+  const int c = s / (kFragChunk / 32), left = k32 - c * (kFragChunk / 32);
+  const int sc = left < kFragChunk / 32 ? left : kFragChunk / 32;  // steps of this column block
+  return (size_t)c * ng * (kFragChunk / 32) + (size_t)g * sc + (s - c * (kFragChunk / 32));
+}
+inline __host__ __device__ size_t frag_index(int r, int c, int rows, int cols) {
+  return (frag_tile(r >> 4, c >> 5, rows, cols) * 64 + 16 * ((c & 31) >> 3) + (r & 15)) * 8 + (c & 7);
+}
 
 // Device tables of one plan.  Sizes: T_cap = pool max_tokens.
 struct PlanTables {
@@ -150,6 +177,7 @@ struct DecodeArgs {
   int32_t NWc;            // waves per K chunk (set by launch_decode)
   int32_t lora;
   int32_t wq;             // INT4 base weights (Wq, Wsz) instead of W
+  int32_t wpacked;        // every W[i] is in fragment tiles (frag_elems(N, K) elements)
 };
 
 // INT4 base weight layout (group size kQ4Group along K; K % kQ4Group == 0).
@@ -164,15 +192,18 @@ hipError_t launch_q4_dequant(const uint32_t* Wq, const uint32_t* Wsz, int N, int
                              hipStream_t s);
 
 // Page layouts inside a slot (rows past the adapter's rank are zero):
-//   A page: A^T, rank-major [rmax][d_in]          (pack mode 0, src d_in x rank)
+//   A page: A^T (rpad x d_in) in fragment tiles, frag_elems(rpad, d_in)
+//           elements (pack mode 0, src d_in x rank)
 //   B page: B^T in 16-rank chunks [rpad/16][d_out][16], element (q, n) at
 //           (q / 16) * d_out * 16 + n * 16 + q % 16  (pack mode 1, src rank x d_out)
+// Pack mode 2 writes a caller's row-major base weight (src N x K, `rank` = N
+// rows) in fragment tiles for the decode kernels.
 struct PackArgs {
-  const uint16_t* src;    // staged A (d_in x rank) or B (rank x d_out), row-major
+  const uint16_t* src;    // staged A (d_in x rank), B (rank x d_out) or W (N x K), row-major
   uint16_t* dst;
-  int32_t rank, rows;     // true rank; page rows (rmax for A, rpad for B)
-  int32_t cols;           // d_in for A, d_out for B
-  int32_t mode;           // 0: A page, 1: B page
+  int32_t rank, rows;     // valid source rows (the true rank; N); page rows (rpad for A and B, N)
+  int32_t cols;           // d_in for A, d_out for B, K for W
+  int32_t mode;           // 0: A page, 1: B page, 2: W in fragment tiles
 };
 
 // Blocks of `fn` (block size `threads`, dynamic LDS `lds`) the current device

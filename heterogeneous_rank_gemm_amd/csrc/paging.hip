@@ -197,12 +197,12 @@ lora_status_t lora_host_register(lora_pool_t P, int32_t id, int32_t rank, float 
   for (int32_t m = 0; m < P->n_modules; ++m) {
     const int32_t din = P->d_in[m], dout = P->d_out[m];
     if (!A[m]) continue;  // not a target of this adapter: its pages stay zero
-    // A (d_in x rank) -> rank-major A^T page [max_rank][d_in]; A may be host or device memory
+    // A (d_in x rank) -> A^T page in fragment tiles; A may be host or device memory
     tmp.resize((size_t)din * rank);
     if (hipMemcpy(tmp.data(), A[m], tmp.size() * 2, hipMemcpyDefault) != hipSuccess) return hip_fail();
     uint16_t* pa = dst + P->a_off[m];
     for (int32_t k = 0; k < din; ++k)
-      for (int32_t q = 0; q < rank; ++q) pa[(size_t)q * din + k] = tmp[(size_t)k * rank + q];
+      for (int32_t q = 0; q < rank; ++q) pa[hrg::frag_index(q, k, P->rpad, din)] = tmp[(size_t)k * rank + q];
     // B (rank x d_out) -> B^T in 16-rank chunks [rpad/16][d_out][16]
     tmp.resize((size_t)rank * dout);
     if (hipMemcpy(tmp.data(), B[m], tmp.size() * 2, hipMemcpyDefault) != hipSuccess) return hip_fail();

@@ -309,26 +309,32 @@ int resident_blocks(const void* fn, int threads, size_t lds) {
 // rows x d_in); B arrives r x d_out and is stored as B^T in 16-rank chunks
 // (rows/16 x d_out x 16), so a 16-byte read gives 8 ranks of one column.
 __global__ void pack_kernel(PackArgs a) {
-  const size_t n = (size_t)a.rows * a.cols;
+  // every destination element once: (row, column) of the padded page, then
+  // its place in the layout (zeros past the source's rows and columns)
+  const int cp = a.mode == 1 ? a.cols : round_up(a.cols, 32);
+  const size_t n = a.mode == 1 ? (size_t)a.rows * a.cols : frag_elems(a.rows, a.cols);
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x) {
     int q, c;
-    if (a.mode == 0) {  // A^T [rows][cols]
-      q = (int)(i / a.cols);
-      c = (int)(i % a.cols);
+    size_t d;
+    if (a.mode != 1) {  // fragment tiles
+      q = (int)(i / cp);
+      c = (int)(i % cp);
+      d = frag_index(q, c, a.rows, a.cols);
     } else {  // B^T chunks [rows/16][cols][16]
       const size_t chunk = i / ((size_t)a.cols * 16), rem = i % ((size_t)a.cols * 16);
       c = (int)(rem / 16);
       q = (int)(chunk * 16 + rem % 16);
+      d = i;
     }
     uint16_t v = 0;
-    if (q < a.rank) v = a.mode == 0 ? a.src[(size_t)c * a.rank + q] : a.src[(size_t)q * a.cols + c];
-    a.dst[i] = v;
+    if (q < a.rank && c < a.cols) v = a.mode == 0 ? a.src[(size_t)c * a.rank + q] : a.src[(size_t)q * a.cols + c];
+    a.dst[d] = v;
   }
 }
 
 hipError_t launch_pack(const PackArgs& a, hipStream_t s) {
-  const size_t n = (size_t)a.rows * a.cols;
+  const size_t n = a.mode == 1 ? (size_t)a.rows * a.cols : frag_elems(a.rows, a.cols);
   const int grid = (int)std::min<size_t>((n + 255) / 256, 4096);
   hipLaunchKernelGGL(pack_kernel, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -4,8 +4,9 @@
 // multi-LoRA batch scheduling"), which keeps the extra work small.
 //
 // Work unit: (shrink tile, K-split).  A tile is up to 64 sorted rows of ONE
-// segment, so the adapter's A^T page (rank-major, r_max x d_in) is streamed
-// once per tile and K-split; the 16x16x32 bf16 MFMA does the contraction.
+// segment, so the adapter's A^T page (fragment tiles: one contiguous 1 KB
+// per 16 ranks x 32-deep MFMA step) is streamed once per tile and K-split;
+// the 16x16x32 bf16 MFMA does the contraction.
 // Each of the 4 waves covers an interleaved quarter of the K range; the four
 // partial results are summed in a fixed order through LDS (deterministic),
 // and each K-split writes its own fp32 partial plane of U.  The small-segment
@@ -56,15 +57,14 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
   const uint16_t* Ap = a.pages + (size_t)slot * a.slot_stride + a.a_off;
 
-  // the A rows follow from the tile entry alone
-  const uint16_t* arow[NQ];
+  // the A tiles follow from the tile entry alone: rank block nb's tile of
+  // step s is 1 KB at frag_tile(nb, s), this lane's 16 bytes at 16 l
+  const int k32 = (K + 31) / 32;
+  const int rp = a.u_ld;  // rows of the page in fragment tiles (the pool's rank rounded up to 16)
+  const uint16_t* Al = Ap + (size_t)l * 8;
   bool qv[NQ];
 #pragma unroll
-  for (int nb = 0; nb < NQ; ++nb) {
-    const int q = 16 * nb + (l & 15);
-    qv[nb] = q < rank;
-    arow[nb] = Ap + (size_t)(qv[nb] ? q : 0) * K;
-  }
+  for (int nb = 0; nb < NQ; ++nb) qv[nb] = 16 * nb + (l & 15) < rank;
   const int koff = 8 * (l >> 4);
   // 512-deep sub-chunks: wave w takes the 32-deep steps 32 w + 128 s of each;
   // all of a sub-chunk's loads go out first (addresses clamped in bounds,
@@ -74,9 +74,9 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
   auto load_a = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const int kc = min(kb + 128 * st + 32 * w + koff, K - 8);
+      const int step = min((kb + 128 * st + 32 * w) / 32, k32 - 1);
 #pragma unroll
-      for (int nb = 0; nb < NQ; ++nb) av[st][nb] = ld16(arow[nb] + kc);
+      for (int nb = 0; nb < NQ; ++nb) av[st][nb] = ld16(Al + frag_tile(nb, step, rp, K) * 512);
     }
   };
   load_a(k0);

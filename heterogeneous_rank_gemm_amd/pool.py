@@ -129,6 +129,38 @@ class LoraPool:
             self._check_linear("lora_base_apply_group", m, X, None, w, o, T)
         _lora.lora_base_apply_group(self.handle, modules, X, T, W, out, stream)
 
+    def pack_weight(self, W, stream=None):
+        """A new device tensor holding row-major W (d_out x d_in bf16) in the
+        decode kernels' fragment-tile layout (lora_pack_weight)."""
+        import torch
+        check_tensor(W, "W", _bf16(), W.shape[1] if W.dim() == 2 else -1, 1, "lora_pack_weight")
+        N, K = W.shape
+        Wp = torch.empty(_lora.lora_packed_weight_elems(N, K), dtype=torch.bfloat16, device=W.device)
+        _lora.lora_pack_weight(W, N, K, Wp, stream)
+        return Wp
+
+    def _check_packed(self, where: str, modules, X, ids, Wp, out, T: int) -> None:
+        import torch
+        for m, w, o in zip(modules, Wp, out):
+            self._check_linear(where, m, X, ids, None, o, T)
+            n = _lora.lora_packed_weight_elems(self.d_out[m], self.d_in[m])
+            if not isinstance(w, torch.Tensor) or w.dtype != torch.bfloat16 or not w.is_contiguous() \
+                    or w.numel() < n or not w.is_cuda:
+                raise LoraError(1, f"{where}: a packed weight of module {m} holds {n} bf16 on a GPU")
+
+    def apply_group_packed(self, modules: Sequence[int], X, ids, Wp: Sequence, out: Sequence, stream=None,
+                           T: Optional[int] = None):
+        """lora_apply_group_packed: decode batches (T <= 64), weights from pack_weight."""
+        T = X.shape[0] if T is None else T
+        self._check_packed("lora_apply_group_packed", modules, X, ids, Wp, out, T)
+        _lora.lora_apply_group_packed(self.handle, modules, X, ids, T, Wp, out, stream)
+
+    def base_apply_group_packed(self, modules: Sequence[int], X, Wp: Sequence, out: Sequence, stream=None,
+                                T: Optional[int] = None):
+        T = X.shape[0] if T is None else T
+        self._check_packed("lora_base_apply_group_packed", modules, X, None, Wp, out, T)
+        _lora.lora_base_apply_group_packed(self.handle, modules, X, T, Wp, out, stream)
+
     def status(self, stream=None) -> str:
         return _lora.lora_status(self.handle, stream)
 

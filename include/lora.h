@@ -250,6 +250,41 @@ lora_status_t lora_base_apply_group(lora_pool_t pool, int32_t n, const int32_t* 
                                     hipStream_t stream);
 
 /*
+ * Decode-layout base weights.  The decode kernels (T <= 64) stream the base
+ * weight once per call and are bound by its bytes; with the row-major layout
+ * every 16-byte MFMA operand load of a wave touches 16 rows, which the memory
+ * path serves at about three quarters of the rate of contiguous reads.  A
+ * weight packed once into fragment tiles (16 rows x 32 columns, 1 KB each,
+ * row-group-major; inside a tile lane l = 16 j + r holds row 16 g + r,
+ * columns 32 s + 8 j .. + 7; rows and columns zero-padded to multiples of 16
+ * and 32) is read as contiguous 1-KB pieces.  The adapters' A pages in the
+ * pool already use this layout.
+ *
+ * lora_packed_weight_elems -- elements (bf16) of the packed form of an N x K
+ *   weight: round_up(N, 16) * round_up(K, 32).  INVALID_ARG on N or K < 1 or
+ *   a NULL elems.
+ * lora_pack_weight -- writes the packed form of the row-major device weight
+ *   W (N x K, bf16) into the device buffer Wp (lora_packed_weight_elems
+ *   elements, caller-owned), on `stream`.  N and K multiples of 8 in
+ *   8..65536 with a packed size under 2 GiB, else INVALID_ARG.  W and Wp must
+ *   not overlap.
+ * lora_apply_group_packed / lora_base_apply_group_packed -- lora_apply_group
+ *   / lora_base_apply_group with every Wp[i] packed from the linear's
+ *   row-major weight; outputs bit-identical to the row-major calls (the same
+ *   products in the same order).  Decode batches only: T <= 64, else
+ *   INVALID_ARG (the batched path takes the row-major weight).  The grouping
+ *   is built in the launch, so there is no plan argument.
+ */
+lora_status_t lora_packed_weight_elems(int32_t N, int32_t K, int64_t* elems);
+lora_status_t lora_pack_weight(const lora_bf16_t* W, int32_t N, int32_t K, lora_bf16_t* Wp, hipStream_t stream);
+lora_status_t lora_apply_group_packed(lora_pool_t pool, int32_t n, const int32_t* modules, const lora_bf16_t* X,
+                                      const int32_t* ids, int32_t T, const lora_bf16_t* const* Wp,
+                                      lora_bf16_t* const* out, hipStream_t stream);
+lora_status_t lora_base_apply_group_packed(lora_pool_t pool, int32_t n, const int32_t* modules,
+                                           const lora_bf16_t* X, int32_t T, const lora_bf16_t* const* Wp,
+                                           lora_bf16_t* const* out, hipStream_t stream);
+
+/*
  * INT4 base weight ([vLLM-ch7] performance notes: an AWQ-INT4 base with bf16
  * adapters).  The frozen base weight is stored group-wise in 4 bits along
  * d_in: groups of 128, q and the zero point z in 0..15, a bf16 scale s per

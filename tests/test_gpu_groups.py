@@ -207,3 +207,75 @@ def test_graph_captured_with_few_adapters_replays_after_more_load(max_ids):
         mx, rl1, _ = oracle.parity_metrics(outs[k].cpu(), oracle.lora_linear(reg, k, X, ids_np, W[k]))
         assert mx <= oracle.MAX_REL_TOL and rl1 <= oracle.RELL1_TOL, (k, mx, rl1)
     pool.close()
+
+
+def _frag_layout_reference(W):
+    """The fragment-tile layout written out with numpy reshapes (not the
+    library's index formula): pad to 16 x 32 multiples; for each block of
+    1024 columns, cut into 16-row x 32-column tiles ordered by row group,
+    then step, and inside a tile order the 8-element pieces by (column
+    octet, row)."""
+    N, K = W.shape
+    Np, Kp = -(-N // 16) * 16, -(-K // 32) * 32
+    P = np.zeros((Np, Kp), dtype=W.dtype)
+    P[:N, :K] = W
+    out = []
+    for c0 in range(0, Kp, 1024):
+        blk = P[:, c0:min(c0 + 1024, Kp)]
+        t = blk.reshape(Np // 16, 16, blk.shape[1] // 32, 4, 8)   # (group, row, step, octet, element)
+        out.append(t.transpose(0, 2, 3, 1, 4).reshape(-1))        # (group, step, octet, row, element)
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("N,K", [(264, 520), (8, 40), (1032, 4096), (64, 32), (40, 2600)])
+def test_pack_weight_layout(N, K):
+    import heterogeneous_rank_gemm_amd as hrg
+    W = (torch.arange(N * K, dtype=torch.int64) % 30011).to(torch.int16).view(N, K)
+    Wd = W.view(torch.bfloat16).cuda()
+    Wp = torch.full((hrg.lora_packed_weight_elems(N, K),), -1, dtype=torch.int16, device="cuda")
+    hrg.lora_pack_weight(Wd, N, K, Wp.view(torch.bfloat16), None)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(Wp.cpu().numpy(), _frag_layout_reference(W.numpy()))
+
+
+@pytest.mark.parametrize("T,max_ids", [(64, 12), (17, 30), (1, 12)])
+def test_packed_group_equals_row_major(T, max_ids):
+    """Fragment-tiled weights give the row-major call's bits (the same
+    products in the same order), LoRA and base-only."""
+    max_adapters, max_rank = 12, 32
+    ranks = [8, 16, 5, 32, 1, 13, 16, 9, 4, 12, 3, 16]
+    pool, reg, X, W = _setup(max_adapters, max_ids, max_rank, ranks, T, 31 + T,
+                             untarget=((2, 1), (4, 6)))
+    ids_np = np.random.default_rng(T).integers(-1, max_adapters, size=T).astype(np.int32)
+    ids = torch.as_tensor(ids_np, device="cuda")
+    Xd = X.cuda()
+    group = [0, 1, 2, 3, 4, 5, 6, 7]
+    Wd = [W[m].cuda() for m in group]
+    Wp = [pool.pack_weight(w) for w in Wd]
+    d_outs = [D_OUTS[m] for m in group]
+    ref, got, refb, gotb = _outs(T, d_outs), _outs(T, d_outs), _outs(T, d_outs), _outs(T, d_outs)
+    pool.apply_group(group, Xd, ids, Wd, ref)
+    pool.apply_group_packed(group, Xd, ids, Wp, got)
+    pool.base_apply_group(group, Xd, Wd, refb)
+    pool.base_apply_group_packed(group, Xd, Wp, gotb)
+    torch.cuda.synchronize()
+    assert pool.status() == "OK"
+    for k, m in enumerate(group):
+        assert torch.equal(got[k], ref[k]), f"linear {m}"
+        assert torch.equal(gotb[k], refb[k]), f"base linear {m}"
+        mx, rl1, _ = oracle.parity_metrics(got[k].cpu(), oracle.lora_linear(reg, m, X, ids_np, W[m]))
+        assert mx <= oracle.MAX_REL_TOL and rl1 <= oracle.RELL1_TOL, (m, mx, rl1)
+    pool.close()
+
+
+def test_packed_rejects_batched_sizes():
+    from heterogeneous_rank_gemm_amd import LoraError, LoraPool
+    pool = LoraPool(2, 2, 8, [64], [64], 128)
+    X = torch.zeros((100, 64), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((64, 64), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((100, 64), dtype=torch.bfloat16, device="cuda")
+    Wp = pool.pack_weight(W)
+    with pytest.raises(LoraError) as e:
+        pool.base_apply_group_packed([0], X, [Wp], [out])
+    assert e.value.status == "INVALID_ARG"
+    pool.close()
