@@ -32,7 +32,7 @@ EXPORTED = (
     "lora_pin_adapter", "lora_paging_query", "lora_paging_stats", "lora_q4_pack", "lora_apply_q4",
     "lora_base_apply_q4", "lora_load_chain", "lora_apply_group", "lora_base_apply_group",
     "lora_packed_weight_elems", "lora_pack_weight", "lora_apply_group_packed",
-    "lora_base_apply_group_packed",
+    "lora_base_apply_group_packed", "lora_apply_noalloc",
 )
 
 _vp = C.c_void_p
@@ -71,6 +71,7 @@ _sigs = {
     "lora_pack_weight": [_vp, _i32, _i32, _vp, _vp],
     "lora_apply_group_packed": [_vp, _i32, _P_i32, _vp, _vp, _i32, C.POINTER(_vp), C.POINTER(_vp), _vp],
     "lora_base_apply_group_packed": [_vp, _i32, _P_i32, _vp, _i32, C.POINTER(_vp), C.POINTER(_vp), _vp],
+    "lora_apply_noalloc": [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp],
 }
 for _name, _args in _sigs.items():
     _f = getattr(_lib, _name)
@@ -217,6 +218,11 @@ def lora_base_apply_group_packed(pool: int, modules: Sequence[int], X, T: int, W
     n, mods, pw, po = _group_arrays(modules, Wp, out)
     _check(_lib.lora_base_apply_group_packed(pool, n, mods, _ptr(X), T, pw, po, _stream(stream)),
            "lora_base_apply_group_packed")
+
+
+def lora_apply_noalloc(pool: int, module: int, X, ids, T: int, W, out, stream=None) -> None:
+    _check(_lib.lora_apply_noalloc(pool, module, _ptr(X), _ptr(ids), T, _ptr(W), _ptr(out), _stream(stream)),
+           "lora_apply_noalloc")
 
 
 def lora_base_apply(pool: int, module: int, X, T: int, W, out, stream=None) -> None:

@@ -654,6 +654,26 @@ lora_status_t lora_base_apply(lora_pool_t P, int32_t module, const lora_bf16_t* 
   return apply_impl(P, 1, &module, X, nullptr, T, &W, nullptr, nullptr, nullptr, &out, nullptr, false, stream);
 }
 
+lora_status_t lora_apply_noalloc(lora_pool_t P, int32_t module, const lora_bf16_t* X, const int32_t* ids,
+                                 int32_t T, const lora_bf16_t* W, lora_bf16_t* out, hipStream_t stream) {
+  const lora_status_t st = check_apply(P, 1, &module, X, ids, T, &W, nullptr, nullptr, nullptr, &out, nullptr, true);
+  if (st != LORA_OK || T == 0) return st;
+  if (T > hrg::kDecodeMaxT) return LORA_ERR_INVALID_ARG;
+  // the partial planes: KS chunks x 64 tokens x the columns (rounded up to
+  // 16), then KS x 64 x the padded rank for the shrink
+  const int K = P->d_in[module], N = P->d_out[module];
+  const size_t ks = (size_t)ceil_div(K, hrg::kDecodeChunk);
+  const size_t part = ks * hrg::kDecodeMaxT * round_up(N, 16);
+  const size_t part_pad = (part + 63) / 64 * 64;  // the shrink planes start 256-byte aligned
+  const size_t upart = ks * hrg::kDecodeMaxT * P->rpad;
+  if (part_pad + upart > hrg::kScratchFloats) return LORA_ERR_INVALID_ARG;
+  DeviceGuard g(P->device);
+  float* scr = nullptr;
+  if (hrg::decode_scratch(&scr) != hipSuccess) return (void)hipGetLastError(), LORA_ERR_HIP;
+  return decode_group(P, 1, &module, X, ids, T, &W, nullptr, nullptr, &out, true, false, scr, scr + part_pad,
+                      stream);
+}
+
 lora_status_t lora_apply_group(lora_pool_t P, int32_t n, const int32_t* modules, const lora_bf16_t* X,
                                const int32_t* ids, int32_t T, const lora_bf16_t* const* W,
                                lora_bf16_t* const* out, lora_plan_t plan, hipStream_t stream) {

@@ -38,6 +38,8 @@
 // expand, so id -1 rows match it bit for bit.  Every combine block validates
 // all the ids the same way (strict mode, icman report section 4.1): on an
 // invalid batch nothing is written to `out`.
+#include <mutex>
+
 #include "common.h"
 #include "internal.h"
 
@@ -818,6 +820,35 @@ hipError_t launch_decode(const DecodeArgs& args, int items_cap, hipStream_t s) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine, dim3(a.ct0[kMaxGroup], (a.T + 15) / 16), dim3(kCombThreads), 0, s, a);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Fixed scratch of the allocation-free decode entry point: the K-chunk
+// partial planes live here instead of in the pool's workspace.  Every GPU the
+// library runs on holds its own copy until the process ends; host code
+// reaches a device's copy only through the address hipGetSymbolAddress
+// returns for it (the array's name is a host-side stand-in).
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(float** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = static_cast<float*>(g_scratch_ptr[dev]);
+  return hipSuccess;
 }
 
 // ---------------------------------------------------------------------------

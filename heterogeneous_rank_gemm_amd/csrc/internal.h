@@ -223,6 +223,12 @@ hipError_t launch_prefill(const GemmArgs& a, bool lora, int shape, hipStream_t s
 // The E rows of the small segments (one launch, before the GEMM).
 hipError_t launch_expand_small(const GemmArgs& a, hipStream_t s);
 int prefill_choose(int T, int N);
+// The allocation-free decode entry point keeps its partial planes in a fixed
+// device array of kScratchFloats floats (16 MiB per GPU).  decode_scratch
+// returns the current device's copy (looked up once per device).
+constexpr size_t kScratchFloats = (size_t)4 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t decode_scratch(float** ptr);
 // Picks the waves per block and the blocks per K chunk for the group's W
 // units plus `items_cap` A items per linear (the most a batch can hold), then
 // launches both kernels.

@@ -285,6 +285,26 @@ lora_status_t lora_base_apply_group_packed(lora_pool_t pool, int32_t n, const in
                                            lora_bf16_t* const* out, hipStream_t stream);
 
 /*
+ * lora_apply_noalloc -- lora_apply for callers that cannot allocate device
+ * memory during the call: code under hipGraph capture that must not meet an
+ * allocation, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results (bit for bit) and errors as lora_apply on a decode batch
+ * (no plan argument: the launch groups the batch itself), but the kernels'
+ * scratch (the K-chunk partial planes) is a fixed array of 16 MiB per GPU
+ * inside the library instead of the pool's workspace, and the call makes no
+ * allocation of any kind.
+ *   limits  T <= 64, and ceil(d_in / 1024) * 64 * (round_up(d_out, 16) +
+ *           rank rounded up to 16) floats <= 4 Mi (e.g. d_in 4096 with d_out
+ *           up to 16320, d_in 11008 with d_out up to 5888); else INVALID_ARG
+ *           with no work enqueued.
+ * The array is shared by every call on a GPU and keeps the last call's
+ * contents (nothing in it needs to start at zero): calls that overlap on one
+ * GPU, from any pool or stream, race.  Serialise them (one stream, or events).
+ */
+lora_status_t lora_apply_noalloc(lora_pool_t pool, int32_t module, const lora_bf16_t* X, const int32_t* ids,
+                                 int32_t T, const lora_bf16_t* W, lora_bf16_t* out, hipStream_t stream);
+
+/*
  * INT4 base weight ([vLLM-ch7] performance notes: an AWQ-INT4 base with bf16
  * adapters).  The frozen base weight is stored group-wise in 4 bits along
  * d_in: groups of 128, q and the zero point z in 0..15, a bf16 scale s per
