@@ -24,13 +24,20 @@
 // The W units come first and the A units last; wave i of a chunk takes units
 // i, i + NWc, i + 2 NWc, ... (NWc waves per chunk), so every wave streams
 // about the same number of bytes and no adapter work is left to a second
-// round of blocks.  A unit is two 512-deep halves through two register
-// buffers: the next half's loads are in flight while the current half's MFMAs
-// run.
+// round of blocks.  A bf16 unit streams through a ring of four 256-deep
+// quarters (three in flight while one is multiplied); an INT4 unit through
+// two 512-deep halves.
+// Where the grid still fills the chip, a block takes two consecutive chunks:
+// it walks its units over the first, restages X, walks them again over the
+// second and adds each unit's two sums in registers, so one fp32 plane is
+// written per chunk pair instead of per chunk.  The sums are added in one
+// order either way: each chunk from zero in K order, the chunks of a pair,
+// then the pairs in order; the combine launch adds pairs of single-chunk
+// planes itself.  So the choice never changes a bit of the output.
 // Launch 2 (decode_combine), one thread per (token, 4 columns):
-//     V[t, q]   = (alpha/r) * sum_chunks upart[c][linear][t][q]
-//     out[t, n] = bf16( sum_chunks part[c][t][n]  +  sum_q V[t, q] B_i[q, n] )
-//   chunks added in order, the expand in fp32, a single rounding (icman
+//     V[t, q]   = (alpha/r) * sum_planes upart[c][linear][t][q]
+//     out[t, n] = bf16( sum_planes part[c][t][n]  +  sum_q V[t, q] B_i[q, n] )
+//   planes added in the order above, the expand in fp32, a single rounding (icman
 //   report, section 2.1: the low-rank branch is added back to the main path).
 //   Rows with id -1 get no LoRA term at all.
 //
@@ -39,6 +46,7 @@
 // all the ids the same way (strict mode, icman report section 4.1): on an
 // invalid batch nothing is written to `out`.
 #include <mutex>
+#include <utility>
 
 #include "common.h"
 #include "internal.h"
@@ -118,6 +126,23 @@ struct UnitDst {
   uint64_t members;           // A: the adapter's tokens
 };
 
+// f(0), f(1), ..., f(n - 1) with compile-time indices, inlined: a loop body
+// too large for the unroller's limit still indexes register arrays only with
+// constants (a variable index would move them to scratch memory).
+template <typename F, int... J>
+__device__ __forceinline__ void static_for(F&& f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>{}), ...);
+}
+
+// a for pass 0, b for pass 1 (chosen at compile time)
+template <int P>
+__device__ __forceinline__ f32x4 (&pick(f32x4 (&a)[4], f32x4 (&b)[4]))[4] {
+  if constexpr (P == 0)
+    return a;
+  else
+    return b;
+}
+
 // Waits until at most N of this wave's vector-memory operations are
 // outstanding and every LDS access has completed, then joins the workgroup
 // barrier (__syncthreads() would wait for all of them).  Exact only where
@@ -134,15 +159,33 @@ __device__ __forceinline__ void barrier_after(void) {
 // The walk: WPB waves per block, all alike.
 // WQ: the base weights are INT4 (a.Wq, a.Wsz); a W unit loads a quarter of
 // the bytes and dequantizes its fragments in registers before the MFMAs.
-template <int WPB, bool WQ>
+// CPB: K chunks per block.  With two, a block keeps X of one chunk at a time
+// in LDS, walks its units over the first chunk, restages X and walks them
+// over the second, its waves holding every unit's sums in registers (at most
+// kMaxUnits per wave; the host sizes the grid for that): one partial plane
+// per pair of chunks, half the fp32 partials written and read back (they are
+// a fifth of the step's traffic otherwise).
+//
+// Either way the sums are added in one order: each chunk's products from
+// zero in K order (an MFMA chain), the two chunks of a pair added, then the
+// pairs in order.  With one chunk per block the combine launch adds the
+// pairs' planes; with two the block does, so both give the same bits and
+// the host may pick either per launch.
+constexpr int kMaxUnits = 8;
+
+template <int WPB, bool WQ, int CPB>
 __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
+  static_assert(CPB == 1 || (CPB == 2 && WPB == 4 && !WQ), "two chunks per block: bf16, one wave per SIMD");
   __shared__ __attribute__((aligned(16))) uint16_t xs[64 * kXs];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g4 = lane >> 4, r16 = lane & 15;
   const int T = a.T, K = a.K, KS = a.KS, n_mod = a.n_mod;
-  const int c = (int)blockIdx.x % KS, bi = (int)blockIdx.x / KS;
-  const int k0 = c * kDecodeChunk, klen = min(K, k0 + kDecodeChunk) - k0;
+  const int KP = a.KP;  // partial planes: the chunk groups (KS / CPB rounded up)
+  const int plane = (int)blockIdx.x % KP, bi = (int)blockIdx.x / KP;
+  const int npass = min(CPB, KS - plane * CPB);  // chunks of this block
+  int c = plane * CPB;  // the chunk in LDS
+  int k0 = c * kDecodeChunk, klen = min(K, k0 + kDecodeChunk) - k0;
   const int wi = bi * WPB + w;  // this wave among the chunk's NWc waves
   const int NWc = a.NWc;
   const int NUW = a.u0[kMaxGroup];  // W units of the group (16 rows each)
@@ -156,19 +199,24 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
 
   // ---- X chunk -> LDS by DMA: the block's waves share the 128 pieces (two
   // 1-KB pieces per token row).  Rows >= T and columns >= K read zeros. ----
-  {
+  auto stage_x = [&]() __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t rx = uniform_rsrc(a.X, T * K * 2);
-    for (int i = w; i < kXPieces; i += WPB) {
+    // (the first piece opaque when the copy runs twice: its addresses are
+    // formed in the loop, not kept from the first copy to the second)
+    int i0 = w;
+    if constexpr (CPB == 2) asm volatile("" : "+s"(i0));
+    for (int i = i0; i < kXPieces; i += WPB) {
       const int r = i >> 1, h = i & 1;
       const int k = k0 + 512 * h + 8 * lane;
       // rows >= T lie past the buffer's range (zeros); columns >= K are sent past it
       const uint32_t off = k < K ? (uint32_t)(r * K + k) * 2u : kOobOff;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(xs + r * kXs + 512 * h), 16, off, 0, 0, 0);
     }
-  }
+  };
+  stage_x();
 
-  // a W unit's rows: row r16 of the 16, at the chunk start
-  auto w_unit = [&](int u, UnitSrc& sr, UnitDst& ds) __attribute__((always_inline)) {
+  // a W unit's rows: row r16 of the 16, at chunk start kk
+  auto w_unit = [&](int u, int kk, UnitSrc& sr, UnitDst& ds) __attribute__((always_inline)) {
     const int m = group_of(a.u0, u);
     const int N = ka->N[m];
     const int row0 = (u - ka->u0[m]) * 16;
@@ -181,8 +229,8 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
       const int KW = K / 8, KG = K / kQ4Group;
       sr.rs = uniform_rsrc(ka->Wq[m], N * KW * 4);
       sr.rz = uniform_rsrc(ka->Wsz[m], N * KG * 4);
-      sr.off = row < N ? (uint32_t)(row * KW + 16 * (k0 / kQ4Group) + 4 * g4) * 4u : kOobOff;
-      sr.offz = row < N ? (uint32_t)(row * KG + k0 / kQ4Group) * 4u : kOobOff;
+      sr.off = row < N ? (uint32_t)(row * KW + 16 * (kk / kQ4Group) + 4 * g4) * 4u : kOobOff;
+      sr.offz = row < N ? (uint32_t)(row * KG + kk / kQ4Group) * 4u : kOobOff;
       sr.istep = 0;
     } else if (a.wpacked) {
       // fragment tiles: the unit's 16 rows are row group u - u0[m]; its
@@ -190,13 +238,13 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
       // step, this lane's 16 bytes at 16 lane)
       sr.rs = uniform_rsrc(ka->W[m], (int)frag_elems(N, K) * 2);
       sr.rz = sr.rs;
-      sr.off = (uint32_t)((frag_tile(u - ka->u0[m], k0 / 32, N, K) * 64 + lane) * 16);
+      sr.off = (uint32_t)((frag_tile(u - ka->u0[m], kk / 32, N, K) * 64 + lane) * 16);
       sr.offz = 0;
       sr.istep = 1024;
     } else {
       sr.rs = uniform_rsrc(ka->W[m], N * K * 2);
       sr.rz = sr.rs;
-      sr.off = row < N ? (uint32_t)(row * K + k0 + 8 * g4) * 2u : kOobOff;
+      sr.off = row < N ? (uint32_t)(row * K + kk + 8 * g4) * 2u : kOobOff;
       sr.offz = 0;
       sr.istep = 64;
     }
@@ -247,7 +295,7 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
   const auto Q2 = std::integral_constant<int, 2>{};
   const auto Q3 = std::integral_constant<int, 3>{};
   if (nw > 0) {
-    w_unit(wi, csrc, cdst);
+    w_unit(wi, k0, csrc, cdst);
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (WQ) {
       load_q(qbuf[0], csrc, H0);
@@ -315,8 +363,9 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
     const int NU = NUW + n_mod * n_items;
     nu = wi < NU ? (NU - wi + NWc - 1) / NWc : 0;
   };
-  // an A unit's rows: rank block qb of the item's adapter on linear m
-  auto a_unit = [&](int v, UnitSrc& sr, UnitDst& ds) __attribute__((always_inline)) {
+  // an A unit's rows: rank block qb of the item's adapter on linear m, at
+  // chunk start kk
+  auto a_unit = [&](int v, int kk, UnitSrc& sr, UnitDst& ds) __attribute__((always_inline)) {
     const int m = v % n_mod, item = v / n_mod;
     const uint64_t hit = __ballot(first && item >= incl - nq && item < incl);
     const int leader = (int)__builtin_ctzll(hit);  // wave-uniform: readlane, not an LDS shuffle
@@ -336,7 +385,7 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
     const uint16_t* page = a.pages + (size_t)sl * a.slot_stride + ka->a_off[m];
     sr.rs = uniform_rsrc(page, (int)frag_elems(a.u_ld, K) * 2);
     sr.rz = sr.rs;
-    sr.off = ok ? (uint32_t)((frag_tile(qb, k0 / 32, a.u_ld, K) * 64 + lane) * 16) : kOobOff;
+    sr.off = ok ? (uint32_t)((frag_tile(qb, kk / 32, a.u_ld, K) * 64 + lane) * 16) : kOobOff;
     sr.offz = 0;
     sr.istep = 1024;
   };
@@ -357,7 +406,7 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
   auto after_w = [&](int j, UnitSrc& sr, UnitDst& ds) __attribute__((always_inline)) {
     group();
     if (j < nu)
-      a_unit(wi + j * NWc - NUW, sr, ds);
+      a_unit(wi + j * NWc - NUW, k0, sr, ds);
     else
       none(sr, ds);
   };
@@ -369,7 +418,7 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
   // half's 16 steps; the unit's rows are the MFMA's A operand, so a lane ends
   // with 4 consecutive rows (columns of the output, or ranks) of one token.
   // The X fragments of step i + 1 are read from LDS while step i's MFMAs run.
-  auto compute_b = [&](const uint4 (&b)[kHS], auto hc) __attribute__((always_inline)) {
+  auto compute_b = [&](const uint4 (&b)[kHS], auto hc, f32x4 (&acc)[4]) __attribute__((always_inline)) {
     constexpr int H = decltype(hc)::value;
     __builtin_amdgcn_sched_barrier(0);
     // the chunk's depth, opaque here: the 16 lane masks of the K tail are
@@ -377,17 +426,21 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
     // (32 live 64-bit masks would spill the scalar registers)
     int kl = klen;
     asm volatile("" : "+s"(kl));
+    // the lane's X offset, opaque too: the fragments are read again for
+    // every unit, never kept across units in registers
+    int xo = r16 * kXs + 8 * g4;
+    asm volatile("" : "+v"(xo));
     bf16x8 xf[2][4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) xf[0][tb] = lds_bf16x8(xs + (16 * tb + r16) * kXs + kHalf * H + 8 * g4);
+    for (int tb = 0; tb < 4; ++tb) xf[0][tb] = lds_bf16x8(xs + xo + 16 * tb * kXs + kHalf * H);
 #pragma unroll
     for (int i = 0; i < kHS; ++i) {
-      const int k = kHalf * H + 32 * i + 8 * g4;
       if (i + 1 < kHS) {
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) xf[(i + 1) & 1][tb] = lds_bf16x8(xs + (16 * tb + r16) * kXs + k + 32);
+        for (int tb = 0; tb < 4; ++tb)
+          xf[(i + 1) & 1][tb] = lds_bf16x8(xs + xo + 16 * tb * kXs + kHalf * H + 32 * i + 32);
       }
-      const bf16x8 wb = __builtin_bit_cast(bf16x8, keep_if(k < kl, b[i]));
+      const bf16x8 wb = __builtin_bit_cast(bf16x8, keep_if(kHalf * H + 32 * i + 8 * g4 < kl, b[i]));
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) acc[tb] = mfma16(wb, xf[i & 1][tb], acc[tb]);
     }
@@ -404,22 +457,24 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto compute_r = [&](const uint4 (&b)[kQS], auto qc) __attribute__((always_inline)) {
+  auto compute_r = [&](const uint4 (&b)[kQS], auto qc, f32x4 (&acc)[4]) __attribute__((always_inline)) {
     constexpr int Q = decltype(qc)::value;
     __builtin_amdgcn_sched_barrier(0);
     int kl = klen;  // opaque: the tail masks are formed where used (see compute_b)
     asm volatile("" : "+s"(kl));
+    int xo = r16 * kXs + 8 * g4;  // opaque likewise (see compute_b)
+    asm volatile("" : "+v"(xo));
     bf16x8 xf[2][4];
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) xf[0][tb] = lds_bf16x8(xs + (16 * tb + r16) * kXs + 32 * kQS * Q + 8 * g4);
+    for (int tb = 0; tb < 4; ++tb) xf[0][tb] = lds_bf16x8(xs + xo + 16 * tb * kXs + 32 * kQS * Q);
 #pragma unroll
     for (int i = 0; i < kQS; ++i) {
-      const int k = 32 * kQS * Q + 32 * i + 8 * g4;
       if (i + 1 < kQS) {
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) xf[(i + 1) & 1][tb] = lds_bf16x8(xs + (16 * tb + r16) * kXs + k + 32);
+        for (int tb = 0; tb < 4; ++tb)
+          xf[(i + 1) & 1][tb] = lds_bf16x8(xs + xo + 16 * tb * kXs + 32 * kQS * Q + 32 * i + 32);
       }
-      const bf16x8 wb = __builtin_bit_cast(bf16x8, keep_if(k < kl, b[i]));
+      const bf16x8 wb = __builtin_bit_cast(bf16x8, keep_if(32 * kQS * Q + 32 * i + 8 * g4 < kl, b[i]));
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) acc[tb] = mfma16(wb, xf[i & 1][tb], acc[tb]);
     }
@@ -435,11 +490,13 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     __builtin_amdgcn_sched_barrier(0);
   };
-  auto compute_q = [&](const uint4 (&b)[WQ ? kQL : 1], auto hc) __attribute__((always_inline)) {
+  auto compute_q = [&](const uint4 (&b)[WQ ? kQL : 1], auto hc, f32x4 (&acc)[4]) __attribute__((always_inline)) {
     if constexpr (WQ) {
       constexpr int H = decltype(hc)::value;
       const uint4 zz = b[4];
       const uint32_t gw[4] = {zz.x, zz.y, zz.z, zz.w};
+      int xo = r16 * kXs + 8 * g4;  // opaque (see compute_b)
+      asm volatile("" : "+v"(xo));
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
         // a group past the chunk (klen is a multiple of the group) gets
@@ -455,23 +512,23 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
           const bf16x8 wb = dequant_q4x8(words[st], g.x, g.y);
 #pragma unroll
           for (int tb = 0; tb < 4; ++tb)
-            acc[tb] = mfma16(wb, lds_bf16x8(xs + (16 * tb + r16) * kXs + k), acc[tb]);
+            acc[tb] = mfma16(wb, lds_bf16x8(xs + xo + 16 * tb * kXs + k - 8 * g4), acc[tb]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
   // acc[tb][e]: token 16 tb + r16, row 4 g4 + e of the unit
-  auto store = [&](const UnitDst& d) __attribute__((always_inline)) {
+  auto store_to = [&](const UnitDst& d, f32x4 (&acc)[4]) __attribute__((always_inline)) {
     if (d.kind == 0) {
       // rows past the linear's N land in its padding columns of `part`
-      float* pp = a.part + (size_t)c * 64 * a.npad + (size_t)r16 * a.npad + d.col + 4 * g4;
+      float* pp = a.part + (size_t)plane * 64 * a.npad + (size_t)r16 * a.npad + d.col + 4 * g4;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
         *reinterpret_cast<float4*>(pp + (size_t)(16 * tb) * a.npad) =
             make_float4(acc[tb][0], acc[tb][1], acc[tb][2], acc[tb][3]);
     } else if (d.kind == 1) {
-      float* up = a.upart + ((size_t)(c * n_mod + d.m) * 64 + r16) * a.u_ld + d.col + 4 * g4;
+      float* up = a.upart + ((size_t)(plane * n_mod + d.m) * 64 + r16) * a.u_ld + d.col + 4 * g4;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb)
         if ((d.members >> (16 * tb + r16)) & 1ull)
@@ -481,26 +538,141 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) acc[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
   };
+  auto store = [&](const UnitDst& d) __attribute__((always_inline)) { store_to(d, acc); };
 
   // Unit j's first half is in flight when its step starts; its second half
   // is requested before its first half's MFMAs, the next unit's first half
   // before its second half's.  Every load is issued unconditionally (past the
   // wave's last unit, rows of no bytes), so the compiler counts each wait
   // exactly.  W units first (INT4 or bf16), then the A units (bf16 pages).
-  if constexpr (WQ) {
+  if constexpr (CPB == 2) {
+    // Two chunks.  The wave's units are the same in both passes (the batch
+    // is grouped once); unit j's first-chunk sums stay in accs[j] until its
+    // second-chunk sums are added to them.  The passes are two copies of
+    // straight code (no loop for the sums to flow around).
+    f32x4 accs[kMaxUnits][4];
+#pragma unroll
+    for (int j = 0; j < kMaxUnits; ++j)
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) accs[j][tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // the second chunk's products of a unit, from zero; then added to the
+    // first chunk's
+    f32x4 acc2[4];
+    auto fresh = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) acc2[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    auto add_pair = [&](f32x4 (&sum)[4]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum[tb][e] += acc2[tb][e];
+    };
+    auto pass = [&](auto pc, bool more) __attribute__((always_inline)) {
+      constexpr int P = decltype(pc)::value;
+      // the wave's first unit, stride and counts, opaque here: the units'
+      // descriptors are formed where they are used, not kept from one pass
+      // to the next
+      int wj = wi, nwc = NWc, nwp = nw, nup = nu;
+      asm volatile("" : "+s"(wj), "+s"(nwc), "+s"(nwp), "+s"(nup));
+      if constexpr (P == 0) {
+        if (nwp == 0) {
+          group();
+          nup = nu;
+          if (nup > 0) {
+            a_unit(wj - NUW, k0, csrc, cdst);
+            load_r(rq[0], csrc, Q0);
+            load_r(rq[1], csrc, Q1);
+            load_r(rq[2], csrc, Q2);
+          }
+        }
+      } else {
+        // every wave is done with the chunk in LDS before the next replaces
+        // it; the pass's first unit is already in flight
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        ++c;
+        k0 += kDecodeChunk;
+        klen = min(K, k0 + kDecodeChunk) - k0;
+        stage_x();
+        barrier_after<0>();
+      }
+      {
+        // the ring as below; after the pass's last unit comes the next
+        // pass's first, at the next chunk
+        static_for([&](auto jc) __attribute__((always_inline)) {
+          constexpr int j = decltype(jc)::value;
+          if (j < nup) {
+            UnitSrc nsrc;
+            UnitDst ndst;
+            auto& acc = pick<P>(accs[j], acc2);
+            if constexpr (P == 1) fresh();
+            load_r(rq[3], csrc, Q3);
+            compute_r(rq[0], Q0, acc);
+            if (j + 1 < nwp) {
+              w_unit(wj + (j + 1) * nwc, k0, nsrc, ndst);
+            } else {
+              if constexpr (P == 0) {
+                if (j + 1 == nwp) {
+                  group();  // nu may grow
+                  nup = nu;
+                }
+              }
+              if (j + 1 < nup)
+                a_unit(wj + (j + 1) * nwc - NUW, k0, nsrc, ndst);
+              else if (more && nwp > 0)
+                w_unit(wj, k0 + kDecodeChunk, nsrc, ndst);
+              else if (more)
+                a_unit(wj - NUW, k0 + kDecodeChunk, nsrc, ndst);
+              else
+                none(nsrc, ndst);
+            }
+            load_r(rq[0], nsrc, Q0);
+            compute_r(rq[1], Q1, acc);
+            load_r(rq[1], nsrc, Q1);
+            compute_r(rq[2], Q2, acc);
+            load_r(rq[2], nsrc, Q2);
+            compute_r(rq[3], Q3, acc);
+            if constexpr (P == 1) add_pair(accs[j]);
+            csrc = nsrc;
+          }
+        }, std::make_integer_sequence<int, kMaxUnits>{});
+      }
+    };
+    pass(std::integral_constant<int, 0>{}, npass > 1);
+    if (npass > 1) pass(std::integral_constant<int, 1>{}, false);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // one plane per pair of chunks
+    int wj = wi, nwc = NWc;  // opaque (see the passes)
+    asm volatile("" : "+s"(wj), "+s"(nwc));
+#pragma unroll
+    for (int j = 0; j < kMaxUnits; ++j) {
+      if (j < nu) {
+        UnitSrc sr;
+        UnitDst ds;
+        if (j < nw)
+          w_unit(wj + j * nwc, k0, sr, ds);
+        else
+          a_unit(wj + j * nwc - NUW, k0, sr, ds);
+        store_to(ds, accs[j]);
+      }
+    }
+    return;
+  } else if constexpr (WQ) {
     int j = 0;
     // W units (INT4, two halves through two register buffers), then the A
     // units (bf16 pages, likewise)
     for (; j < nw; ++j) {
       UnitDst ndst;
       load_q(qbuf[1], csrc, H1);
-      compute_q(qbuf[0], H0);
+      compute_q(qbuf[0], H0, acc);
       if (j + 1 < nw) {
-        w_unit(wi + (j + 1) * NWc, csrc, ndst);
+        w_unit(wi + (j + 1) * NWc, k0, csrc, ndst);
         load_q(qbuf[0], csrc, H0);
-        compute_q(qbuf[1], H1);
+        compute_q(qbuf[1], H1, acc);
       } else {
-        compute_q(qbuf[1], H1);
+        compute_q(qbuf[1], H1, acc);
         after_w(j + 1, csrc, ndst);
         load_b(buf[0], csrc, H0);
       }
@@ -510,19 +682,19 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
     if (nw == 0) {
       group();
       if (nu == 0) return;  // nothing in flight: the barrier waited for every load
-      a_unit(wi - NUW, csrc, cdst);
+      a_unit(wi - NUW, k0, csrc, cdst);
       load_b(buf[0], csrc, H0);
     }
     for (; j < nu; ++j) {
       load_b(buf[1], csrc, H1);
-      compute_b(buf[0], H0);
+      compute_b(buf[0], H0, acc);
       UnitDst ndst;
       if (j + 1 < nu)
-        a_unit(wi + (j + 1) * NWc - NUW, csrc, ndst);
+        a_unit(wi + (j + 1) * NWc - NUW, k0, csrc, ndst);
       else
         none(csrc, ndst);
       load_b(buf[0], csrc, H0);
-      compute_b(buf[1], H1);
+      compute_b(buf[1], H1, acc);
       store(cdst);
       cdst = ndst;
     }
@@ -532,7 +704,7 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
     if (nw == 0) {
       group();
       if (nu == 0) return;  // nothing in flight: the barrier waited for every load
-      a_unit(wi - NUW, csrc, cdst);
+      a_unit(wi - NUW, k0, csrc, cdst);
       load_r(rq[0], csrc, Q0);
       load_r(rq[1], csrc, Q1);
       load_r(rq[2], csrc, Q2);
@@ -541,21 +713,21 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
       UnitSrc nsrc;
       UnitDst ndst;
       load_r(rq[3], csrc, Q3);
-      compute_r(rq[0], Q0);
+      compute_r(rq[0], Q0, acc);
       if (j + 1 < nw)
-        w_unit(wi + (j + 1) * NWc, nsrc, ndst);
+        w_unit(wi + (j + 1) * NWc, k0, nsrc, ndst);
       else if (j + 1 == nw)
         after_w(j + 1, nsrc, ndst);  // groups the batch; nu may grow
       else if (j + 1 < nu)
-        a_unit(wi + (j + 1) * NWc - NUW, nsrc, ndst);
+        a_unit(wi + (j + 1) * NWc - NUW, k0, nsrc, ndst);
       else
         none(nsrc, ndst);
       load_r(rq[0], nsrc, Q0);
-      compute_r(rq[1], Q1);
+      compute_r(rq[1], Q1, acc);
       load_r(rq[1], nsrc, Q1);
-      compute_r(rq[2], Q2);
+      compute_r(rq[2], Q2, acc);
       load_r(rq[2], nsrc, Q2);
-      compute_r(rq[3], Q3);
+      compute_r(rq[3], Q3, acc);
       store(cdst);
       csrc = nsrc;
       cdst = ndst;
@@ -581,7 +753,10 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
   __shared__ float4 s_bsc[16];  // the block's tokens: scale of each 16-rank block
   __shared__ int s_bad;
   const int tid = threadIdx.x;
-  const int T = a.T, KS = a.KS;
+  const int T = a.T, KS = a.KP;  // (here: the partial planes, summed in K order)
+  // one chunk per plane: the planes of a chunk pair are added first, as a
+  // two-chunk block adds them
+  const bool pair = a.CPB == 1;
   const KArgs ka = kargs();
   const int mg = group_of(a.ct0, (int)blockIdx.x);  // the block's linear
   const int N = ka->N[mg];
@@ -590,7 +765,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
   const int t = t0 + tr;
   const int n = ((int)blockIdx.x - ka->ct0[mg]) * 64 + quad * 4;
   const bool mine = t < T && n < N;
-  const size_t pstr = (size_t)64 * a.npad;  // one chunk plane of `part`
+  const size_t pstr = (size_t)64 * a.npad;  // one plane of `part`
 
   // ---- round 1 ----
   // (the ids for the whole-batch check are stored to LDS only after every
@@ -640,7 +815,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
       up[e] = a.upart + ((size_t)mg * 64 + min(t0 + r, T - 1)) * a.u_ld + (uq[e] ? q : 0);
       u[e] = 0.f;
     }
-    const size_t ustr = (size_t)a.n_mod * 64 * a.u_ld;  // one chunk plane of upart
+    const size_t ustr = (size_t)a.n_mod * 64 * a.u_ld;  // one plane of upart
     // the first four chunks' V partial loads go out now, the rest after the
     // routing lookups
     float v[kVPer][4];
@@ -681,10 +856,17 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
           for (int j = 0; j < 4; ++j) v[e][j] = up[e][(size_t)min(c0 + j, KS - 1) * ustr];
       }
 #pragma unroll
-      for (int e = 0; e < kVPer; ++e)
+      for (int e = 0; e < kVPer; ++e) {
+        if (pair) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (c0 + j < KS && uq[e]) u[e] += v[e][j];
+          for (int h = 0; h < 2; ++h)
+            if (c0 + 2 * h < KS && uq[e]) u[e] += c0 + 2 * h + 1 < KS ? v[e][2 * h] + v[e][2 * h + 1] : v[e][2 * h];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (c0 + j < KS && uq[e]) u[e] += v[e][j];
+        }
+      }
     }
     __syncthreads();  // s_bad, s_info
     if (s_bad) {
@@ -712,22 +894,28 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
     for (int k = 0; k < 8; ++k) bv[k] = *reinterpret_cast<const uint4*>(Bp + 8 * k);
   }
 
-  // base: chunk partials in chunk order
-  float4 s = pv[0];
+  // base: the partial planes in K order (chunk pairs first)
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto add4 = [](float4 x, float4 y) { return make_float4(x.x + y.x, x.y + y.y, x.z + y.z, x.w + y.w); };
   for (int c0 = 0; c0 < KS; c0 += 4) {
     if (c0 > 0) {
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         pv[j] = *reinterpret_cast<const float4*>(pp + (size_t)min(c0 + j, KS - 1) * pstr);
     }
+    if (pair) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (c0 + j > 0 && c0 + j < KS) {
-        s.x += pv[j].x;
-        s.y += pv[j].y;
-        s.z += pv[j].z;
-        s.w += pv[j].w;
+      for (int h = 0; h < 2; ++h) {
+        const int c = c0 + 2 * h;
+        if (c < KS) {
+          const float4 q = c + 1 < KS ? add4(pv[2 * h], pv[2 * h + 1]) : pv[2 * h];
+          s = c == 0 ? q : add4(s, q);
+        }
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (c0 + j < KS) s = c0 + j == 0 ? pv[j] : add4(s, pv[j]);
     }
   }
   if (slot >= 0) {
@@ -765,25 +953,72 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
   *reinterpret_cast<uint2*>(ka->out[mg] + (size_t)t * N + n) = make_uint2(o0, o1);
 }
 
-template <bool WQ>
+template <bool WQ, int CPB>
 hipError_t launch_main(const DecodeArgs& a, int wpb, int grid, hipStream_t s) {
-  switch (wpb) {
-    case 4: hipLaunchKernelGGL((decode_main<4, WQ>), dim3(grid), dim3(256), 0, s, a); break;
-    case 5: hipLaunchKernelGGL((decode_main<5, WQ>), dim3(grid), dim3(320), 0, s, a); break;
-    case 6: hipLaunchKernelGGL((decode_main<6, WQ>), dim3(grid), dim3(384), 0, s, a); break;
-    default: return hipErrorInvalidValue;
+  if constexpr (CPB == 2 || WQ) {
+    // (the units' sums of two chunks, or both kinds of register buffers:
+    // one wave per SIMD)
+    if (wpb != 4) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((decode_main<4, WQ, CPB>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    switch (wpb) {
+      case 4: hipLaunchKernelGGL((decode_main<4, WQ, 1>), dim3(grid), dim3(256), 0, s, a); break;
+      case 5: hipLaunchKernelGGL((decode_main<5, WQ, 1>), dim3(grid), dim3(320), 0, s, a); break;
+      case 6: hipLaunchKernelGGL((decode_main<6, WQ, 1>), dim3(grid), dim3(384), 0, s, a); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }
 
-template <bool WQ>
-int main_resident(int wpb) {
-  switch (wpb) {
-    case 4: return resident_blocks(reinterpret_cast<const void*>(&decode_main<4, WQ>), 256, 0);
-    case 5: return resident_blocks(reinterpret_cast<const void*>(&decode_main<5, WQ>), 320, 0);
-    case 6: return resident_blocks(reinterpret_cast<const void*>(&decode_main<6, WQ>), 384, 0);
+static int resident_of(bool wq, int cpb, int wpb) {
+  const int threads = 64 * wpb;
+  const void* fn = nullptr;
+  if (cpb == 2) {
+    fn = reinterpret_cast<const void*>(&decode_main<4, false, 2>);
+  } else if (wq) {
+    fn = reinterpret_cast<const void*>(&decode_main<4, true, 1>);
+  } else {
+    fn = wpb == 4 ? reinterpret_cast<const void*>(&decode_main<4, false, 1>)
+                  : wpb == 5 ? reinterpret_cast<const void*>(&decode_main<5, false, 1>)
+                             : reinterpret_cast<const void*>(&decode_main<6, false, 1>);
   }
-  return 1;
+  return resident_blocks(fn, threads, 0);
+}
+
+// The launch shape for `cpb` chunks per block: waves per block and blocks
+// per plane.  Waves per block: the shape whose waves are busiest on average
+// relative to the busiest one (the launch lasts as long as its busiest wave,
+// and the compute units' share of the bandwidth does not depend on how many
+// waves split it); one block per compute unit (the X chunk fills most of
+// the LDS); a tie keeps fewer waves.  With two chunks per block a wave holds
+// at most kMaxUnits units' sums, which may take more blocks than the compute
+// units hold at once.
+struct Shape {
+  int wpb, nbc, resident;
+};
+static Shape decode_shape(const DecodeArgs& a, int cpb, int units) {
+  const int KP = ceil_div(a.KS, cpb);
+  Shape best{4, 1, 1};
+  double best_eff = -1.0;
+  // (at most six waves: with two halves of 16 KB in flight per wave, more
+  // outstanding reads per compute unit lower the stream rate -- measured
+  // 6.0 TB/s at 128 KB per compute unit, 5.4 at 256 KB)
+  for (int wpb : {4, 5, 6}) {
+    // the INT4 walk holds both kinds of buffers, the two-chunk walk every
+    // unit's sums: one wave per SIMD
+    if ((a.wq || cpb == 2) && wpb != 4) continue;
+    const int resident = resident_of(a.wq != 0, cpb, wpb);
+    int nbc = std::max(1, std::min(resident / KP, ceil_div(units, wpb)));
+    if (cpb == 2) nbc = std::max(nbc, ceil_div(units, wpb * kMaxUnits));
+    const int mx = ceil_div(units, nbc * wpb);
+    const double eff = (double)units / ((double)nbc * wpb * mx);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = Shape{wpb, nbc, resident};
+    }
+  }
+  return best;
 }
 
 hipError_t launch_decode(const DecodeArgs& args, int items_cap, hipStream_t s) {
@@ -791,32 +1026,30 @@ hipError_t launch_decode(const DecodeArgs& args, int items_cap, hipStream_t s) {
   // units per K chunk the grid must hold: every W unit plus every A item the
   // batch could have on every linear
   const int units = a.u0[kMaxGroup] + (a.lora ? a.n_mod * items_cap : 0);
-  // waves per block: the shape whose waves are busiest on average relative
-  // to the busiest one (the launch lasts as long as its busiest wave, and the
-  // compute units' share of the bandwidth does not depend on how many waves
-  // split it); one block per compute unit (the X chunk fills most of the
-  // LDS); a tie keeps fewer waves
-  int best_w = 4, best_nbc = 1;
-  double best_eff = -1.0;
-  // (at most six waves: with two halves of 16 KB in flight per wave, more
-  // outstanding reads per compute unit lower the stream rate -- measured
-  // 6.0 TB/s at 128 KB per compute unit, 5.4 at 256 KB)
-  for (int wpb : {4, 5, 6}) {
-    // the INT4 walk holds both kinds of buffers: one wave per SIMD
-    if (a.wq && wpb != 4) continue;
-    const int resident = a.wq ? main_resident<true>(wpb) : main_resident<false>(wpb);
-    const int nbc = std::max(1, std::min(resident / a.KS, ceil_div(units, wpb)));
-    const int mx = ceil_div(units, nbc * wpb);
-    const double eff = (double)units / ((double)nbc * wpb * mx);
-    if (eff > best_eff + 1e-9) {
-      best_eff = eff;
-      best_w = wpb;
-      best_nbc = nbc;
+  // Chunks per block: two (half the partial planes) where the two-chunk
+  // grid still fills nine tenths of the compute units' block slots, else one
+  // (a small linear needs every compute unit streaming).  Both add in the
+  // same order, so the choice never changes a bit of the output.
+  int cpb = 1;
+  Shape sh = decode_shape(a, 1, units);
+  if (a.KS >= 2 && !a.wq) {
+    const Shape s2 = decode_shape(a, 2, units);
+    if (10 * s2.nbc * ceil_div(a.KS, 2) >= 9 * s2.resident) {
+      cpb = 2;
+      sh = s2;
     }
   }
-  a.NWc = best_nbc * best_w;
-  const int grid = best_nbc * a.KS;
-  const hipError_t e = a.wq ? launch_main<true>(a, best_w, grid, s) : launch_main<false>(a, best_w, grid, s);
+  a.CPB = cpb;
+  a.KP = ceil_div(a.KS, cpb);
+  a.NWc = sh.nbc * sh.wpb;
+  const int grid = sh.nbc * a.KP;
+  hipError_t e;
+  if (cpb == 2)
+    e = launch_main<false, 2>(a, sh.wpb, grid, s);
+  else if (a.wq)
+    e = launch_main<true, 1>(a, sh.wpb, grid, s);
+  else
+    e = launch_main<false, 1>(a, sh.wpb, grid, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine, dim3(a.ct0[kMaxGroup], (a.T + 15) / 16), dim3(kCombThreads), 0, s, a);
   return hipGetLastError();

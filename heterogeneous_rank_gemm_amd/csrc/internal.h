@@ -149,6 +149,8 @@ struct DecodeArgs {
   const uint16_t* X;      // [T][K], shared by every linear of the group
   const int32_t* ids;     // [T]
   int32_t T, K, KS;       // KS = ceil(K / kDecodeChunk)
+  int32_t CPB, KP;        // K chunks per block (1 or 2) and partial planes, ceil(KS / CPB)
+                          // (set by launch_decode)
   int32_t n_mod;          // linears in the group, 1..kMaxGroup
   // per linear of the group (entries >= n_mod unused)
   const uint16_t* W[kMaxGroup];    // [N][K] bf16 base weight, or
@@ -166,8 +168,8 @@ struct DecodeArgs {
   const float4* id_bscale; // [max_ids] scale of each 16-rank block
   const uint16_t* pages;
   size_t slot_stride;
-  float* part;            // [KS][64][npad]
-  float* upart;           // [KS][n_mod][64][u_ld]
+  float* part;            // [KP][64][npad] (room for KS planes)
+  float* upart;           // [KP][n_mod][64][u_ld] (room for KS planes)
   int32_t npad;           // n0[n_mod]
   int32_t direct;         // pool keeps adapter id in slot id (max_ids <= max_adapters)
   int32_t max_slots;      // resident slots of the pool

@@ -279,3 +279,46 @@ def test_packed_rejects_batched_sizes():
         pool.base_apply_group_packed([0], X, [Wp], [out])
     assert e.value.status == "INVALID_ARG"
     pool.close()
+
+
+@pytest.mark.parametrize("K", [2048, 3000, 5000, 11008])
+def test_deep_group_equals_single_linears(K):
+    """Deep K (2 to 11 chunks of 1024, ragged tails): a group of eight
+    linears fills the chip with blocks that each take two chunks, while each
+    linear alone is small enough to take one chunk per block.  Both add the
+    chunk sums in pairs, so every output must be the same bits; both must
+    meet the oracle's bar."""
+    from heterogeneous_rank_gemm_amd import LoraPool
+    T, n_ad, r, n_lin, N = 64, 64, 16, 8, 1024
+    pool = LoraPool(n_ad, n_ad, r, [K] * n_lin, [N] * n_lin, T)
+    reg = oracle.Registry(n_ad, n_ad, r, [K] * n_lin, [N] * n_lin, T)
+    gen = torch.Generator().manual_seed(K)
+    ids_np = np.random.default_rng(K).integers(-1, n_ad, size=T).astype(np.int32)
+    for i in sorted(set(ids_np[ids_np >= 0].tolist())):
+        A = [(torch.randn((K, r), generator=gen) * 0.02).to(torch.bfloat16) for _ in range(n_lin)]
+        B = [(torch.randn((r, N), generator=gen) * 0.02).to(torch.bfloat16) for _ in range(n_lin)]
+        pool.load_adapter(i, r, 32.0, [a.cuda() for a in A], [b.cuda() for b in B])
+        reg.load(i, r, 32.0, A, B)
+    X = torch.randn((T, K), generator=gen).to(torch.bfloat16)
+    W = [(torch.randn((N, K), generator=gen) * 0.02).to(torch.bfloat16) for _ in range(n_lin)]
+    Xd, Wd = X.cuda(), [w.cuda() for w in W]
+    ids = torch.as_tensor(ids_np, device="cuda")
+    mods = list(range(n_lin))
+    outs, base = _outs(T, [N] * n_lin), _outs(T, [N] * n_lin)
+    pool.apply_group(mods, Xd, ids, Wd, outs)
+    pool.base_apply_group(mods, Xd, Wd, base)
+    single, sbase = _outs(T, [N] * n_lin), _outs(T, [N] * n_lin)
+    for m in mods:
+        pool.apply(m, Xd, ids, Wd[m], single[m])
+        pool.base_apply(m, Xd, Wd[m], sbase[m])
+    torch.cuda.synchronize()
+    assert pool.status() == "OK"
+    keep = torch.as_tensor(ids_np < 0, device="cuda")
+    for m in mods:
+        assert torch.equal(outs[m], single[m]), f"linear {m}: group differs from lora_apply"
+        assert torch.equal(base[m], sbase[m]), f"linear {m}: base group differs from lora_base_apply"
+        assert torch.equal(outs[m][keep], base[m][keep])
+    for m in (0, n_lin - 1):
+        mx, rl1, _ = oracle.parity_metrics(outs[m].cpu(), oracle.lora_linear(reg, m, X, ids_np, W[m]))
+        assert mx <= oracle.MAX_REL_TOL and rl1 <= oracle.RELL1_TOL, (m, mx, rl1)
+    pool.close()
