@@ -155,7 +155,7 @@ class Replica:
 def input_groups(wl: wk.Workload):
     """The workload's linears in call order, those that read one X together
     (at most 8 per group, in order of first appearance): for a Llama layer
-    [q, k, v, gate, up], [o], [down]."""
+    [q, k, v], [o], [gate, up], [down]."""
     groups, where = [], {}
     for j, m in enumerate(wl.modules):
         k = where.get(m.input_group)

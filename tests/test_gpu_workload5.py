@@ -2,8 +2,10 @@
 stack (7 LoRA-augmented linears per layer, 224 in all), 64 tokens, 200
 resident rank-16 adapters in one pool of 224 modules.
 
-A layer runs as three calls: one lora_apply_group over the five linears that
-read the hidden state h (q, k, v, gate, up), then o and down.  Checked:
+A layer runs as four calls in the order of a Llama decoder layer: one
+lora_apply_group over q, k, v (they read the attention block's input), then
+o, then one group over gate and up (they read the MLP block's input), then
+down.  Checked:
   * every row of every one of the 224 linears against the oracle (a registry
     of one layer at a time, so the host holds one layer's adapters);
   * the per-linear step (224 lora_apply calls) equals the grouped step bit
@@ -24,8 +26,8 @@ pytestmark = pytest.mark.gpu
 import oracle  # noqa: E402
 import workloads as wk  # noqa: E402
 
-# positions within a layer: the h-fed linears, then o, then down
-LAYER_GROUPS = ((0, 1, 2, 4, 5), (3,), (6,))
+# positions within a layer: q/k/v, o, gate/up, down
+LAYER_GROUPS = ((0, 1, 2), (3,), (4, 5), (6,))
 LAYERS = 32
 
 

@@ -51,10 +51,14 @@ LLAMA3_8B_TARGETS: Tuple[Tuple[str, int, int], ...] = (
     ("o_proj", 4096, 4096), ("gate_proj", 4096, 14336), ("up_proj", 4096, 14336),
     ("down_proj", 14336, 4096),
 )
-# Which activation feeds each target: the hidden state h feeds q/k/v/gate/up,
-# the attention output a feeds o, the MLP activation m feeds down.
-TARGET_INPUT = {"q_proj": "h", "k_proj": "h", "v_proj": "h", "gate_proj": "h",
-                "up_proj": "h", "o_proj": "a", "down_proj": "m"}
+# Which activation feeds each target in a Llama decoder layer: the attention
+# block's normalised input feeds q/k/v, the attention output feeds o, the MLP
+# block's normalised input (taken after the attention residual, so a different
+# tensor) feeds gate/up, and the gated activation feeds down.  Linears with
+# one input can share a launch; the four inputs of a layer come one after
+# another in a real forward pass.
+TARGET_INPUT = {"q_proj": "attn_in", "k_proj": "attn_in", "v_proj": "attn_in", "o_proj": "attn_out",
+                "gate_proj": "mlp_in", "up_proj": "mlp_in", "down_proj": "mlp_act"}
 
 X_STD = 1.0
 W_STD = 0.02
