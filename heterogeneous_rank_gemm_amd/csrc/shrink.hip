@@ -69,14 +69,17 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
   // 512-deep sub-chunks: wave w takes the 32-deep steps 32 w + 128 s of each;
   // all of a sub-chunk's loads go out first (addresses clamped in bounds,
   // values past the range masked), then its MFMAs.  The first sub-chunk's A
-  // loads go out before the token order is read.
+  // loads go out before the token order is read.  Only the adapter's own
+  // 16-rank blocks are read (a page padded to a larger rank holds zeros
+  // past it), and only the tile's own 16-row blocks of X.
   uint4 av[4][NQ];
   auto load_a = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int step = min((kb + 128 * st + 32 * w) / 32, k32 - 1);
 #pragma unroll
-      for (int nb = 0; nb < NQ; ++nb) av[st][nb] = ld16(Al + frag_tile(nb, step, rp, K) * 512);
+      for (int nb = 0; nb < NQ; ++nb)
+        if (nb < nq) av[st][nb] = ld16(Al + frag_tile(nb, step, rp, K) * 512);
     }
   };
   load_a(k0);
@@ -102,7 +105,8 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
     for (int st = 0; st < 4; ++st) {
       const int kc = min(kb + 128 * st + 32 * w + koff, K - 8);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) xv[st][mb] = ld16(xrow[mb] + kc);
+      for (int mb = 0; mb < 4; ++mb)
+        if (mb < nm) xv[st][mb] = ld16(xrow[mb] + kc);
     }
     if (kb == k0) {
       *tn = a.tile_info[next];
