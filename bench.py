@@ -780,6 +780,16 @@ def main(argv=None) -> int:
                 "traffic": None, "kernel": kernel, "algorithmic_flops_per_step": round(f0),
                 "launch_seconds_per_step": t_calls, "calls_per_step": n_calls}
 
+    # the chip's measured peaks beside the published ones (the same probes as
+    # --peaks), and the dominant unit's fraction of the measured one
+    print("[bench] peak probes", file=sys.stderr, flush=True)
+    pk = peaks(torch)
+    if hbm_bound:
+        roof["measured_peak"] = pk["hbm_read_GBps"]
+    else:
+        roof["measured_peak"] = pk["mfma_bf16_TFLOPs"]
+    roof["frac_of_measured_peak"] = round(achieved / roof["measured_peak"], 4)
+
     cpu = None
     if not args.no_cpu_baseline and not args.int4:
         print("[bench] cpu oracle baseline", file=sys.stderr, flush=True)
@@ -818,6 +828,7 @@ def main(argv=None) -> int:
                         "t_roof_us": round(t_roof * 1e6, 3),
                         "lora_overhead_floor_pct": round(100.0 * lb / bb, 2) if hbm_bound else None},
         "roofline": roof,
+        "measured_peaks": pk,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
