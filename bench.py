@@ -178,9 +178,8 @@ def _apply_group(rep: Replica, hrg, g, plan):
         hrg.lora_apply_group_packed(rep.pool.handle, g, rep.xin[g[0]], rep.ids, rep.T, [rep.Wp[j] for j in g],
                                     [rep.out[j] for j in g])
     elif rep.int4:
-        for j in g:
-            hrg.lora_apply_q4(rep.pool.handle, j, rep.xin[j], rep.ids, rep.T, rep.Wq[j][0], rep.Wq[j][1],
-                              rep.scratch, rep.out[j], plan)
+        hrg.lora_apply_group_q4(rep.pool.handle, g, rep.xin[g[0]], rep.ids, rep.T, [rep.Wq[j][0] for j in g],
+                                [rep.Wq[j][1] for j in g], rep.scratch, [rep.out[j] for j in g], plan)
     else:
         hrg.lora_apply_group(rep.pool.handle, g, rep.xin[g[0]], rep.ids, rep.T, [rep.W[j] for j in g],
                              [rep.out[j] for j in g], plan)
@@ -191,9 +190,8 @@ def _base_group(rep: Replica, hrg, g):
         hrg.lora_base_apply_group_packed(rep.pool.handle, g, rep.xin[g[0]], rep.T, [rep.Wp[j] for j in g],
                                          [rep.out[j] for j in g])
     elif rep.int4:
-        for j in g:
-            hrg.lora_base_apply_q4(rep.pool.handle, j, rep.xin[j], rep.T, rep.Wq[j][0], rep.Wq[j][1],
-                                   rep.scratch, rep.out[j])
+        hrg.lora_base_apply_group_q4(rep.pool.handle, g, rep.xin[g[0]], rep.T, [rep.Wq[j][0] for j in g],
+                                     [rep.Wq[j][1] for j in g], rep.scratch, [rep.out[j] for j in g])
     else:
         hrg.lora_base_apply_group(rep.pool.handle, g, rep.xin[g[0]], rep.T, [rep.W[j] for j in g],
                                   [rep.out[j] for j in g])
@@ -228,7 +226,8 @@ def per_linear_step(rep: Replica, hrg):
         plan = rep.plan
     for j in range(len(rep.out)):
         if rep.int4:
-            _apply_group(rep, hrg, [j], plan)
+            hrg.lora_apply_q4(rep.pool.handle, j, rep.xin[j], rep.ids, rep.T, rep.Wq[j][0], rep.Wq[j][1],
+                              rep.scratch, rep.out[j], plan)
         else:
             hrg.lora_apply(rep.pool.handle, j, rep.xin[j], rep.ids, rep.T, rep.W[j], rep.out[j], plan)
 
@@ -667,7 +666,7 @@ def main(argv=None) -> int:
                     help="decode batches: base weights in fragment tiles (lora_pack_weight) or "
                          "row-major")
     ap.add_argument("--int4", action="store_true",
-                    help="INT4 (group 128) base weights instead of bf16 (lora_apply_q4)")
+                    help="INT4 (group 128) base weights instead of bf16 (lora_apply_group_q4)")
     ap.add_argument("--chains", action="store_true",
                     help="measure adapter chains instead (prints its own JSON line)")
     ap.add_argument("--target-sets", action="store_true",

@@ -14,7 +14,8 @@ from ._lora import (LoraError, STATUS_NAMES, EXPORTED, lora_status_string, lora_
                     lora_paging_query, lora_paging_stats, lora_q4_pack, lora_apply_q4,
                     lora_base_apply_q4, lora_load_chain, lora_apply_group, lora_base_apply_group,
                     lora_packed_weight_elems, lora_pack_weight, lora_apply_group_packed,
-                    lora_base_apply_group_packed, lora_apply_noalloc)
+                    lora_base_apply_group_packed, lora_apply_noalloc, lora_apply_group_q4,
+                    lora_base_apply_group_q4)
 from .pool import LoraPool
 
 __all__ = [
@@ -26,4 +27,5 @@ __all__ = [
     "lora_paging_query", "lora_paging_stats", "lora_q4_pack", "lora_apply_q4", "lora_base_apply_q4",
     "lora_load_chain", "lora_apply_group", "lora_base_apply_group", "lora_packed_weight_elems",
     "lora_pack_weight", "lora_apply_group_packed", "lora_base_apply_group_packed", "lora_apply_noalloc",
+    "lora_apply_group_q4", "lora_base_apply_group_q4",
 ]

@@ -32,7 +32,7 @@ EXPORTED = (
     "lora_pin_adapter", "lora_paging_query", "lora_paging_stats", "lora_q4_pack", "lora_apply_q4",
     "lora_base_apply_q4", "lora_load_chain", "lora_apply_group", "lora_base_apply_group",
     "lora_packed_weight_elems", "lora_pack_weight", "lora_apply_group_packed",
-    "lora_base_apply_group_packed", "lora_apply_noalloc",
+    "lora_base_apply_group_packed", "lora_apply_noalloc", "lora_apply_group_q4", "lora_base_apply_group_q4",
 )
 
 _vp = C.c_void_p
@@ -70,6 +70,10 @@ _sigs = {
     "lora_packed_weight_elems": [_i32, _i32, C.POINTER(C.c_int64)],
     "lora_pack_weight": [_vp, _i32, _i32, _vp, _vp],
     "lora_apply_group_packed": [_vp, _i32, _P_i32, _vp, _vp, _i32, C.POINTER(_vp), C.POINTER(_vp), _vp],
+    "lora_apply_group_q4": [_vp, _i32, _P_i32, _vp, _vp, _i32, C.POINTER(_vp), C.POINTER(_vp), _vp,
+                            C.POINTER(_vp), _vp, _vp],
+    "lora_base_apply_group_q4": [_vp, _i32, _P_i32, _vp, _i32, C.POINTER(_vp), C.POINTER(_vp), _vp,
+                                 C.POINTER(_vp), _vp],
     "lora_base_apply_group_packed": [_vp, _i32, _P_i32, _vp, _i32, C.POINTER(_vp), C.POINTER(_vp), _vp],
     "lora_apply_noalloc": [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp],
 }
@@ -334,6 +338,22 @@ def lora_base_apply_q4(pool: int, module: int, X, T: int, Wq, Wsz, W_scratch, ou
                        stream=None) -> None:
     _check(_lib.lora_base_apply_q4(pool, module, _ptr(X), T, _ptr(Wq), _ptr(Wsz), _ptr(W_scratch),
                                    _ptr(out), _stream(stream)), "lora_base_apply_q4")
+
+
+def lora_apply_group_q4(pool: int, modules: Sequence[int], X, ids, T: int, Wq: Sequence, Wsz: Sequence,
+                        W_scratch, out: Sequence, plan: Optional[int] = None, stream=None) -> None:
+    n, mods, pq, po = _group_arrays(modules, Wq, out)
+    pz = (_vp * max(n, 1))(*[_ptr(z) for z in Wsz])
+    _check(_lib.lora_apply_group_q4(pool, n, mods, _ptr(X), _ptr(ids), T, pq, pz, _ptr(W_scratch), po, plan,
+                                    _stream(stream)), "lora_apply_group_q4")
+
+
+def lora_base_apply_group_q4(pool: int, modules: Sequence[int], X, T: int, Wq: Sequence, Wsz: Sequence,
+                             W_scratch, out: Sequence, stream=None) -> None:
+    n, mods, pq, po = _group_arrays(modules, Wq, out)
+    pz = (_vp * max(n, 1))(*[_ptr(z) for z in Wsz])
+    _check(_lib.lora_base_apply_group_q4(pool, n, mods, _ptr(X), T, pq, pz, _ptr(W_scratch), po,
+                                         _stream(stream)), "lora_base_apply_group_q4")
 
 
 def lora_load_chain(pool: int, chain_id: int, members: Sequence[int], stream=None) -> None:

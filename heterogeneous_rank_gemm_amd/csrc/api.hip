@@ -735,6 +735,21 @@ lora_status_t lora_base_apply_q4(lora_pool_t P, int32_t module, const lora_bf16_
   return apply_impl(P, 1, &module, X, nullptr, T, nullptr, &Wq, &Wsz, W_scratch, &out, nullptr, false, stream);
 }
 
+lora_status_t lora_apply_group_q4(lora_pool_t P, int32_t n, const int32_t* modules, const lora_bf16_t* X,
+                                  const int32_t* ids, int32_t T, const uint32_t* const* Wq,
+                                  const uint32_t* const* Wsz, lora_bf16_t* W_scratch, lora_bf16_t* const* out,
+                                  lora_plan_t plan, hipStream_t stream) {
+  if (!Wq || !Wsz) return LORA_ERR_INVALID_ARG;
+  return apply_impl(P, n, modules, X, ids, T, nullptr, Wq, Wsz, W_scratch, out, plan, true, stream);
+}
+
+lora_status_t lora_base_apply_group_q4(lora_pool_t P, int32_t n, const int32_t* modules, const lora_bf16_t* X,
+                                       int32_t T, const uint32_t* const* Wq, const uint32_t* const* Wsz,
+                                       lora_bf16_t* W_scratch, lora_bf16_t* const* out, hipStream_t stream) {
+  if (!Wq || !Wsz) return LORA_ERR_INVALID_ARG;
+  return apply_impl(P, n, modules, X, nullptr, T, nullptr, Wq, Wsz, W_scratch, out, nullptr, false, stream);
+}
+
 lora_status_t lora_q4_pack(const uint8_t* q, const uint8_t* z, const lora_bf16_t* s, int32_t N, int32_t K,
                            uint32_t* Wq, uint32_t* Wsz) {
   if (!q || !z || !s || !Wq || !Wsz || N < 1 || K < hrg::kQ4Group || K % hrg::kQ4Group != 0)

@@ -216,5 +216,31 @@ class LoraPool:
         self._check_q4("lora_base_apply_q4", module, Wq, Wsz, W_scratch)
         _lora.lora_base_apply_q4(self.handle, module, X, T, Wq, Wsz, W_scratch, out, stream)
 
+    def _check_q4_scratch(self, where: str, modules, W_scratch) -> None:
+        import torch
+        need = max(self.d_in[m] * self.d_out[m] for m in modules) if len(modules) else 0
+        if W_scratch is not None and (W_scratch.dtype != torch.bfloat16 or not W_scratch.is_contiguous()
+                                      or W_scratch.numel() < need or not W_scratch.is_cuda):
+            raise LoraError(1, f"{where}: W_scratch must hold {need} bf16 on a GPU")
+
+    def apply_group_q4(self, modules: Sequence[int], X, ids, Wq: Sequence, Wsz: Sequence, out: Sequence,
+                       W_scratch=None, plan: Optional[int] = None, stream=None, T: Optional[int] = None):
+        """lora_apply_group_q4: the linears ``modules`` (one d_in) on the same X, INT4 weights."""
+        T = X.shape[0] if T is None else T
+        for m, q, z, o in zip(modules, Wq, Wsz, out):
+            self._check_linear("lora_apply_group_q4", m, X, ids, None, o, T)
+            self._check_q4("lora_apply_group_q4", m, q, z, None)
+        self._check_q4_scratch("lora_apply_group_q4", modules, W_scratch)
+        _lora.lora_apply_group_q4(self.handle, modules, X, ids, T, Wq, Wsz, W_scratch, out, plan, stream)
+
+    def base_apply_group_q4(self, modules: Sequence[int], X, Wq: Sequence, Wsz: Sequence, out: Sequence,
+                            W_scratch=None, stream=None, T: Optional[int] = None):
+        T = X.shape[0] if T is None else T
+        for m, q, z, o in zip(modules, Wq, Wsz, out):
+            self._check_linear("lora_base_apply_group_q4", m, X, None, None, o, T)
+            self._check_q4("lora_base_apply_group_q4", m, q, z, None)
+        self._check_q4_scratch("lora_base_apply_group_q4", modules, W_scratch)
+        _lora.lora_base_apply_group_q4(self.handle, modules, X, T, Wq, Wsz, W_scratch, out, stream)
+
     def load_chain(self, chain_id: int, members, stream=None):
         _lora.lora_load_chain(self.handle, chain_id, members, stream)

@@ -255,9 +255,11 @@ lora_status_t lora_base_apply_group(lora_pool_t pool, int32_t n, const int32_t* 
  * every 16-byte MFMA operand load of a wave touches 16 rows, which the memory
  * path serves at about three quarters of the rate of contiguous reads.  A
  * weight packed once into fragment tiles (16 rows x 32 columns, 1 KB each,
- * row-group-major; inside a tile lane l = 16 j + r holds row 16 g + r,
+ * inside a tile lane l = 16 j + r holds row 16 g + r,
  * columns 32 s + 8 j .. + 7; rows and columns zero-padded to multiples of 16
- * and 32) is read as contiguous 1-KB pieces.  The adapters' A pages in the
+ * and 32; tiles ordered by 1024-column block, then row group, then column)
+ * is read as contiguous 1-KB pieces, a 16-row unit of one 1024-deep chunk
+ * as 32 contiguous kilobytes.  The adapters' A pages in the
  * pool already use this layout.
  *
  * lora_packed_weight_elems -- elements (bf16) of the packed form of an N x K
@@ -340,6 +342,28 @@ lora_status_t lora_apply_q4(lora_pool_t pool, int32_t module, const lora_bf16_t*
 lora_status_t lora_base_apply_q4(lora_pool_t pool, int32_t module, const lora_bf16_t* X, int32_t T,
                                  const uint32_t* Wq, const uint32_t* Wsz, lora_bf16_t* W_scratch,
                                  lora_bf16_t* out, hipStream_t stream);
+
+/*
+ * lora_apply_group_q4 / lora_base_apply_group_q4 -- lora_apply_group /
+ * lora_base_apply_group with INT4 base weights ([vLLM-ch7] performance
+ * notes; [LoRA-Land] section "2. multi-LoRA batch scheduling" for the
+ * grouping): Wq and Wsz are host arrays [n] of device pointers, Wq[i] and
+ * Wsz[i] the packed weight of linear modules[i] (layout above).  At T <= 64
+ * the n linears run as one launch pair that stages X once; at larger T
+ * each linear is dequantized into W_scratch in turn (caller-owned, at least
+ * the largest d_out x d_in of the group in bf16; required then, else may be
+ * NULL) before its GEMM.  Each out[i] equals lora_apply_q4
+ * (lora_base_apply_q4) on that linear alone, bit for bit.  Errors as
+ * lora_apply_group, plus INVALID_ARG if d_in % 128 != 0.
+ */
+lora_status_t lora_apply_group_q4(lora_pool_t pool, int32_t n, const int32_t* modules, const lora_bf16_t* X,
+                                  const int32_t* ids, int32_t T, const uint32_t* const* Wq,
+                                  const uint32_t* const* Wsz, lora_bf16_t* W_scratch, lora_bf16_t* const* out,
+                                  lora_plan_t plan, hipStream_t stream);
+lora_status_t lora_base_apply_group_q4(lora_pool_t pool, int32_t n, const int32_t* modules,
+                                       const lora_bf16_t* X, int32_t T, const uint32_t* const* Wq,
+                                       const uint32_t* const* Wsz, lora_bf16_t* W_scratch,
+                                       lora_bf16_t* const* out, hipStream_t stream);
 
 /*
  * lora_status -- synchronise `stream`, return the pool's sticky device

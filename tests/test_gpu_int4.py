@@ -98,3 +98,63 @@ def test_int4_argument_errors():
         pool.base_apply_q4(1, X[:8, :200].contiguous(), Wq_d, Wsz_d, out[:8])
     assert e.value.status == "INVALID_ARG"
     pool.close()
+
+
+@pytest.mark.parametrize("T,K", [(64, 4096), (17, 2048), (130, 1024)])
+def test_int4_group_equals_single_linears(T, K):
+    """lora_apply_group_q4 / lora_base_apply_group_q4 over linears that read
+    one X: each output equals the INT4 call on that linear alone and the
+    bf16 group call on the dequantized weights, bit for bit, and meets the
+    oracle's bar."""
+    import heterogeneous_rank_gemm_amd as hrg
+    from heterogeneous_rank_gemm_amd import LoraPool
+    # (at K = 4096 and 64 tokens the bf16 group is large enough for blocks of
+    # two K chunks, the INT4 one always takes one: the sums must still agree)
+    d_outs = [4104, 264, 4096]
+    n = len(d_outs)
+    seed = T + K
+    pool = LoraPool(6, 6, 16, [K] * n, d_outs, T)
+    reg = oracle.Registry(6, 6, 16, [K] * n, d_outs, T)
+    gen = torch.Generator().manual_seed(seed)
+    for i, r in enumerate([16, 8, 5, 16, 12, 1]):
+        A = [(torch.randn((K, r), generator=gen) * 0.02).to(torch.bfloat16) for _ in d_outs]
+        B = [(torch.randn((r, d), generator=gen) * 0.02).to(torch.bfloat16) for d in d_outs]
+        pool.load_adapter(i, r, 2.0 * r, [a.cuda() for a in A], [b.cuda() for b in B])
+        reg.load(i, r, 2.0 * r, A, B)
+    Wq, Wsz, Wdeq = [], [], []
+    for m, d in enumerate(d_outs):
+        q, z, s = _q4(d, K, seed + m)
+        a, b = hrg.lora_q4_pack(q, z, s)
+        Wq.append(torch.as_tensor(a.view(np.int32)).cuda())
+        Wsz.append(torch.as_tensor(b.view(np.int32)).cuda())
+        Wdeq.append(oracle.dequant_q4(q, z, s))
+    Wbf = [torch.as_tensor(w.astype(np.float32)).to(torch.bfloat16).cuda() for w in Wdeq]
+    ids_np = np.random.default_rng(seed).integers(-1, 6, T).astype(np.int32)
+    ids = torch.as_tensor(ids_np, device="cuda")
+    X = torch.randn((T, K), generator=gen).to(torch.bfloat16)
+    Xd = X.cuda()
+    scratch = torch.empty(max(d_outs) * K, dtype=torch.bfloat16, device="cuda") if T > 64 else None
+    mods = list(range(n))
+
+    def outs():
+        return [torch.empty((T, d), dtype=torch.bfloat16, device="cuda") for d in d_outs]
+    g, gb, bf, bfb = outs(), outs(), outs(), outs()
+    pool.apply_group_q4(mods, Xd, ids, Wq, Wsz, g, W_scratch=scratch)
+    pool.base_apply_group_q4(mods, Xd, Wq, Wsz, gb, W_scratch=scratch)
+    pool.apply_group(mods, Xd, ids, Wbf, bf)
+    pool.base_apply_group(mods, Xd, Wbf, bfb)
+    torch.cuda.synchronize()
+    assert pool.status() == "OK"
+    for m in mods:
+        one = torch.empty((T, d_outs[m]), dtype=torch.bfloat16, device="cuda")
+        oneb = torch.empty_like(one)
+        pool.apply_q4(m, Xd, ids, Wq[m], Wsz[m], one, W_scratch=scratch)
+        pool.base_apply_q4(m, Xd, Wq[m], Wsz[m], oneb, W_scratch=scratch)
+        torch.cuda.synchronize()
+        assert torch.equal(g[m], one), f"linear {m}: INT4 group differs from lora_apply_q4"
+        assert torch.equal(gb[m], oneb), f"linear {m}: INT4 base group differs from lora_base_apply_q4"
+        assert torch.equal(g[m], bf[m]) and torch.equal(gb[m], bfb[m]), f"linear {m}: INT4 differs from bf16"
+        ref = oracle.lora_linear(reg, m, X, ids_np, Wdeq[m])
+        mx, rl1, _ = oracle.parity_metrics(g[m].cpu(), ref)
+        assert mx <= oracle.MAX_REL_TOL and rl1 <= oracle.RELL1_TOL, (m, mx, rl1)
+    pool.close()
