@@ -66,6 +66,20 @@ __device__ __forceinline__ void tile_coords(int b, int nblocks, int tiles_m, int
   tn = in / gsize;
 }
 
+// Scheduling hint: kM MFMAs with kV buffer loads and kD LDS reads spread
+// evenly between them.
+template <int kM, int kV, int kD, int Q = 0>
+__device__ __forceinline__ void interleave_vd() {
+  if constexpr (Q < kM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int nv = kV * (Q + 1) / kM - kV * Q / kM;
+    if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x020, nv, 0);
+    constexpr int nd = kD * (Q + 1) / kM - kD * Q / kM;
+    if constexpr (nd > 0) __builtin_amdgcn_sched_group_barrier(0x100, nd, 0);
+    interleave_vd<kM, kV, kD, Q + 1>();
+  }
+}
+
 // Scheduling hint: kM MFMAs with kX instructions of class kMask spread
 // evenly between them (0x020 = global/buffer load, 0x100 = LDS read).
 template <int kM, int kX, int kMask, int Q = 0>
@@ -479,7 +493,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
   // One barrier per K-step.  Between two barriers: the DMA of the step NS-1
   // ahead (into the stage read by the step before), this step's fragment
   // reads, the previous step's last 16-deep MFMA group and this step's first
-  // three.  The barrier waits only for the next step's DMA.
+  // three.  The barrier waits only for the next step's DMA.  The DMA is
+  // spread over the MFMA groups: issued in one burst it fills the texture
+  // address queue and stalls the issuing wave (SQ_VMEM_TA_CMD_FIFO_FULL).
+  // With two stages the DMA must land within the step, so it goes out over
+  // the first half; with three or four it may trail, and goes out over the
+  // whole step (MI355X: Llama-3-8B layer base-only 1.89 -> 1.80 ms with
+  // 256x256 tiles over half a step, 1.88 over the whole; 4096-wide linear
+  // with 1024 tokens, 128x128 tiles, 43.4 -> 40.6 us over the whole step).
   constexpr int kM = FN * FM, kD = FN + FM, kV = NWB + NXB;
   // stage S's arrays, named directly (through a pointer table the compiler
   // loses which LDS object a read touches and waits for every DMA in flight)
@@ -509,10 +530,17 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
     rd(ws, xs, 3, 1);
     mm(0);
     __builtin_amdgcn_sched_group_barrier(0x100, kD, 0);
-    interleave<kM, kV, 0x020>();
-    interleave<kM, kD, 0x100>();
-    interleave<kM, kD, 0x100>();
-    interleave<kM, kD, 0x100>();
+    if constexpr (NS == 2) {
+      interleave<kM, kV / 2, 0x020>();
+      interleave_vd<kM, kV - kV / 2, kD>();
+      interleave<kM, kD, 0x100>();
+      interleave<kM, kD, 0x100>();
+    } else {
+      interleave<kM, kV / 4, 0x020>();
+      interleave_vd<kM, kV / 4, kD>();
+      interleave_vd<kM, kV / 4, kD>();
+      interleave_vd<kM, kV - 3 * (kV / 4), kD>();
+    }
     barrier_after_dma<(NS - 2) * kV>();
   };
 #pragma unroll
