@@ -525,13 +525,15 @@ static lora_status_t batched_apply(lora_pool_s* P, int32_t module, const lora_bf
     return hrg::launch_prefill(ga, false, -1, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
   }
   // shrink: a fixed grid walks the plan's (tile, K-split) items; K splits of
-  // at least 512 (at most kMaxSplits planes).  An item is a short chain of
-  // dependent loads, so up to 1024 blocks (two rounds of resident blocks)
-  // take them one each rather than fewer blocks walking two or more
+  // at least 1024 (at most kMaxSplits planes), streamed as 256-deep
+  // sub-chunks with the next one's loads in flight.  An item is a short
+  // chain of dependent loads, so up to 1024 blocks (two rounds of resident
+  // blocks) take them one each rather than fewer blocks walking two or more
   // (MI355X, 4096-deep linear, 1024 tokens over about 105 adapters of ranks
-  // 8-64: 17.6 us with 512 blocks, 15.2 with 1024; 1024-deep splits 21.8,
-  // 256-deep 24.7)
-  const int kchunk = std::max(512, round_up(ceil_div(K, hrg::kMaxSplits), 128));
+  // 8-64: 17.6 us with 512 blocks, 15.2 with 1024; with the sub-chunk ring,
+  // splits of 512, 1024, 2048: step 83.5, 83.0, 85.4 us; Llama-3-8B layer
+  // 1.964, 1.954, 1.952 ms)
+  const int kchunk = std::max(1024, round_up(ceil_div(K, hrg::kMaxSplits), 256));
   const int ksplit = ceil_div(K, kchunk);
   const int max_items = max_tiles_for(P) * ksplit;
   const int grid = std::min(max_items, 1024);

@@ -5,8 +5,9 @@
 //
 // Work unit: (shrink tile, K-split).  A tile is up to 64 sorted rows of ONE
 // segment, so the adapter's A^T page (fragment tiles: one contiguous 1 KB
-// per 16 ranks x 32-deep MFMA step) is streamed once per tile and K-split;
-// the 16x16x32 bf16 MFMA does the contraction.
+// per 16 ranks x 32-deep MFMA step) is streamed once per tile and K-split,
+// 256 deep at a time through two register sets; the 16x16x32 bf16 MFMA does
+// the contraction.
 // Each of the 4 waves covers an interleaved quarter of the K range; the four
 // partial results are summed in a fixed order through LDS (deterministic),
 // and each K-split writes its own fp32 partial plane of U.  The small-segment
@@ -66,23 +67,17 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
 #pragma unroll
   for (int nb = 0; nb < NQ; ++nb) qv[nb] = 16 * nb + (l & 15) < rank;
   const int koff = 8 * (l >> 4);
-  // 512-deep sub-chunks: wave w takes the 32-deep steps 32 w + 128 s of each;
-  // all of a sub-chunk's loads go out first (addresses clamped in bounds,
-  // values past the range masked), then its MFMAs.  The first sub-chunk's A
-  // loads go out before the token order is read.  Only the adapter's own
-  // 16-rank blocks are read (a page padded to a larger rank holds zeros
-  // past it), and only the tile's own 16-row blocks of X.
-  uint4 av[4][NQ];
-  auto load_a = [&](int kb) __attribute__((always_inline)) {
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int step = min((kb + 128 * st + 32 * w) / 32, k32 - 1);
-#pragma unroll
-      for (int nb = 0; nb < NQ; ++nb)
-        if (nb < nq) av[st][nb] = ld16(Al + frag_tile(nb, step, rp, K) * 512);
-    }
-  };
-  load_a(k0);
+  // 256-deep sub-chunks: wave w takes the 32-deep steps 32 w + 128 s
+  // (s = 0, 1) of each, through two register sets: the next sub-chunk's A
+  // and X loads are in flight while the current one's MFMAs run.  Every load
+  // is issued whatever the item's rank and rows (a rank block past the
+  // adapter's rank re-reads block 0, a row past the tile re-reads row 0, a
+  // sub-chunk past the item's range re-reads its last one: L2 hits, never
+  // applied), so the compiler counts each wait exactly instead of waiting
+  // for both sets before the first MFMA.
+  constexpr int kSub = 256;
+  const int nsub = (k1 - k0 + kSub - 1) / kSub;
+  const int klast = k0 + (nsub - 1) * kSub;
   const uint16_t* xrow[4];
   bool rv[4];
 #pragma unroll
@@ -91,41 +86,59 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
     rv[mb] = p < rows;
     xrow[mb] = a.X + (size_t)tok[mb] * K;
   }
+  uint4 av[2][2][NQ], xv[2][2][4];
+  auto load = [&](auto bc, int kb) __attribute__((always_inline)) {
+    constexpr int b = decltype(bc)::value;
+    kb = min(kb, klast);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int step = min((kb + 128 * st + 32 * w) / 32, k32 - 1);
+#pragma unroll
+      for (int nb = 0; nb < NQ; ++nb) av[b][st][nb] = ld16(Al + frag_tile(nb < nq ? nb : 0, step, rp, K) * 512);
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int kc = min(kb + 128 * st + 32 * w + koff, K - 8);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) xv[b][st][mb] = ld16(xrow[mb] + kc);
+    }
+  };
 
   f32x4 acc[4][NQ];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < NQ; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int kb = k0; kb < k1; kb += 512) {
-    if (kb > k0) load_a(kb);
-    uint4 xv[4][4];
+  auto mm = [&](auto bc, int kb) __attribute__((always_inline)) {
+    constexpr int b = decltype(bc)::value;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int kc = min(kb + 128 * st + 32 * w + koff, K - 8);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        if (mb < nm) xv[st][mb] = ld16(xrow[mb] + kc);
-    }
-    if (kb == k0) {
-      *tn = a.tile_info[next];
-      tile_tokens(a, *tn, tokn);  // waits for the entry only; lands during the MFMAs
-    }
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int st = 0; st < 2; ++st) {
       const bool kv = kb + 128 * st + 32 * w + koff < k1;  // a lane's 8 elements are all in or out
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
         if (mb >= nm) continue;
-        const bf16x8 xa = keep_bf(rv[mb] && kv, xv[st][mb]);
+        const bf16x8 xa = keep_bf(rv[mb] && kv, xv[b][st][mb]);
 #pragma unroll
         for (int nb = 0; nb < NQ; ++nb) {
           if (nb >= nq) continue;
-          acc[mb][nb] = mfma16(xa, keep_bf(qv[nb] && kv, av[st][nb]), acc[mb][nb]);
+          acc[mb][nb] = mfma16(xa, keep_bf(qv[nb] && kv, av[b][st][nb]), acc[mb][nb]);
         }
       }
     }
+  };
+  const auto B0 = std::integral_constant<int, 0>{};
+  const auto B1 = std::integral_constant<int, 1>{};
+  load(B0, k0);
+  // the next item's tile entry, then its tokens (they land during the MFMAs)
+  *tn = a.tile_info[next];
+  tile_tokens(a, *tn, tokn);
+  for (int i = 0;; i += 2) {
+    load(B1, k0 + (i + 1) * kSub);
+    mm(B0, k0 + i * kSub);
+    if (i + 1 >= nsub) break;
+    load(B0, k0 + (i + 2) * kSub);
+    mm(B1, k0 + (i + 1) * kSub);
+    if (i + 2 >= nsub) break;
   }
 
   // cross-wave reduction in fixed wave order
