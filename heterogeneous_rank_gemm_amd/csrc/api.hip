@@ -505,12 +505,52 @@ lora_status_t lora_plan(lora_pool_t P, const int32_t* ids, int32_t T, lora_plan_
   return run_plan(P, ids, T, plan, stream);
 }
 
-// The batched path (T > kDecodeMaxT) of one linear: the shrink, the
-// small-segment expand and the GEMM with the fused expand, on a plan `pl`
-// already built for the batch (lora), or the plain GEMM (base only).
-static lora_status_t batched_apply(lora_pool_s* P, int32_t module, const lora_bf16_t* X, int32_t T,
-                                   const lora_bf16_t* W, lora_bf16_t* out, lora_plan_s* pl, bool lora,
-                                   hipStream_t stream) {
+// The batched path (T > kDecodeMaxT): K splits of the shrink for linears of
+// depth K.  Splits of at least 1024 (at most kMaxSplits planes), streamed as
+// 256-deep sub-chunks with the next one's loads in flight.  An item is a
+// short chain of dependent loads, so up to 1024 blocks (two rounds of
+// resident blocks) take them one each rather than fewer blocks walking two
+// or more (MI355X, 4096-deep linear, 1024 tokens over about 105 adapters of
+// ranks 8-64: 17.6 us with 512 blocks, 15.2 with 1024; with the sub-chunk
+// ring, splits of 512, 1024, 2048: step 83.5, 83.0, 85.4 us; Llama-3-8B
+// layer 1.964, 1.954, 1.952 ms).
+static int shrink_kchunk(int K) { return std::max(1024, round_up(ceil_div(K, hrg::kMaxSplits), 256)); }
+
+// The shrink of nl linears that read the same X (one launch: each item
+// loads its X rows once for all of them), on a plan `pl` built for the
+// batch.  Linear i's U planes land at P->upart + (i * ksplit + split) *
+// split_stride.
+static lora_status_t batched_shrink(lora_pool_s* P, int nl, const int32_t* modules, const lora_bf16_t* X,
+                                    int32_t T, lora_plan_s* pl, hipStream_t stream) {
+  const int K = P->d_in[modules[0]];
+  const int kchunk = shrink_kchunk(K);
+  const int ksplit = ceil_div(K, kchunk);
+  const int max_items = max_tiles_for(P) * ksplit;
+  const int grid = std::min(max_items, 1024);
+  hrg::ShrinkArgs sa{};
+  sa.X = X;
+  sa.K = K;
+  sa.perm = pl->tab.perm;
+  sa.tile_info = pl->tab.tile_info;
+  sa.counts = pl->tab.counts;
+  sa.pages = P->pages;
+  sa.slot_stride = P->slot_elems;
+  for (int i = 0; i < nl; ++i) sa.a_off[i] = P->a_off[modules[i]];
+  sa.upart = P->upart;
+  sa.split_stride = P->split_stride;
+  sa.u_ld = P->rpad;
+  sa.kchunk = kchunk;
+  sa.nsplit = ksplit;
+  sa.status = P->status;
+  return hrg::launch_shrink(sa, nl, grid, ksplit, T, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+// The rest of one linear's batched apply: the small-segment expand and the
+// GEMM with the fused expand, reading the linear's U planes at `upart`
+// (lora), or the plain GEMM (base only).
+static lora_status_t batched_finish(lora_pool_s* P, int32_t module, const lora_bf16_t* X, int32_t T,
+                                    const lora_bf16_t* W, lora_bf16_t* out, lora_plan_s* pl, float* upart,
+                                    bool lora, hipStream_t stream) {
   const int K = P->d_in[module], N = P->d_out[module];
   hrg::GemmArgs ga{};
   ga.X = X;
@@ -524,35 +564,6 @@ static lora_status_t batched_apply(lora_pool_s* P, int32_t module, const lora_bf
     ga.perm = nullptr;
     return hrg::launch_prefill(ga, false, -1, stream) == hipSuccess ? LORA_OK : LORA_ERR_HIP;
   }
-  // shrink: a fixed grid walks the plan's (tile, K-split) items; K splits of
-  // at least 1024 (at most kMaxSplits planes), streamed as 256-deep
-  // sub-chunks with the next one's loads in flight.  An item is a short
-  // chain of dependent loads, so up to 1024 blocks (two rounds of resident
-  // blocks) take them one each rather than fewer blocks walking two or more
-  // (MI355X, 4096-deep linear, 1024 tokens over about 105 adapters of ranks
-  // 8-64: 17.6 us with 512 blocks, 15.2 with 1024; with the sub-chunk ring,
-  // splits of 512, 1024, 2048: step 83.5, 83.0, 85.4 us; Llama-3-8B layer
-  // 1.964, 1.954, 1.952 ms)
-  const int kchunk = std::max(1024, round_up(ceil_div(K, hrg::kMaxSplits), 256));
-  const int ksplit = ceil_div(K, kchunk);
-  const int max_items = max_tiles_for(P) * ksplit;
-  const int grid = std::min(max_items, 1024);
-  hrg::ShrinkArgs sa{};
-  sa.X = X;
-  sa.K = K;
-  sa.perm = pl->tab.perm;
-  sa.tile_info = pl->tab.tile_info;
-  sa.counts = pl->tab.counts;
-  sa.pages = P->pages;
-  sa.slot_stride = P->slot_elems;
-  sa.a_off = P->a_off[module];
-  sa.upart = P->upart;
-  sa.split_stride = P->split_stride;
-  sa.u_ld = P->rpad;
-  sa.kchunk = kchunk;
-  sa.nsplit = ksplit;
-  sa.status = P->status;
-  if (hrg::launch_shrink(sa, grid, ksplit, T, stream) != hipSuccess) return LORA_ERR_HIP;
   ga.perm = pl->tab.perm;
   ga.v_hi = P->v_hi;
   ga.v_lo = P->v_lo;
@@ -565,9 +576,9 @@ static lora_status_t batched_apply(lora_pool_s* P, int32_t module, const lora_bf
   ga.pages = P->pages;
   ga.slot_stride = P->slot_elems;
   ga.b_off = P->b_off[module];
-  ga.upart = P->upart;
+  ga.upart = upart;
   ga.split_stride = P->split_stride;
-  ga.nsplit = ksplit;
+  ga.nsplit = ceil_div(K, shrink_kchunk(K));
   ga.seg_scale = pl->tab.seg_scale;
   ga.seg_bscale = pl->tab.seg_bscale;
   ga.small_bscale = pl->tab.small_bscale;
@@ -636,16 +647,28 @@ static lora_status_t apply_impl(lora_pool_t P, int32_t n, const int32_t* modules
     const lora_status_t s2 = run_plan(P, ids, T, pl, stream);
     if (s2 != LORA_OK) return s2;
   }
-  for (int32_t i = 0; i < n; ++i) {
-    const int32_t m = modules[i];
-    const lora_bf16_t* Wi = W ? W[i] : nullptr;
-    if (Wq) {
-      if (hrg::launch_q4_dequant(Wq[i], Wsz[i], P->d_out[m], P->d_in[m], scratch, stream) != hipSuccess)
-        return LORA_ERR_HIP;
-      Wi = scratch;
+  // the linears in runs of up to L: one shrink launch per run (their U
+  // planes side by side in the workspace), then each linear's expand and GEMM
+  const int ksplit = ceil_div(P->d_in[modules[0]], shrink_kchunk(P->d_in[modules[0]]));
+  const int L = lora ? std::max(1, std::min(hrg::shrink_linears(P->rpad), hrg::kMaxSplits / ksplit)) : n;
+  for (int32_t i0 = 0; i0 < n; i0 += L) {
+    const int nl = std::min<int>(L, n - i0);
+    if (lora) {
+      const lora_status_t s1 = batched_shrink(P, nl, modules + i0, X, T, pl, stream);
+      if (s1 != LORA_OK) return s1;
     }
-    const lora_status_t s3 = batched_apply(P, m, X, T, Wi, out[i], pl, lora, stream);
-    if (s3 != LORA_OK) return s3;
+    for (int32_t i = i0; i < i0 + nl; ++i) {
+      const int32_t m = modules[i];
+      const lora_bf16_t* Wi = W ? W[i] : nullptr;
+      if (Wq) {
+        if (hrg::launch_q4_dequant(Wq[i], Wsz[i], P->d_out[m], P->d_in[m], scratch, stream) != hipSuccess)
+          return LORA_ERR_HIP;
+        Wi = scratch;
+      }
+      float* up = P->upart + (size_t)(i - i0) * ksplit * P->split_stride;
+      const lora_status_t s3 = batched_finish(P, m, X, T, Wi, out[i], pl, up, lora, stream);
+      if (s3 != LORA_OK) return s3;
+    }
   }
   return LORA_OK;
 }

@@ -84,16 +84,20 @@ struct PlanArgs {
   PlanTables tab;
 };
 
+// Linears whose shrink one launch computes together (they read the same X):
+// rank blocks of all of them per item, at most 4.
+constexpr int kMaxShrinkLinears = 4;
+
 struct ShrinkArgs {
   const uint16_t* X;      // [T][K]
   int32_t K;
   const int32_t* perm;
   const int4* tile_info;
   const int32_t* counts;
-  const uint16_t* pages;  // A^T page of (slot, module): pages + slot*slot_stride + a_off, [rmax][K]
+  const uint16_t* pages;  // A^T page of (slot, module): pages + slot*slot_stride + a_off[m]
   size_t slot_stride;
-  size_t a_off;
-  float* upart;           // [split][T_cap][u_ld] fp32 partial planes
+  size_t a_off[kMaxShrinkLinears];  // the item's linears (nl of them, one d_in)
+  float* upart;           // [linear][split][T_cap][u_ld] fp32 partial planes (plane m * nsplit + split)
   size_t split_stride;
   int32_t u_ld;
   int32_t kchunk;         // K per split
@@ -216,7 +220,9 @@ int resident_blocks(const void* fn, int threads, size_t lds);
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 // Shrink partial planes, then the split reduction into V (two launches).
-hipError_t launch_shrink(const ShrinkArgs& a, int grid, int ksplit, int T, hipStream_t s);
+// nl linears (1 .. 4 / (rank blocks of the pool), see shrink_linears)
+hipError_t launch_shrink(const ShrinkArgs& a, int nl, int grid, int ksplit, int T, hipStream_t s);
+inline int shrink_linears(int u_ld) { return kMaxShrinkLinears / (u_ld <= 16 ? 1 : u_ld <= 32 ? 2 : 4); }
 // shape < 0 picks the tile shapes from (T, N): one shape for every row, or
 // 256x256 tiles over the first rows (whole 256-row tiles) and 128x128 tiles
 // over the rest, as two launches; 0..3 force 256x256, 256x128, 128x256,

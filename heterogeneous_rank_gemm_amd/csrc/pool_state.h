@@ -35,7 +35,8 @@ struct lora_pool_s {
   float4* id_bscale = nullptr;       // [max_ids] scale of each 16-rank block (chains: per member)
   int32_t* status = nullptr;         // sticky device status
   uint16_t* staging = nullptr;       // one module's A or B as received
-  float* upart = nullptr;            // [kMaxSplits][max_tokens][rpad] shrink partial planes
+  float* upart = nullptr;            // [kMaxSplits][max_tokens][rpad] shrink partial planes (those of a
+                                     // run of linears side by side, linear-major)
   size_t split_stride = 0;
   uint16_t* v_hi = nullptr;          // [max_tokens][rpad] s * U, bf16 high part (sorted rows)
   uint16_t* v_lo = nullptr;          // [max_tokens][rpad] bf16 low part

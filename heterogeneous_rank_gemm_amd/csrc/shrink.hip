@@ -7,7 +7,9 @@
 // segment, so the adapter's A^T page (fragment tiles: one contiguous 1 KB
 // per 16 ranks x 32-deep MFMA step) is streamed once per tile and K-split,
 // 256 deep at a time through two register sets; the 16x16x32 bf16 MFMA does
-// the contraction.
+// the contraction.  Linears that read the same X (q/k/v, gate/up) are shrunk
+// by one launch: an item multiplies the X rows it loads once by the pages of
+// all of them (NL linears of NQ rank blocks, NL * NQ <= 4).
 // Each of the 4 waves covers an interleaved quarter of the K range; the four
 // partial results are summed in a fixed order through LDS (deterministic),
 // and each K-split writes its own fp32 partial plane of U.  The small-segment
@@ -46,9 +48,10 @@ __device__ __forceinline__ void tile_tokens(const ShrinkArgs& a, int4 ti, int (&
 // item), so the A and X loads go out together.  The next item's tile entry
 // (index `next`) is requested into *tn with them and its tokens into tokn
 // once it lands, so neither lookup costs a round of its own.
-template <int NQ>
+template <int NQ, int NL>
 __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64 * kRedLd], int4 ti, int split,
                                             int next, const int (&tok)[4], int4* tn, int (&tokn)[4]) {
+  constexpr int NB = NQ * NL;  // rank blocks of the item: linear j / NQ, block j % NQ
   const int row0 = ti.x, rows = ti.y, slot = ti.z, rank = ti.w;
   const int nq = (rank + 15) / 16;  // 16-wide rank blocks actually computed
   const int nm = (rows + 15) / 16;  // 16-row blocks with at least one row
@@ -56,13 +59,15 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
   const int k0 = split * a.kchunk;
   const int k1 = min(K, k0 + a.kchunk);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const uint16_t* Ap = a.pages + (size_t)slot * a.slot_stride + a.a_off;
+  const uint16_t* Ap = a.pages + (size_t)slot * a.slot_stride;
 
   // the A tiles follow from the tile entry alone: rank block nb's tile of
   // step s is 1 KB at frag_tile(nb, s), this lane's 16 bytes at 16 l
   const int k32 = (K + 31) / 32;
   const int rp = a.u_ld;  // rows of the page in fragment tiles (the pool's rank rounded up to 16)
-  const uint16_t* Al = Ap + (size_t)l * 8;
+  const uint16_t* Al[NL];
+#pragma unroll
+  for (int m = 0; m < NL; ++m) Al[m] = Ap + a.a_off[m] + (size_t)l * 8;
   bool qv[NQ];
 #pragma unroll
   for (int nb = 0; nb < NQ; ++nb) qv[nb] = 16 * nb + (l & 15) < rank;
@@ -86,7 +91,7 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
     rv[mb] = p < rows;
     xrow[mb] = a.X + (size_t)tok[mb] * K;
   }
-  uint4 av[2][2][NQ], xv[2][2][4];
+  uint4 av[2][2][NB], xv[2][2][4];
   auto load = [&](auto bc, int kb) __attribute__((always_inline)) {
     constexpr int b = decltype(bc)::value;
     kb = min(kb, klast);
@@ -94,7 +99,10 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
     for (int st = 0; st < 2; ++st) {
       const int step = min((kb + 128 * st + 32 * w) / 32, k32 - 1);
 #pragma unroll
-      for (int nb = 0; nb < NQ; ++nb) av[b][st][nb] = ld16(Al + frag_tile(nb < nq ? nb : 0, step, rp, K) * 512);
+      for (int j = 0; j < NB; ++j) {
+        const int nb = j % NQ;
+        av[b][st][j] = ld16(Al[j / NQ] + frag_tile(nb < nq ? nb : 0, step, rp, K) * 512);
+      }
     }
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -104,11 +112,11 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
     }
   };
 
-  f32x4 acc[4][NQ];
+  f32x4 acc[4][NB];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < NQ; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NB; ++j) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto mm = [&](auto bc, int kb) __attribute__((always_inline)) {
     constexpr int b = decltype(bc)::value;
 #pragma unroll
@@ -119,9 +127,10 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
         if (mb >= nm) continue;
         const bf16x8 xa = keep_bf(rv[mb] && kv, xv[b][st][mb]);
 #pragma unroll
-        for (int nb = 0; nb < NQ; ++nb) {
+        for (int j = 0; j < NB; ++j) {
+          const int nb = j % NQ;
           if (nb >= nq) continue;
-          acc[mb][nb] = mfma16(xa, keep_bf(qv[nb] && kv, av[b][st][nb]), acc[mb][nb]);
+          acc[mb][j] = mfma16(xa, keep_bf(qv[nb] && kv, av[b][st][j]), acc[mb][j]);
         }
       }
     }
@@ -141,36 +150,41 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
     if (i + 2 >= nsub) break;
   }
 
-  // cross-wave reduction in fixed wave order
+  // cross-wave reduction in fixed wave order (column 16 j + q of the
+  // buffer: rank 16 (j % NQ) + q of linear j / NQ)
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     if (mb >= nm) continue;
 #pragma unroll
-    for (int nb = 0; nb < NQ; ++nb) {
-      if (nb >= nq) continue;
+    for (int j = 0; j < NB; ++j) {
+      if (j % NQ >= nq) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * mb + 4 * (l >> 4) + i;
-        const int q = 16 * nb + (l & 15);
-        red[w][r * kRedLd + q] = acc[mb][nb][i];
+        const int q = 16 * j + (l & 15);
+        red[w][r * kRedLd + q] = acc[mb][j][i];
       }
     }
   }
   __syncthreads();
   const int width = nq * 16;
-  float* up = a.upart + (size_t)split * a.split_stride + (size_t)row0 * a.u_ld;
-  for (int idx = threadIdx.x; idx < rows * width; idx += kShrinkThreads) {
-    const int r = idx / width, q = idx % width;
-    const float v = ((red[0][r * kRedLd + q] + red[1][r * kRedLd + q]) + red[2][r * kRedLd + q]) +
-                    red[3][r * kRedLd + q];
-    up[(size_t)r * a.u_ld + q] = v;
+#pragma unroll
+  for (int m = 0; m < NL; ++m) {
+    float* up = a.upart + (size_t)(m * a.nsplit + split) * a.split_stride + (size_t)row0 * a.u_ld;
+    for (int idx = threadIdx.x; idx < rows * width; idx += kShrinkThreads) {
+      const int r = idx / width, q = idx % width;
+      const int c = 16 * NQ * m + q;
+      const float v = ((red[0][r * kRedLd + c] + red[1][r * kRedLd + c]) + red[2][r * kRedLd + c]) +
+                      red[3][r * kRedLd + c];
+      up[(size_t)r * a.u_ld + q] = v;
+    }
   }
 
 }
 
 // A fixed grid walks the (tile, split) items of the plan's tile list; the
 // split count is fixed by K on the host, the tile count only on the device.
-template <int NQ>
+template <int NQ, int NL>
 __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
   __shared__ float red[4][64 * kRedLd];
   // the first item's tile entry is requested with the status and the count
@@ -187,7 +201,7 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
     int4 tn;
     int tokn[4];
     __syncthreads();  // the previous item is done with red
-    shrink_item<NQ>(a, red, ti, item % a.nsplit, min(item + (int)gridDim.x, nitems - 1) / a.nsplit, tok, &tn,
+    shrink_item<NQ, NL>(a, red, ti, item % a.nsplit, min(item + (int)gridDim.x, nitems - 1) / a.nsplit, tok, &tn,
                     tokn);
     ti = tn;
 #pragma unroll
@@ -195,15 +209,25 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
   }
 }
 
-hipError_t launch_shrink(const ShrinkArgs& a, int grid, int ksplit, int T, hipStream_t s) {
+hipError_t launch_shrink(const ShrinkArgs& a, int nl, int grid, int ksplit, int T, hipStream_t s) {
   if (grid <= 0 || ksplit <= 0 || T <= 0) return hipSuccess;
   const int nq = a.u_ld / 16;
-  if (nq <= 1)
-    hipLaunchKernelGGL(shrink_kernel<1>, dim3(grid), dim3(kShrinkThreads), 0, s, a);
-  else if (nq == 2)
-    hipLaunchKernelGGL(shrink_kernel<2>, dim3(grid), dim3(kShrinkThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL(shrink_kernel<4>, dim3(grid), dim3(kShrinkThreads), 0, s, a);
+  if (nl < 1 || nl > shrink_linears(a.u_ld)) return hipErrorInvalidValue;
+  if (nq <= 1) {
+    switch (nl) {
+      case 1: hipLaunchKernelGGL((shrink_kernel<1, 1>), dim3(grid), dim3(kShrinkThreads), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((shrink_kernel<1, 2>), dim3(grid), dim3(kShrinkThreads), 0, s, a); break;
+      case 3: hipLaunchKernelGGL((shrink_kernel<1, 3>), dim3(grid), dim3(kShrinkThreads), 0, s, a); break;
+      default: hipLaunchKernelGGL((shrink_kernel<1, 4>), dim3(grid), dim3(kShrinkThreads), 0, s, a); break;
+    }
+  } else if (nq == 2) {
+    if (nl == 1)
+      hipLaunchKernelGGL((shrink_kernel<2, 1>), dim3(grid), dim3(kShrinkThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((shrink_kernel<2, 2>), dim3(grid), dim3(kShrinkThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((shrink_kernel<4, 1>), dim3(grid), dim3(kShrinkThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 
