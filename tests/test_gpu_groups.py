@@ -281,19 +281,20 @@ def test_packed_rejects_batched_sizes():
     pool.close()
 
 
+@pytest.mark.parametrize("T", [64, 17, 1])
 @pytest.mark.parametrize("K", [2048, 3000, 5000, 11008])
-def test_deep_group_equals_single_linears(K):
+def test_deep_group_equals_single_linears(K, T):
     """Deep K (2 to 11 chunks of 1024, ragged tails): a group of eight
     linears fills the chip with blocks that each take two chunks, while each
     linear alone is small enough to take one chunk per block.  Both add the
     chunk sums in pairs, so every output must be the same bits; both must
     meet the oracle's bar."""
     from heterogeneous_rank_gemm_amd import LoraPool
-    T, n_ad, r, n_lin, N = 64, 64, 16, 8, 1024
-    pool = LoraPool(n_ad, n_ad, r, [K] * n_lin, [N] * n_lin, T)
-    reg = oracle.Registry(n_ad, n_ad, r, [K] * n_lin, [N] * n_lin, T)
-    gen = torch.Generator().manual_seed(K)
-    ids_np = np.random.default_rng(K).integers(-1, n_ad, size=T).astype(np.int32)
+    n_ad, r, n_lin, N = 64, 16, 8, 1024
+    pool = LoraPool(n_ad, n_ad, r, [K] * n_lin, [N] * n_lin, 64)
+    reg = oracle.Registry(n_ad, n_ad, r, [K] * n_lin, [N] * n_lin, 64)
+    gen = torch.Generator().manual_seed(K + T)
+    ids_np = np.random.default_rng(K + T).integers(-1, n_ad, size=T).astype(np.int32)
     for i in sorted(set(ids_np[ids_np >= 0].tolist())):
         A = [(torch.randn((K, r), generator=gen) * 0.02).to(torch.bfloat16) for _ in range(n_lin)]
         B = [(torch.randn((r, N), generator=gen) * 0.02).to(torch.bfloat16) for _ in range(n_lin)]
