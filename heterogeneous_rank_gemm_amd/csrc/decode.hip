@@ -249,10 +249,11 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
       sr.istep = 64;
     }
   };
-  // Register buffers of two halves: bf16 rows (W or A units) take 16 loads of
-  // 16 bytes per lane per half; INT4 W units 4 of codes and 1 of group words.
+  // Register buffers of the INT4 walk, two halves each: its bf16 A units
+  // take 16 loads of 16 bytes per lane per half, its INT4 W units 4 of codes
+  // and 1 of group words.  (The bf16 walk uses the quarter ring below.)
   constexpr int kQL = 5;
-  uint4 buf[2][kHS];            // bf16 halves (every unit, or the A units with WQ)
+  uint4 buf[2][WQ ? kHS : 1];   // bf16 halves (the A units of the INT4 walk)
   uint4 qbuf[2][WQ ? kQL : 1];  // INT4 W halves (WQ only)
   auto load_b = [&](uint4 (&b)[kHS], const UnitSrc& sr, auto hc) __attribute__((always_inline)) {
     constexpr int H = decltype(hc)::value;
@@ -286,8 +287,9 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
   const auto H0 = std::integral_constant<int, 0>{};
   const auto H1 = std::integral_constant<int, 1>{};
 
-  // ---- the first half of the wave's first W unit goes out after the X copy;
-  // the barrier waits for the copy (and the ids before it), not for it ----
+  // ---- the start of the wave's first W unit (three quarters, or an INT4
+  // half) goes out after the X copy; the barrier waits for the copy (and the
+  // ids before it), not for it ----
   UnitSrc csrc;
   UnitDst cdst;
   const auto Q0 = std::integral_constant<int, 0>{};
@@ -540,9 +542,11 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
   };
   auto store = [&](const UnitDst& d) __attribute__((always_inline)) { store_to(d, acc); };
 
-  // Unit j's first half is in flight when its step starts; its second half
-  // is requested before its first half's MFMAs, the next unit's first half
-  // before its second half's.  Every load is issued unconditionally (past the
+  // bf16: unit j's first three quarters are in flight when its step starts;
+  // each quarter's MFMAs run while the next unit's corresponding quarter is
+  // requested.  INT4: unit j's first half is in flight, its second half is
+  // requested before the first half's MFMAs, the next unit's first half
+  // before the second half's.  Every load is issued unconditionally (past the
   // wave's last unit, rows of no bytes), so the compiler counts each wait
   // exactly.  W units first (INT4 or bf16), then the A units (bf16 pages).
   if constexpr (CPB == 2) {
@@ -1001,9 +1005,9 @@ static Shape decode_shape(const DecodeArgs& a, int cpb, int units) {
   const int KP = ceil_div(a.KS, cpb);
   Shape best{4, 1, 1};
   double best_eff = -1.0;
-  // (at most six waves: with two halves of 16 KB in flight per wave, more
-  // outstanding reads per compute unit lower the stream rate -- measured
-  // 6.0 TB/s at 128 KB per compute unit, 5.4 at 256 KB)
+  // (at most six waves: with 24 KB in flight per wave, more outstanding
+  // reads per compute unit lower the stream rate -- measured 6.0 TB/s at
+  // 128 KB per compute unit, 5.4 at 256 KB)
   for (int wpb : {4, 5, 6}) {
     // the INT4 walk holds both kinds of buffers, the two-chunk walk every
     // unit's sums: one wave per SIMD
