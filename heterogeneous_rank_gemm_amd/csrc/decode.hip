@@ -748,10 +748,15 @@ __global__ __launch_bounds__(64 * WPB) void decode_main(DecodeArgs a) {
 // thread's B rows (its token's id comes by a scalar load).  Round 2: every
 // token's {slot, rank, scale} (each block checks the whole batch, strict
 // mode).  Otherwise the B rows need the slot and come in a third round.
+// RP: the pool's rank rounded up to 16, 32 or 64 (the block's V is 16 x RP).
+// A rank-16 pool's combine asks for six waves per SIMD (74 registers, no
+// spills), so that a large group's blocks (gate/up: 1376) are all resident at
+// once instead of a quarter of them starting a generation late.
 constexpr int kCombThreads = 256;
-constexpr int kVPer = 16 * kMaxRank / kCombThreads;  // V elements per thread
 
-__global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
+template <int RP>
+__global__ __launch_bounds__(kCombThreads, RP == 16 ? 6 : 1) void decode_combine(DecodeArgs a) {
+  constexpr int kVPer = 16 * RP / kCombThreads;  // V elements per thread
   __shared__ float vsh[16][kMaxRank + 1];
   __shared__ int4 s_info[16];  // the block's tokens: {slot (-1: none), rank, scale bits, 0}
   __shared__ float4 s_bsc[16];  // the block's tokens: scale of each 16-rank block
@@ -814,7 +819,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < kVPer; ++e) {
       const int idx = tid + kCombThreads * e;
-      const int r = idx / kMaxRank, q = idx % kMaxRank;
+      const int r = idx / RP, q = idx % RP;
       uq[e] = q < a.u_ld;
       up[e] = a.upart + ((size_t)mg * 64 + min(t0 + r, T - 1)) * a.u_ld + (uq[e] ? q : 0);
       u[e] = 0.f;
@@ -881,7 +886,7 @@ __global__ __launch_bounds__(kCombThreads) void decode_combine(DecodeArgs a) {
 #pragma unroll
     for (int e = 0; e < kVPer; ++e) {
       const int idx = tid + kCombThreads * e;
-      const int r = idx / kMaxRank, q = idx % kMaxRank;
+      const int r = idx / RP, q = idx % RP;
       const int4 inf = s_info[r];
       const bool on = t0 + r < T && inf.x >= 0 && q < inf.y;
       vsh[r][q] = on ? pick4(s_bsc[r], q >> 4) * u[e] : 0.f;
@@ -1055,7 +1060,13 @@ hipError_t launch_decode(const DecodeArgs& args, int items_cap, hipStream_t s) {
   else
     e = launch_main<false, 1>(a, sh.wpb, grid, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_combine, dim3(a.ct0[kMaxGroup], (a.T + 15) / 16), dim3(kCombThreads), 0, s, a);
+  const dim3 cgrid(a.ct0[kMaxGroup], (a.T + 15) / 16);
+  if (a.u_ld <= 16)
+    hipLaunchKernelGGL(decode_combine<16>, cgrid, dim3(kCombThreads), 0, s, a);
+  else if (a.u_ld <= 32)
+    hipLaunchKernelGGL(decode_combine<32>, cgrid, dim3(kCombThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(decode_combine<64>, cgrid, dim3(kCombThreads), 0, s, a);
   return hipGetLastError();
 }
 
