@@ -224,9 +224,10 @@ hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_shrink(const ShrinkArgs& a, int nl, int grid, int ksplit, int T, hipStream_t s);
 inline int shrink_linears(int u_ld) { return kMaxShrinkLinears / (u_ld <= 16 ? 1 : u_ld <= 32 ? 2 : 4); }
 // shape < 0 picks the tile shapes from (T, N): one shape for every row, or
-// 256x256 tiles over the first rows (whole 256-row tiles) and 128x128 tiles
-// over the rest, as two launches; 0..3 force 256x256, 256x128, 128x256,
-// 128x128 (tokens x columns) for every row.  Every shape gives the same bits.
+// 256x256 tiles over the first rows (whole 256-row tiles) and 128x128 or
+// 64x64 tiles over the rest, as two launches; 0..4 force 256x256, 256x128,
+// 128x256, 128x128, 64x64 (tokens x columns) for every row.  Every shape
+// gives the same bits.
 hipError_t launch_prefill(const GemmArgs& a, bool lora, int shape, hipStream_t s);
 // The E rows of the small segments (one launch, before the GEMM).
 hipError_t launch_expand_small(const GemmArgs& a, hipStream_t s);

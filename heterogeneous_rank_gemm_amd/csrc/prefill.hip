@@ -782,23 +782,37 @@ static hipError_t launch_cfg(const GemmArgs& a, bool lora, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Relative time of one tile (per unit of K) for each shape, measured on
-// MI355X; the launcher picks the shapes with the least estimated time,
-// counting whole rounds of 256 tiles (one tile per compute unit).
+// Relative time of a round of tiles (per unit of K) for each shape, measured
+// on MI355X; the launcher picks the shapes with the least estimated time,
+// counting whole rounds.  The shapes up to 128x128 fill the LDS with their
+// stages: one tile per compute unit, a round of 256.  A 64x64 tile (64 KB of
+// LDS) runs two per compute unit: a round of 512 costs 0.26, one with at
+// most one tile per unit 0.16 (measured on the Llama-3-8B layer: 256 tiles
+// over the last 256 rows of a 4096-column linear in 20 us, 1088 tiles over
+// all 4352 rows of a 1024-column one in 71 us).
 struct Shape {
   int bm, bn;
-  double cost;
+  double cost;       // a full round
+  double cost_half;  // a last round with at most one tile per compute unit
+  int per_round;
 };
-static const Shape kShapes[] = {{256, 256, 1.00}, {256, 128, 0.56}, {128, 256, 0.56}, {128, 128, 0.32}};
+constexpr int kNumShapes = 5;
+static const Shape kShapes[kNumShapes] = {{256, 256, 1.00, 1.00, 256},
+                                          {256, 128, 0.56, 0.56, 256},
+                                          {128, 256, 0.56, 0.56, 256},
+                                          {128, 128, 0.32, 0.32, 256},
+                                          {64, 64, 0.26, 0.16, 512}};
 static double shape_time(int i, int rows, int N) {
-  const long tiles = (long)((rows + kShapes[i].bm - 1) / kShapes[i].bm) * ((N + kShapes[i].bn - 1) / kShapes[i].bn);
-  return (double)((tiles + 255) / 256) * kShapes[i].cost;
+  const Shape& sh = kShapes[i];
+  const long tiles = (long)((rows + sh.bm - 1) / sh.bm) * ((N + sh.bn - 1) / sh.bn);
+  const long full = tiles / sh.per_round, rem = tiles % sh.per_round;
+  return (double)full * sh.cost + (rem == 0 ? 0.0 : rem <= 256 ? sh.cost_half : sh.cost);
 }
 
 int prefill_choose(int T, int N) {
   int best = 0;
   double best_t = 1e30;
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kNumShapes; ++i) {
     const double t = shape_time(i, T, N);
     if (t < best_t * 0.999) {
       best_t = t;
@@ -813,7 +827,8 @@ static hipError_t launch_shape(const GemmArgs& a, bool lora, int shape, hipStrea
     case 0: return launch_cfg<256, 256>(a, lora, s);
     case 1: return launch_cfg<256, 128>(a, lora, s);
     case 2: return launch_cfg<128, 256>(a, lora, s);
-    default: return launch_cfg<128, 128>(a, lora, s);
+    case 3: return launch_cfg<128, 128>(a, lora, s);
+    default: return launch_cfg<64, 64>(a, lora, s);
   }
 }
 
@@ -824,19 +839,23 @@ hipError_t launch_prefill(const GemmArgs& args, bool lora, int shape, hipStream_
   a.row1 = a.T;
   if (shape >= 0) return launch_shape(a, lora, shape, s);
   // one shape for every row, or 256x256 tiles over the first rows (a whole
-  // number of 256-row tiles) and 128x128 tiles over the rest: a second,
-  // short round of small tiles instead of a mostly empty round of big ones
+  // number of 256-row tiles) and small tiles (128x128 or 64x64) over the
+  // rest: a second, short round of small tiles instead of a mostly empty
+  // round of big ones
   const int one = prefill_choose(a.T, a.N);
   const double t_one = shape_time(one, a.T, a.N);
   // (among equal estimates the most rows in big tiles: the small tiles then
   // share the memory with fewer others)
-  int tm = 0;
+  int tm = 0, tail = 3;
   double t_two = 1e30;
   for (int r = 256; r < a.T; r += 256) {
-    const double t = shape_time(0, r, a.N) + shape_time(3, a.T - r, a.N) + 0.03;
-    if (t <= t_two * 1.001) {
-      t_two = std::min(t, t_two);
-      tm = r;
+    for (int sh : {3, 4}) {
+      const double t = shape_time(0, r, a.N) + shape_time(sh, a.T - r, a.N) + 0.03;
+      if (t <= t_two * 1.001) {
+        t_two = std::min(t, t_two);
+        tm = r;
+        tail = sh;
+      }
     }
   }
   if (tm > 0) {
@@ -846,7 +865,7 @@ hipError_t launch_prefill(const GemmArgs& args, bool lora, int shape, hipStream_
       if (e != hipSuccess) return e;
       a.row0 = tm;
       a.row1 = a.T;
-      return launch_shape(a, lora, 3, s);
+      return launch_shape(a, lora, tail, s);
     }
   }
   return launch_shape(a, lora, one, s);
