@@ -87,13 +87,35 @@ __device__ __forceinline__ float pick4(float4 v, int b) {
 
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int l = __lane_id();
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int u = __shfl_up(v, d, 64);
-    if (l >= d) v += u;
-  }
+  // DPP lane moves (register to register, no LDS round trip): shifts by
+  // 1, 2, 4, 8 within each row of 16 lanes (lanes shifted in read zero),
+  // then the last lane of row 0 to row 1 and of row 2 to row 3, then lane 31
+  // to rows 2 and 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return v;
+}
+
+// counter[key] += 1 for every lane with `valid`, as one LDS atomic per run of
+// equal keys in consecutive valid lanes (a batch whose requests each hold many
+// tokens has long runs; 64 lanes adding to one address serialise).  Every
+// lane of the wave must call it.
+__device__ __forceinline__ void count_runs(int* counter, int key, bool valid) {
+  const int lane = __lane_id();
+  const uint64_t vmask = __ballot(valid);
+  const int left = __shfl_up(key, 1, 64);
+  const bool joins = lane > 0 && ((vmask >> (lane - 1)) & 1) && left == key;
+  const uint64_t heads = __ballot(valid && !joins);
+  const bool last = lane == 63 || !((vmask >> (lane + 1)) & 1) || ((heads >> (lane + 1)) & 1);
+  if (valid && last) {
+    const uint64_t upto = lane == 63 ? ~0ull : ((2ull << lane) - 1);
+    const int first = 63 - __builtin_clzll(heads & upto);
+    atomicAdd(&counter[key], lane - first + 1);
+  }
 }
 
 }  // namespace hrg

@@ -79,16 +79,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
   for (int b = tid; b < nb; b += kPlanThreads) start[b] = 0;
   __syncthreads();
 
-  // 1. validate every id and count tokens per bucket
-  for (int t = tid; t < T; t += kPlanThreads) {
-    const int id = a.ids[t];
-    if (id < -1 || id >= a.max_ids) {
-      atomicMax(&s_err, kStatusIdRange);
-    } else {
+  // 1. validate every id and count tokens per bucket (a wave takes 64
+  // consecutive tokens at a time, every lane through every round)
+  for (int base = tid - lane; base < T; base += kPlanThreads) {
+    const int t = base + lane;
+    const int id = t < T ? a.ids[t] : -1;
+    const bool ok = t < T && id >= -1 && id < a.max_ids;
+    if (t < T && !ok) atomicMax(&s_err, kStatusIdRange);
+    if (ok) {
       if (id >= 0 && a.id_info[id].x < 0) atomicMax(&s_err, kStatusNotLoaded);
-      atomicAdd(&start[id + 1], 1);
       if (t < kStageTok) s_bucket[t] = (uint16_t)(id + 1);  // the first placement block, staged now
     }
+    count_runs(start, id + 1, ok);
   }
   if (st != 0) return;
   __syncthreads();
@@ -211,7 +213,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(PlanArgs a) {
     if (PW > 1) {
       if (wave < PW) {
         // counts only: the order of the LDS increments does not matter
-        for (int t = t0 + lane; t < t1; t += 64) atomicAdd(&mycur[s_bucket[t - blk0]], 1);
+        for (int t = t0 + lane; t - lane < t1; t += 64) {
+          const bool in = t < t1;
+          count_runs(mycur, in ? (int)s_bucket[t - blk0] : 0, in);
+        }
       }
       __syncthreads();
       for (int b = tid; b < nb; b += kPlanThreads) {
