@@ -964,11 +964,19 @@ __global__ __launch_bounds__(kCombThreads, RP == 16 ? 6 : 1) void decode_combine
 
 template <bool WQ, int CPB>
 hipError_t launch_main(const DecodeArgs& a, int wpb, int grid, hipStream_t s) {
-  if constexpr (CPB == 2 || WQ) {
-    // (the units' sums of two chunks, or both kinds of register buffers:
-    // one wave per SIMD)
+  if constexpr (WQ) {
+    // the INT4 walk: one or two waves per SIMD (its registers fit in half
+    // of a SIMD's file)
+    if (wpb == 8)
+      hipLaunchKernelGGL((decode_main<8, true, 1>), dim3(grid), dim3(512), 0, s, a);
+    else if (wpb == 4)
+      hipLaunchKernelGGL((decode_main<4, true, 1>), dim3(grid), dim3(256), 0, s, a);
+    else
+      return hipErrorInvalidValue;
+  } else if constexpr (CPB == 2) {
+    // (the units' sums of two chunks: one wave per SIMD)
     if (wpb != 4) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((decode_main<4, WQ, CPB>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_main<4, false, 2>), dim3(grid), dim3(256), 0, s, a);
   } else {
     switch (wpb) {
       case 4: hipLaunchKernelGGL((decode_main<4, WQ, 1>), dim3(grid), dim3(256), 0, s, a); break;
@@ -986,7 +994,8 @@ static int resident_of(bool wq, int cpb, int wpb) {
   if (cpb == 2) {
     fn = reinterpret_cast<const void*>(&decode_main<4, false, 2>);
   } else if (wq) {
-    fn = reinterpret_cast<const void*>(&decode_main<4, true, 1>);
+    fn = wpb == 8 ? reinterpret_cast<const void*>(&decode_main<8, true, 1>)
+                  : reinterpret_cast<const void*>(&decode_main<4, true, 1>);
   } else {
     fn = wpb == 4 ? reinterpret_cast<const void*>(&decode_main<4, false, 1>)
                   : wpb == 5 ? reinterpret_cast<const void*>(&decode_main<5, false, 1>)
@@ -1013,16 +1022,21 @@ static Shape decode_shape(const DecodeArgs& a, int cpb, int units) {
   // (at most six waves: with 24 KB in flight per wave, more outstanding
   // reads per compute unit lower the stream rate -- measured 6.0 TB/s at
   // 128 KB per compute unit, 5.4 at 256 KB)
-  for (int wpb : {4, 5, 6}) {
-    // the INT4 walk holds both kinds of buffers, the two-chunk walk every
-    // unit's sums: one wave per SIMD
-    if ((a.wq || cpb == 2) && wpb != 4) continue;
+  for (int wpb : {4, 5, 6, 8}) {
+    // the two-chunk walk holds every unit's sums: one wave per SIMD; the
+    // INT4 walk runs one or two per SIMD (eight waves per block), the bf16
+    // one-chunk walk four to six waves per block
+    if (cpb == 2 && wpb != 4) continue;
+    if (a.wq ? (wpb != 4 && wpb != 8) : wpb == 8) continue;
     const int resident = resident_of(a.wq != 0, cpb, wpb);
     int nbc = std::max(1, std::min(resident / KP, ceil_div(units, wpb)));
     if (cpb == 2) nbc = std::max(nbc, ceil_div(units, wpb * kMaxUnits));
     const int mx = ceil_div(units, nbc * wpb);
     const double eff = (double)units / ((double)nbc * wpb * mx);
-    if (eff > best_eff + 1e-9) {
+    // (the INT4 walk is bound by each SIMD's issue, not by the bytes: two
+    // waves per SIMD hide each other's waits, worth some idle waves)
+    const bool pair_waves = a.wq && wpb == 8 && eff >= best_eff - 0.25;
+    if (eff > best_eff + 1e-9 || pair_waves) {
       best_eff = eff;
       best = Shape{wpb, nbc, resident};
     }
