@@ -170,6 +170,9 @@ RAGGED = [
     (257, 264, 1160, (4, 64, 17), 64, -1),
     (333, 4104, 136, (16,), 16, 0),
     (9000, 72, 136, (16, 5, 64), 64, -1),  # above one 8192-token placement block
+    # 15 rows of 256x256 tiles, then 356 rows (a ragged 64-row tile last) of
+    # 64x64 tiles in a second launch; rank-64 pages, ragged K and columns
+    (4196, 264, 4104, (8, 16, 32, 64), 64, -1),
 ]
 
 
