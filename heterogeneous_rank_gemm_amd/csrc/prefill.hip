@@ -49,11 +49,15 @@ __device__ __forceinline__ bf16x8 masked(bool keep, uint4 v) {
 }
 
 // XCD-aware tile order: workgroup b runs on XCD (b mod 8); each XCD gets a
-// contiguous range of logical tiles, walked in groups of 8 token-tiles so that
-// neighbours share X and W rows in that XCD's L2.
+// contiguous range of logical tiles, walked in groups of GM token-tiles so
+// that neighbours share X and W rows in that XCD's L2.  (256-row tiles: 4;
+// the Llama-3-8B layer's base GEMMs 1685 -> 1658 us against groups of 8, 1745
+// with 1, 1683 with 2, 1673 with 3, 1656 with 6; 128x128 tiles of the S-LoRA
+// pool: 8 and 4 alike.)
+template <int GM>
 __device__ __forceinline__ void tile_coords(int b, int nblocks, int tiles_m, int tiles_n, int& tm,
                                             int& tn) {
-  constexpr int kXcd = 8, kGroupM = 8;
+  constexpr int kXcd = 8, kGroupM = GM;
   const int xcd = b % kXcd, idx = b / kXcd;
   const int q = nblocks / kXcd, r = nblocks % kXcd;
   const int logical = xcd * q + min(xcd, r) + idx;
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
   // multiple of BM unless row1 = T)
   const int tiles_m = (a.row1 - a.row0 + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  tile_coords<BM >= 256 ? 4 : 8>(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int m0 = a.row0 + tm * BM, n0 = tn * BN;
   const int l = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
