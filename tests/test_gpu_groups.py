@@ -323,3 +323,49 @@ def test_deep_group_equals_single_linears(K, T):
         mx, rl1, _ = oracle.parity_metrics(outs[m].cpu(), oracle.lora_linear(reg, m, X, ids_np, W[m]))
         assert mx <= oracle.MAX_REL_TOL and rl1 <= oracle.RELL1_TOL, (m, mx, rl1)
     pool.close()
+
+
+N_RANDOM_GROUPS = int(__import__("os").environ.get("HRG_GROUP_RANDOM_CASES", 12))
+
+
+@pytest.mark.parametrize("k", range(N_RANDOM_GROUPS))
+def test_random_groups_equal_single_linears(k):
+    """Seeded random groups: 1 to 8 linears of one d_in (any multiple of 8)
+    in random order, T on both paths, pool ranks up to 64.  Every output must
+    equal its single call bit for bit and meet the oracle's bar.
+    HRG_GROUP_RANDOM_CASES scales the count (400 cases have passed)."""
+    from heterogeneous_rank_gemm_amd import LoraPool
+    g = np.random.default_rng(670000 + k)
+    T = int(g.choice([int(g.integers(1, 65)), int(g.integers(65, 900))]))
+    K, nl = int(8 * g.integers(1, 400)), int(g.integers(1, 9))
+    d_outs = [int(8 * g.integers(1, 500)) for _ in range(nl)]
+    max_rank, n = int(g.choice([1, 8, 16, 24, 48, 64])), int(g.integers(1, 10))
+    ranks = [int(g.integers(1, max_rank + 1)) for _ in range(n)]
+    print(f"[group random {k}] T={T} K={K} d_outs={d_outs} max_rank={max_rank} ranks={ranks}", flush=True)
+    pool = LoraPool(n, n, max_rank, [K] * nl, d_outs, T)
+    reg = oracle.Registry(n, n, max_rank, [K] * nl, d_outs, T)
+    gen = torch.Generator().manual_seed(k)
+    for i, r in enumerate(ranks):
+        A = [(torch.randn((K, r), generator=gen) * 0.02).to(torch.bfloat16) for _ in d_outs]
+        B = [(torch.randn((r, d), generator=gen) * 0.02).to(torch.bfloat16) for d in d_outs]
+        pool.load_adapter(i, r, 2.0 * r, [a.cuda() for a in A], [b.cuda() for b in B])
+        reg.load(i, r, 2.0 * r, A, B)
+    ids_np = g.integers(-1, n, T).astype(np.int32)
+    ids = torch.as_tensor(ids_np, device="cuda")
+    X = torch.randn((T, K), generator=gen).to(torch.bfloat16)
+    Xd = X.cuda()
+    W = [(torch.randn((d, K), generator=gen) * 0.02).to(torch.bfloat16) for d in d_outs]
+    Wd = [w.cuda() for w in W]
+    group = [int(m) for m in g.permutation(nl)]
+    outs = [torch.empty((T, d_outs[m]), dtype=torch.bfloat16, device="cuda") for m in group]
+    pool.apply_group(group, Xd, ids, [Wd[m] for m in group], outs)
+    torch.cuda.synchronize()
+    assert pool.status() == "OK"
+    for j, m in enumerate(group):
+        single = torch.empty_like(outs[j])
+        pool.apply(m, Xd, ids, Wd[m], single)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[j], single), f"linear {m}: group differs from lora_apply"
+        mx, rl1, _ = oracle.parity_metrics(outs[j].cpu(), oracle.lora_linear(reg, m, X, ids_np, W[m]))
+        assert mx <= oracle.MAX_REL_TOL and rl1 <= oracle.RELL1_TOL, (m, mx, rl1)
+    pool.close()

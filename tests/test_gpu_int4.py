@@ -158,3 +158,54 @@ def test_int4_group_equals_single_linears(T, K):
         mx, rl1, _ = oracle.parity_metrics(g[m].cpu(), ref)
         assert mx <= oracle.MAX_REL_TOL and rl1 <= oracle.RELL1_TOL, (m, mx, rl1)
     pool.close()
+
+
+N_RANDOM = int(__import__("os").environ.get("HRG_INT4_RANDOM_CASES", 12))
+
+
+@pytest.mark.parametrize("k", range(N_RANDOM))
+def test_int4_random_shapes(k):
+    """Seeded random shapes on both paths (K any multiple of 128, N any
+    multiple of 8, pool ranks up to 64, zero points over 0..15): the oracle's
+    values, the bf16 call's bits on the dequantized weight, id -1 rows equal
+    to the base-only call.  HRG_INT4_RANDOM_CASES scales the count (300
+    cases have passed)."""
+    import heterogeneous_rank_gemm_amd as hrg
+    from heterogeneous_rank_gemm_amd import LoraPool
+    g = np.random.default_rng(660000 + k)
+    T = int(g.choice([int(g.integers(1, 65)), int(g.integers(65, 1200))]))
+    K, N = int(128 * g.integers(1, 40)), int(8 * g.integers(1, 700))
+    max_rank, n = int(g.choice([4, 16, 32, 64])), int(g.integers(1, 8))
+    ranks = [int(g.integers(1, max_rank + 1)) for _ in range(n)]
+    print(f"[int4 random {k}] T={T} K={K} N={N} max_rank={max_rank} ranks={ranks}", flush=True)
+    q, z = g.integers(0, 16, (N, K)), g.integers(0, 16, (N, K // 128))
+    s = torch.as_tensor(np.abs(g.normal(0.0045, 0.002, (N, K // 128))).astype(np.float32)).to(torch.bfloat16)
+    Wq, Wsz = hrg.lora_q4_pack(q, z, s)
+    Wq_d, Wsz_d = torch.as_tensor(Wq.view(np.int32)).cuda(), torch.as_tensor(Wsz.view(np.int32)).cuda()
+    Wdeq = oracle.dequant_q4(q, z, s)
+    Wdeq_bf = torch.as_tensor(Wdeq.astype(np.float32)).to(torch.bfloat16)
+    pool, reg = LoraPool(n, n, max_rank, [K], [N], T), oracle.Registry(n, n, max_rank, [K], [N], T)
+    gen = torch.Generator().manual_seed(k)
+    for i, r in enumerate(ranks):
+        A = (torch.randn((K, r), generator=gen) * 0.02).to(torch.bfloat16)
+        B = (torch.randn((r, N), generator=gen) * 0.02).to(torch.bfloat16)
+        pool.load_adapter(i, r, 2.0 * r, [A.cuda()], [B.cuda()])
+        reg.load(i, r, 2.0 * r, [A], [B])
+    ids_np = g.integers(-1, n, T).astype(np.int32)
+    ids = torch.as_tensor(ids_np, device="cuda")
+    X = torch.randn((T, K), generator=gen).to(torch.bfloat16)
+    Xd = X.cuda()
+    scratch = torch.empty((N, K), dtype=torch.bfloat16, device="cuda") if T > 64 else None
+    out = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+    out_bf, base = torch.empty_like(out), torch.empty_like(out)
+    pool.apply_q4(0, Xd, ids, Wq_d, Wsz_d, out, W_scratch=scratch)
+    pool.base_apply_q4(0, Xd, Wq_d, Wsz_d, base, W_scratch=scratch)
+    pool.apply(0, Xd, ids, Wdeq_bf.cuda(), out_bf)
+    torch.cuda.synchronize()
+    assert pool.status() == "OK"
+    mx, rl1, _ = oracle.parity_metrics(out.cpu(), oracle.lora_linear(reg, 0, X, ids_np, Wdeq))
+    assert mx <= oracle.MAX_REL_TOL and rl1 <= oracle.RELL1_TOL, (mx, rl1)
+    assert torch.equal(out, out_bf)
+    m = torch.as_tensor(ids_np < 0, device="cuda")
+    assert torch.equal(out[m], base[m])
+    pool.close()
