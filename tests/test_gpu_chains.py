@@ -129,3 +129,50 @@ def test_chain_block_layout_limit():
                 pool.load_chain(5, [0, 1, 2])
             assert e.value.status == "RANK"
         pool.close()
+
+
+@pytest.mark.parametrize("k", range(int(__import__("os").environ.get("HRG_CHAIN_RANDOM_CASES", 8))))
+def test_random_chains_match_oracle(k):
+    """Seeded random chains (1 to 3 members of ranks up to 16, pool ranks 32
+    to 64, one or two linears, both paths) within the library's page layout
+    (each member but the last takes whole 16-rank blocks): the oracle's
+    values for a batch over adapters, chains and id -1.
+    HRG_CHAIN_RANDOM_CASES scales the count (300 have passed)."""
+    from heterogeneous_rank_gemm_amd import LoraPool
+    g = np.random.default_rng(700000 + k)
+    T = int(g.choice([int(g.integers(1, 65)), int(g.integers(65, 700))]))
+    K = int(8 * g.integers(2, 300))
+    d_outs = [int(8 * g.integers(2, 300)) for _ in range(int(g.integers(1, 3)))]
+    max_rank, n = int(g.choice([32, 48, 64])), int(g.integers(2, 9))
+    ranks = [int(g.integers(1, 17)) for _ in range(n)]
+    max_ids = n + 6
+    print(f"[chain random {k}] T={T} K={K} d_outs={d_outs} max_rank={max_rank} ranks={ranks}", flush=True)
+    pool = LoraPool(max_ids, max_ids, max_rank, [K] * len(d_outs), d_outs, T)
+    reg = oracle.Registry(max_ids, max_ids, max_rank, [K] * len(d_outs), d_outs, T)
+    gen = torch.Generator().manual_seed(k)
+    for i, r in enumerate(ranks):
+        A = [(torch.randn((K, r), generator=gen) * 0.02).to(torch.bfloat16) for _ in d_outs]
+        B = [(torch.randn((r, d), generator=gen) * 0.02).to(torch.bfloat16) for d in d_outs]
+        al = float(2 * r if i % 2 else 24)
+        pool.load_adapter(i, r, al, [a.cuda() for a in A], [b.cuda() for b in B])
+        reg.load(i, r, al, A, B)
+    X = torch.randn((T, K), generator=gen).to(torch.bfloat16)
+    W = [(torch.randn((d, K), generator=gen) * 0.02).to(torch.bfloat16) for d in d_outs]
+    made = []
+    for c in range(n, max_ids):
+        members = [int(x) for x in g.choice(n, size=min(int(g.integers(1, 4)), n), replace=False)]
+        if 16 * sum((ranks[x] + 15) // 16 for x in members[:-1]) + ranks[members[-1]] > max_rank:
+            continue
+        pool.load_chain(c, members)
+        reg.load_chain(c, members)
+        made.append(c)
+    ids_np = g.choice(np.array([-1] + list(range(n)) + made, np.int32), size=T)
+    ids = torch.as_tensor(ids_np, device="cuda")
+    for m in range(len(d_outs)):
+        out = torch.empty((T, d_outs[m]), dtype=torch.bfloat16, device="cuda")
+        pool.apply(m, X.cuda(), ids, W[m].cuda(), out)
+        torch.cuda.synchronize()
+        assert pool.status() == "OK"
+        mx, rl1, _ = oracle.parity_metrics(out.cpu(), oracle.lora_linear(reg, m, X, ids_np, W[m]))
+        assert mx <= oracle.MAX_REL_TOL and rl1 <= oracle.RELL1_TOL, (m, mx, rl1)
+    pool.close()

@@ -369,3 +369,46 @@ def test_random_groups_equal_single_linears(k):
         mx, rl1, _ = oracle.parity_metrics(outs[j].cpu(), oracle.lora_linear(reg, m, X, ids_np, W[m]))
         assert mx <= oracle.MAX_REL_TOL and rl1 <= oracle.RELL1_TOL, (m, mx, rl1)
     pool.close()
+
+
+@pytest.mark.parametrize("k", range(int(__import__("os").environ.get("HRG_PACKED_RANDOM_CASES", 8))))
+def test_random_packed_groups_equal_row_major(k):
+    """Seeded random decode groups (T <= 64, 1 to 8 linears of any multiple of
+    8, in random order) on fragment-tiled weights: bit for bit the row-major
+    group call, and the oracle's values.  HRG_PACKED_RANDOM_CASES scales the
+    count (300 have passed)."""
+    from heterogeneous_rank_gemm_amd import LoraPool
+    g = np.random.default_rng(680000 + k)
+    T, K, nl = int(g.integers(1, 65)), int(8 * g.integers(1, 600)), int(g.integers(1, 9))
+    d_outs = [int(8 * g.integers(1, 700)) for _ in range(nl)]
+    max_rank = int(g.choice([1, 8, 16, 32, 64]))
+    ranks = [int(g.integers(1, max_rank + 1)) for _ in range(int(g.integers(1, 12)))]
+    n = len(ranks)
+    print(f"[packed random {k}] T={T} K={K} d_outs={d_outs} max_rank={max_rank} ranks={ranks}", flush=True)
+    pool = LoraPool(n, n, max_rank, [K] * nl, d_outs, T)
+    reg = oracle.Registry(n, n, max_rank, [K] * nl, d_outs, T)
+    gen = torch.Generator().manual_seed(k)
+    for i, r in enumerate(ranks):
+        A = [(torch.randn((K, r), generator=gen) * 0.02).to(torch.bfloat16) for _ in d_outs]
+        B = [(torch.randn((r, d), generator=gen) * 0.02).to(torch.bfloat16) for d in d_outs]
+        al = float(2 * r if i % 2 else 24)
+        pool.load_adapter(i, r, al, [a.cuda() for a in A], [b.cuda() for b in B])
+        reg.load(i, r, al, A, B)
+    X = torch.randn((T, K), generator=gen).to(torch.bfloat16)
+    W = [(torch.randn((d, K), generator=gen) * 0.02).to(torch.bfloat16) for d in d_outs]
+    ids_np = g.integers(-1, n, T).astype(np.int32)
+    ids = torch.as_tensor(ids_np, device="cuda")
+    Xd, Wd = X.cuda(), [w.cuda() for w in W]
+    Wp = [pool.pack_weight(w) for w in Wd]
+    group = [int(m) for m in g.permutation(nl)]
+    packed = [torch.empty((T, d_outs[m]), dtype=torch.bfloat16, device="cuda") for m in group]
+    rowmaj = [torch.empty_like(x) for x in packed]
+    pool.apply_group_packed(group, Xd, ids, [Wp[m] for m in group], packed)
+    pool.apply_group(group, Xd, ids, [Wd[m] for m in group], rowmaj)
+    torch.cuda.synchronize()
+    assert pool.status() == "OK"
+    for j, m in enumerate(group):
+        assert torch.equal(packed[j], rowmaj[j]), f"linear {m}: packed differs from row-major"
+        mx, rl1, _ = oracle.parity_metrics(packed[j].cpu(), oracle.lora_linear(reg, m, X, ids_np, W[m]))
+        assert mx <= oracle.MAX_REL_TOL and rl1 <= oracle.RELL1_TOL, (m, mx, rl1)
+    pool.close()
