@@ -205,3 +205,54 @@ def test_paging_errors_match_oracle():
         p.host_cache_create(2)
     assert e.value.status == "INVALID_ARG"
     p.close()
+
+
+@pytest.mark.parametrize("k", range(int(__import__("os").environ.get("HRG_PAGING_RANDOM_CASES", 6))))
+def test_random_paging_sequences_match_oracle(k):
+    """Seeded random pools (slots, ids, host cache, ranks, one or two linears)
+    driven by random sequences: prefetches of random id sets (some over
+    capacity, some naming unregistered ids), pins and unpins,
+    unregistrations.  After every call the statuses and every id's place
+    equal the oracle's; after every successful prefetch the batch meets the
+    oracle's bar.  HRG_PAGING_RANDOM_CASES scales the count (200 have
+    passed)."""
+    g = np.random.default_rng(720000 + k)
+    T = int(g.choice([int(g.integers(1, 65)), int(g.integers(65, 400))]))
+    shapes = [(int(8 * g.integers(2, 80)), int(8 * g.integers(2, 80))) for _ in range(int(g.integers(1, 3)))]
+    max_adapters = int(g.integers(2, 12))
+    max_ids = int(g.integers(max_adapters, 40))
+    max_cpu = int(g.integers(2, max_ids + 1))
+    max_rank, n_reg = int(g.choice([8, 16, 32])), int(g.integers(1, max_cpu + 1))
+    print(f"[paging random {k}] T={T} shapes={shapes} slots={max_adapters} ids={max_ids} cpu={max_cpu}",
+          flush=True)
+    pg = Paged(shapes, max_adapters, max_ids, max_cpu, max_rank, max(T, 8), seed=k)
+    ids_reg = [int(x) for x in g.choice(max_ids, size=n_reg, replace=False)]
+    for i in ids_reg:
+        r = int(g.integers(1, max_rank + 1))
+        pg.register(i, r, 2.0 * r if i % 2 else 24.0)
+    pg.check_where()
+    for step in range(12):
+        op = g.random()
+        if op < 0.1 and ids_reg:
+            pg.call("pin", int(g.choice(ids_reg)), bool(g.random() < 0.6))
+            pg.check_where()
+            continue
+        if op < 0.15 and ids_reg:
+            i = int(g.choice(ids_reg))
+            if pg.call("host_unregister", i) == "OK":
+                ids_reg.remove(i)
+            pg.check_where()
+            continue
+        pool_ids = ids_reg + [int(x) for x in g.integers(0, max_ids, size=1)]
+        n_req = int(g.integers(1, min(len(pool_ids), max_adapters + 2) + 1))
+        req = [int(x) for x in g.choice(pool_ids, size=n_req, replace=False)]
+        ids_np = g.choice(req + [-1], size=T).astype(np.int32)
+        st = pg.call("prefetch", ids_np.tolist())
+        pg.check_where()
+        if st != "OK":
+            continue
+        _, res = pg.batch(T, ids_np, seed=1000 * k + step)
+        torch.cuda.synchronize()
+        assert pg.pool.status() == "OK"
+        pg.check_batch(ids_np, res, f"step {step}")
+    pg.pool.close()
