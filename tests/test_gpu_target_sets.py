@@ -103,3 +103,53 @@ def test_target_set_argument_errors():
     assert e.value.status == "INVALID_ARG"
     pool.load_adapter(0, RANKS[1], 32.0, A, B)
     pool.close()
+
+
+@pytest.mark.parametrize("k", range(int(__import__("os").environ.get("HRG_TARGET_RANDOM_CASES", 8))))
+def test_random_target_sets(k):
+    """Seeded random pools of 2 to 4 linears of one d_in (direct-mapped), each
+    adapter targeting a random non-empty subset, both paths: the oracle's
+    values, and rows whose adapter skips a linear equal to lora_base_apply
+    there bit for bit.  HRG_TARGET_RANDOM_CASES scales the count (200 have
+    passed)."""
+    from heterogeneous_rank_gemm_amd import LoraPool
+    g = np.random.default_rng(730000 + k)
+    T = int(g.choice([int(g.integers(1, 65)), int(g.integers(65, 600))]))
+    K, nl = int(8 * g.integers(2, 200)), int(g.integers(2, 5))
+    d_outs = [int(8 * g.integers(2, 300)) for _ in range(nl)]
+    max_rank, n = int(g.choice([8, 16, 32])), int(g.integers(2, 10))
+    ranks = [int(g.integers(1, max_rank + 1)) for _ in range(n)]
+    targets = []
+    for _ in range(n):
+        t = [m for m in range(nl) if g.random() < 0.6]
+        targets.append(t or [int(g.integers(0, nl))])
+    print(f"[targets random {k}] T={T} K={K} d_outs={d_outs} ranks={ranks} targets={targets}", flush=True)
+    pool = LoraPool(n, n, max_rank, [K] * nl, d_outs, T)
+    reg = oracle.Registry(n, n, max_rank, [K] * nl, d_outs, T)
+    gen = torch.Generator().manual_seed(k)
+    for i, r in enumerate(ranks):
+        A = [(torch.randn((K, r), generator=gen) * 0.02).to(torch.bfloat16) if m in targets[i] else None
+             for m in range(nl)]
+        B = [(torch.randn((r, d_outs[m]), generator=gen) * 0.02).to(torch.bfloat16) if m in targets[i] else None
+             for m in range(nl)]
+        pool.load_adapter(i, r, 2.0 * r, [a.cuda() if a is not None else None for a in A],
+                          [b.cuda() if b is not None else None for b in B])
+        reg.load(i, r, 2.0 * r, A, B)
+    ids_np = g.integers(-1, n, T).astype(np.int32)
+    ids = torch.as_tensor(ids_np, device="cuda")
+    X = torch.randn((T, K), generator=gen).to(torch.bfloat16)
+    Xd = X.cuda()
+    for m in range(nl):
+        W = (torch.randn((d_outs[m], K), generator=gen) * 0.02).to(torch.bfloat16)
+        out = torch.empty((T, d_outs[m]), dtype=torch.bfloat16, device="cuda")
+        base = torch.empty_like(out)
+        pool.apply(m, Xd, ids, W.cuda(), out)
+        pool.base_apply(m, Xd, W.cuda(), base)
+        torch.cuda.synchronize()
+        assert pool.status() == "OK"
+        mx, rl1, _ = oracle.parity_metrics(out.cpu(), oracle.lora_linear(reg, m, X, ids_np, W))
+        assert mx <= oracle.MAX_REL_TOL and rl1 <= oracle.RELL1_TOL, (m, mx, rl1)
+        skip = np.array([i < 0 or m not in targets[i] for i in ids_np])
+        keep = torch.as_tensor(skip, device="cuda")
+        assert torch.equal(out[keep], base[keep]), f"linear {m}: skipped rows differ from base-only"
+    pool.close()
