@@ -195,6 +195,31 @@ def test_ragged_parity(T, d_in, d_out, ranks, max_rank, id_lo):
     c.close()
 
 
+# the largest batches a pool accepts: 65536 tokens, and X of just under
+# 2 GiB (the batched path's 32-bit X offsets)
+LARGEST = [(65536, 1024, 520, (16, 8, 3), 16, 40), (65536, 16376, 64, (64, 17), 64, 12),
+           (32768, 4096, 1032, (8, 16, 32, 64), 64, 2000)]
+
+
+@pytest.mark.parametrize("T,d_in,d_out,ranks,max_rank,n_ids", LARGEST)
+def test_largest_batches_parity(T, d_in, d_out, ranks, max_rank, n_ids):
+    _say(f"[largest] T={T} d_in={d_in} d_out={d_out} ranks={ranks} ids={n_ids}")
+    assert T * d_in * 2 < 2 ** 31
+    g = np.random.default_rng(T + d_in)
+    hot = g.choice(n_ids, size=min(5, n_ids), replace=False)
+    ids = np.where(g.random(T) < 0.8, g.choice(hot, size=T), g.integers(-1, n_ids, size=T)).astype(np.int32)
+    wl = wk.small_workload(T, d_in, d_out, n_ids, max_rank, ranks, key=930000 + d_in)
+    c = _case(wl, ids=ids, adapters=list(range(n_ids)))
+    out = c.apply(0)
+    torch.cuda.synchronize()
+    assert c.pool.status() == "OK"
+    _parity(out, c.oracle(0), f"largest T={T}")
+    base = c.base_apply(0)
+    m = torch.as_tensor(ids < 0, device="cuda")
+    assert torch.equal(out[m], base[m])
+    c.close()
+
+
 # a pool with more ids than slots reaches pages through the slot table (slot !=
 # id); one with as many slots as ids keeps adapter id in slot id
 INDIRECT = [
