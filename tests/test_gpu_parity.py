@@ -220,6 +220,30 @@ def test_largest_batches_parity(T, d_in, d_out, ranks, max_rank, n_ids):
     c.close()
 
 
+# the largest dims a pool accepts (d_in, d_out up to 65536 with a weight of
+# at most 2^31 - 1 bytes, the decode kernels' 32-bit offsets), both paths
+LARGEST_DIMS = [(64, 65536, 16376, (16, 5), 16, 6), (17, 8, 65536, (64, 9), 64, 4),
+                (64, 16376, 65528, (32, 1), 32, 5), (1, 65536, 8, (8,), 8, 2),
+                (200, 65536, 4096, (16, 2), 16, 6), (300, 4096, 65536, (16,), 16, 3)]
+
+
+@pytest.mark.parametrize("T,d_in,d_out,ranks,max_rank,n_ids", LARGEST_DIMS)
+def test_largest_dims_parity(T, d_in, d_out, ranks, max_rank, n_ids):
+    _say(f"[largest dims] T={T} d_in={d_in} d_out={d_out} ranks={ranks}")
+    assert d_in * d_out * 2 <= 2 ** 31 - 1
+    ids = np.random.default_rng(d_in + d_out).integers(-1, n_ids, size=T).astype(np.int32)
+    wl = wk.small_workload(T, d_in, d_out, n_ids, max_rank, ranks, key=940000 + T)
+    c = _case(wl, ids=ids, adapters=list(range(n_ids)))
+    out = c.apply(0)
+    torch.cuda.synchronize()
+    assert c.pool.status() == "OK"
+    _parity(out, c.oracle(0), f"largest dims {d_in}x{d_out}")
+    base = c.base_apply(0)
+    m = torch.as_tensor(ids < 0, device="cuda")
+    assert torch.equal(out[m], base[m])
+    c.close()
+
+
 # a pool with more ids than slots reaches pages through the slot table (slot !=
 # id); one with as many slots as ids keeps adapter id in slot id
 INDIRECT = [
