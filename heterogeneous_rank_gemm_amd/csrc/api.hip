@@ -529,6 +529,7 @@ static lora_status_t batched_shrink(lora_pool_s* P, int nl, const int32_t* modul
   const int grid = std::min(max_items, 1024);
   hrg::ShrinkArgs sa{};
   sa.X = X;
+  sa.T = T;
   sa.K = K;
   sa.perm = pl->tab.perm;
   sa.tile_info = pl->tab.tile_info;

@@ -89,8 +89,8 @@ struct PlanArgs {
 constexpr int kMaxShrinkLinears = 4;
 
 struct ShrinkArgs {
-  const uint16_t* X;      // [T][K]
-  int32_t K;
+  const uint16_t* X;      // [T][K], T * K * 2 < 2^31
+  int32_t T, K;
   const int32_t* perm;
   const int4* tile_info;
   const int32_t* counts;

@@ -17,6 +17,7 @@
 // by s = alpha/r and forms V = s U as bf16 hi + lo parts (V ~= hi + lo to
 // about 2^-16) for the expand.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -26,11 +27,26 @@ namespace hrg {
 constexpr int kShrinkThreads = 256;
 constexpr int kRedLd = 65;  // padded row of the cross-wave reduction buffer
 
-__device__ __forceinline__ uint4 ld16(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ bf16x8 keep_bf(bool keep, uint4 v) {
   const uint32_t m = keep ? 0xffffffffu : 0u;
   return __builtin_bit_cast(bf16x8, make_uint4(v.x & m, v.y & m, v.z & m, v.w & m));
 }
+
+// Calls f(integral_constant<int, S>) for S = 0 .. N-1, in order.
+template <int N, int S = 0, class F>
+__device__ __forceinline__ void for_each_set(F&& f) {
+  if constexpr (S < N) {
+    f(std::integral_constant<int, S>{});
+    for_each_set<N, S + 1>(f);
+  }
+}
+
+// Register sets of the sub-chunk ring: two (the next sub-chunk in flight
+// during the current one's MFMAs).  Three or four sets, where the registers
+// allow them, measured no faster.
+constexpr int kShrinkSets = 2;
+
+constexpr uint32_t kShrinkOob = 0x80000000u;  // buffer offset past every operand (< 2 GiB)
 
 // The tokens of a tile's rows this lane gathers: row 16 mb + (lane & 15).
 __device__ __forceinline__ void tile_tokens(const ShrinkArgs& a, int4 ti, int (&tok)[4]) {
@@ -48,7 +64,7 @@ __device__ __forceinline__ void tile_tokens(const ShrinkArgs& a, int4 ti, int (&
 // item), so the A and X loads go out together.  The next item's tile entry
 // (index `next`) is requested into *tn with them and its tokens into tokn
 // once it lands, so neither lookup costs a round of its own.
-template <int NQ, int NL>
+template <int NQ, int NL, int NS>
 __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64 * kRedLd], int4 ti, int split,
                                             int next, const int (&tok)[4], int4* tn, int (&tokn)[4]) {
   constexpr int NB = NQ * NL;  // rank blocks of the item: linear j / NQ, block j % NQ
@@ -65,35 +81,44 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
   // step s is 1 KB at frag_tile(nb, s), this lane's 16 bytes at 16 l
   const int k32 = (K + 31) / 32;
   const int rp = a.u_ld;  // rows of the page in fragment tiles (the pool's rank rounded up to 16)
-  const uint16_t* Al[NL];
+  // the A pages and X through buffer resources: a sub-chunk past the item's
+  // range is requested with an offset past the operand (zeros, no memory
+  // traffic), so every load is still issued and the waits stay exact
+  __amdgpu_buffer_rsrc_t ra[NL];
+  const int a_bytes = (int)(frag_elems(a.u_ld, K) * 2);
 #pragma unroll
-  for (int m = 0; m < NL; ++m) Al[m] = Ap + a.a_off[m] + (size_t)l * 8;
+  for (int m = 0; m < NL; ++m)
+    ra[m] = __builtin_amdgcn_make_buffer_rsrc((void*)(Ap + a.a_off[m]), (short)0, a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)a.X, (short)0, a.T * K * 2, 0x00020000);
   bool qv[NQ];
 #pragma unroll
   for (int nb = 0; nb < NQ; ++nb) qv[nb] = 16 * nb + (l & 15) < rank;
   const int koff = 8 * (l >> 4);
   // 256-deep sub-chunks: wave w takes the 32-deep steps 32 w + 128 s
-  // (s = 0, 1) of each, through two register sets: the next sub-chunk's A
-  // and X loads are in flight while the current one's MFMAs run.  Every load
-  // is issued whatever the item's rank and rows (a rank block past the
-  // adapter's rank re-reads block 0, a row past the tile re-reads row 0, a
-  // sub-chunk past the item's range re-reads its last one: L2 hits, never
-  // applied), so the compiler counts each wait exactly instead of waiting
-  // for both sets before the first MFMA.
+  // (s = 0, 1) of each, through a ring of NS register sets: the next
+  // sub-chunks' A and X loads are in flight while the current one's MFMAs
+  // run.  Every load is issued whatever the item's rank and rows (a rank
+  // block past the adapter's rank re-reads block 0 and a row past the tile
+  // re-reads row 0: L2 hits, never applied; a sub-chunk past the item's
+  // range goes out of range: zeros, no memory traffic), so the compiler
+  // counts each wait exactly instead of waiting for every set before the
+  // first MFMA.  (Out-of-range requests in place of re-reading the last
+  // sub-chunk: Llama-3-8B layer step 1844 -> 1837 us.)
   constexpr int kSub = 256;
   const int nsub = (k1 - k0 + kSub - 1) / kSub;
   const int klast = k0 + (nsub - 1) * kSub;
-  const uint16_t* xrow[4];
+  uint32_t xrow[4];
   bool rv[4];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     const int p = 16 * mb + (l & 15);
     rv[mb] = p < rows;
-    xrow[mb] = a.X + (size_t)tok[mb] * K;
+    xrow[mb] = (uint32_t)tok[mb] * (uint32_t)K * 2u;
   }
-  uint4 av[2][2][NB], xv[2][2][4];
+  uint4 av[NS][2][NB], xv[NS][2][4];
   auto load = [&](auto bc, int kb) __attribute__((always_inline)) {
     constexpr int b = decltype(bc)::value;
+    const uint32_t past = kb > klast ? kShrinkOob : 0u;  // wave-uniform
     kb = min(kb, klast);
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -101,14 +126,16 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const int nb = j % NQ;
-        av[b][st][j] = ld16(Al[j / NQ] + frag_tile(nb < nq ? nb : 0, step, rp, K) * 512);
+        const uint32_t off = (uint32_t)((frag_tile(nb < nq ? nb : 0, step, rp, K) * 512 + (size_t)l * 8) * 2);
+        av[b][st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra[j / NQ], off | past, 0, 0));
       }
     }
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const int kc = min(kb + 128 * st + 32 * w + koff, K - 8);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) xv[b][st][mb] = ld16(xrow[mb] + kc);
+      for (int mb = 0; mb < 4; ++mb)
+        xv[b][st][mb] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, (xrow[mb] + (uint32_t)kc * 2u) | past, 0, 0));
     }
   };
 
@@ -135,19 +162,21 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
       }
     }
   };
-  const auto B0 = std::integral_constant<int, 0>{};
-  const auto B1 = std::integral_constant<int, 1>{};
-  load(B0, k0);
+  for_each_set<NS - 1>([&](auto bc) __attribute__((always_inline)) {
+    load(bc, k0 + decltype(bc)::value * kSub);
+  });
   // the next item's tile entry, then its tokens (they land during the MFMAs)
   *tn = a.tile_info[next];
   tile_tokens(a, *tn, tokn);
-  for (int i = 0;; i += 2) {
-    load(B1, k0 + (i + 1) * kSub);
-    mm(B0, k0 + i * kSub);
-    if (i + 1 >= nsub) break;
-    load(B0, k0 + (i + 2) * kSub);
-    mm(B1, k0 + (i + 1) * kSub);
-    if (i + 2 >= nsub) break;
+  bool more = true;
+  for (int i = 0; more; i += NS) {
+    for_each_set<NS>([&](auto pc) __attribute__((always_inline)) {
+      constexpr int P = decltype(pc)::value;
+      if (!more) return;
+      load(std::integral_constant<int, (P + NS - 1) % NS>{}, k0 + (i + P + NS - 1) * kSub);
+      mm(pc, k0 + (i + P) * kSub);
+      more = i + P + 1 < nsub;
+    });
   }
 
   // cross-wave reduction in fixed wave order (column 16 j + q of the
@@ -201,8 +230,8 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkArgs a) {
     int4 tn;
     int tokn[4];
     __syncthreads();  // the previous item is done with red
-    shrink_item<NQ, NL>(a, red, ti, item % a.nsplit, min(item + (int)gridDim.x, nitems - 1) / a.nsplit, tok, &tn,
-                    tokn);
+    const int next = min(item + (int)gridDim.x, nitems - 1) / a.nsplit;
+    shrink_item<NQ, NL, kShrinkSets>(a, red, ti, item % a.nsplit, next, tok, &tn, tokn);
     ti = tn;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) tok[mb] = tokn[mb];
