@@ -127,7 +127,8 @@ __device__ __forceinline__ void shrink_item(const ShrinkArgs& a, float (*red)[64
       for (int j = 0; j < NB; ++j) {
         const int nb = j % NQ;
         const uint32_t off = (uint32_t)((frag_tile(nb < nq ? nb : 0, step, rp, K) * 512 + (size_t)l * 8) * 2);
-        av[b][st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra[j / NQ], off | past, 0, 0));
+        const uint32_t skip = nb < nq ? past : kShrinkOob;  // a block past the adapter's rank: nothing read
+        av[b][st][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra[j / NQ], off | skip, 0, 0));
       }
     }
 #pragma unroll
