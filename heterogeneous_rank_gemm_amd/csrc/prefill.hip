@@ -301,8 +301,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
     // of loads (lane i: the block's i-th segment), so an item's slot, rows
     // and rank are register reads; the FM walkers advance in lockstep through
     // a ring of D items whose B fragments are requested D-1 items ahead.
-    // Every ring load is issued (an item past a walker's last reads a valid
-    // page and is not applied), so the loads' completion is counted exactly.
+    // Every ring load is issued (an item past a walker's last, and a chunk
+    // past an adapter's rank, go out of range: nothing read, never applied),
+    // so the loads' completion is counted exactly.
     constexpr int QB = QC < 2 ? QC : 2;  // rank chunks per work item
     constexpr int kBudget = FN >= 4 ? 96 : 198;  // 256-column tiles keep 256 accumulators live
     // ring of D items in flight per walker: deeper where the tile leaves
@@ -377,19 +378,27 @@ __global__ __launch_bounds__(256) void prefill_kernel(GemmArgs a) {
       auto load_b = [&](bf16x8 (&bb)[QB][FN], int j, int k) __attribute__((always_inline)) {
         const int il = item_lane(j, k);
         const uint16_t* bt = dummy_page;
-        int c = 0;
+        int c = 0, nq = 0;
         if (il >= 0) {
           bt = a.pages + (size_t)__builtin_amdgcn_readlane(s_slot[j], il) * a.slot_stride + a.b_off;
           c = (k - __builtin_amdgcn_readlane(s_it0[j], il)) * QB;
+          nq = __builtin_amdgcn_readlane(s_nqc[j], il);
         }
-        // a chunk past the adapter's rank reads chunk 0 again (not applied)
+        // the page through a buffer resource: a chunk past the adapter's
+        // rank, or any chunk of an item past the walker's last, is requested
+        // out of range (zeros, nothing read; never applied)
+        const __amdgpu_buffer_rsrc_t rbt =
+            __builtin_amdgcn_make_buffer_rsrc((void*)bt, (short)0, a.u_ld * N * 2, 0x00020000);
 #pragma unroll
         for (int qc = 0; qc < QB; ++qc) {
-          const int cq = il >= 0 && c + qc < __builtin_amdgcn_readlane(s_nqc[j], max(il, 0)) ? c + qc : 0;
+          const bool real = c + qc < nq;
+          const uint32_t cq = real ? (uint32_t)(c + qc) : 0u;
 #pragma unroll
           for (int i = 0; i < FN; ++i) {
             const int n = min(n0 + wn * (BN / 2) + 32 * i + (l & 31), N - 1);
-            bb[qc][i] = __builtin_bit_cast(bf16x8, ld16(bt + ((size_t)cq * N + n) * 16 + 8 * (l >> 5)));
+            const uint32_t off = ((cq * (uint32_t)N + (uint32_t)n) * 16u + 8u * (uint32_t)(l >> 5)) * 2u;
+            bb[qc][i] = __builtin_bit_cast(
+                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rbt, off | (real ? 0u : kOob), 0, 0));
           }
         }
       };
